@@ -1,0 +1,304 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Tolerances (fixed by the workload definition, not tuned):
+  * int4 unpack, gathers, K/V-share identity: bit-exact;
+  * logits: max |GPU - oracle| <= 2e-2 (bf16) / 3e-2 (W4A16) of max |oracle logit|;
+  * greedy token: equal to the oracle's wherever the oracle's top-2 gap exceeds
+    1e-2, and equal on >= 99% of all steps (teacher-forced comparison: the
+    oracle replays the GPU's tokens, so one flip cannot cascade).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": 2e-2, "w4a16": 3e-2}
+
+
+@pytest.fixture(scope="module")
+def torch_dev():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    arch = torch.cuda.get_device_properties(0).gcnArchName
+    assert arch.startswith("gfx950"), arch
+    return torch, torch.device("cuda:0")
+
+
+def _engine(cfg, quant, w, max_batch, max_ctx, max_rows):
+    from w4a16_weight_streaming_amd import Engine
+    return Engine(cfg, quant, w, max_batch=max_batch, max_ctx=max_ctx, max_rows=max_rows)
+
+
+class Stats:
+    def __init__(self, quant):
+        self.tol, self.n, self.agree, self.worst = TOL[quant], 0, 0, 0.0
+
+    def add(self, got_logits, got_tok, ref_logits, where=""):
+        got = np.asarray(got_logits, np.float64)
+        err = float(np.max(np.abs(got - ref_logits)) / np.max(np.abs(ref_logits)))
+        self.worst = max(self.worst, err)
+        assert err <= self.tol, f"{where}: logit error {err:.3e} > {self.tol}"
+        ref_tok = int(np.argmax(ref_logits))
+        top2 = np.sort(ref_logits)[-2:]
+        if top2[1] - top2[0] > 1e-2:
+            assert got_tok == ref_tok, f"{where}: token {got_tok} != oracle {ref_tok} (gap {top2[1]-top2[0]:.3e})"
+        self.n += 1
+        self.agree += int(got_tok == ref_tok)
+
+    def finish(self):
+        assert self.agree >= 0.99 * self.n, f"greedy agreement {self.agree}/{self.n}"
+        print(f"steps {self.n} agree {self.agree} worst rel err {self.worst:.3e}", flush=True)
+
+
+def run_greedy(torch, eng, orc, prompts, steps, quant, logits=True):
+    """Prefill each sequence, then `steps` batched greedy decode steps, comparing
+    every step's logits with the teacher-forced oracle."""
+    dev = eng.device
+    V = eng.cfg.vocab_size
+    B = len(prompts)
+    st = Stats(quant)
+    am = torch.zeros(B, dtype=torch.int32, device=dev)
+    lg = torch.zeros(B, V, dtype=torch.float32, device=dev)
+    nxt = []
+    for b, p in enumerate(prompts):
+        a1 = torch.zeros(1, dtype=torch.int32, device=dev)
+        l1 = torch.zeros(1, V, dtype=torch.float32, device=dev)
+        eng.prefill(b, torch.from_numpy(np.asarray(p, np.int32)).to(dev), 0, a1, l1)
+        eng.check()
+        _, ref = orc.prefill(b, p)
+        st.add(l1.cpu().numpy()[0], int(a1.item()), ref, f"prefill seq {b}")
+        nxt.append(int(a1.item()))
+    lens = [len(p) for p in prompts]
+    for i in range(steps):
+        tok = torch.tensor(nxt, dtype=torch.int32, device=dev)
+        pos = torch.tensor(lens, dtype=torch.int32, device=dev)
+        eng.decode_step(tok, pos, am, lg)
+        eng.check()
+        got_l, got_t = lg.cpu().numpy(), am.cpu().numpy()
+        for b in range(B):
+            _, ref, _ = orc.step(b, nxt[b], lens[b])
+            st.add(got_l[b], int(got_t[b]), ref, f"step {i} seq {b}")
+        nxt = [int(t) for t in got_t]
+        lens = [x + 1 for x in lens]
+    st.finish()
+    return st
+
+
+# ---------------------------------------------------------------- matvec
+def _as_dev(torch, a, dev):
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to(dev)
+    return torch.from_numpy(a).to(dev)
+
+
+@pytest.mark.parametrize("quant", ["bf16", "w4a16"])
+@pytest.mark.parametrize("N,K", [(64, 32), (40, 128), (96, 256), (256, 512), (300, 1536),
+                                 (128, 2048), (64, 4096), (32, 6144), (24, 12288)])
+def test_matvec_one_hot_is_exact(torch_dev, quant, N, K):
+    """x = e_k returns column k of the decoded matrix bit for bit (int4 unpack
+    and scale exact; nibble order natural; K slices summed correctly)."""
+    torch, dev = torch_dev
+    from w4a16_weight_streaming_amd import matvec
+    seed = 100 + K
+    if quant == "bf16":
+        w = synth.normal_bf16((N, K), seed, "w")
+        scale = None
+    else:
+        w = synth.bits32((N, K // 8), seed, "w")
+        scale = synth.uniform_bf16((N, K // 32), seed, "s", 0.002, 0.02)
+    ks = sorted(set([0, 1, 7, 8, 31, 32, 33, K // 2, K - 1] + list(range(3, K, max(1, K // 13)))))
+    x = np.zeros((len(ks), K), np.float32)
+    for r, k in enumerate(ks):
+        x[r, k] = 1.0
+    y = torch.zeros(len(ks), N, dtype=torch.float32, device=dev)
+    matvec(quant, _as_dev(torch, w, dev), None if scale is None else _as_dev(torch, scale, dev),
+           torch.from_numpy(x).to(dev), y)
+    got = y.cpu().numpy()
+    for r, k in enumerate(ks):
+        e = np.zeros(K)
+        e[k] = 1.0
+        ref = oracle.linear(quant, w, scale, N, K, e)          # exact decoded column
+        assert np.array_equal(got[r].astype(np.float64), ref), (k, np.max(np.abs(got[r] - ref)))
+
+
+@pytest.mark.parametrize("quant", ["bf16", "w4a16"])
+@pytest.mark.parametrize("N,K,rows", [(1536, 1536, 1), (2560, 1536, 3), (1536, 4096, 1),
+                                      (1536, 12288, 2), (160, 256, 5), (32, 32, 1)])
+def test_matvec_random_matches_oracle(torch_dev, quant, N, K, rows):
+    """Random x: |y - y_oracle| <= 1e-4 * sum_k |w_nk x_k| (x carried as a bf16
+    hi/lo pair, ~2^-17 relative, plus fp32 accumulation)."""
+    torch, dev = torch_dev
+    from w4a16_weight_streaming_amd import matvec
+    rng = np.random.default_rng(K + N)
+    if quant == "bf16":
+        w = synth.normal_bf16((N, K), 7, "w")
+        scale = None
+        wd = synth.bf16_to_f32(w).astype(np.float64)
+    else:
+        w = synth.bits32((N, K // 8), 7, "w")
+        scale = synth.uniform_bf16((N, K // 32), 7, "s", 0.002, 0.02)
+        wd = np.stack([[oracle.decode_weight("w4a16", w, scale, N, K, n, k) for k in range(K)]
+                       for n in range(min(N, 4))])
+    x = rng.normal(size=(rows, K)).astype(np.float32)
+    y = torch.zeros(rows, N, dtype=torch.float32, device=dev)
+    matvec(quant, _as_dev(torch, w, dev), None if scale is None else _as_dev(torch, scale, dev),
+           torch.from_numpy(x).to(dev), y)
+    got = y.cpu().numpy()
+    for r in range(rows):
+        ref = oracle.linear(quant, w, scale, N, K, x[r].astype(np.float64))
+        nb = wd.shape[0]
+        bound = 1e-4 * (np.abs(wd) @ np.abs(x[r].astype(np.float64)))
+        assert np.all(np.abs(got[r, :nb] - ref[:nb]) <= bound + 1e-30)
+        scale_all = np.max(np.abs(ref))
+        assert np.max(np.abs(got[r] - ref)) <= 1e-4 * scale_all * np.sqrt(K)
+
+
+# ---------------------------------------------------------------- whole step, toy
+@pytest.mark.parametrize("name", ["toy", "toy10"])
+@pytest.mark.parametrize("quant", ["bf16", "w4a16"])
+def test_toy_greedy_parity(torch_dev, name, quant):
+    """8-token prompt, 32 greedy steps (crosses the 16-wide window)."""
+    torch, dev = torch_dev
+    cfg = synth.get_config(name)
+    w = synth.generate(cfg, quant, seed=0)
+    eng = _engine(cfg, quant, w, 1, 48, 8)
+    orc = oracle.Oracle(cfg, quant, w, 1, 48)
+    run_greedy(torch, eng, orc, [synth.tokens(8, 1, cfg["vocab_size"])], 32, quant)
+
+
+def test_toy_batched_ragged(torch_dev):
+    """Four sequences at different positions in one batched step; a long
+    context (max_ctx 2048: 64 attention chunks of 32 keys) with prefill split
+    into several passes (max_rows 16)."""
+    torch, dev = torch_dev
+    cfg = synth.get_config("toy10")
+    w = synth.generate(cfg, "w4a16", seed=3)
+    eng = _engine(cfg, "w4a16", w, 4, 2048, 16)
+    orc = oracle.Oracle(cfg, "w4a16", w, 4, 2048)
+    prompts = [synth.tokens(n, 20 + n, cfg["vocab_size"]) for n in (8, 37, 1, 70)]
+    run_greedy(torch, eng, orc, prompts, 12, "w4a16")
+
+
+def test_wide_heads_long_window(torch_dev):
+    """Head dims 256/512 with 8 query heads (the E2B attention shapes) at a
+    small width, window 32, 100 positions."""
+    torch, dev = torch_dev
+    cfg = dict(synth.get_config("toy10"), name="wide", num_attention_heads=8, head_dim=256,
+               global_head_dim=512, sliding_window=32)
+    w = synth.generate(cfg, "bf16", seed=4)
+    eng = _engine(cfg, "bf16", w, 2, 128, 64)
+    orc = oracle.Oracle(cfg, "bf16", w, 2, 128)
+    prompts = [synth.tokens(90, 5, cfg["vocab_size"]), synth.tokens(40, 6, cfg["vocab_size"])]
+    run_greedy(torch, eng, orc, prompts, 8, "bf16")
+
+
+def test_prefill_equals_decode_loop_bitwise(torch_dev):
+    """A prefill pass computes each row exactly as a decode step does."""
+    torch, dev = torch_dev
+    cfg = synth.get_config("toy10")
+    w = synth.generate(cfg, "w4a16", seed=5)
+    V = cfg["vocab_size"]
+    p = synth.tokens(20, 9, V)
+    eng = _engine(cfg, "w4a16", w, 2, 32, 32)
+    a = torch.zeros(1, dtype=torch.int32, device=dev)
+    l_pre = torch.zeros(1, V, dtype=torch.float32, device=dev)
+    eng.prefill(0, torch.from_numpy(p).to(dev), 0, a, l_pre)
+    l_dec = torch.zeros(1, V, dtype=torch.float32, device=dev)
+    for i, t in enumerate(p):   # same tokens, one by one, into cache row 1
+        eng.prefill(1, torch.tensor([t], dtype=torch.int32, device=dev), i, a, l_dec)
+    eng.check()
+    assert torch.equal(l_pre, l_dec)
+    for l in range(cfg["num_hidden_layers"]):
+        hd = synth.layer_head_dim(cfg, l)
+        for which in (0, 1):
+            kv = eng.kv_tensor(l, which, hd)
+            assert torch.equal(kv[0, :20], kv[1, :20])
+
+
+def test_kv_sharing_and_cache_contents(torch_dev):
+    """Shared layers read their source layer's region (same address, hence
+    bit-identical K/V); the cached K/V match the oracle's to bf16 rounding."""
+    torch, dev = torch_dev
+    cfg = synth.get_config("toy10")
+    w = synth.generate(cfg, "bf16", seed=6)
+    eng = _engine(cfg, "bf16", w, 1, 32, 16)
+    orc = oracle.Oracle(cfg, "bf16", w, 1, 32)
+    p = synth.tokens(12, 2, cfg["vocab_size"])
+    a = torch.zeros(1, dtype=torch.int32, device=dev)
+    eng.prefill(0, torch.from_numpy(p).to(dev), 0, a)
+    eng.check()
+    orc.prefill(0, p)
+    smap = eng.model.kv_share_map()
+    for l in range(cfg["num_hidden_layers"]):
+        for which in (0, 1):
+            assert eng.kv_view(l, which) == eng.kv_view(smap[l], which)
+            assert orc.kv_source(l) == smap[l]
+    for l in sorted(set(smap)):
+        hd = synth.layer_head_dim(cfg, l)
+        for which in (0, 1):
+            got = synth.bf16_to_f32(eng.kv_tensor(l, which, hd)[0, :12].cpu().numpy().view(np.uint16))
+            for pos in range(12):
+                ref = orc.kv_row(l, which, 0, pos, hd)
+                assert np.max(np.abs(got[pos] - ref)) <= 2 ** -8 * np.max(np.abs(ref)) + 1e-6
+
+
+def test_deterministic_replay(torch_dev):
+    torch, dev = torch_dev
+    cfg = synth.get_config("toy")
+    w = synth.generate(cfg, "w4a16", seed=7)
+    V = cfg["vocab_size"]
+    outs = []
+    for _ in range(2):
+        eng = _engine(cfg, "w4a16", w, 2, 32, 8)
+        a = torch.zeros(2, dtype=torch.int32, device=dev)
+        lg = torch.zeros(2, V, dtype=torch.float32, device=dev)
+        for b in range(2):
+            eng.prefill(b, torch.from_numpy(synth.tokens(8, 30 + b, V)).to(dev), 0, a[b:b + 1])
+        for i in range(6):
+            eng.decode_step(a.clone(), torch.full((2,), 8 + i, dtype=torch.int32, device=dev), a, lg)
+        eng.check()
+        outs.append(lg.clone())
+    assert torch.equal(outs[0], outs[1])
+
+
+def test_device_error_word(torch_dev):
+    """Out-of-range tokens and positions are flagged, not read or written."""
+    torch, dev = torch_dev
+    from w4a16_weight_streaming_amd import E2BError
+    from w4a16_weight_streaming_amd.binding import E2B_EDEVICE
+    cfg = synth.get_config("toy")
+    w = synth.generate(cfg, "bf16", seed=8)
+    eng = _engine(cfg, "bf16", w, 1, 16, 8)
+    a = torch.zeros(1, dtype=torch.int32, device=dev)
+    ok_tok = torch.tensor([5], dtype=torch.int32, device=dev)
+    eng.decode_step(torch.tensor([cfg["vocab_size"] + 3], dtype=torch.int32, device=dev),
+                    torch.tensor([0], dtype=torch.int32, device=dev), a)
+    with pytest.raises(E2BError) as e:
+        eng.check()
+    assert e.value.code == E2B_EDEVICE and "vocabulary" in str(e.value)
+    eng.decode_step(ok_tok, torch.tensor([16], dtype=torch.int32, device=dev), a)
+    with pytest.raises(E2BError) as e:
+        eng.check()
+    assert "position" in str(e.value)
+    eng.decode_step(ok_tok, torch.tensor([0], dtype=torch.int32, device=dev), a)
+    eng.check()   # cleared, and a valid step passes
+
+
+# ---------------------------------------------------------------- E2B shape
+@pytest.fixture(scope="module", params=["bf16", "w4a16"])
+def e2b_model(request):
+    cfg = synth.get_config("e2b")
+    return cfg, request.param, synth.generate(cfg, request.param, seed=0)
+
+
+def test_e2b_greedy_parity(torch_dev, e2b_model):
+    """Full E2B shape: 16-token prompt, 16 greedy decode steps, every step's
+    262,144 logits against the oracle."""
+    torch, dev = torch_dev
+    cfg, quant, w = e2b_model
+    eng = _engine(cfg, quant, w, 1, 64, 16)
+    orc = oracle.Oracle(cfg, quant, w, 1, 64)
+    run_greedy(torch, eng, orc, [synth.tokens(16, 1, cfg["vocab_size"])], 16, quant)

@@ -1,0 +1,118 @@
+// Internal declarations shared by the host side (host.cpp) and the HIP
+// kernels (kernels.hip) of libe2b.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace e2b {
+
+constexpr int kMaxChunks = 64;   // attention key chunks per (row, layer)
+constexpr int kMaxSplitK = 8;    // K slices of one matrix-vector product
+constexpr int kGemvThreads = 256;
+constexpr int kLmBlocks = 1024;  // blocks of the lm_head pass (argmax candidates)
+
+// Matrix kinds; each gets its own kernel symbol so profiles tell them apart.
+enum : int {
+  kTagOther = 0, kTagQkv, kTagO, kTagGateUp, kTagDown, kTagPleGate, kTagPleProj, kTagPleModel,
+  kTagLmHead
+};
+
+// Device error word bits (first 16 bytes of the workspace).
+enum : int { kErrToken = 1, kErrPos = 2 };
+
+// One linear layer resident in the weight arena.  bf16: w [N, K].
+// W4A16: q [N, K/8] packed int4 codes, s [N, K/32] bf16 group scales.
+struct Lin {
+  const uint16_t* w = nullptr;
+  const uint32_t* q = nullptr;
+  const uint16_t* s = nullptr;
+  int N = 0, K = 0;
+};
+
+// Which sequence / position / token each processed row is.
+// Decode: row b is sequence b at positions[b].  Prefill: every row is the
+// same sequence, at positions pos0 + row.
+struct Rows {
+  const int32_t* tokens = nullptr;
+  const int32_t* positions = nullptr;  // null: pos0 + row
+  int pos0 = 0, seq0 = 0, seq_stride = 1, n = 0;
+  int max_ctx = 0, vocab = 0;
+};
+
+// How a matrix-vector product builds its fp32 input x for one row.
+enum PrologueKind : int {
+  kPlain = 0,    // x = a[row][k]
+  kResNorm = 1,  // h' = (a + rms(sum_s d[s]) * gd) * scalar; x = rms(h') * gx; block 0 stores h'
+  kRes = 2,      // same h', x = h'
+  kGeglu = 3,    // x = gelu_tanh(a[row][k]) * a[row][I + k]   (I = K)
+  kPleGate = 4   // x = gelu_tanh(a[row][k]) * pli[row][k]
+};
+
+struct Prologue {
+  int kind = kPlain;
+  const float* a = nullptr;   // kPlain: x [rows, lda]; kRes*: h [rows, K]; kGeglu: [rows, 2K]; kPleGate: [rows, K]
+  int lda = 0;                // row stride of a (elements)
+  const float* d = nullptr;   // delta partials [nd][rows][K] (kRes*), may be null
+  int nd = 0;
+  const uint16_t* gd = nullptr;      // gain of rms(delta)
+  const uint16_t* scalar = nullptr;  // layer scalar (bf16[1]) or null
+  const uint16_t* gx = nullptr;      // gain of rms(h') (kResNorm)
+  float* h_out = nullptr;            // [rows, K] (kRes*), written when d != null
+  const float* pli = nullptr;        // kPleGate: row stride pli_ld
+  int pli_ld = 0;
+  float eps = 1e-6f;
+};
+
+// Output of a matrix-vector product: y [nks][rows][N] fp32 partial sums over
+// K slices, or (argmax mode) per-block best (value, index) candidates.
+struct Epilogue {
+  float* y = nullptr;
+  int argmax = 0;
+  float* logits = nullptr;      // argmax mode: optional fp32 [rows, N]
+  float* cand_val = nullptr;    // [rows][gridDim.x]
+  int32_t* cand_idx = nullptr;  // [rows][gridDim.x]
+};
+
+struct AttnArgs {
+  const float* q = nullptr;     // normed, rotated queries [rows][nq][hd] fp32
+  const uint16_t* kc = nullptr; // K cache of the source layer [max_batch][max_ctx][hd]
+  const uint16_t* vc = nullptr;
+  float* part = nullptr;        // [rows][nq][kMaxChunks][hd + 2]
+  float* out = nullptr;         // [rows][nq * hd]
+  int nq = 0, hd = 0, window = 0 /* 0: full */, chunk = 0, nchunk = 0;
+};
+
+struct QkvPostArgs {
+  const float* qkv = nullptr;   // [rows][(nq + 2*owns) * hd] raw projections
+  const uint16_t* gq = nullptr;
+  const uint16_t* gk = nullptr;
+  const double* inv_freq = nullptr;  // [hd/2]
+  float* q_out = nullptr;       // [rows][nq][hd]
+  uint16_t* kc = nullptr;       // this layer's cache when it owns K/V, else null
+  uint16_t* vc = nullptr;
+  int nq = 0, hd = 0;
+  float eps = 1e-6f;
+};
+
+// ---- launchers (kernels.hip) ----------------------------------------------
+hipError_t launch_embed(const Rows& R, const uint16_t* E, const uint16_t* Eple, int H, int LP,
+                        float sqrtH, float sqrtP, float* h, float* tokple, int* err,
+                        hipStream_t st);
+hipError_t launch_ple_finish(const Rows& R, const float* u, const float* tokple,
+                             const uint16_t* g, int L, int P, float inv_sqrtH, float eps,
+                             float* pli, hipStream_t st);
+// blocks_hint > 0 fixes the number of blocks along N (else chosen from N);
+// *blocks_out (nullable) receives it -- the argmax candidate count per row.
+hipError_t launch_gemv(int quant, int tag, const Lin& W, int rows, const Prologue& pro,
+                       const Epilogue& epi, int blocks_hint, int* blocks_out, hipStream_t st);
+int gemv_splits(int K);
+hipError_t launch_qkv_post(const Rows& R, const QkvPostArgs& a, hipStream_t st);
+hipError_t launch_attention(const Rows& R, const AttnArgs& a, hipStream_t st);
+hipError_t launch_advance(int32_t* pos, int n, hipStream_t st);
+hipError_t launch_sum_partials(int nparts, size_t n, const float* parts, float* out,
+                               hipStream_t st);
+hipError_t launch_argmax_final(int rows, int nblk, const float* cand_val,
+                               const int32_t* cand_idx, int32_t* out, hipStream_t st);
+
+}  // namespace e2b

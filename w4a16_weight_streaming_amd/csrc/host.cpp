@@ -1,0 +1,946 @@
+// Host side of libe2b: configuration, layer table and K/V share map, device
+// arena plan, weight upload, K/V binding and the orchestration of one decode
+// step (or a prefill pass) as a sequence of HIP kernel launches on the
+// caller's stream.  Nothing here allocates device memory.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "e2b.h"
+#include "e2b_internal.h"
+
+using e2b::Lin;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[1024];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(E2B_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct LayerInfo {
+  int full = 0, hd = 0, I = 0, src = 0;
+  double theta = 0;
+};
+
+struct LinOff {  // a linear layer as offsets into the arena
+  size_t w = 0, q = 0, s = 0;
+  int N = 0, K = 0;
+};
+
+struct Copy {  // one canonical tensor -> arena offset
+  std::string name;
+  int dtype = 0;
+  int ndim = 0;
+  int64_t d0 = 0, d1 = 0;
+  size_t dst = 0;
+};
+
+struct LayerOff {
+  LinOff qkv, o, gu, down, pg, pp;
+  size_t g_in = 0, g_q = 0, g_k = 0, g_pa = 0, g_pf = 0, g_ff = 0, g_pple = 0, scalar = 0;
+};
+
+struct LayerDev {
+  Lin qkv, o, gu, down, pg, pp;
+  const uint16_t *g_in = nullptr, *g_q = nullptr, *g_k = nullptr, *g_pa = nullptr,
+                 *g_pf = nullptr, *g_ff = nullptr, *g_pple = nullptr, *scalar = nullptr;
+};
+
+}  // namespace
+
+struct e2b_model {
+  e2b_config c{};
+  int L = 0, H = 0, P = 0, V = 0, nq = 0, first = 0, quant = 0;
+  std::vector<LayerInfo> li;
+  // arena plan
+  std::vector<Copy> plan;
+  size_t arena_bytes = 0, weight_bytes = 0;
+  size_t off_embed = 0, off_ple = 0, off_plpn = 0, off_final = 0, off_invf[2] = {0, 0};
+  LinOff plmp_off;
+  std::vector<LayerOff> lo;
+  // device views (valid after load)
+  char* arena = nullptr;
+  bool loaded = false;
+  const uint16_t *embed = nullptr, *ple = nullptr, *g_plpn = nullptr, *g_final = nullptr;
+  const double* invf[2] = {nullptr, nullptr};
+  Lin plmp;
+  std::vector<LayerDev> ld;
+  // K/V binding
+  char* kv = nullptr;
+  int max_batch = 0, max_ctx = 0;
+  std::vector<uint16_t*> kc, vc;
+  // per-kernel timing
+  int prof_kind = 0;
+  struct Mark {
+    hipEvent_t a, b;
+    double bytes;
+  };
+  std::vector<Mark> marks;
+};
+
+struct e2b_graph {
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+};
+
+namespace {
+
+bool is_full(const e2b_config& c, int l) {
+  return (l % c.layer_pattern_period) == c.layer_pattern_period - 1;
+}
+
+// Source layer of layer l's K/V: itself below the first shared layer; above
+// it the last non-shared layer of the same attention type; a shared layer
+// with no such layer keeps its own K/V.
+int kv_src(const e2b_config& c, int l) {
+  const int first = c.num_hidden_layers - c.num_kv_shared_layers;
+  if (l < first) return l;
+  int s = -1;
+  for (int i = 0; i < first; ++i)
+    if (is_full(c, i) == is_full(c, l)) s = i;
+  return s < 0 ? l : s;
+}
+
+bool supported_k(int K) { return e2b::gemv_splits(K) > 0 && e2b::gemv_splits(K) <= e2b::kMaxSplitK; }
+
+struct Planner {
+  e2b_model* m;
+  size_t cur = 0;
+  size_t alloc(size_t bytes) {
+    size_t o = cur;
+    cur = align_up(cur + bytes);
+    return o;
+  }
+  void copy(const std::string& name, int dtype, int ndim, int64_t d0, int64_t d1, size_t dst,
+            size_t bytes) {
+    m->plan.push_back(Copy{name, dtype, ndim, d0, d1, dst});
+    m->weight_bytes += bytes;
+  }
+  size_t vec(const std::string& name, int64_t n) {  // bf16 1-D
+    size_t o = alloc(n * 2);
+    copy(name, E2B_DTYPE_BF16, 1, n, 0, o, n * 2);
+    return o;
+  }
+  size_t mat(const std::string& name, int64_t r, int64_t c) {  // bf16 2-D
+    size_t o = alloc(r * c * 2);
+    copy(name, E2B_DTYPE_BF16, 2, r, c, o, r * c * 2);
+    return o;
+  }
+  // linears stacked along N into one matrix [sum N, K]
+  LinOff lin(const std::vector<std::string>& names, const std::vector<int>& Ns, int K) {
+    LinOff L;
+    int N = 0;
+    for (int n : Ns) N += n;
+    L.N = N;
+    L.K = K;
+    if (m->quant == E2B_QUANT_BF16) {
+      L.w = alloc((size_t)N * K * 2);
+      size_t r = 0;
+      for (size_t i = 0; i < names.size(); ++i) {
+        copy(names[i], E2B_DTYPE_BF16, 2, Ns[i], K, L.w + r * K * 2, (size_t)Ns[i] * K * 2);
+        r += Ns[i];
+      }
+    } else {
+      L.q = alloc((size_t)N * K / 2);
+      L.s = alloc((size_t)N * (K / 32) * 2);
+      size_t r = 0;
+      for (size_t i = 0; i < names.size(); ++i) {
+        copy(names[i] + "_packed", E2B_DTYPE_INT32, 2, Ns[i], K / 8, L.q + r * K / 2,
+             (size_t)Ns[i] * K / 2);
+        copy(names[i] + "_scale", E2B_DTYPE_BF16, 2, Ns[i], K / 32, L.s + r * (K / 32) * 2,
+             (size_t)Ns[i] * (K / 32) * 2);
+        r += Ns[i];
+      }
+    }
+    return L;
+  }
+};
+
+int build_plan(e2b_model* m) {
+  Planner p{m};
+  const int L = m->L, H = m->H, P = m->P, V = m->V, nq = m->nq;
+  m->off_embed = p.mat("model.embed_tokens.weight", V, H);
+  m->off_ple = p.mat("model.embed_tokens_per_layer.weight", V, (int64_t)L * P);
+  m->plmp_off = p.lin({"model.per_layer_model_projection.weight"}, {L * P}, H);
+  m->off_plpn = p.vec("model.per_layer_projection_norm.weight", P);
+  m->off_final = p.vec("model.norm.weight", H);
+  m->lo.resize(L);
+  for (int l = 0; l < L; ++l) {
+    const LayerInfo& y = m->li[l];
+    LayerOff& o = m->lo[l];
+    const std::string pre = "model.layers." + std::to_string(l) + ".";
+    o.g_in = p.vec(pre + "input_layernorm.weight", H);
+    if (y.src == l)
+      o.qkv = p.lin({pre + "self_attn.q_proj.weight", pre + "self_attn.k_proj.weight",
+                     pre + "self_attn.v_proj.weight"},
+                    {nq * y.hd, y.hd, y.hd}, H);
+    else
+      o.qkv = p.lin({pre + "self_attn.q_proj.weight"}, {nq * y.hd}, H);
+    o.o = p.lin({pre + "self_attn.o_proj.weight"}, {H}, nq * y.hd);
+    o.g_q = p.vec(pre + "self_attn.q_norm.weight", y.hd);
+    if (y.src == l) o.g_k = p.vec(pre + "self_attn.k_norm.weight", y.hd);
+    o.g_pa = p.vec(pre + "post_attention_layernorm.weight", H);
+    o.g_pf = p.vec(pre + "pre_feedforward_layernorm.weight", H);
+    o.gu = p.lin({pre + "mlp.gate_proj.weight", pre + "mlp.up_proj.weight"}, {y.I, y.I}, H);
+    o.down = p.lin({pre + "mlp.down_proj.weight"}, {H}, y.I);
+    o.g_ff = p.vec(pre + "post_feedforward_layernorm.weight", H);
+    o.pg = p.lin({pre + "per_layer_input_gate.weight"}, {P}, H);
+    o.pp = p.lin({pre + "per_layer_projection.weight"}, {H}, P);
+    o.g_pple = p.vec(pre + "post_per_layer_input_norm.weight", H);
+    o.scalar = p.vec(pre + "layer_scalar", 1);
+  }
+  // RoPE inverse frequencies theta^(-2i/hd), double, per attention type
+  m->off_invf[0] = p.alloc(sizeof(double) * m->c.head_dim / 2);
+  m->off_invf[1] = p.alloc(sizeof(double) * m->c.global_head_dim / 2);
+  m->arena_bytes = p.cur;
+  return E2B_OK;
+}
+
+// K-side tensors of layers that read another layer's K/V: accepted and ignored
+bool ignorable(const e2b_model* m, const char* name) {
+  int l = -1;
+  char rest[128];
+  if (sscanf(name, "model.layers.%d.%127s", &l, rest) != 2) return false;
+  if (l < 0 || l >= m->L || m->li[l].src == l) return false;
+  return strncmp(rest, "self_attn.k_proj.", 17) == 0 || strncmp(rest, "self_attn.v_proj.", 17) == 0 ||
+         strcmp(rest, "self_attn.k_norm.weight") == 0;
+}
+
+Lin resolve(const e2b_model* m, const LinOff& o) {
+  Lin L;
+  L.N = o.N;
+  L.K = o.K;
+  if (m->quant == E2B_QUANT_BF16) {
+    L.w = reinterpret_cast<const uint16_t*>(m->arena + o.w);
+  } else {
+    L.q = reinterpret_cast<const uint32_t*>(m->arena + o.q);
+    L.s = reinterpret_cast<const uint16_t*>(m->arena + o.s);
+  }
+  return L;
+}
+
+// ---- workspace layout ------------------------------------------------------
+struct Ws {
+  size_t err, h0, h1, tokple, u, pli, qkv, qn, part, attn, oo, gu, dn, pgy, ppo, cv, ci, total;
+};
+
+Ws ws_layout(const e2b_model* m, int R) {
+  Ws w{};
+  size_t cur = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = cur;
+    cur = align_up(cur + bytes);
+    return o;
+  };
+  const size_t f = sizeof(float);
+  const int hdm = std::max(m->c.head_dim, m->c.global_head_dim);
+  int Imax = 0, nko = 1, nkd = 1;
+  for (const LayerInfo& y : m->li) {
+    Imax = std::max(Imax, y.I);
+    nko = std::max(nko, e2b::gemv_splits(m->nq * y.hd));
+    nkd = std::max(nkd, e2b::gemv_splits(y.I));
+  }
+  const size_t LP = (size_t)m->L * m->P;
+  w.err = take(64);
+  w.h0 = take(f * R * m->H);
+  w.h1 = take(f * R * m->H);
+  w.tokple = take(f * R * LP);
+  w.u = take(f * R * LP);
+  w.pli = take(f * R * LP);
+  w.qkv = take(f * R * (m->nq + 2) * hdm);
+  w.qn = take(f * R * m->nq * hdm);
+  w.part = take(f * R * m->nq * e2b::kMaxChunks * (hdm + 2));
+  w.attn = take(f * R * m->nq * hdm);
+  w.oo = take(f * nko * R * m->H);
+  w.gu = take(f * R * 2 * Imax);
+  w.dn = take(f * nkd * R * m->H);
+  w.pgy = take(f * R * m->P);
+  w.ppo = take(f * R * m->H);
+  w.cv = take(f * R * e2b::kLmBlocks);
+  w.ci = take(sizeof(int32_t) * R * e2b::kLmBlocks);
+  w.total = cur;
+  return w;
+}
+
+void attn_chunks(const e2b_model* m, bool full, int* chunk, int* nchunk) {
+  const int span = full ? m->max_ctx : std::min(m->c.sliding_window, m->max_ctx);
+  int n = (span + 15) / 16;
+  if (n > e2b::kMaxChunks) n = e2b::kMaxChunks;
+  if (n < 1) n = 1;
+  *nchunk = n;
+  *chunk = (span + n - 1) / n;
+}
+
+// launch_gemv, bracketed by events when this kind is being profiled
+hipError_t gemv(e2b_model* m, int quant, int tag, const Lin& W, int rows,
+                const e2b::Prologue& pr, const e2b::Epilogue& ep, int* nblk, hipStream_t st) {
+  if (m->prof_kind != tag) return e2b::launch_gemv(quant, tag, W, rows, pr, ep, 0, nblk, st);
+  e2b_model::Mark mk{};
+  hipError_t e = hipEventCreate(&mk.a);
+  if (e == hipSuccess) e = hipEventCreate(&mk.b);
+  if (e == hipSuccess) e = hipEventRecord(mk.a, st);
+  if (e == hipSuccess) e = e2b::launch_gemv(quant, tag, W, rows, pr, ep, 0, nblk, st);
+  if (e == hipSuccess) e = hipEventRecord(mk.b, st);
+  if (e != hipSuccess) return e;
+  const double wb = quant ? (double)W.N * W.K / 2 + (double)W.N * (W.K / 32) * 2
+                          : (double)W.N * W.K * 2;
+  mk.bytes = wb + (double)rows * (W.K + W.N) * sizeof(float);
+  m->marks.push_back(mk);
+  return hipSuccess;
+}
+
+#define CK(call, what)                         \
+  do {                                         \
+    hipError_t e_ = (call);                    \
+    if (e_ != hipSuccess) return hip_fail(e_, what); \
+  } while (0)
+
+// One pass over R.n rows: all layers, then (if head) the final norm, lm_head
+// and argmax for every row (head_row < 0) or for row head_row only.
+int run_rows(e2b_model* m, const e2b::Rows& R, bool head, int head_row, float* d_logits,
+             int32_t* d_argmax, char* ws, const Ws& W, hipStream_t st) {
+  using namespace e2b;
+  const int n = R.n, H = m->H, P = m->P, L = m->L, LP = L * P, q = m->quant;
+  const float eps = m->c.rms_eps;
+  auto F = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
+  int* err = reinterpret_cast<int*>(ws + W.err);
+
+  CK(launch_embed(R, m->embed, m->ple, H, LP, std::sqrt((float)H), std::sqrt((float)P), F(W.h0),
+                  F(W.tokple), err, st),
+     "embed");
+  {
+    Prologue pr;
+    pr.kind = kPlain;
+    pr.a = F(W.h0);
+    pr.lda = H;
+    Epilogue ep;
+    ep.y = F(W.u);
+    CK(gemv(m, q, kTagPleModel, m->plmp, n, pr, ep, nullptr, st), "per-layer model projection");
+  }
+  CK(launch_ple_finish(R, F(W.u), F(W.tokple), m->g_plpn, L, P, 1.0f / std::sqrt((float)H), eps,
+                       F(W.pli), st),
+     "per-layer inputs");
+
+  float* cur = F(W.h0);
+  float* oth = F(W.h1);
+  const float* pend = nullptr;  // per-layer projection output not yet added
+  const uint16_t *pend_g = nullptr, *pend_s = nullptr;
+  for (int l = 0; l < L; ++l) {
+    const LayerInfo& y = m->li[l];
+    const LayerDev& d = m->ld[l];
+    const bool owns = y.src == l;
+    {  // QKV with the residual update of the previous layer fused in front
+      Prologue pr;
+      pr.kind = kResNorm;
+      pr.a = cur;
+      pr.d = pend;
+      pr.nd = 1;
+      pr.gd = pend_g;
+      pr.scalar = pend_s;
+      pr.gx = d.g_in;
+      pr.h_out = oth;
+      pr.eps = eps;
+      Epilogue ep;
+      ep.y = F(W.qkv);
+      CK(gemv(m, q, kTagQkv, d.qkv, n, pr, ep, nullptr, st), "qkv projection");
+      if (pend) std::swap(cur, oth);
+    }
+    {
+      QkvPostArgs a;
+      a.qkv = F(W.qkv);
+      a.gq = d.g_q;
+      a.gk = d.g_k;
+      a.inv_freq = m->invf[y.full];
+      a.q_out = F(W.qn);
+      a.kc = owns ? m->kc[l] : nullptr;
+      a.vc = owns ? m->vc[l] : nullptr;
+      a.nq = m->nq;
+      a.hd = y.hd;
+      a.eps = eps;
+      CK(launch_qkv_post(R, a, st), "head norms / rope / kv write");
+    }
+    {
+      AttnArgs a;
+      a.q = F(W.qn);
+      a.kc = m->kc[y.src];
+      a.vc = m->vc[y.src];
+      a.part = F(W.part);
+      a.out = F(W.attn);
+      a.nq = m->nq;
+      a.hd = y.hd;
+      a.window = y.full ? 0 : m->c.sliding_window;
+      attn_chunks(m, y.full, &a.chunk, &a.nchunk);
+      CK(launch_attention(R, a, st), "attention");
+    }
+    {
+      Prologue pr;
+      pr.kind = kPlain;
+      pr.a = F(W.attn);
+      pr.lda = m->nq * y.hd;
+      Epilogue ep;
+      ep.y = F(W.oo);
+      CK(gemv(m, q, kTagO, d.o, n, pr, ep, nullptr, st), "o projection");
+    }
+    {  // post-attention norm + residual, pre-FFN norm, gate/up
+      Prologue pr;
+      pr.kind = kResNorm;
+      pr.a = cur;
+      pr.d = F(W.oo);
+      pr.nd = gemv_splits(d.o.K);
+      pr.gd = d.g_pa;
+      pr.gx = d.g_pf;
+      pr.h_out = oth;
+      pr.eps = eps;
+      Epilogue ep;
+      ep.y = F(W.gu);
+      CK(gemv(m, q, kTagGateUp, d.gu, n, pr, ep, nullptr, st), "gate/up projection");
+      std::swap(cur, oth);
+    }
+    {  // GeGLU then down
+      Prologue pr;
+      pr.kind = kGeglu;
+      pr.a = F(W.gu);
+      pr.lda = 2 * y.I;
+      Epilogue ep;
+      ep.y = F(W.dn);
+      CK(gemv(m, q, kTagDown, d.down, n, pr, ep, nullptr, st), "down projection");
+    }
+    {  // post-FFN norm + residual, per-layer input gate
+      Prologue pr;
+      pr.kind = kRes;
+      pr.a = cur;
+      pr.d = F(W.dn);
+      pr.nd = gemv_splits(d.down.K);
+      pr.gd = d.g_ff;
+      pr.h_out = oth;
+      pr.eps = eps;
+      Epilogue ep;
+      ep.y = F(W.pgy);
+      CK(gemv(m, q, kTagPleGate, d.pg, n, pr, ep, nullptr, st), "per-layer input gate");
+      std::swap(cur, oth);
+    }
+    {  // gelu(gate) * pli[l], per-layer projection
+      Prologue pr;
+      pr.kind = kPleGate;
+      pr.a = F(W.pgy);
+      pr.lda = P;
+      pr.pli = F(W.pli) + (size_t)l * P;
+      pr.pli_ld = LP;
+      Epilogue ep;
+      ep.y = F(W.ppo);
+      CK(gemv(m, q, kTagPleProj, d.pp, n, pr, ep, nullptr, st), "per-layer projection");
+    }
+    pend = F(W.ppo);
+    pend_g = d.g_pple;
+    pend_s = d.scalar;
+  }
+  if (!head) return E2B_OK;
+  const int hr = head_row < 0 ? 0 : head_row;
+  const int nh = head_row < 0 ? n : 1;
+  Lin E;
+  E.w = m->embed;
+  E.N = m->V;
+  E.K = H;
+  Prologue pr;
+  pr.kind = kResNorm;
+  pr.a = cur + (size_t)hr * H;
+  pr.d = pend + (size_t)hr * H;
+  pr.nd = 1;
+  pr.gd = pend_g;
+  pr.scalar = pend_s;
+  pr.gx = m->g_final;
+  pr.h_out = oth + (size_t)hr * H;
+  pr.eps = eps;
+  Epilogue ep;
+  ep.argmax = 1;
+  ep.logits = d_logits;
+  ep.cand_val = F(W.cv);
+  ep.cand_idx = reinterpret_cast<int32_t*>(ws + W.ci);
+  int nblk = 0;
+  CK(gemv(m, E2B_QUANT_BF16, kTagLmHead, E, nh, pr, ep, &nblk, st), "lm_head");
+  if (nblk > kLmBlocks) return fail(E2B_EINVAL, "lm_head: %d candidate blocks", nblk);
+  CK(launch_argmax_final(nh, nblk, ep.cand_val, ep.cand_idx, d_argmax, st), "argmax");
+  return E2B_OK;
+}
+
+}  // namespace
+
+// ============================================================== public ABI
+extern "C" {
+
+const char* e2b_last_error(void) { return g_err.c_str(); }
+
+int e2b_config_preset(const char* name, e2b_config* out) {
+  if (!name || !out) return fail(E2B_EINVAL, "null argument");
+  e2b_config c{};
+  c.num_key_value_heads = 1;
+  c.layer_pattern_period = 5;
+  c.use_double_wide_mlp = 1;
+  c.quant = E2B_QUANT_BF16;
+  c.group_size = 32;
+  c.rms_eps = 1e-6f;
+  c.rope_theta_sliding = 1.0e4f;
+  c.rope_theta_full = 1.0e6f;
+  if (!strcmp(name, "e2b")) {
+    c.num_hidden_layers = 35;
+    c.num_kv_shared_layers = 20;
+    c.hidden_size = 1536;
+    c.num_attention_heads = 8;
+    c.head_dim = 256;
+    c.global_head_dim = 512;
+    c.sliding_window = 512;
+    c.intermediate_size = 6144;
+    c.hidden_size_per_layer_input = 256;
+    c.vocab_size = 262144;
+  } else if (!strcmp(name, "toy") || !strcmp(name, "toy10")) {
+    const bool ten = !strcmp(name, "toy10");
+    c.num_hidden_layers = ten ? 10 : 5;
+    c.num_kv_shared_layers = ten ? 5 : 2;
+    c.hidden_size = 256;
+    c.num_attention_heads = 2;
+    c.head_dim = 64;
+    c.global_head_dim = 128;
+    c.sliding_window = 16;
+    c.intermediate_size = 512;
+    c.hidden_size_per_layer_input = 32;
+    c.vocab_size = 4096;
+  } else {
+    return fail(E2B_EINVAL, "unknown preset '%s'", name);
+  }
+  *out = c;
+  return E2B_OK;
+}
+
+int e2b_create(const e2b_config* cfg, e2b_model** out) {
+  if (!cfg || !out) return fail(E2B_EINVAL, "null argument");
+  *out = nullptr;
+  const e2b_config& c = *cfg;
+  auto hd_ok = [](int h) { return h == 64 || h == 128 || h == 256 || h == 512; };
+  if (c.num_key_value_heads != 1) return fail(E2B_EINVAL, "num_key_value_heads must be 1");
+  if (c.num_hidden_layers < 1 || c.num_hidden_layers > 256)
+    return fail(E2B_EINVAL, "num_hidden_layers out of range");
+  if (c.num_kv_shared_layers < 0 || c.num_kv_shared_layers >= c.num_hidden_layers)
+    return fail(E2B_EINVAL, "num_kv_shared_layers out of range");
+  if (!hd_ok(c.head_dim) || !hd_ok(c.global_head_dim))
+    return fail(E2B_EINVAL, "head dims must be 64, 128, 256 or 512");
+  if (c.num_attention_heads < 1 || c.num_attention_heads > 8)
+    return fail(E2B_EINVAL, "num_attention_heads must be 1..8");
+  if (c.group_size != 32) return fail(E2B_EINVAL, "group_size must be 32");
+  if (c.layer_pattern_period < 1) return fail(E2B_EINVAL, "layer_pattern_period < 1");
+  if (c.sliding_window < 1) return fail(E2B_EINVAL, "sliding_window < 1");
+  if (c.vocab_size < 1 || c.hidden_size_per_layer_input < 1 ||
+      c.hidden_size_per_layer_input > 256)
+    return fail(E2B_EINVAL, "vocab_size / hidden_size_per_layer_input out of range");
+  if (c.quant != E2B_QUANT_BF16 && c.quant != E2B_QUANT_W4A16)
+    return fail(E2B_EINVAL, "unknown quant mode %d", c.quant);
+  if (!(c.rms_eps > 0) || !(c.rope_theta_sliding > 1) || !(c.rope_theta_full > 1))
+    return fail(E2B_EINVAL, "rms_eps / rope thetas out of range");
+  e2b_model* m = new e2b_model();
+  m->c = c;
+  m->L = c.num_hidden_layers;
+  m->H = c.hidden_size;
+  m->P = c.hidden_size_per_layer_input;
+  m->V = c.vocab_size;
+  m->nq = c.num_attention_heads;
+  m->first = c.num_hidden_layers - c.num_kv_shared_layers;
+  m->quant = c.quant;
+  m->li.resize(m->L);
+  for (int l = 0; l < m->L; ++l) {
+    LayerInfo& y = m->li[l];
+    y.full = is_full(c, l);
+    y.hd = y.full ? c.global_head_dim : c.head_dim;
+    y.theta = y.full ? c.rope_theta_full : c.rope_theta_sliding;
+    y.I = c.intermediate_size * ((c.use_double_wide_mlp && l >= m->first) ? 2 : 1);
+    y.src = kv_src(c, l);
+  }
+  // every matrix-vector product must have a supported K and widths in 32-groups
+  std::vector<int> Ks = {m->H, m->P};
+  for (const LayerInfo& y : m->li) {
+    Ks.push_back(m->nq * y.hd);
+    Ks.push_back(y.I);
+  }
+  for (int K : Ks)
+    if (K % 32 || !supported_k(K)) {
+      delete m;
+      return fail(E2B_EINVAL, "unsupported reduction width %d", K);
+    }
+  if (e2b::gemv_splits(m->H) != 1) {
+    delete m;
+    return fail(E2B_EINVAL, "hidden_size %d must be a single slice (<=512, 1536 or 2048)", m->H);
+  }
+  build_plan(m);
+  *out = m;
+  return E2B_OK;
+}
+
+void e2b_destroy(e2b_model* m) { delete m; }
+
+int e2b_kv_share_map(const e2b_model* m, int32_t* out) {
+  if (!m || !out) return fail(E2B_EINVAL, "null argument");
+  for (int l = 0; l < m->L; ++l) out[l] = m->li[l].src;
+  return E2B_OK;
+}
+
+size_t e2b_weight_bytes(const e2b_model* m) { return m ? m->weight_bytes : 0; }
+size_t e2b_arena_bytes(const e2b_model* m) { return m ? m->arena_bytes : 0; }
+
+size_t e2b_kv_bytes(const e2b_model* m, int max_batch, int max_ctx) {
+  if (!m || max_batch < 1 || max_ctx < 1) return 0;
+  size_t b = 0;
+  for (int l = 0; l < m->L; ++l)
+    if (m->li[l].src == l) b += 2ull * max_batch * max_ctx * m->li[l].hd * sizeof(uint16_t);
+  return b;
+}
+
+size_t e2b_workspace_bytes(const e2b_model* m, int max_rows) {
+  if (!m || max_rows < 1) return 0;
+  return ws_layout(m, max_rows).total;
+}
+
+int e2b_load_weights(e2b_model* m, const e2b_tensor* t, int n, void* d_arena, size_t arena_bytes,
+                     void* stream) {
+  if (!m || (!t && n) || !d_arena) return fail(E2B_EINVAL, "null argument");
+  if (arena_bytes < m->arena_bytes)
+    return fail(E2B_ENOMEM, "arena of %zu bytes < %zu required", arena_bytes, m->arena_bytes);
+  if (reinterpret_cast<uintptr_t>(d_arena) % kAlign)
+    return fail(E2B_EINVAL, "arena must be %zu-byte aligned", kAlign);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  // match every planned copy to exactly one tensor; reject strays
+  std::vector<int> used(n, 0);
+  std::vector<int> src(m->plan.size(), -1);
+  for (size_t i = 0; i < m->plan.size(); ++i) {
+    const Copy& cp = m->plan[i];
+    for (int j = 0; j < n; ++j) {
+      if (!t[j].name || strcmp(t[j].name, cp.name.c_str())) continue;
+      if (src[i] >= 0) return fail(E2B_EINVAL, "duplicate tensor %s", cp.name.c_str());
+      src[i] = j;
+    }
+    if (src[i] < 0) return fail(E2B_EINVAL, "missing tensor %s", cp.name.c_str());
+    const e2b_tensor& x = t[src[i]];
+    const bool shape_ok = x.ndim == cp.ndim && x.shape[0] == cp.d0 && (cp.ndim == 1 || x.shape[1] == cp.d1);
+    if (x.dtype != cp.dtype || !shape_ok || !x.data)
+      return fail(E2B_EINVAL, "tensor %s: expected dtype %d shape [%lld%s%lld], got dtype %d ndim %d [%lld, %lld]",
+                  cp.name.c_str(), cp.dtype, (long long)cp.d0, cp.ndim == 2 ? ", " : "",
+                  cp.ndim == 2 ? (long long)cp.d1 : 0LL, x.dtype, x.ndim,
+                  (long long)x.shape[0], (long long)(x.ndim > 1 ? x.shape[1] : 0));
+    used[src[i]] = 1;
+  }
+  for (int j = 0; j < n; ++j)
+    if (!used[j] && !(t[j].name && ignorable(m, t[j].name)))
+      return fail(E2B_EINVAL, "unexpected tensor %s", t[j].name ? t[j].name : "(null)");
+  char* A = reinterpret_cast<char*>(d_arena);
+  for (size_t i = 0; i < m->plan.size(); ++i) {
+    const Copy& cp = m->plan[i];
+    const size_t esz = cp.dtype == E2B_DTYPE_INT32 ? 4 : 2;
+    const size_t bytes = esz * cp.d0 * (cp.ndim == 2 ? cp.d1 : 1);
+    CK(hipMemcpyAsync(A + cp.dst, t[src[i]].data, bytes, hipMemcpyHostToDevice, st),
+       "weight upload");
+  }
+  for (int k = 0; k < 2; ++k) {
+    const int hd = k ? m->c.global_head_dim : m->c.head_dim;
+    const double theta = k ? m->c.rope_theta_full : m->c.rope_theta_sliding;
+    std::vector<double> f(hd / 2);
+    for (int i = 0; i < hd / 2; ++i) f[i] = std::pow(theta, -2.0 * i / hd);
+    CK(hipMemcpyAsync(A + m->off_invf[k], f.data(), f.size() * sizeof(double),
+                      hipMemcpyHostToDevice, st),
+       "rope table upload");
+    CK(hipStreamSynchronize(st), "weight upload sync");  // f must outlive the copy
+  }
+  m->arena = A;
+  auto U = [&](size_t off) { return reinterpret_cast<const uint16_t*>(A + off); };
+  m->embed = U(m->off_embed);
+  m->ple = U(m->off_ple);
+  m->g_plpn = U(m->off_plpn);
+  m->g_final = U(m->off_final);
+  m->invf[0] = reinterpret_cast<const double*>(A + m->off_invf[0]);
+  m->invf[1] = reinterpret_cast<const double*>(A + m->off_invf[1]);
+  m->plmp = resolve(m, m->plmp_off);
+  m->ld.assign(m->L, LayerDev());
+  for (int l = 0; l < m->L; ++l) {
+    const LayerOff& o = m->lo[l];
+    LayerDev& d = m->ld[l];
+    d.qkv = resolve(m, o.qkv);
+    d.o = resolve(m, o.o);
+    d.gu = resolve(m, o.gu);
+    d.down = resolve(m, o.down);
+    d.pg = resolve(m, o.pg);
+    d.pp = resolve(m, o.pp);
+    d.g_in = U(o.g_in);
+    d.g_q = U(o.g_q);
+    d.g_k = m->li[l].src == l ? U(o.g_k) : nullptr;
+    d.g_pa = U(o.g_pa);
+    d.g_pf = U(o.g_pf);
+    d.g_ff = U(o.g_ff);
+    d.g_pple = U(o.g_pple);
+    d.scalar = U(o.scalar);
+  }
+  m->loaded = true;
+  return E2B_OK;
+}
+
+int e2b_kv_alloc(e2b_model* m, void* d_kv, size_t bytes, int max_batch, int max_ctx) {
+  if (!m || !d_kv) return fail(E2B_EINVAL, "null argument");
+  if (max_batch < 1 || max_ctx < 1) return fail(E2B_EINVAL, "max_batch and max_ctx must be >= 1");
+  const size_t need = e2b_kv_bytes(m, max_batch, max_ctx);
+  if (bytes < need) return fail(E2B_ENOMEM, "kv buffer of %zu bytes < %zu required", bytes, need);
+  if (reinterpret_cast<uintptr_t>(d_kv) % 16) return fail(E2B_EINVAL, "kv buffer must be 16-byte aligned");
+  m->kv = reinterpret_cast<char*>(d_kv);
+  m->max_batch = max_batch;
+  m->max_ctx = max_ctx;
+  m->kc.assign(m->L, nullptr);
+  m->vc.assign(m->L, nullptr);
+  size_t off = 0;
+  for (int l = 0; l < m->L; ++l) {
+    if (m->li[l].src != l) continue;
+    const size_t one = (size_t)max_batch * max_ctx * m->li[l].hd * sizeof(uint16_t);
+    m->kc[l] = reinterpret_cast<uint16_t*>(m->kv + off);
+    m->vc[l] = reinterpret_cast<uint16_t*>(m->kv + off + one);
+    off += 2 * one;
+  }
+  return E2B_OK;
+}
+
+int e2b_decode_step(e2b_model* m, const int32_t* d_tokens, const int32_t* d_positions, int batch,
+                    float* d_logits, int32_t* d_argmax, void* d_ws, size_t ws_bytes,
+                    void* stream) {
+  if (!m || !d_tokens || !d_positions || !d_argmax || !d_ws)
+    return fail(E2B_EINVAL, "null argument");
+  if (!m->loaded) return fail(E2B_ESTATE, "weights not loaded");
+  if (!m->kv) return fail(E2B_ESTATE, "kv cache not bound");
+  if (batch < 1 || batch > m->max_batch)
+    return fail(E2B_ERANGE, "batch %d outside [1, %d]", batch, m->max_batch);
+  const Ws W = ws_layout(m, batch);
+  if (ws_bytes < W.total)
+    return fail(E2B_ENOMEM, "workspace of %zu bytes < %zu required", ws_bytes, W.total);
+  if (reinterpret_cast<uintptr_t>(d_ws) % kAlign)
+    return fail(E2B_EINVAL, "workspace must be %zu-byte aligned", kAlign);
+  e2b::Rows R;
+  R.tokens = d_tokens;
+  R.positions = d_positions;
+  R.seq0 = 0;
+  R.seq_stride = 1;
+  R.n = batch;
+  R.max_ctx = m->max_ctx;
+  R.vocab = m->V;
+  return run_rows(m, R, true, -1, d_logits, d_argmax, reinterpret_cast<char*>(d_ws), W,
+                  reinterpret_cast<hipStream_t>(stream));
+}
+
+int e2b_prefill(e2b_model* m, int seq, const int32_t* d_tokens, int n_tokens, int pos0,
+                float* d_logits_last, int32_t* d_argmax_last, void* d_ws, size_t ws_bytes,
+                void* stream) {
+  if (!m || !d_tokens || !d_argmax_last || !d_ws) return fail(E2B_EINVAL, "null argument");
+  if (!m->loaded) return fail(E2B_ESTATE, "weights not loaded");
+  if (!m->kv) return fail(E2B_ESTATE, "kv cache not bound");
+  if (seq < 0 || seq >= m->max_batch) return fail(E2B_ERANGE, "sequence %d outside [0, %d)", seq, m->max_batch);
+  if (n_tokens < 1 || pos0 < 0 || (int64_t)pos0 + n_tokens > m->max_ctx)
+    return fail(E2B_ERANGE, "positions [%d, %lld) outside [0, %d)", pos0,
+                (long long)pos0 + n_tokens, m->max_ctx);
+  if (reinterpret_cast<uintptr_t>(d_ws) % kAlign)
+    return fail(E2B_EINVAL, "workspace must be %zu-byte aligned", kAlign);
+  int cap = std::min(n_tokens, 128);
+  while (cap > 0 && ws_layout(m, cap).total > ws_bytes) --cap;
+  if (cap < 1)
+    return fail(E2B_ENOMEM, "workspace of %zu bytes < %zu required for one row", ws_bytes,
+                ws_layout(m, 1).total);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  for (int off = 0; off < n_tokens; off += cap) {
+    const int r = std::min(cap, n_tokens - off);
+    e2b::Rows R;
+    R.tokens = d_tokens + off;
+    R.positions = nullptr;
+    R.pos0 = pos0 + off;
+    R.seq0 = seq;
+    R.seq_stride = 0;
+    R.n = r;
+    R.max_ctx = m->max_ctx;
+    R.vocab = m->V;
+    const bool last = off + r == n_tokens;
+    int rc = run_rows(m, R, last, r - 1, d_logits_last, d_argmax_last,
+                      reinterpret_cast<char*>(d_ws), ws_layout(m, r), st);
+    if (rc) return rc;
+  }
+  return E2B_OK;
+}
+
+int e2b_kv_view(const e2b_model* m, int layer, int which, void** out) {
+  if (!m || !out) return fail(E2B_EINVAL, "null argument");
+  if (!m->kv) return fail(E2B_ESTATE, "kv cache not bound");
+  if (layer < 0 || layer >= m->L || (which != 0 && which != 1))
+    return fail(E2B_EINVAL, "bad layer %d / which %d", layer, which);
+  const int s = m->li[layer].src;
+  *out = which ? static_cast<void*>(m->vc[s]) : static_cast<void*>(m->kc[s]);
+  return E2B_OK;
+}
+
+size_t e2b_matvec_workspace_bytes(int N, int K, int rows) {
+  const int nks = e2b::gemv_splits(K);
+  if (N < 1 || rows < 1 || nks < 1) return 0;
+  return nks > 1 ? (size_t)nks * rows * N * sizeof(float) : 0;
+}
+
+int e2b_matvec(int quant, const void* d_w, const uint16_t* d_scale, int N, int K,
+               const float* d_x, int rows, float* d_y, void* d_ws, size_t ws_bytes,
+               void* stream) {
+  if (!d_w || !d_x || !d_y || (quant == E2B_QUANT_W4A16 && !d_scale))
+    return fail(E2B_EINVAL, "null argument");
+  if (quant != E2B_QUANT_BF16 && quant != E2B_QUANT_W4A16)
+    return fail(E2B_EINVAL, "unknown quant mode %d", quant);
+  if (N < 1 || rows < 1 || rows > 65535 || K % 32 || !supported_k(K))
+    return fail(E2B_EINVAL, "unsupported shape N=%d K=%d rows=%d", N, K, rows);
+  if (reinterpret_cast<uintptr_t>(d_w) % 16) return fail(E2B_EINVAL, "weights must be 16-byte aligned");
+  const int nks = e2b::gemv_splits(K);
+  const size_t need = e2b_matvec_workspace_bytes(N, K, rows);
+  if (need && (!d_ws || ws_bytes < need))
+    return fail(E2B_ENOMEM, "workspace of %zu bytes < %zu required", ws_bytes, need);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  Lin W;
+  W.N = N;
+  W.K = K;
+  if (quant == E2B_QUANT_BF16) {
+    W.w = reinterpret_cast<const uint16_t*>(d_w);
+  } else {
+    W.q = reinterpret_cast<const uint32_t*>(d_w);
+    W.s = d_scale;
+  }
+  e2b::Prologue pr;
+  pr.kind = e2b::kPlain;
+  pr.a = d_x;
+  pr.lda = K;
+  e2b::Epilogue ep;
+  ep.y = nks > 1 ? reinterpret_cast<float*>(d_ws) : d_y;
+  CK(e2b::launch_gemv(quant, e2b::kTagOther, W, rows, pr, ep, 0, nullptr, st), "matvec");
+  if (nks > 1) CK(e2b::launch_sum_partials(nks, (size_t)rows * N, ep.y, d_y, st), "matvec sum");
+  return E2B_OK;
+}
+
+int e2b_graph_capture(e2b_model* m, const int32_t* d_tokens, int32_t* d_positions, int batch,
+                      float* d_logits, int32_t* d_argmax, void* d_ws, size_t ws_bytes,
+                      int advance_positions, void* stream, e2b_graph** out) {
+  if (!out) return fail(E2B_EINVAL, "null argument");
+  *out = nullptr;
+  if (!stream) return fail(E2B_EINVAL, "graph capture needs a non-null stream");
+  if (m && m->prof_kind) return fail(E2B_ESTATE, "cannot capture while profiling");
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  e2b_graph* g = new e2b_graph();
+  hipError_t e = hipStreamBeginCapture(st, hipStreamCaptureModeThreadLocal);
+  if (e != hipSuccess) {
+    delete g;
+    return hip_fail(e, "begin capture");
+  }
+  int rc = e2b_decode_step(m, d_tokens, d_positions, batch, d_logits, d_argmax, d_ws, ws_bytes,
+                           stream);
+  if (rc == E2B_OK && advance_positions) {
+    hipError_t ea = e2b::launch_advance(d_positions, batch, st);
+    if (ea != hipSuccess) rc = hip_fail(ea, "advance positions");
+  }
+  const std::string saved = g_err;
+  e = hipStreamEndCapture(st, &g->graph);
+  if (rc != E2B_OK) {
+    if (g->graph) (void)hipGraphDestroy(g->graph);
+    delete g;
+    g_err = saved;
+    return rc;
+  }
+  if (e != hipSuccess) {
+    delete g;
+    return hip_fail(e, "end capture");
+  }
+  e = hipGraphInstantiate(&g->exec, g->graph, nullptr, nullptr, 0);
+  if (e != hipSuccess) {
+    (void)hipGraphDestroy(g->graph);
+    delete g;
+    return hip_fail(e, "graph instantiate");
+  }
+  *out = g;
+  return E2B_OK;
+}
+
+int e2b_graph_replay(e2b_graph* g, void* stream) {
+  if (!g || !g->exec) return fail(E2B_EINVAL, "null graph");
+  CK(hipGraphLaunch(g->exec, reinterpret_cast<hipStream_t>(stream)), "graph launch");
+  return E2B_OK;
+}
+
+void e2b_graph_destroy(e2b_graph* g) {
+  if (!g) return;
+  if (g->exec) (void)hipGraphExecDestroy(g->exec);
+  if (g->graph) (void)hipGraphDestroy(g->graph);
+  delete g;
+}
+
+static void drop_marks(e2b_model* m) {
+  for (auto& mk : m->marks) {
+    (void)hipEventDestroy(mk.a);
+    (void)hipEventDestroy(mk.b);
+  }
+  m->marks.clear();
+}
+
+int e2b_profile_begin(e2b_model* m, int kind) {
+  if (!m) return fail(E2B_EINVAL, "null argument");
+  if (kind < E2B_KIND_NONE || kind > E2B_KIND_LM_HEAD) return fail(E2B_EINVAL, "bad kind %d", kind);
+  drop_marks(m);
+  m->prof_kind = kind;
+  return E2B_OK;
+}
+
+int e2b_profile_read(e2b_model* m, int* launches, double* total_ms, double* total_bytes) {
+  if (!m || !launches || !total_ms || !total_bytes) return fail(E2B_EINVAL, "null argument");
+  *launches = 0;
+  *total_ms = 0;
+  *total_bytes = 0;
+  for (auto& mk : m->marks) {
+    hipError_t e = hipEventSynchronize(mk.b);
+    float ms = 0;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, mk.a, mk.b);
+    if (e != hipSuccess) {
+      drop_marks(m);
+      m->prof_kind = 0;
+      return hip_fail(e, "profile read");
+    }
+    *launches += 1;
+    *total_ms += ms;
+    *total_bytes += mk.bytes;
+  }
+  drop_marks(m);
+  m->prof_kind = 0;
+  return E2B_OK;
+}
+
+int e2b_check(e2b_model* m, void* d_ws, void* stream) {
+  if (!m || !d_ws) return fail(E2B_EINVAL, "null argument");
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  CK(hipStreamSynchronize(st), "check: stream sync");
+  int w[4] = {0, 0, 0, 0};
+  CK(hipMemcpy(w, d_ws, sizeof w, hipMemcpyDeviceToHost), "check: read error word");
+  if (!w[0]) return E2B_OK;
+  const int zero[4] = {0, 0, 0, 0};
+  CK(hipMemcpy(d_ws, zero, sizeof zero, hipMemcpyHostToDevice), "check: clear error word");
+  return fail(E2B_EDEVICE, "device flagged%s%s (token %d, position %d, row %d)",
+              (w[0] & e2b::kErrToken) ? " a token outside the vocabulary" : "",
+              (w[0] & e2b::kErrPos) ? " a position outside [0, max_ctx)" : "", w[1], w[2], w[3]);
+}
+
+}  // extern "C"
