@@ -40,7 +40,8 @@ class OrcConfig(ctypes.Structure):
         "num_key_value_heads", "head_dim", "global_head_dim", "sliding_window",
         "layer_pattern_period", "intermediate_size", "use_double_wide_mlp",
         "hidden_size_per_layer_input", "vocab_size", "quant", "group_size")] + \
-        [(n, ctypes.c_double) for n in ("rms_eps", "rope_theta_sliding", "rope_theta_full")]
+        [(n, ctypes.c_double) for n in ("rms_eps", "rope_theta_sliding", "rope_theta_full")] + \
+        [("kv_bf16", ctypes.c_int)]
 
 
 def build(force: bool = False) -> str:
@@ -95,11 +96,13 @@ def _ptr(a: np.ndarray) -> int:
     return a.ctypes.data
 
 
-def make_config(cfg: dict, quant: str) -> OrcConfig:
+def make_config(cfg: dict, quant: str, kv_bf16: bool = True) -> OrcConfig:
     c = OrcConfig()
     for name, _ in OrcConfig._fields_:
         if name == "quant":
             c.quant = 1 if quant == "w4a16" else 0
+        elif name == "kv_bf16":
+            c.kv_bf16 = 1 if kv_bf16 else 0
         else:
             setattr(c, name, cfg[name])
     return c
@@ -109,14 +112,14 @@ class Oracle:
     """The C reference over one synthetic model (tensors from ``synth``)."""
 
     def __init__(self, cfg: dict, quant: str, tensors: Dict[str, np.ndarray], max_seq: int,
-                 max_ctx: int):
+                 max_ctx: int, kv_bf16: bool = True):
         self.cfg, self.quant = cfg, quant
         self.V, self.H = cfg["vocab_size"], cfg["hidden_size"]
         self._keep = {k: np.ascontiguousarray(v) for k, v in tensors.items()}
         names = list(self._keep)
         self._names = (ctypes.c_char_p * len(names))(*[n.encode() for n in names])
         self._ptrs = (ctypes.c_void_p * len(names))(*[_ptr(self._keep[n]) for n in names])
-        self._cfg = make_config(cfg, quant)
+        self._cfg = make_config(cfg, quant, kv_bf16)
         self.max_seq, self.max_ctx = max_seq, max_ctx
         h = lib().orc_create(ctypes.byref(self._cfg), len(names), self._names, self._ptrs,
                              max_seq, max_ctx)

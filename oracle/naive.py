@@ -8,7 +8,8 @@ TPU chip, eight agents", The engine):
 
 * weights are decoded to whole float64 matrices with vectorised bit ops;
 * attention is one masked score matrix per head over the whole sequence
-  (causal, plus the sliding-window band on sliding layers);
+  (causal, plus the sliding-window band on sliding layers); with kv_bf16 the
+  keys and values are rounded to bf16 as the cache stores them;
 * RoPE is a complex rotation of the (i, i + hd/2) pairs;
 * RMSNorm uses a vector norm.
 """
@@ -19,6 +20,13 @@ import numpy as np
 
 def _bf(a):
     return (np.asarray(a, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def _round_bf16(a):
+    """fp64 -> fp32 -> nearest-even bf16, back to fp64 (the cache stores bf16)."""
+    u = np.asarray(a, np.float32).view(np.uint32).astype(np.uint64)
+    u = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return u.astype(np.uint32).view(np.float32).astype(np.float64)
 
 
 def _layer_is_full(cfg, l):
@@ -59,8 +67,8 @@ def _rope(x, positions, theta):
 
 
 class Naive:
-    def __init__(self, cfg: dict, quant: str, tensors: dict):
-        self.cfg, self.quant = cfg, quant
+    def __init__(self, cfg: dict, quant: str, tensors: dict, kv_bf16: bool = True):
+        self.cfg, self.quant, self.kv_bf16 = cfg, quant, kv_bf16
         c = cfg
         self.L, self.H, self.P = c["num_hidden_layers"], c["hidden_size"], c["hidden_size_per_layer_input"]
         self.nq, self.V = c["num_attention_heads"], c["vocab_size"]
@@ -116,6 +124,8 @@ class Naive:
             if d["src"] == l:
                 k = _rope(_norm(a @ d["self_attn.k_proj"].T, d["k_norm"]), pos, d["theta"])
                 v = _norm(a @ d["self_attn.v_proj"].T)
+                if self.kv_bf16:
+                    k, v = _round_bf16(k), _round_bf16(v)
                 kv[l] = (k, v)
             k, v = kv[d["src"]]
             s = q @ k.T / np.sqrt(hd)                      # [nq, T, T]

@@ -6,7 +6,12 @@
  *
  * Everything is computed in double.  Stored weights are decoded exactly:
  * bf16 -> double is a widening; an int4 code c (offset binary, q = c - 8)
- * times its bf16 group scale is exact in double.  The K/V cache is double.
+ * times its bf16 group scale is exact in double.  The K/V cache holds double
+ * values; with kv_bf16 set (the default of the Python wrapper) each stored K
+ * and V element is rounded to bf16 first, because the pages fix the cache
+ * dtype at bf16 ("Gemma 4 E2B in JAX on One TPU v5e", Step 2: "KV cache:
+ * bf16"; "One TPU chip, eight agents", Feasibility part 1: 18.00 KiB/token
+ * at bf16).
  *
  * Sources (pages named by title; sections as printed on them):
  *  - RMSNorm in f32/f64: mean of squares, + eps, rsqrt, optional gain
@@ -40,6 +45,7 @@ typedef struct {
       layer_pattern_period, intermediate_size, use_double_wide_mlp,
       hidden_size_per_layer_input, vocab_size, quant /* 0 bf16, 1 w4a16 */, group_size;
   double rms_eps, rope_theta_sliding, rope_theta_full;
+  int kv_bf16; /* 1: K/V stored in the cache rounded to bf16 (the pages' cache dtype) */
 } orc_config;
 
 typedef struct {
@@ -74,6 +80,17 @@ const char* orc_error(void) { return g_err; }
 static double bf(uint16_t b) {
   uint32_t u = (uint32_t)b << 16;
   float f;
+  memcpy(&f, &u, 4);
+  return (double)f;
+}
+
+/* nearest-even bf16 of the fp32 value of x (the cache stores bf16) */
+static double round_bf16(double x) {
+  float f = (float)x;
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  u &= 0xFFFF0000u;
   memcpy(&f, &u, 4);
   return (double)f;
 }
@@ -362,6 +379,11 @@ int orc_step_ex(void* p, int seq, int x, int pos, int head, double* logits, doub
       orc_rope(kr, hd, pos, y->theta);
       linear(&y->v, m->a, m->kv);
       orc_rmsnorm(m->kv, hd, NULL, eps, vr);
+      if (c->kv_bf16)
+        for (int i = 0; i < hd; ++i) {
+          kr[i] = round_bf16(kr[i]);
+          vr[i] = round_bf16(vr[i]);
+        }
     }
     {
       const double* K = m->kc[y->src] + (size_t)seq * m->max_ctx * hd;

@@ -17,7 +17,8 @@ Canonical tensor format (what both consumers read):
 Distributions (synthetic random init; no trained checkpoint is used):
 
 * linear weights (bf16 mode) and both embedding tables: N(0, 0.02)
-* W4A16 codes: uniform; scales: U(0.002, 0.02)
+* W4A16 codes: uniform; scales: U(0.002, 0.02) for the toy workloads and
+  U(0.002, 0.0066) for the E2B workload (dequantized rms 0.02, as bf16)
 * RMSNorm gains: 1 + N(0, 0.02); layer scalars: U(0.5, 1.0)
 * prompt tokens: uniform over the vocabulary
 
@@ -47,7 +48,8 @@ _lib = None
 # workload presets (plain data; HF-style field names)
 # ---------------------------------------------------------------------------
 _BASE = dict(num_key_value_heads=1, layer_pattern_period=5, use_double_wide_mlp=1,
-             group_size=32, rms_eps=1e-6, rope_theta_sliding=1.0e4, rope_theta_full=1.0e6)
+             group_size=32, rms_eps=1e-6, rope_theta_sliding=1.0e4, rope_theta_full=1.0e6,
+             w4a16_scale=(0.002, 0.02))
 
 CONFIGS: Dict[str, dict] = {
     # 5 layers (4 sliding + 1 full), last 2 KV-shared, window 16
@@ -59,9 +61,13 @@ CONFIGS: Dict[str, dict] = {
                   num_attention_heads=2, head_dim=64, global_head_dim=128, sliding_window=16,
                   intermediate_size=512, hidden_size_per_layer_input=32, vocab_size=4096),
     # full E2B shape
+    # full E2B shape.  W4A16 group scales U(0.002, 0.0066): the dequantized
+    # weights then have rms 0.02, the same as the bf16 workload's N(0, 0.02)
+    # (the W4A16 workload is the bf16 one with quantized storage).
     "e2b": dict(_BASE, name="e2b", num_hidden_layers=35, num_kv_shared_layers=20, hidden_size=1536,
                 num_attention_heads=8, head_dim=256, global_head_dim=512, sliding_window=512,
-                intermediate_size=6144, hidden_size_per_layer_input=256, vocab_size=262144),
+                intermediate_size=6144, hidden_size_per_layer_input=256, vocab_size=262144,
+                w4a16_scale=(0.002, 0.0066)),
 }
 
 
@@ -195,7 +201,7 @@ def tokens(n: int, seed: int, vocab: int, stream: str = "prompt") -> np.ndarray:
 
 
 def generate(cfg: dict, quant: str = "bf16", seed: int = 0, kv_all_layers: bool = True,
-             scale_lo: float = 0.002, scale_hi: float = 0.02) -> Dict[str, np.ndarray]:
+             scale_lo: float = None, scale_hi: float = None) -> Dict[str, np.ndarray]:
     """All tensors of one synthetic model, keyed by canonical name.
 
     quant "bf16": linears are ``<name>`` bf16 [N, K].
@@ -205,6 +211,9 @@ def generate(cfg: dict, quant: str = "bf16", seed: int = 0, kv_all_layers: bool 
     """
     assert quant in ("bf16", "w4a16")
     G = cfg["group_size"]
+    lo, hi = cfg.get("w4a16_scale", (0.002, 0.02))
+    scale_lo = lo if scale_lo is None else scale_lo
+    scale_hi = hi if scale_hi is None else scale_hi
     out: Dict[str, np.ndarray] = {}
     for s in tensor_specs(cfg, kv_all_layers=kv_all_layers):
         if s.kind == "embed":

@@ -1,5 +1,8 @@
 """GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
 
+The oracle stores K/V rounded to bf16, as the cache the pages describe does
+(the GPU path stores bf16 K/V too); everything else in it is fp64.
+
 Tolerances (fixed by the workload definition, not tuned):
   * int4 unpack, gathers, K/V-share identity: bit-exact;
   * logits: max |GPU - oracle| <= 2e-2 (bf16) / 3e-2 (W4A16) of max |oracle logit|;
@@ -109,7 +112,8 @@ def test_matvec_one_hot_is_exact(torch_dev, quant, N, K):
     else:
         w = synth.bits32((N, K // 8), seed, "w")
         scale = synth.uniform_bf16((N, K // 32), seed, "s", 0.002, 0.02)
-    ks = sorted(set([0, 1, 7, 8, 31, 32, 33, K // 2, K - 1] + list(range(3, K, max(1, K // 13)))))
+    ks = sorted(k for k in set([0, 1, 7, 8, 31, 32, 33, K // 2, K - 1] +
+                                list(range(3, K, max(1, K // 13)))) if k < K)
     x = np.zeros((len(ks), K), np.float32)
     for r, k in enumerate(ks):
         x[r, k] = 1.0
@@ -128,8 +132,10 @@ def test_matvec_one_hot_is_exact(torch_dev, quant, N, K):
 @pytest.mark.parametrize("N,K,rows", [(1536, 1536, 1), (2560, 1536, 3), (1536, 4096, 1),
                                       (1536, 12288, 2), (160, 256, 5), (32, 32, 1)])
 def test_matvec_random_matches_oracle(torch_dev, quant, N, K, rows):
-    """Random x: |y - y_oracle| <= 1e-4 * sum_k |w_nk x_k| (x carried as a bf16
-    hi/lo pair, ~2^-17 relative, plus fp32 accumulation)."""
+    """Random x: |y - y_oracle| <= c * sum_k |w_nk x_k|.  x is carried as a bf16
+    hi/lo pair (<= 2^-18 relative) and sums are fp32: c = 1e-5 for bf16 weights
+    (a dropped lo part would show as ~2^-9); for W4A16 the biased code sums
+    (128 + c) x cancel against 136 sum x, worst case ~6e-5, so c = 1e-4."""
     torch, dev = torch_dev
     from w4a16_weight_streaming_amd import matvec
     rng = np.random.default_rng(K + N)
@@ -150,7 +156,8 @@ def test_matvec_random_matches_oracle(torch_dev, quant, N, K, rows):
     for r in range(rows):
         ref = oracle.linear(quant, w, scale, N, K, x[r].astype(np.float64))
         nb = wd.shape[0]
-        bound = 1e-4 * (np.abs(wd) @ np.abs(x[r].astype(np.float64)))
+        c = 1e-5 if quant == "bf16" else 1e-4
+        bound = c * (np.abs(wd) @ np.abs(x[r].astype(np.float64)))
         assert np.all(np.abs(got[r, :nb] - ref[:nb]) <= bound + 1e-30)
         scale_all = np.max(np.abs(ref))
         assert np.max(np.abs(got[r] - ref)) <= 1e-4 * scale_all * np.sqrt(K)
@@ -236,13 +243,25 @@ def test_kv_sharing_and_cache_contents(torch_dev):
         for which in (0, 1):
             assert eng.kv_view(l, which) == eng.kv_view(smap[l], which)
             assert orc.kv_source(l) == smap[l]
+    # layer 0's K/V depend on the token alone: at most one bf16 ulp from the
+    # oracle (the rounding sees fp32 vs fp64 inputs), almost always equal.
+    # Later layers also carry the effect of such one-ulp differences at earlier
+    # positions through attention, so they are held to a vector-relative bound.
+    exact = total = 0
     for l in sorted(set(smap)):
         hd = synth.layer_head_dim(cfg, l)
         for which in (0, 1):
             got = synth.bf16_to_f32(eng.kv_tensor(l, which, hd)[0, :12].cpu().numpy().view(np.uint16))
             for pos in range(12):
-                ref = orc.kv_row(l, which, 0, pos, hd)
-                assert np.max(np.abs(got[pos] - ref)) <= 2 ** -8 * np.max(np.abs(ref)) + 1e-6
+                ref = orc.kv_row(l, which, 0, pos, hd)     # already bf16-valued
+                if l == 0:
+                    tol = 2.0 ** -7 * np.abs(ref) + 1e-5 * np.max(np.abs(ref))
+                    exact += int(np.sum(got[pos] == ref))
+                    total += hd
+                else:
+                    tol = 2.0 ** -7 * np.abs(ref) + 2e-3 * np.max(np.abs(ref))
+                assert np.all(np.abs(got[pos] - ref) <= tol), (l, which, pos)
+    assert exact >= 0.99 * total, (exact, total)
 
 
 def test_deterministic_replay(torch_dev):

@@ -179,6 +179,26 @@ def test_shared_layers_read_their_source_kv():
                 assert np.array_equal(o.kv_row(l, which, 0, p, hd), o.kv_row(src, which, 0, p, hd))
 
 
+def test_bf16_cache_rounds_stored_kv():
+    """With the bf16 cache, stored K/V are bf16 values: the nearest-even bf16 of
+    what the fp64 cache stores for the same inputs (layer 0, position 0)."""
+    cfg, w = _small("toy", "bf16")
+    a = oracle.Oracle(cfg, "bf16", w, 1, 8, kv_bf16=False)
+    b = oracle.Oracle(cfg, "bf16", w, 1, 8, kv_bf16=True)
+    for o in (a, b):
+        for p, t in enumerate((5, 9, 11)):
+            o.step(0, t, p, logits=False)
+    hd = synth.layer_head_dim(cfg, 0)
+    for which in (0, 1):
+        full = a.kv_row(0, which, 0, 0, hd)
+        rounded = b.kv_row(0, which, 0, 0, hd)
+        assert not np.array_equal(full, rounded)
+        assert np.array_equal(rounded, synth.bf16_to_f32(synth.f32_to_bf16(full.astype(np.float32))))
+        for p in range(3):
+            r = b.kv_row(2, which, 0, p, hd)
+            assert np.array_equal(r, synth.bf16_to_f32(synth.f32_to_bf16(r.astype(np.float32))))
+
+
 def test_sliding_equals_full_within_window():
     toks = synth.tokens(16, 9, 4096)
     cfg_w, w = _small("toy10", "w4a16")
@@ -221,12 +241,14 @@ def test_per_layer_inputs_closed_forms():
 # ---------------------------------------------------------------- cached vs brute force
 @pytest.mark.parametrize("name", ["toy", "toy10"])
 @pytest.mark.parametrize("quant", ["bf16", "w4a16"])
-def test_cached_oracle_matches_bruteforce(name, quant):
+@pytest.mark.parametrize("kv_bf16", [True, False])
+def test_cached_oracle_matches_bruteforce(name, quant, kv_bf16):
     """Cached decode == re-running the whole sequence (tolerance: fp64 roundoff),
-    across the sliding-window edge (sequence 26 > window 16)."""
+    across the sliding-window edge (sequence 26 > window 16), with the cache
+    in bf16 and in fp64."""
     cfg, w = _small(name, quant)
-    o = oracle.Oracle(cfg, quant, w, 2, 40)
-    nv = Naive(cfg, quant, w)
+    o = oracle.Oracle(cfg, quant, w, 2, 40, kv_bf16=kv_bf16)
+    nv = Naive(cfg, quant, w, kv_bf16=kv_bf16)
     toks = list(synth.tokens(26, 11, cfg["vocab_size"]))
     ref = nv.forward(toks)
     for p, t in enumerate(toks):
