@@ -203,26 +203,37 @@ def test_wide_heads_long_window(torch_dev):
 
 
 def test_prefill_equals_decode_loop_bitwise(torch_dev):
-    """A prefill pass computes each row exactly as a decode step does."""
+    """A prefill pass computes each row exactly as one-token passes do, and
+    the decode path (which writes its own K/V inside the attention kernel)
+    produces the same cache bits and logits as prefill."""
     torch, dev = torch_dev
     cfg = synth.get_config("toy10")
     w = synth.generate(cfg, "w4a16", seed=5)
     V = cfg["vocab_size"]
     p = synth.tokens(20, 9, V)
-    eng = _engine(cfg, "w4a16", w, 2, 32, 32)
+    eng = _engine(cfg, "w4a16", w, 3, 48, 32)
     a = torch.zeros(1, dtype=torch.int32, device=dev)
     l_pre = torch.zeros(1, V, dtype=torch.float32, device=dev)
     eng.prefill(0, torch.from_numpy(p).to(dev), 0, a, l_pre)
-    l_dec = torch.zeros(1, V, dtype=torch.float32, device=dev)
+    l_one = torch.zeros(1, V, dtype=torch.float32, device=dev)
     for i, t in enumerate(p):   # same tokens, one by one, into cache row 1
-        eng.prefill(1, torch.tensor([t], dtype=torch.int32, device=dev), i, a, l_dec)
+        eng.prefill(1, torch.tensor([t], dtype=torch.int32, device=dev), i, a, l_one)
+    # decode path into cache row 2 (rows 0 and 1 decode at positions 20.. meanwhile)
+    a3 = torch.zeros(3, dtype=torch.int32, device=dev)
+    l_dec = torch.zeros(3, V, dtype=torch.float32, device=dev)
+    for i, t in enumerate(p):
+        tok = torch.tensor([t, t, t], dtype=torch.int32, device=dev)
+        pos = torch.tensor([20 + i, 20 + i, i], dtype=torch.int32, device=dev)
+        eng.decode_step(tok, pos, a3, l_dec)
     eng.check()
-    assert torch.equal(l_pre, l_dec)
+    assert torch.equal(l_pre, l_one)
+    assert torch.equal(l_pre[0], l_dec[2])
     for l in range(cfg["num_hidden_layers"]):
         hd = synth.layer_head_dim(cfg, l)
         for which in (0, 1):
             kv = eng.kv_tensor(l, which, hd)
             assert torch.equal(kv[0, :20], kv[1, :20])
+            assert torch.equal(kv[0, :20], kv[2, :20])
 
 
 def test_kv_sharing_and_cache_contents(torch_dev):

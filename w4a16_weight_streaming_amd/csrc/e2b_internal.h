@@ -75,12 +75,19 @@ struct Epilogue {
 };
 
 struct AttnArgs {
-  const float* q = nullptr;     // normed, rotated queries [rows][nq][hd] fp32
-  const uint16_t* kc = nullptr; // K cache of the source layer [max_batch][max_ctx][hd]
+  const float* qkv = nullptr;   // raw projections [rows][(nq + 2 * (kc_own != null)) * hd]
+  const uint16_t* gq = nullptr; // q_norm gain
+  const uint16_t* gk = nullptr; // k_norm gain (own K/V)
+  const double* inv_freq = nullptr;  // [hd/2]
+  const uint16_t* kc = nullptr; // K cache read (the source layer's) [max_batch][max_ctx][hd]
   const uint16_t* vc = nullptr;
+  uint16_t* kc_own = nullptr;   // decode: cache to write this position's K/V into (layer owns
+  uint16_t* vc_own = nullptr;   // K/V); null when the layer shares or the K/V are already written
   float* part = nullptr;        // [rows][nq][kMaxChunks][hd + 2]
   float* out = nullptr;         // [rows][nq * hd]
   int nq = 0, hd = 0, window = 0 /* 0: full */, chunk = 0, nchunk = 0;
+  int owns = 0;                 // the layer computes K/V (raw rows hold q, k, v)
+  float eps = 1e-6f;
 };
 
 struct QkvPostArgs {

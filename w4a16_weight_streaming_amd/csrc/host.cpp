@@ -285,7 +285,7 @@ Ws ws_layout(const e2b_model* m, int R) {
 
 void attn_chunks(const e2b_model* m, bool full, int* chunk, int* nchunk) {
   const int span = full ? m->max_ctx : std::min(m->c.sliding_window, m->max_ctx);
-  int n = (span + 15) / 16;
+  int n = (span + 31) / 32;
   if (n > e2b::kMaxChunks) n = e2b::kMaxChunks;
   if (n < 1) n = 1;
   *nchunk = n;
@@ -366,30 +366,40 @@ int run_rows(e2b_model* m, const e2b::Rows& R, bool head, int head_row, float* d
       CK(gemv(m, q, kTagQkv, d.qkv, n, pr, ep, nullptr, st), "qkv projection");
       if (pend) std::swap(cur, oth);
     }
-    {
+    // decode rows are distinct sequences: the attention kernel writes the new
+    // K/V itself; prefill rows attend to each other's K/V, written first
+    const bool fused_kv = R.seq_stride != 0;
+    if (owns && !fused_kv) {
       QkvPostArgs a;
       a.qkv = F(W.qkv);
       a.gq = d.g_q;
       a.gk = d.g_k;
       a.inv_freq = m->invf[y.full];
       a.q_out = F(W.qn);
-      a.kc = owns ? m->kc[l] : nullptr;
-      a.vc = owns ? m->vc[l] : nullptr;
+      a.kc = m->kc[l];
+      a.vc = m->vc[l];
       a.nq = m->nq;
       a.hd = y.hd;
       a.eps = eps;
-      CK(launch_qkv_post(R, a, st), "head norms / rope / kv write");
+      CK(launch_qkv_post(R, a, st), "k/v write");
     }
     {
       AttnArgs a;
-      a.q = F(W.qn);
+      a.qkv = F(W.qkv);
+      a.gq = d.g_q;
+      a.gk = d.g_k;
+      a.inv_freq = m->invf[y.full];
       a.kc = m->kc[y.src];
       a.vc = m->vc[y.src];
+      a.kc_own = (owns && fused_kv) ? m->kc[l] : nullptr;
+      a.vc_own = (owns && fused_kv) ? m->vc[l] : nullptr;
+      a.owns = owns;
       a.part = F(W.part);
       a.out = F(W.attn);
       a.nq = m->nq;
       a.hd = y.hd;
       a.window = y.full ? 0 : m->c.sliding_window;
+      a.eps = eps;
       attn_chunks(m, y.full, &a.chunk, &a.nchunk);
       CK(launch_attention(R, a, st), "attention");
     }

@@ -146,163 +146,259 @@ struct Lay {
   static_assert(64 % S == 0, "lanes per row must divide the wave");
 };
 
-// Build the block's fp32 input slice xs[0..KS) for row b (slice k0..k0+KS).
+// The block's fp32 input slice xs[0..KS) for row b (K slice k0..k0+KS), in two
+// halves: load() issues every global read the prologue needs at once (one
+// round trip; the weight prefetch is issued after it), finish() does the
+// arithmetic and writes xs.
 template <int KS>
-__device__ void build_x(const Prologue& p, int rows, int b, int k0, int K, float* xs,
-                        float* red) {
-  const int t = threadIdx.x;
-  if (p.kind == kPlain) {
-    for (int i = t; i < KS; i += kGemvThreads) xs[i] = p.a[(size_t)b * p.lda + k0 + i];
-  } else if (p.kind == kGeglu) {
-    for (int i = t; i < KS; i += kGemvThreads) {
-      const float g = p.a[(size_t)b * p.lda + k0 + i];
-      const float u = p.a[(size_t)b * p.lda + K + k0 + i];
-      xs[i] = gelu_tanh(g) * u;
-    }
-  } else if (p.kind == kPleGate) {
-    for (int i = t; i < KS; i += kGemvThreads)
-      xs[i] = gelu_tanh(p.a[(size_t)b * p.lda + k0 + i]) * p.pli[(size_t)b * p.pli_ld + k0 + i];
-  } else {  // kRes / kResNorm: KS == K == hidden size (host guarantees)
-    constexpr int PT = (KS + kGemvThreads - 1) / kGemvThreads;
-    float dv[PT];
-    float ss = 0.f;
+struct PrologueRegs {
+  static constexpr int PT = (KS + kGemvThreads - 1) / kGemvThreads;
+  float a0[PT], a1[PT], g0[PT], g1[PT];
+  float dq[PT][kMaxSplitK];
+
+  __device__ __forceinline__ void load(const Prologue& p, int rows, int b, int k0, int K) {
+    const int t = threadIdx.x;
 #pragma unroll
     for (int j = 0; j < PT; ++j) {
       const int i = t + j * kGemvThreads;
-      float s = 0.f;
-      if (i < KS && p.d)
-        for (int q = 0; q < p.nd; ++q) s += p.d[((size_t)q * rows + b) * K + i];
-      dv[j] = s;
-      ss += s * s;
-    }
-    float rd = 0.f;
-    if (p.d) rd = rsqrtf(block_sum<kGemvThreads>(ss, red) / (float)K + p.eps);
-    const float sc = p.scalar ? bf2f(p.scalar[0]) : 1.0f;
-    const bool store = p.d && p.h_out && blockIdx.x == 0 && blockIdx.y == 0;
-    float hs = 0.f;
+      a0[j] = a1[j] = g0[j] = g1[j] = 0.f;
 #pragma unroll
-    for (int j = 0; j < PT; ++j) {
-      const int i = t + j * kGemvThreads;
-      if (i < KS) {
-        float hn = p.a[(size_t)b * K + i];
-        if (p.d) hn = (hn + dv[j] * rd * bf2f(p.gd[i])) * sc;
-        xs[i] = hn;
-        hs += hn * hn;
-        if (store) p.h_out[(size_t)b * K + i] = hn;
+      for (int q = 0; q < kMaxSplitK; ++q) dq[j][q] = 0.f;
+      if (i >= KS) continue;
+      if (p.kind == kPlain) {
+        a0[j] = p.a[(size_t)b * p.lda + k0 + i];
+      } else if (p.kind == kGeglu) {
+        a0[j] = p.a[(size_t)b * p.lda + k0 + i];
+        a1[j] = p.a[(size_t)b * p.lda + K + k0 + i];
+      } else if (p.kind == kPleGate) {
+        a0[j] = p.a[(size_t)b * p.lda + k0 + i];
+        a1[j] = p.pli[(size_t)b * p.pli_ld + k0 + i];
+      } else {  // kRes / kResNorm: KS == K == hidden size
+        a0[j] = p.a[(size_t)b * K + i];
+        if (p.d) {
+#pragma unroll
+          for (int q = 0; q < kMaxSplitK; ++q)
+            if (q < p.nd) dq[j][q] = p.d[((size_t)q * rows + b) * K + i];
+          g0[j] = bf2f(p.gd[i]);
+        }
+        if (p.kind == kResNorm) g1[j] = bf2f(p.gx[i]);
       }
     }
-    if (p.kind == kResNorm) {
-      const float rh = rsqrtf(block_sum<kGemvThreads>(hs, red) / (float)K + p.eps);
-      for (int i = t; i < KS; i += kGemvThreads) xs[i] = xs[i] * rh * bf2f(p.gx[i]);
+  }
+
+  __device__ __forceinline__ void finish(const Prologue& p, int b, int K, float* xs, float* red) {
+    const int t = threadIdx.x;
+    if (p.kind == kPlain) {
+#pragma unroll
+      for (int j = 0; j < PT; ++j)
+        if (t + j * kGemvThreads < KS) xs[t + j * kGemvThreads] = a0[j];
+    } else if (p.kind == kGeglu || p.kind == kPleGate) {
+#pragma unroll
+      for (int j = 0; j < PT; ++j)
+        if (t + j * kGemvThreads < KS) xs[t + j * kGemvThreads] = gelu_tanh(a0[j]) * a1[j];
+    } else {
+      float dv[PT], ss = 0.f;
+#pragma unroll
+      for (int j = 0; j < PT; ++j) {
+        float s = 0.f;
+#pragma unroll
+        for (int q = 0; q < kMaxSplitK; ++q) s += dq[j][q];
+        dv[j] = s;
+        ss += s * s;
+      }
+      float rd = 0.f;
+      if (p.d) rd = rsqrtf(block_sum<kGemvThreads>(ss, red) / (float)K + p.eps);
+      const float sc = p.scalar ? bf2f(p.scalar[0]) : 1.0f;
+      const bool store = p.d && p.h_out && blockIdx.x == 0 && blockIdx.y == 0;
+      float hv[PT], hs = 0.f;
+#pragma unroll
+      for (int j = 0; j < PT; ++j) {
+        const int i = t + j * kGemvThreads;
+        float hn = a0[j];
+        if (p.d) hn = (hn + dv[j] * rd * g0[j]) * sc;
+        hv[j] = hn;
+        if (i < KS) {
+          hs += hn * hn;
+          if (store) p.h_out[(size_t)b * K + i] = hn;
+        }
+      }
+      if (p.kind == kResNorm) {
+        const float rh = rsqrtf(block_sum<kGemvThreads>(hs, red) / (float)K + p.eps);
+#pragma unroll
+        for (int j = 0; j < PT; ++j)
+          if (t + j * kGemvThreads < KS) xs[t + j * kGemvThreads] = hv[j] * rh * g1[j];
+      } else {
+#pragma unroll
+        for (int j = 0; j < PT; ++j)
+          if (t + j * kGemvThreads < KS) xs[t + j * kGemvThreads] = hv[j];
+      }
+    }
+    __syncthreads();
+  }
+};
+
+// split an fp32 pair into a bf16 hi pair and a bf16 lo pair (x = hi + lo)
+__device__ __forceinline__ void split_pair(float a, float b, uint32_t& hi, uint32_t& lo) {
+  const uint32_t ha = f2bf(a), hb = f2bf(b);
+  const uint32_t la = f2bf(a - bf2f(ha)), lb = f2bf(b - bf2f(hb));
+  hi = ha | (hb << 16);
+  lo = la | (lb << 16);
+}
+
+// LDS words of the packed input: bf16 layout 8 words per (chunk, lane slot)
+// [4 hi pairs | 4 lo pairs]; W4A16 layout 36 words per 32-group
+// [16 hi pairs | 16 lo pairs | group sum | pad].
+template <int WQ, int KS>
+struct Packed {
+  static constexpr int kWordsW4 = 36;
+  static constexpr int words = WQ ? (KS / 32) * kWordsW4 : KS;
+};
+
+// xs (fp32, KS) -> xp (packed pairs in the order lanes consume them)
+template <int WQ, int KS>
+__device__ void pack_x(const float* xs, uint32_t* xp) {
+  using Y = Lay<WQ, KS>;
+  for (int p = threadIdx.x; p < KS / 2; p += kGemvThreads) {
+    uint32_t hi, lo;
+    if (WQ) {
+      const int g = p / 16, q = p % 16, j = q / 4, i = q % 4;
+      const int k = 32 * g + 8 * j + i;  // pair (k, k + 4) matches the nibble unpack
+      split_pair(xs[k], xs[k + 4], hi, lo);
+      xp[g * Packed<WQ, KS>::kWordsW4 + q] = hi;
+      xp[g * Packed<WQ, KS>::kWordsW4 + 16 + q] = lo;
+    } else {
+      const int k = 2 * p, c = k / 512, o = k % 512, ls = o / 8, j = (o % 8) / 2;
+      split_pair(xs[k], xs[k + 1], hi, lo);
+      xp[(c * Y::S + ls) * 8 + j] = hi;
+      xp[(c * Y::S + ls) * 8 + 4 + j] = lo;
+    }
+  }
+  if (WQ) {
+    __syncthreads();
+    for (int g = threadIdx.x; g < KS / 32; g += kGemvThreads) {
+      float s = 0.f;
+      for (int q = 0; q < 16; ++q) {
+        const uint32_t hi = xp[g * Packed<WQ, KS>::kWordsW4 + q];
+        const uint32_t lo = xp[g * Packed<WQ, KS>::kWordsW4 + 16 + q];
+        s += (bf2f(hi) + bf2f(lo)) + (bf2f(hi >> 16) + bf2f(lo >> 16));
+      }
+      xp[g * Packed<WQ, KS>::kWordsW4 + 32] = __float_as_uint(s);
     }
   }
   __syncthreads();
 }
 
-// split an fp32 pair into bf16 hi pair and bf16 lo pair
-__device__ __forceinline__ void split_pair(float a, float b, uint32_t& hi, uint32_t& lo,
-                                           float& sum) {
-  const uint32_t ha = f2bf(a), hb = f2bf(b);
-  const float ra = a - bf2f(ha), rb = b - bf2f(hb);
-  const uint32_t la = f2bf(ra), lb = f2bf(rb);
-  hi = ha | (hb << 16);
-  lo = la | (lb << 16);
-  sum += (bf2f(ha) + bf2f(la)) + (bf2f(hb) + bf2f(lb));
-}
-
-// TAG only names the kernel after the matrix it streams (QKV, O, gate/up, ...)
-// so that per-kernel profiles separate them; the code is identical.
 template <int WQ, int KS, int U, int TAG>
 __global__ __launch_bounds__(kGemvThreads) void k_gemv(Lin W, int rows, Prologue pro,
                                                        Epilogue epi) {
   using Y = Lay<WQ, KS>;
   extern __shared__ float smem[];
-  float* xs = smem;       // KS
-  float* red = smem + KS; // 8 floats of reduction scratch + 16 for argmax
+  float* xs = smem;                                              // KS floats
+  uint32_t* xp = reinterpret_cast<uint32_t*>(smem + KS);         // packed pairs
+  float* red = smem + KS + Packed<WQ, KS>::words;                // reduction scratch
   const int ks = blockIdx.y, b = blockIdx.z;
   const int K = W.K, N = W.N;
-  build_x<KS>(pro, rows, b, ks * KS, K, xs, red);
-
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int ls = lane % Y::S, rsub = lane / Y::S;
+  const int NU = (N + Y::RPL - 1) / Y::RPL;
+  const int stride = gridDim.x * 4;
+  const size_t ldq = (size_t)K / 8, lds = (size_t)K / 32;
 
-  // x of this lane as bf16 hi/lo pairs (and group sums for W4A16)
+  // A batch is U units (RPL rows each) of this wave; batches are double
+  // buffered: batch i+1 is requested before batch i is reduced.
+  struct Batch {
+    uint4 wv[U][Y::C];
+    float sc[U][Y::C];
+    int n[U];
+  };
+  auto load_batch = [&](Batch& B, int u0) {
+#pragma unroll
+    for (int uu = 0; uu < U; ++uu) {
+      const int u = u0 + uu * stride;
+      B.n[uu] = u * Y::RPL + rsub;
+      const bool ok = (u < NU) && (B.n[uu] < N);
+#pragma unroll
+      for (int c = 0; c < Y::C; ++c) {
+        B.wv[uu][c] = make_uint4(0, 0, 0, 0);
+        B.sc[uu][c] = 0.f;
+        if (ok) {
+          if (WQ) {
+            const int g = ls + Y::S * c;
+            B.wv[uu][c] = *reinterpret_cast<const uint4*>(W.q + (size_t)B.n[uu] * ldq +
+                                                          (size_t)ks * (KS / 8) + 4 * g);
+            B.sc[uu][c] = bf2f(W.s[(size_t)B.n[uu] * lds + (size_t)ks * Y::G + g]);
+          } else {
+            B.wv[uu][c] = *reinterpret_cast<const uint4*>(W.w + (size_t)B.n[uu] * K +
+                                                          (size_t)ks * KS + 512 * c + 8 * ls);
+          }
+        }
+      }
+    }
+  };
+
+  PrologueRegs<KS> pr;
+  pr.load(pro, rows, b, ks * KS, K);  // input reads first: they gate the compute
+  int u0 = blockIdx.x * 4 + wave;
+  Batch A, Bq;
+  load_batch(A, u0);                  // then the weights (independent of x)
+  pr.finish(pro, b, K, xs, red);
+  pack_x<WQ, KS>(xs, xp);
+
+  // this lane's x pairs (and group sums for W4A16), read once
   uint32_t xh[Y::NP], xl[Y::NP];
   float gsum[Y::C];
 #pragma unroll
   for (int c = 0; c < Y::C; ++c) {
-    gsum[c] = 0.f;
     if (WQ) {
-      const int g = ls + Y::S * c;
+      const uint4* src = reinterpret_cast<const uint4*>(xp + (ls + Y::S * c) * Packed<WQ, KS>::kWordsW4);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int k = 32 * g + 8 * j + i;  // pair (k, k + 4): matches the nibble unpack
-          split_pair(xs[k], xs[k + 4], xh[c * 16 + j * 4 + i], xl[c * 16 + j * 4 + i], gsum[c]);
-        }
-    } else {
-      const int k0 = 512 * c + 8 * ls;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float dummy = 0.f;
-        split_pair(xs[k0 + 2 * j], xs[k0 + 2 * j + 1], xh[c * 4 + j], xl[c * 4 + j], dummy);
+      for (int v = 0; v < 4; ++v) {
+        const uint4 h4 = src[v], l4 = src[4 + v];
+        xh[c * 16 + 4 * v + 0] = h4.x; xh[c * 16 + 4 * v + 1] = h4.y;
+        xh[c * 16 + 4 * v + 2] = h4.z; xh[c * 16 + 4 * v + 3] = h4.w;
+        xl[c * 16 + 4 * v + 0] = l4.x; xl[c * 16 + 4 * v + 1] = l4.y;
+        xl[c * 16 + 4 * v + 2] = l4.z; xl[c * 16 + 4 * v + 3] = l4.w;
       }
+      gsum[c] = __uint_as_float(xp[(ls + Y::S * c) * Packed<WQ, KS>::kWordsW4 + 32]);
+    } else {
+      const uint4* src = reinterpret_cast<const uint4*>(xp + (c * Y::S + ls) * 8);
+      const uint4 h4 = src[0], l4 = src[1];
+      xh[c * 4 + 0] = h4.x; xh[c * 4 + 1] = h4.y; xh[c * 4 + 2] = h4.z; xh[c * 4 + 3] = h4.w;
+      xl[c * 4 + 0] = l4.x; xl[c * 4 + 1] = l4.y; xl[c * 4 + 2] = l4.z; xl[c * 4 + 3] = l4.w;
+      gsum[c] = 0.f;
     }
   }
 
-  const int NU = (N + Y::RPL - 1) / Y::RPL;
-  const int stride = gridDim.x * 4;
   float best = -FLT_MAX;
   int bidx = 0x7FFFFFFF;
-  const size_t ldq = (size_t)K / 8, lds = (size_t)K / 32;
-
-  for (int u0 = blockIdx.x * 4 + wave; u0 < NU; u0 += stride * U) {
-    uint4 wv[U][Y::C];
-    float sc[U][Y::C];
-    int n[U];
-#pragma unroll
-    for (int uu = 0; uu < U; ++uu) {
-      const int u = u0 + uu * stride;
-      n[uu] = u * Y::RPL + rsub;
-      const bool ok = (u < NU) && (n[uu] < N);
-#pragma unroll
-      for (int c = 0; c < Y::C; ++c) {
-        if (ok) {
-          if (WQ) {
-            const int g = ls + Y::S * c;
-            const uint32_t* src = W.q + (size_t)n[uu] * ldq + (size_t)ks * (KS / 8) + 4 * g;
-            wv[uu][c] = *reinterpret_cast<const uint4*>(src);
-            sc[uu][c] = bf2f(W.s[(size_t)n[uu] * lds + (size_t)ks * Y::G + g]);
-          } else {
-            const uint16_t* src = W.w + (size_t)n[uu] * K + (size_t)ks * KS + 512 * c + 8 * ls;
-            wv[uu][c] = *reinterpret_cast<const uint4*>(src);
-            sc[uu][c] = 0.f;
-          }
-        } else {
-          wv[uu][c] = make_uint4(0, 0, 0, 0);
-          sc[uu][c] = 0.f;
-        }
-      }
-    }
+  auto reduce_batch = [&](const Batch& B, int ub) {
 #pragma unroll
     for (int uu = 0; uu < U; ++uu) {
       float acc = 0.f;
 #pragma unroll
       for (int c = 0; c < Y::C; ++c) {
-        const uint32_t w4[4] = {wv[uu][c].x, wv[uu][c].y, wv[uu][c].z, wv[uu][c].w};
+        const uint32_t w4[4] = {B.wv[uu][c].x, B.wv[uu][c].y, B.wv[uu][c].z, B.wv[uu][c].w};
         if (WQ) {
           float a = 0.f;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const uint32_t p = ((w4[j] >> (4 * i)) & 0x000F000Fu) | 0x43004300u;
-              a = dot2(p, xh[c * 16 + j * 4 + i], a);
-              a = dot2(p, xl[c * 16 + j * 4 + i], a);
-            }
+            // bytes of lo: codes 6,4,2,0 of the word; bytes of hi: codes 7,5,3,1.
+            // v_perm puts two codes under the bf16 exponent byte 0x43 (128 + c).
+            const uint32_t lo = w4[j] & 0x0F0F0F0Fu, hi = (w4[j] >> 4) & 0x0F0F0F0Fu;
+            const uint32_t p0 = __builtin_amdgcn_perm(0x43434343u, lo, 0x04020400u);  // codes 0, 4
+            const uint32_t p1 = __builtin_amdgcn_perm(0x43434343u, hi, 0x04020400u);  // codes 1, 5
+            const uint32_t p2 = __builtin_amdgcn_perm(0x43434343u, lo, 0x04030401u);  // codes 2, 6
+            const uint32_t p3 = __builtin_amdgcn_perm(0x43434343u, hi, 0x04030401u);  // codes 3, 7
+            a = dot2(p0, xh[c * 16 + j * 4 + 0], a);
+            a = dot2(p0, xl[c * 16 + j * 4 + 0], a);
+            a = dot2(p1, xh[c * 16 + j * 4 + 1], a);
+            a = dot2(p1, xl[c * 16 + j * 4 + 1], a);
+            a = dot2(p2, xh[c * 16 + j * 4 + 2], a);
+            a = dot2(p2, xl[c * 16 + j * 4 + 2], a);
+            a = dot2(p3, xh[c * 16 + j * 4 + 3], a);
+            a = dot2(p3, xl[c * 16 + j * 4 + 3], a);
           }
-          acc += sc[uu][c] * (a - 136.0f * gsum[c]);
+          acc += B.sc[uu][c] * (a - 136.0f * gsum[c]);
         } else {
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
@@ -313,19 +409,30 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv(Lin W, int rows, Prologue
       }
 #pragma unroll
       for (int o = Y::S / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
-      const int u = u0 + uu * stride;
-      if (ls == 0 && u < NU && n[uu] < N) {
+      const int u = ub + uu * stride;
+      const int nn = B.n[uu];
+      if (ls == 0 && u < NU && nn < N) {
         if (epi.argmax) {
-          if (epi.logits) epi.logits[(size_t)b * N + n[uu]] = acc;
-          if (acc > best || (acc == best && n[uu] < bidx)) {
+          if (epi.logits) epi.logits[(size_t)b * N + nn] = acc;
+          if (acc > best || (acc == best && nn < bidx)) {
             best = acc;
-            bidx = n[uu];
+            bidx = nn;
           }
         } else {
-          epi.y[((size_t)ks * rows + b) * N + n[uu]] = acc;
+          epi.y[((size_t)ks * rows + b) * N + nn] = acc;
         }
       }
     }
+  };
+  while (u0 < NU) {
+    const int u1 = u0 + stride * U;
+    if (u1 < NU) load_batch(Bq, u1);
+    reduce_batch(A, u0);
+    if (u1 >= NU) break;
+    const int u2 = u1 + stride * U;
+    if (u2 < NU) load_batch(A, u2);
+    reduce_batch(Bq, u1);
+    u0 = u2;
   }
 
   if (epi.argmax) {
@@ -379,11 +486,16 @@ static hipError_t run_gemv(const Lin& W, int rows, const Prologue& pro, const Ep
   using Y = Lay<WQ, KS>;
   const int nks = W.K / KS;
   const int NU = (W.N + Y::RPL - 1) / Y::RPL;
-  int bx = blocks_hint > 0 ? blocks_hint : (NU + 4 * U - 1) / (4 * U);
-  if (bx > 1024) bx = 1024;
+  // one unit per wave when N is small (latency); at most ~512 blocks in all
+  // (two per CU, K slices and rows included) so that every block is resident
+  // and waves of large matrices stream many units back to back
+  int cap = 512 / (nks * rows);
+  if (cap < 1) cap = 1;
+  int bx = blocks_hint > 0 ? blocks_hint : (NU + 3) / 4;
+  if (bx > cap) bx = cap;
   if (bx < 1) bx = 1;
   if (blocks_out) *blocks_out = bx;
-  const size_t shm = (size_t)KS * sizeof(float) + 32 * sizeof(float);
+  const size_t shm = ((size_t)KS + Packed<WQ, KS>::words + 32) * sizeof(float);
   hipLaunchKernelGGL((k_gemv<WQ, KS, U, TAG>), dim3(bx, nks, rows), dim3(kGemvThreads), shm, st,
                      W, rows, pro, epi);
   return hipGetLastError();
@@ -431,79 +543,124 @@ hipError_t launch_gemv(int quant, int tag, const Lin& W, int rows, const Prologu
                : dispatch_tag<0>(tag, W, rows, pro, epi, blocks_hint, blocks_out, st);
 }
 
-// ------------------------------------------------ head norms, RoPE, K/V write
-// One block per (row, head).  Heads 0..nq-1 are queries; when the layer owns
-// its K/V, head nq is the key and nq+1 the value.  Keys and queries: RMS norm
-// with gain, then rotate-half RoPE at the logical position; values: RMS norm
-// without gain.  K/V go to the cache slot = position, as bf16.
-__global__ __launch_bounds__(256) void k_qkv_post(Rows R, QkvPostArgs a) {
-  __shared__ float sh[4];
-  const int r = blockIdx.x, hh = blockIdx.y, hd = a.hd, half = hd / 2;
-  const int pos = clamp_pos(R, row_pos(R, r));
-  const int seq = row_seq(R, r);
-  const int nh = a.nq + (a.kc ? 2 : 0);
-  const float* src = a.qkv + (size_t)r * nh * hd + (size_t)hh * hd;
-  const int i = threadIdx.x;
-  const bool act = i < half;
-  const float x0 = act ? src[i] : 0.f, x1 = act ? src[i + half] : 0.f;
-  const float ss = block_sum<256>(x0 * x0 + x1 * x1, sh);
-  const float rr = rsqrtf(ss / (float)hd + a.eps);
-  if (!act) return;
-  const bool is_v = hh == a.nq + 1;
-  const uint16_t* g = hh < a.nq ? a.gq : a.gk;
-  float y0 = x0 * rr, y1 = x1 * rr;
-  if (!is_v) {
-    y0 *= bf2f(g[i]);
-    y1 *= bf2f(g[i + half]);
-    double sn, cs;
-    sincos((double)pos * a.inv_freq[i], &sn, &cs);
-    const float c = (float)cs, s = (float)sn;
-    const float z0 = y0 * c - y1 * s, z1 = y0 * s + y1 * c;
-    y0 = z0;
-    y1 = z1;
-  }
-  if (hh < a.nq) {
-    float* q = a.q_out + ((size_t)r * a.nq + hh) * hd;
-    q[i] = y0;
-    q[i + half] = y1;
-  } else {
-    uint16_t* dst = (is_v ? a.vc : a.kc) + ((size_t)seq * R.max_ctx + pos) * hd;
-    dst[i] = (uint16_t)f2bf(y0);
-    dst[i + half] = (uint16_t)f2bf(y1);
-  }
-}
-
-hipError_t launch_qkv_post(const Rows& R, const QkvPostArgs& a, hipStream_t st) {
-  if (a.hd > 512 || a.hd % 2) return hipErrorInvalidValue;
-  const int nh = a.nq + (a.kc ? 2 : 0);
-  hipLaunchKernelGGL(k_qkv_post, dim3(R.n, nh), dim3(256), 0, st, R, a);
-  return hipGetLastError();
-}
-
+// ------------------------------------------------------------ prefill K/V write
+// Prefill rows of one sequence attend to each other's keys, so every row's
+// K/V is written before attention: block per row, wave 0 the key (norm with
+// gain + RoPE), wave 1 the value (norm), bf16 at slot = position.
 // ------------------------------------------------------------ decode attention
-// Block (chunk c, row r): keys j0..j1-1 of the row's window, all query heads
-// against one K/V head.  Key tiles of TK rows are staged in LDS (bf16); an
-// online softmax keeps (max, sum, o) per head.  Partial results per chunk go to
-// `part`; k_attn_combine merges the chunks of a (row, head).
-constexpr int kTK = 16;
+// Block (chunk c, row r): the keys j0..j1-1 of chunk c of the row's window,
+// all query heads against the single K/V head.  The block normalises and
+// rotates the row's queries itself (q_norm with gain, rotate-half RoPE at the
+// logical position).  With own_kv (decode: every row is its own sequence) the
+// block whose chunk holds the row's position also norms, rotates and stores
+// that position's key and value (bf16) before attending, so no separate pass
+// is needed; for prefill the cache is written by k_kv_write first.
+// Lanes own hd/64 consecutive dims; each wave takes groups of 4 keys, reduces
+// the 32 (key, head) dot products with a transposing butterfly (31 shuffles),
+// and keeps an online softmax (max, sum, o) per head.  The 4 waves merge in
+// LDS and write one (max, sum, o) partial per (row, head, chunk).
 constexpr int kMaxHeads = 8;
 
+// One butterfly step of a transposing reduction: lanes whose bit `o` is set
+// keep the upper half of their values, the others the lower half; each adds
+// its partner's copy of the half it keeps.
+template <int H>
+__device__ __forceinline__ void tr_step(float* cur, int lane, int o) {
+  const bool upper = (lane & o) != 0;
+#pragma unroll
+  for (int i = 0; i < H; ++i) {
+    const float send = upper ? cur[i] : cur[i + H];
+    const float keep = upper ? cur[i + H] : cur[i];
+    cur[i] = keep + __shfl_xor(send, o, 64);
+  }
+}
+
+// 32 values per lane -> lane l ends with the full 64-lane sum of value l >> 1
+__device__ __forceinline__ float transpose_reduce32(float (&v)[32], int lane) {
+  tr_step<16>(v, lane, 32);
+  tr_step<8>(v, lane, 16);
+  tr_step<4>(v, lane, 8);
+  tr_step<2>(v, lane, 4);
+  tr_step<1>(v, lane, 2);
+  return v[0] + __shfl_xor(v[0], 1, 64);
+}
+
+template <int DPL>
+__device__ __forceinline__ void load_row(const uint16_t* p, float (&out)[DPL]) {
+  if constexpr (DPL == 8) {
+    const uint4 v = *reinterpret_cast<const uint4*>(p);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { out[2 * i] = bf2f(w[i]); out[2 * i + 1] = bf2f(w[i] >> 16); }
+  } else if constexpr (DPL == 4) {
+    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    out[0] = bf2f(v.x); out[1] = bf2f(v.x >> 16); out[2] = bf2f(v.y); out[3] = bf2f(v.y >> 16);
+  } else if constexpr (DPL == 2) {
+    const uint32_t v = *reinterpret_cast<const uint32_t*>(p);
+    out[0] = bf2f(v); out[1] = bf2f(v >> 16);
+  } else {
+    out[0] = bf2f(*p);
+  }
+}
+
+// One head vector of a row: RMS norm over hd (gain optional), then (rope)
+// rotate-half RoPE with the position's angles cs/sn [hd/2].  Lane l holds dims
+// l*DPL .. l*DPL+DPL-1; the rotation partner of dim d < hd/2 is d + hd/2, held
+// by lane l ^ 32.  Used for queries, and for the keys and values written to
+// the cache, by both the decode and the prefill path (identical arithmetic).
 template <int HD>
-__global__ __launch_bounds__(256) void k_attn(Rows R, AttnArgs a) {
-  __shared__ float qs[kMaxHeads * HD];
-  __shared__ uint16_t ks[kTK * (HD + 2)];
-  __shared__ uint16_t vs[kTK * HD];
-  __shared__ float p[kMaxHeads * kTK];
-  __shared__ float mh[kMaxHeads], lh[kMaxHeads], corr[kMaxHeads];
-  constexpr int NO = (kMaxHeads * HD + 255) / 256;
-  const int c = blockIdx.x, r = blockIdx.y, t = threadIdx.x, nq = a.nq;
+__device__ __forceinline__ void head_vec(const float* raw, const uint16_t* gain, bool rope,
+                                         const float* cs, const float* sn, int lane, float eps,
+                                         float (&y)[HD / 64]) {
+  constexpr int DPL = HD / 64;
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) {
+    y[i] = raw[lane * DPL + i];
+    ss += y[i] * y[i];
+  }
+  const float rr = rsqrtf(wave_sum(ss) / (float)HD + eps);
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) y[i] = y[i] * rr * (gain ? bf2f(gain[lane * DPL + i]) : 1.0f);
+  if (rope) {
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) {
+      const float other = __shfl_xor(y[i], 32, 64);
+      const int ii = (lane & 31) * DPL + i;
+      y[i] = lane < 32 ? y[i] * cs[ii] - other * sn[ii] : other * sn[ii] + y[i] * cs[ii];
+    }
+  }
+}
+
+template <int HD>
+__device__ __forceinline__ void rope_angles(int pos, const double* inv_freq, float* cs, float* sn) {
+  for (int i = threadIdx.x; i < HD / 2; i += blockDim.x) {
+    double sd, cd;
+    sincos((double)pos * inv_freq[i], &sd, &cd);
+    cs[i] = (float)cd;
+    sn[i] = (float)sd;
+  }
+}
+
+template <int HD>
+__global__ __launch_bounds__(256) void k_attn_dec(Rows R, AttnArgs a) {
+  constexpr int DPL = HD / 64;
+  constexpr int NH = kMaxHeads;
+  __shared__ float qs[NH * HD];
+  __shared__ float cs[HD / 2], sn[HD / 2];
+  __shared__ float pw[4][32];
+  __shared__ float cw[4][NH];
+  __shared__ float wm[4][NH], wl[4][NH];
+  __shared__ float red[4];
+  const int c = blockIdx.x, r = blockIdx.y, t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6, nq = a.nq;
   const int pos = clamp_pos(R, row_pos(R, r));
   const int seq = row_seq(R, r);
   const int lo = a.window ? max(0, pos - a.window + 1) : 0;
   const int j0 = lo + c * a.chunk;
   const int j1 = min(j0 + a.chunk, pos + 1);
-  float* part = a.part + ((size_t)r * nq * kMaxChunks + c) * (HD + 2);
   const size_t hstride = (size_t)kMaxChunks * (HD + 2);
+  float* part = a.part + ((size_t)r * nq * kMaxChunks + c) * (HD + 2);
   if (j0 >= j1) {
     if (t < nq) {
       part[t * hstride + HD] = -INFINITY;
@@ -511,104 +668,217 @@ __global__ __launch_bounds__(256) void k_attn(Rows R, AttnArgs a) {
     }
     return;
   }
-  for (int i = t; i < nq * HD; i += 256) qs[i] = a.q[(size_t)r * nq * HD + i];
-  if (t < nq) {
-    mh[t] = -INFINITY;
-    lh[t] = 0.f;
-  }
-  float acc[NO];
+  const int nraw = nq + (a.owns ? 2 : 0);
+  const float* raw = a.qkv + (size_t)r * nraw * HD;
+
+  rope_angles<HD>(pos, a.inv_freq, cs, sn);
+  __syncthreads();
+  // query heads (wave per head)
+  for (int h = wave; h < nq; h += 4) {
+    float y[DPL];
+    head_vec<HD>(raw + h * HD, a.gq, true, cs, sn, lane, a.eps, y);
 #pragma unroll
-  for (int j = 0; j < NO; ++j) acc[j] = 0.f;
+    for (int i = 0; i < DPL; ++i) qs[h * HD + lane * DPL + i] = y[i];
+  }
+  // this position's key and value, stored as bf16 (decode: the block holding
+  // the position writes them before any wave reads the cache)
   const uint16_t* kb = a.kc + (size_t)seq * R.max_ctx * HD;
   const uint16_t* vb = a.vc + (size_t)seq * R.max_ctx * HD;
-  const float scale = rsqrtf((float)HD);
-  for (int jt = j0; jt < j1; jt += kTK) {
-    const int nk = min(kTK, j1 - jt);
-    __syncthreads();
-    for (int i = t; i < nk * HD; i += 256) {
-      const int kk = i / HD, d = i % HD;
-      ks[kk * (HD + 2) + d] = kb[(size_t)(jt + kk) * HD + d];
-      vs[kk * HD + d] = vb[(size_t)(jt + kk) * HD + d];
-    }
-    __syncthreads();
-    for (int idx = t; idx < nq * kTK; idx += 256) {
-      const int h = idx / kTK, kk = idx % kTK;
-      float s = -INFINITY;
-      if (kk < nk) {
-        float d0 = 0.f;
-        const float* qh = qs + h * HD;
-        const uint16_t* kr = ks + kk * (HD + 2);
-        for (int d = 0; d < HD; ++d) d0 += qh[d] * bf2f(kr[d]);
-        s = d0 * scale;
-      }
-      p[idx] = s;
-    }
-    __syncthreads();
-    if (t < nq) {
-      float mt = -INFINITY;
-      for (int kk = 0; kk < nk; ++kk) mt = fmaxf(mt, p[t * kTK + kk]);
-      const float mn = fmaxf(mh[t], mt);
-      const float cr = (mh[t] == -INFINITY) ? 0.f : expf(mh[t] - mn);
-      float sum = 0.f;
-      for (int kk = 0; kk < kTK; ++kk) {
-        const float e = (kk < nk) ? expf(p[t * kTK + kk] - mn) : 0.f;
-        p[t * kTK + kk] = e;
-        sum += e;
-      }
-      lh[t] = lh[t] * cr + sum;
-      mh[t] = mn;
-      corr[t] = cr;
-    }
-    __syncthreads();
+  if (a.kc_own && j1 == pos + 1 && wave < 2) {
+    const bool is_v = wave == 1;
+    float y[DPL];
+    head_vec<HD>(raw + (nq + wave) * HD, is_v ? nullptr : a.gk, !is_v, cs, sn, lane, a.eps, y);
+    uint16_t* dst = (is_v ? a.vc_own : a.kc_own) + ((size_t)seq * R.max_ctx + pos) * HD;
 #pragma unroll
-    for (int j = 0; j < NO; ++j) {
-      const int o = t + 256 * j;
-      if (o < nq * HD) {
-        const int h = o / HD, d = o % HD;
-        float s = acc[j] * corr[h];
-        for (int kk = 0; kk < nk; ++kk) s += p[h * kTK + kk] * bf2f(vs[kk * HD + d]);
-        acc[j] = s;
-      }
-    }
+    for (int i = 0; i < DPL; ++i) dst[lane * DPL + i] = (uint16_t)f2bf(y[i]);
+    __threadfence_block();
   }
   __syncthreads();
+
+  // this lane's query dims for every head
+  float qr[NH][DPL];
 #pragma unroll
-  for (int j = 0; j < NO; ++j) {
-    const int o = t + 256 * j;
-    if (o < nq * HD) {
-      const int h = o / HD, d = o % HD;
-      part[h * hstride + d] = acc[j];
+  for (int h = 0; h < NH; ++h)
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) qr[h][i] = h < nq ? qs[h * HD + lane * DPL + i] : 0.f;
+
+  const float scale = rsqrtf((float)HD);
+  const int myh = (lane >> 1) & 7, myk = lane >> 4;  // value index lane>>1 = k*8 + h
+  float m_run = -INFINITY, l_run = 0.f;
+  float o[NH][DPL];
+#pragma unroll
+  for (int h = 0; h < NH; ++h)
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) o[h][i] = 0.f;
+
+  const int ngroups = (j1 - j0 + 3) / 4;
+  for (int gi = wave; gi < ngroups; gi += 4) {
+    const int key0 = j0 + 4 * gi;
+    float kr[4][DPL], vr[4][DPL];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int key = key0 + k;
+      if (key < j1) {
+        load_row<DPL>(kb + (size_t)key * HD + lane * DPL, kr[k]);
+        load_row<DPL>(vb + (size_t)key * HD + lane * DPL, vr[k]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < DPL; ++i) { kr[k][i] = 0.f; vr[k][i] = 0.f; }
+      }
     }
+    float part32[32];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int h = 0; h < NH; ++h) {
+        float d = 0.f;
+#pragma unroll
+        for (int i = 0; i < DPL; ++i) d += qr[h][i] * kr[k][i];
+        part32[k * NH + h] = d;
+      }
+    float sc_ = transpose_reduce32(part32, lane) * scale;
+    if (key0 + myk >= j1 || myh >= nq) sc_ = -INFINITY;
+    float mx = fmaxf(sc_, __shfl_xor(sc_, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx);
+    const float pr = (m_new == -INFINITY || sc_ == -INFINITY) ? 0.f : expf(sc_ - m_new);
+    const float corr = (m_new == -INFINITY || m_run == -INFINITY) ? (m_run == -INFINITY ? 0.f : 1.f)
+                                                                   : expf(m_run - m_new);
+    float ps = pr + __shfl_xor(pr, 16, 64);
+    ps += __shfl_xor(ps, 32, 64);
+    l_run = l_run * corr + ps;
+    m_run = m_new;
+    if ((lane & 1) == 0) pw[wave][lane >> 1] = pr;
+    if (lane < 16 && (lane & 1) == 0) cw[wave][lane >> 1] = corr;
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+      const float cf = cw[wave][h];
+      const float p0 = pw[wave][h], p1 = pw[wave][NH + h], p2 = pw[wave][2 * NH + h],
+                  p3 = pw[wave][3 * NH + h];
+#pragma unroll
+      for (int i = 0; i < DPL; ++i)
+        o[h][i] = o[h][i] * cf + p0 * vr[0][i] + p1 * vr[1][i] + p2 * vr[2][i] + p3 * vr[3][i];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+  }
+  // merge the four waves: per head max M, then rescale and sum
+  if (lane < 16 && (lane & 1) == 0) {
+    wm[wave][lane >> 1] = m_run;
+    wl[wave][lane >> 1] = l_run;
+  }
+  __syncthreads();
+  float* acc = qs;  // reuse: [NH][HD]
+  for (int w = 0; w < 4; ++w) {
+    if (wave == w) {
+#pragma unroll
+      for (int h = 0; h < NH; ++h) {
+        float M = wm[0][h];
+        for (int x = 1; x < 4; ++x) M = fmaxf(M, wm[x][h]);
+        const float f = (wm[w][h] == -INFINITY) ? 0.f : expf(wm[w][h] - M);
+#pragma unroll
+        for (int i = 0; i < DPL; ++i) {
+          const float v = o[h][i] * f;
+          acc[h * HD + lane * DPL + i] = (w == 0) ? v : acc[h * HD + lane * DPL + i] + v;
+        }
+      }
+    }
+    __syncthreads();
+  }
+  for (int idx = t; idx < nq * HD; idx += 256) {
+    const int h = idx / HD, d = idx % HD;
+    part[h * hstride + d] = acc[idx];
   }
   if (t < nq) {
-    part[t * hstride + HD] = mh[t];
-    part[t * hstride + HD + 1] = lh[t];
+    float M = wm[0][t];
+    for (int x = 1; x < 4; ++x) M = fmaxf(M, wm[x][t]);
+    float L = 0.f;
+    for (int x = 0; x < 4; ++x)
+      if (wm[x][t] != -INFINITY) L += wl[x][t] * expf(wm[x][t] - M);
+    part[t * hstride + HD] = M;
+    part[t * hstride + HD + 1] = L;
+  }
+  (void)red;
+}
+
+// out[r][h*hd + d] = sum_c e^(m_c - M) o_c[d] / sum_c e^(m_c - M) l_c over the
+// chunks holding keys.  Those are a prefix of the chunk list (keys are split in
+// order); empty chunks leave o unwritten, so they are never read.
+__global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a) {
+  __shared__ float wn[kMaxChunks];
+  __shared__ float sh[8];
+  __shared__ int na[4];
+  const int r = blockIdx.x, h = blockIdx.y, hd = a.hd, t = threadIdx.x;
+  const size_t hstride = (size_t)kMaxChunks * (hd + 2);
+  const float* part = a.part + ((size_t)r * a.nq + h) * hstride;
+  float mc = -INFINITY, lc = 0.f;
+  if (t < a.nchunk) {
+    mc = part[(size_t)t * (hd + 2) + hd];
+    lc = part[(size_t)t * (hd + 2) + hd + 1];
+  }
+  const bool act = lc > 0.f;
+  float M = act ? mc : -INFINITY;
+  int nact = act ? t + 1 : 0;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    M = fmaxf(M, __shfl_xor(M, o, 64));
+    nact = max(nact, __shfl_xor(nact, o, 64));
+  }
+  if ((t & 63) == 0) {
+    sh[t >> 6] = M;
+    na[t >> 6] = nact;
+  }
+  __syncthreads();
+  M = fmaxf(fmaxf(sh[0], sh[1]), fmaxf(sh[2], sh[3]));
+  nact = max(max(na[0], na[1]), max(na[2], na[3]));
+  const float w = act ? expf(mc - M) : 0.f;
+  const float L = block_sum<256>(w * lc, sh + 4);
+  if (t < kMaxChunks) wn[t] = w / L;
+  __syncthreads();
+  for (int d = t; d < hd; d += 256) {
+    float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
+    int cc = 0;
+    for (; cc + 4 <= nact; cc += 4) {
+      o0 += wn[cc] * part[(size_t)cc * (hd + 2) + d];
+      o1 += wn[cc + 1] * part[(size_t)(cc + 1) * (hd + 2) + d];
+      o2 += wn[cc + 2] * part[(size_t)(cc + 2) * (hd + 2) + d];
+      o3 += wn[cc + 3] * part[(size_t)(cc + 3) * (hd + 2) + d];
+    }
+    for (; cc < nact; ++cc) o0 += wn[cc] * part[(size_t)cc * (hd + 2) + d];
+    a.out[(size_t)r * a.nq * hd + (size_t)h * hd + d] = (o0 + o1) + (o2 + o3);
   }
 }
 
-// out[r][h*hd + d] = sum_c e^(m_c - M) o_c[d] / sum_c e^(m_c - M) l_c
-__global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a) {
-  const int r = blockIdx.x, h = blockIdx.y, hd = a.hd;
-  const size_t hstride = (size_t)kMaxChunks * (hd + 2);
-  const float* part = a.part + ((size_t)r * a.nq + h) * hstride;
-  float M = -INFINITY;
-  for (int c = 0; c < a.nchunk; ++c) {
-    const float* pc = part + (size_t)c * (hd + 2);
-    if (pc[hd + 1] > 0.f) M = fmaxf(M, pc[hd]);
+template <int HD>
+__global__ __launch_bounds__(128) void k_kv_write(Rows R, QkvPostArgs a) {
+  constexpr int DPL = HD / 64;
+  __shared__ float cs[HD / 2], sn[HD / 2];
+  const int r = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int pos = clamp_pos(R, row_pos(R, r));
+  const int seq = row_seq(R, r);
+  rope_angles<HD>(pos, a.inv_freq, cs, sn);
+  __syncthreads();
+  const float* raw = a.qkv + (size_t)r * (a.nq + 2) * HD + (size_t)(a.nq + wave) * HD;
+  const bool is_v = wave == 1;
+  float y[DPL];
+  head_vec<HD>(raw, is_v ? nullptr : a.gk, !is_v, cs, sn, lane, a.eps, y);
+  uint16_t* dst = (is_v ? a.vc : a.kc) + ((size_t)seq * R.max_ctx + pos) * HD;
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) dst[lane * DPL + i] = (uint16_t)f2bf(y[i]);
+}
+
+hipError_t launch_qkv_post(const Rows& R, const QkvPostArgs& a, hipStream_t st) {
+  if (!a.kc || !a.vc) return hipErrorInvalidValue;
+  switch (a.hd) {
+    case 64: hipLaunchKernelGGL(k_kv_write<64>, dim3(R.n), dim3(128), 0, st, R, a); break;
+    case 128: hipLaunchKernelGGL(k_kv_write<128>, dim3(R.n), dim3(128), 0, st, R, a); break;
+    case 256: hipLaunchKernelGGL(k_kv_write<256>, dim3(R.n), dim3(128), 0, st, R, a); break;
+    case 512: hipLaunchKernelGGL(k_kv_write<512>, dim3(R.n), dim3(128), 0, st, R, a); break;
+    default: return hipErrorInvalidValue;
   }
-  float L = 0.f;
-  for (int c = 0; c < a.nchunk; ++c) {
-    const float* pc = part + (size_t)c * (hd + 2);
-    if (pc[hd + 1] > 0.f) L += pc[hd + 1] * expf(pc[hd] - M);
-  }
-  for (int d = threadIdx.x; d < hd; d += blockDim.x) {
-    float o = 0.f;
-    for (int c = 0; c < a.nchunk; ++c) {
-      const float* pc = part + (size_t)c * (hd + 2);
-      if (pc[hd + 1] > 0.f) o += pc[d] * expf(pc[hd] - M);
-    }
-    a.out[(size_t)r * a.nq * hd + (size_t)h * hd + d] = o / L;
-  }
+  return hipGetLastError();
 }
 
 hipError_t launch_attention(const Rows& R, const AttnArgs& a, hipStream_t st) {
@@ -616,10 +886,10 @@ hipError_t launch_attention(const Rows& R, const AttnArgs& a, hipStream_t st) {
     return hipErrorInvalidValue;
   dim3 grid(a.nchunk, R.n);
   switch (a.hd) {
-    case 64: hipLaunchKernelGGL(k_attn<64>, grid, dim3(256), 0, st, R, a); break;
-    case 128: hipLaunchKernelGGL(k_attn<128>, grid, dim3(256), 0, st, R, a); break;
-    case 256: hipLaunchKernelGGL(k_attn<256>, grid, dim3(256), 0, st, R, a); break;
-    case 512: hipLaunchKernelGGL(k_attn<512>, grid, dim3(256), 0, st, R, a); break;
+    case 64: hipLaunchKernelGGL(k_attn_dec<64>, grid, dim3(256), 0, st, R, a); break;
+    case 128: hipLaunchKernelGGL(k_attn_dec<128>, grid, dim3(256), 0, st, R, a); break;
+    case 256: hipLaunchKernelGGL(k_attn_dec<256>, grid, dim3(256), 0, st, R, a); break;
+    case 512: hipLaunchKernelGGL(k_attn_dec<512>, grid, dim3(256), 0, st, R, a); break;
     default: return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();
