@@ -194,9 +194,14 @@ int e2b_kv_view(const e2b_model* model, int layer, int which, void** out);
  * E2B_QUANT_W4A16: d_w is the packed int32 [N, K/8] (format of e2b_tensor)
  * and d_scale the bf16 [N, K/32] group scales; each code is decoded exactly
  * as (c - 8) * scale in fp32 ([P4] cell 3.1).  x: fp32 [rows, K]; y: fp32
- * [rows, N].  K must be one of the widths the library supports (multiples of
- * 32 up to 512, multiples of 512 up to 4096, 6144, 12288); d_ws must hold
- * e2b_matvec_workspace_bytes(N, K, rows) bytes (may be 0).  Asynchronous. */
+ * [rows, N].  K must be one of the widths the library supports: K split into
+ * at most 8 equal slices of width 32, 128, 256, 512, 1536 or 2048 (the first
+ * that divides K among 2048, 1536; else K itself when K <= 512; else 512);
+ * other K -> E2B_EINVAL.  d_ws (256-byte
+ * aligned) must hold e2b_matvec_workspace_bytes(N, K, rows) bytes (0 for
+ * one row with K <= 2048, else nonzero).  One row streams the weights through
+ * the matvec kernel; two or more rows share one pass over the weights on the
+ * matrix cores.  Asynchronous. */
 size_t e2b_matvec_workspace_bytes(int N, int K, int rows);
 int e2b_matvec(int quant, const void* d_w, const uint16_t* d_scale, int N, int K,
                const float* d_x, int rows, float* d_y, void* d_ws, size_t ws_bytes,

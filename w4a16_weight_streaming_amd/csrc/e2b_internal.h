@@ -114,9 +114,18 @@ hipError_t launch_ple_finish(const Rows& R, const float* u, const float* tokple,
 hipError_t launch_gemv(int quant, int tag, const Lin& W, int rows, const Prologue& pro,
                        const Epilogue& epi, int blocks_hint, int* blocks_out, hipStream_t st);
 int gemv_splits(int K);
+bool gemv_supported(int K);  // K is one of the widths the matvec kernel handles
 hipError_t launch_qkv_post(const Rows& R, const QkvPostArgs& a, hipStream_t st);
 hipError_t launch_attention(const Rows& R, const AttnArgs& a, hipStream_t st);
 hipError_t launch_advance(int32_t* pos, int n, hipStream_t st);
+// batched rows (>= 2): prologue into bf16 hi/lo rows + group sums, then MFMA
+hipError_t launch_xprep(const Prologue& p, int rows, int K, uint16_t* xh, uint16_t* xl, float* xg,
+                        hipStream_t st);
+int gemm_splits(int K, bool partial_ok);
+// *nblk receives the number of column blocks (argmax candidates per row)
+hipError_t launch_gemm(int quant, int tag, const Lin& W, int rows, const uint16_t* xh,
+                       const uint16_t* xl, const float* xg, int nks, const Epilogue& epi,
+                       int* nblk, hipStream_t st);
 hipError_t launch_sum_partials(int nparts, size_t n, const float* parts, float* out,
                                hipStream_t st);
 hipError_t launch_argmax_final(int rows, int nblk, const float* cand_val,

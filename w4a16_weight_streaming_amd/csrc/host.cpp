@@ -122,7 +122,7 @@ int kv_src(const e2b_config& c, int l) {
   return s < 0 ? l : s;
 }
 
-bool supported_k(int K) { return e2b::gemv_splits(K) > 0 && e2b::gemv_splits(K) <= e2b::kMaxSplitK; }
+bool supported_k(int K) { return e2b::gemv_supported(K); }
 
 struct Planner {
   e2b_model* m;
@@ -242,7 +242,9 @@ Lin resolve(const e2b_model* m, const LinOff& o) {
 
 // ---- workspace layout ------------------------------------------------------
 struct Ws {
-  size_t err, h0, h1, tokple, u, pli, qkv, qn, part, attn, oo, gu, dn, pgy, ppo, cv, ci, total;
+  size_t err, h0, h1, tokple, u, pli, qkv, qn, part, attn, oo, gu, dn, pgy, ppo, cv, ci, xh, xl, xg,
+      total;
+  int ncand;  // argmax candidates per row
 };
 
 Ws ws_layout(const e2b_model* m, int R) {
@@ -255,12 +257,14 @@ Ws ws_layout(const e2b_model* m, int R) {
   };
   const size_t f = sizeof(float);
   const int hdm = std::max(m->c.head_dim, m->c.global_head_dim);
-  int Imax = 0, nko = 1, nkd = 1;
+  int Imax = 0, nko = 1, nkd = 1, Kmax = std::max(m->H, m->P);
   for (const LayerInfo& y : m->li) {
     Imax = std::max(Imax, y.I);
-    nko = std::max(nko, e2b::gemv_splits(m->nq * y.hd));
-    nkd = std::max(nkd, e2b::gemv_splits(y.I));
+    Kmax = std::max(Kmax, std::max(y.I, m->nq * y.hd));
+    nko = std::max(nko, std::max(e2b::gemv_splits(m->nq * y.hd), e2b::gemm_splits(m->nq * y.hd, true)));
+    nkd = std::max(nkd, std::max(e2b::gemv_splits(y.I), e2b::gemm_splits(y.I, true)));
   }
+  w.ncand = std::max(e2b::kLmBlocks, (m->V + 63) / 64);
   const size_t LP = (size_t)m->L * m->P;
   w.err = take(64);
   w.h0 = take(f * R * m->H);
@@ -277,8 +281,15 @@ Ws ws_layout(const e2b_model* m, int R) {
   w.dn = take(f * nkd * R * m->H);
   w.pgy = take(f * R * m->P);
   w.ppo = take(f * R * m->H);
-  w.cv = take(f * R * e2b::kLmBlocks);
-  w.ci = take(sizeof(int32_t) * R * e2b::kLmBlocks);
+  w.cv = take(f * R * w.ncand);
+  w.ci = take(sizeof(int32_t) * R * w.ncand);
+  if (R > 1) {  // batched rows go through the MFMA path
+    w.xh = take(2 * (size_t)R * Kmax);
+    w.xl = take(2 * (size_t)R * Kmax);
+    w.xg = take(f * (size_t)R * (Kmax / 32));
+  } else {
+    w.xh = w.xl = w.xg = 0;
+  }
   w.total = cur;
   return w;
 }
@@ -292,29 +303,59 @@ void attn_chunks(const e2b_model* m, bool full, int* chunk, int* nchunk) {
   *chunk = (span + n - 1) / n;
 }
 
-// launch_gemv, bracketed by events when this kind is being profiled
-hipError_t gemv(e2b_model* m, int quant, int tag, const Lin& W, int rows,
-                const e2b::Prologue& pr, const e2b::Epilogue& ep, int* nblk, hipStream_t st) {
-  if (m->prof_kind != tag) return e2b::launch_gemv(quant, tag, W, rows, pr, ep, 0, nblk, st);
-  e2b_model::Mark mk{};
-  hipError_t e = hipEventCreate(&mk.a);
-  if (e == hipSuccess) e = hipEventCreate(&mk.b);
-  if (e == hipSuccess) e = hipEventRecord(mk.a, st);
-  if (e == hipSuccess) e = e2b::launch_gemv(quant, tag, W, rows, pr, ep, 0, nblk, st);
-  if (e == hipSuccess) e = hipEventRecord(mk.b, st);
-  if (e != hipSuccess) return e;
-  const double wb = quant ? (double)W.N * W.K / 2 + (double)W.N * (W.K / 32) * 2
-                          : (double)W.N * W.K * 2;
-  mk.bytes = wb + (double)rows * (W.K + W.N) * sizeof(float);
-  m->marks.push_back(mk);
-  return hipSuccess;
-}
+// One product of a linear layer with `rows` input rows built by `pr`:
+// a one-row pass streams through the matvec kernel, a batched pass (even
+// where only one of its rows reaches this product, as the last-row lm_head of
+// prefill does) through the x-prep + MFMA kernels, so that a row's result
+// does not depend on the other rows of its pass.  *nd receives the number of K-slice partials written
+// (only where partial_ok: the consumer sums them).  Bracketed by events when
+// this kind is being profiled.
+hipError_t matmul(e2b_model* m, int quant, int tag, const Lin& W, int rows, bool batched,
+                  const e2b::Prologue& pr, const e2b::Epilogue& ep, bool partial_ok, int* nd,
+                  int* nblk, char* ws, const struct Ws& L, hipStream_t st);
 
 #define CK(call, what)                         \
   do {                                         \
     hipError_t e_ = (call);                    \
     if (e_ != hipSuccess) return hip_fail(e_, what); \
   } while (0)
+
+hipError_t matmul(e2b_model* m, int quant, int tag, const Lin& W, int rows, bool batched,
+                  const e2b::Prologue& pr, const e2b::Epilogue& ep, bool partial_ok, int* nd,
+                  int* nblk, char* ws, const Ws& L, hipStream_t st) {
+  const bool prof = m->prof_kind == tag;
+  e2b_model::Mark mk{};
+  hipError_t e = hipSuccess;
+  if (prof) {
+    e = hipEventCreate(&mk.a);
+    if (e == hipSuccess) e = hipEventCreate(&mk.b);
+    if (e == hipSuccess) e = hipEventRecord(mk.a, st);
+    if (e != hipSuccess) return e;
+  }
+  int splits = 1;
+  if (!batched) {
+    splits = e2b::gemv_splits(W.K);
+    e = e2b::launch_gemv(quant, tag, W, rows, pr, ep, 0, nblk, st);
+  } else {
+    uint16_t* xh = reinterpret_cast<uint16_t*>(ws + L.xh);
+    uint16_t* xl = reinterpret_cast<uint16_t*>(ws + L.xl);
+    float* xg = reinterpret_cast<float*>(ws + L.xg);
+    splits = e2b::gemm_splits(W.K, partial_ok);
+    e = e2b::launch_xprep(pr, rows, W.K, xh, xl, xg, st);
+    if (e == hipSuccess) e = e2b::launch_gemm(quant, tag, W, rows, xh, xl, xg, splits, ep, nblk, st);
+  }
+  if (nd) *nd = splits;
+  if (e != hipSuccess) return e;
+  if (prof) {
+    e = hipEventRecord(mk.b, st);
+    if (e != hipSuccess) return e;
+    const double wb = quant ? (double)W.N * W.K / 2 + (double)W.N * (W.K / 32) * 2
+                            : (double)W.N * W.K * 2;
+    mk.bytes = wb + (double)rows * (W.K + W.N) * sizeof(float);
+    m->marks.push_back(mk);
+  }
+  return hipSuccess;
+}
 
 // One pass over R.n rows: all layers, then (if head) the final norm, lm_head
 // and argmax for every row (head_row < 0) or for row head_row only.
@@ -336,7 +377,7 @@ int run_rows(e2b_model* m, const e2b::Rows& R, bool head, int head_row, float* d
     pr.lda = H;
     Epilogue ep;
     ep.y = F(W.u);
-    CK(gemv(m, q, kTagPleModel, m->plmp, n, pr, ep, nullptr, st), "per-layer model projection");
+    CK(matmul(m, q, kTagPleModel, m->plmp, n, n > 1, pr, ep, false, nullptr, nullptr, ws, W, st), "per-layer model projection");
   }
   CK(launch_ple_finish(R, F(W.u), F(W.tokple), m->g_plpn, L, P, 1.0f / std::sqrt((float)H), eps,
                        F(W.pli), st),
@@ -350,6 +391,7 @@ int run_rows(e2b_model* m, const e2b::Rows& R, bool head, int head_row, float* d
     const LayerInfo& y = m->li[l];
     const LayerDev& d = m->ld[l];
     const bool owns = y.src == l;
+    int nd_o = 1, nd_dn = 1;  // K-slice partials of the O and down products
     {  // QKV with the residual update of the previous layer fused in front
       Prologue pr;
       pr.kind = kResNorm;
@@ -363,7 +405,7 @@ int run_rows(e2b_model* m, const e2b::Rows& R, bool head, int head_row, float* d
       pr.eps = eps;
       Epilogue ep;
       ep.y = F(W.qkv);
-      CK(gemv(m, q, kTagQkv, d.qkv, n, pr, ep, nullptr, st), "qkv projection");
+      CK(matmul(m, q, kTagQkv, d.qkv, n, n > 1, pr, ep, false, nullptr, nullptr, ws, W, st), "qkv projection");
       if (pend) std::swap(cur, oth);
     }
     // decode rows are distinct sequences: the attention kernel writes the new
@@ -410,21 +452,21 @@ int run_rows(e2b_model* m, const e2b::Rows& R, bool head, int head_row, float* d
       pr.lda = m->nq * y.hd;
       Epilogue ep;
       ep.y = F(W.oo);
-      CK(gemv(m, q, kTagO, d.o, n, pr, ep, nullptr, st), "o projection");
+      CK(matmul(m, q, kTagO, d.o, n, n > 1, pr, ep, true, &nd_o, nullptr, ws, W, st), "o projection");
     }
     {  // post-attention norm + residual, pre-FFN norm, gate/up
       Prologue pr;
       pr.kind = kResNorm;
       pr.a = cur;
       pr.d = F(W.oo);
-      pr.nd = gemv_splits(d.o.K);
+      pr.nd = nd_o;
       pr.gd = d.g_pa;
       pr.gx = d.g_pf;
       pr.h_out = oth;
       pr.eps = eps;
       Epilogue ep;
       ep.y = F(W.gu);
-      CK(gemv(m, q, kTagGateUp, d.gu, n, pr, ep, nullptr, st), "gate/up projection");
+      CK(matmul(m, q, kTagGateUp, d.gu, n, n > 1, pr, ep, false, nullptr, nullptr, ws, W, st), "gate/up projection");
       std::swap(cur, oth);
     }
     {  // GeGLU then down
@@ -434,20 +476,20 @@ int run_rows(e2b_model* m, const e2b::Rows& R, bool head, int head_row, float* d
       pr.lda = 2 * y.I;
       Epilogue ep;
       ep.y = F(W.dn);
-      CK(gemv(m, q, kTagDown, d.down, n, pr, ep, nullptr, st), "down projection");
+      CK(matmul(m, q, kTagDown, d.down, n, n > 1, pr, ep, true, &nd_dn, nullptr, ws, W, st), "down projection");
     }
     {  // post-FFN norm + residual, per-layer input gate
       Prologue pr;
       pr.kind = kRes;
       pr.a = cur;
       pr.d = F(W.dn);
-      pr.nd = gemv_splits(d.down.K);
+      pr.nd = nd_dn;
       pr.gd = d.g_ff;
       pr.h_out = oth;
       pr.eps = eps;
       Epilogue ep;
       ep.y = F(W.pgy);
-      CK(gemv(m, q, kTagPleGate, d.pg, n, pr, ep, nullptr, st), "per-layer input gate");
+      CK(matmul(m, q, kTagPleGate, d.pg, n, n > 1, pr, ep, false, nullptr, nullptr, ws, W, st), "per-layer input gate");
       std::swap(cur, oth);
     }
     {  // gelu(gate) * pli[l], per-layer projection
@@ -459,7 +501,7 @@ int run_rows(e2b_model* m, const e2b::Rows& R, bool head, int head_row, float* d
       pr.pli_ld = LP;
       Epilogue ep;
       ep.y = F(W.ppo);
-      CK(gemv(m, q, kTagPleProj, d.pp, n, pr, ep, nullptr, st), "per-layer projection");
+      CK(matmul(m, q, kTagPleProj, d.pp, n, n > 1, pr, ep, false, nullptr, nullptr, ws, W, st), "per-layer projection");
     }
     pend = F(W.ppo);
     pend_g = d.g_pple;
@@ -488,8 +530,8 @@ int run_rows(e2b_model* m, const e2b::Rows& R, bool head, int head_row, float* d
   ep.cand_val = F(W.cv);
   ep.cand_idx = reinterpret_cast<int32_t*>(ws + W.ci);
   int nblk = 0;
-  CK(gemv(m, E2B_QUANT_BF16, kTagLmHead, E, nh, pr, ep, &nblk, st), "lm_head");
-  if (nblk > kLmBlocks) return fail(E2B_EINVAL, "lm_head: %d candidate blocks", nblk);
+  CK(matmul(m, E2B_QUANT_BF16, kTagLmHead, E, nh, n > 1, pr, ep, false, nullptr, &nblk, ws, W, st), "lm_head");
+  if (nblk > W.ncand) return fail(E2B_EINVAL, "lm_head: %d candidate blocks", nblk);
   CK(launch_argmax_final(nh, nblk, ep.cand_val, ep.cand_idx, d_argmax, st), "argmax");
   return E2B_OK;
 }
@@ -804,10 +846,35 @@ int e2b_kv_view(const e2b_model* m, int layer, int which, void** out) {
   return E2B_OK;
 }
 
+namespace {
+// Workspace of e2b_matvec: one row -> the matvec kernel's K-slice partials;
+// several rows -> the MFMA path's prepared rows (bf16 hi/lo + group sums,
+// each region 256-byte aligned) then its K-slice partials.
+struct MvWs {
+  size_t xh, xl, xg, part, total;
+  int nks;
+};
+MvWs matvec_ws(int N, int K, int rows) {
+  MvWs w{};
+  auto up = [](size_t b) { return (b + 255) & ~(size_t)255; };
+  if (rows == 1) {
+    w.nks = e2b::gemv_splits(K);
+    w.part = 0;
+  } else {
+    w.nks = e2b::gemm_splits(K, true);
+    w.xh = 0;
+    w.xl = up(2 * (size_t)rows * K);
+    w.xg = w.xl + up(2 * (size_t)rows * K);
+    w.part = w.xg + up(sizeof(float) * (size_t)rows * (K / 32));
+  }
+  w.total = w.part + (w.nks > 1 ? (size_t)w.nks * rows * N * sizeof(float) : 0);
+  return w;
+}
+}  // namespace
+
 size_t e2b_matvec_workspace_bytes(int N, int K, int rows) {
-  const int nks = e2b::gemv_splits(K);
-  if (N < 1 || rows < 1 || nks < 1) return 0;
-  return nks > 1 ? (size_t)nks * rows * N * sizeof(float) : 0;
+  if (N < 1 || rows < 1 || K < 32 || K % 32 || !supported_k(K)) return 0;
+  return matvec_ws(N, K, rows).total;
 }
 
 int e2b_matvec(int quant, const void* d_w, const uint16_t* d_scale, int N, int K,
@@ -820,11 +887,13 @@ int e2b_matvec(int quant, const void* d_w, const uint16_t* d_scale, int N, int K
   if (N < 1 || rows < 1 || rows > 65535 || K % 32 || !supported_k(K))
     return fail(E2B_EINVAL, "unsupported shape N=%d K=%d rows=%d", N, K, rows);
   if (reinterpret_cast<uintptr_t>(d_w) % 16) return fail(E2B_EINVAL, "weights must be 16-byte aligned");
-  const int nks = e2b::gemv_splits(K);
-  const size_t need = e2b_matvec_workspace_bytes(N, K, rows);
-  if (need && (!d_ws || ws_bytes < need))
-    return fail(E2B_ENOMEM, "workspace of %zu bytes < %zu required", ws_bytes, need);
+  const MvWs L = matvec_ws(N, K, rows);
+  if (L.total && (!d_ws || ws_bytes < L.total))
+    return fail(E2B_ENOMEM, "workspace of %zu bytes < %zu required", ws_bytes, L.total);
+  if (L.total && reinterpret_cast<uintptr_t>(d_ws) % 256)
+    return fail(E2B_EINVAL, "workspace must be 256-byte aligned");
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  char* ws = reinterpret_cast<char*>(d_ws);
   Lin W;
   W.N = N;
   W.K = K;
@@ -839,9 +908,18 @@ int e2b_matvec(int quant, const void* d_w, const uint16_t* d_scale, int N, int K
   pr.a = d_x;
   pr.lda = K;
   e2b::Epilogue ep;
-  ep.y = nks > 1 ? reinterpret_cast<float*>(d_ws) : d_y;
-  CK(e2b::launch_gemv(quant, e2b::kTagOther, W, rows, pr, ep, 0, nullptr, st), "matvec");
-  if (nks > 1) CK(e2b::launch_sum_partials(nks, (size_t)rows * N, ep.y, d_y, st), "matvec sum");
+  ep.y = L.nks > 1 ? reinterpret_cast<float*>(ws + L.part) : d_y;
+  if (rows == 1) {
+    CK(e2b::launch_gemv(quant, e2b::kTagOther, W, rows, pr, ep, 0, nullptr, st), "matvec");
+  } else {
+    uint16_t* xh = reinterpret_cast<uint16_t*>(ws + L.xh);
+    uint16_t* xl = reinterpret_cast<uint16_t*>(ws + L.xl);
+    float* xg = reinterpret_cast<float*>(ws + L.xg);
+    CK(e2b::launch_xprep(pr, rows, K, xh, xl, xg, st), "matvec input prep");
+    CK(e2b::launch_gemm(quant, e2b::kTagOther, W, rows, xh, xl, xg, L.nks, ep, nullptr, st),
+       "matvec mfma");
+  }
+  if (L.nks > 1) CK(e2b::launch_sum_partials(L.nks, (size_t)rows * N, ep.y, d_y, st), "matvec sum");
   return E2B_OK;
 }
 

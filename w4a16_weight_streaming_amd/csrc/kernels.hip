@@ -480,6 +480,13 @@ static int gemv_slice(int K) {
   return n > 0 ? K / n : -1;
 }
 
+// the slice widths the matvec kernel is instantiated for (dispatch_gemv)
+bool gemv_supported(int K) {
+  const int n = gemv_splits(K), ks = gemv_slice(K);
+  return n >= 1 && n <= kMaxSplitK &&
+         (ks == 32 || ks == 128 || ks == 256 || ks == 512 || ks == 1536 || ks == 2048);
+}
+
 template <int WQ, int KS, int U, int TAG>
 static hipError_t run_gemv(const Lin& W, int rows, const Prologue& pro, const Epilogue& epi,
                            int blocks_hint, int* blocks_out, hipStream_t st) {
@@ -896,6 +903,276 @@ hipError_t launch_attention(const Rows& R, const AttnArgs& a, hipStream_t st) {
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_attn_combine, dim3(R.n, a.nq), dim3(256), 0, st, a);
   return hipGetLastError();
+}
+
+// ===================================================== batched rows: MFMA path
+// For rows >= 2 (batched decode, prefill) the input rows are prepared once by
+// k_xprep (same prologue arithmetic as the single-row matvec) as bf16 hi/lo
+// pairs [rows][K] plus per-32-group sums of hi+lo, and k_gemm streams each
+// weight row once for up to 64 rows with v_mfma_f32_16x16x32_bf16:
+//   D[m][n] += A_hi[m][k] W[n][k] + A_lo[m][k] W[n][k]
+// A (16 rows x 32 k): lane l holds row l%16, k = 8(l/16)..8(l/16)+7.
+// B (32 k x 16 cols): lane l holds col l%16, the same k range.
+// D (16 x 16): lane l holds rows 4(l/16)..4(l/16)+3 of col l%16.
+// W4A16: the B operand holds 128 + c (code c under the bf16 exponent byte);
+// each 32-wide k step is one scale group, so per group
+//   acc += s[n][g] * (D_group - 136 * sum_k (A_hi + A_lo)[m][k]).
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kMB = 64;   // input rows per block
+constexpr int kNB = 64;   // weight rows per block (4 waves x 16)
+constexpr int kKC = 128;  // k per LDS chunk
+
+__global__ __launch_bounds__(256) void k_xprep(Prologue p, int rows, int K, uint16_t* __restrict__ xh,
+                                               uint16_t* __restrict__ xl, float* __restrict__ xg) {
+  extern __shared__ float xs[];  // K floats
+  __shared__ float red[8];
+  const int b = blockIdx.x, t = threadIdx.x;
+  if (p.kind == kRes || p.kind == kResNorm) {  // K == hidden size <= 2048
+    constexpr int PT = 2048 / 256;
+    float dv[PT], av[PT], ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < PT; ++j) {
+      const int i = t + 256 * j;
+      float s_ = 0.f, a_ = 0.f;
+      if (i < K) {
+        a_ = p.a[(size_t)b * K + i];
+        if (p.d)
+          for (int q = 0; q < p.nd; ++q) s_ += p.d[((size_t)q * rows + b) * K + i];
+      }
+      dv[j] = s_;
+      av[j] = a_;
+      ss += s_ * s_;
+    }
+    float rd = 0.f;
+    if (p.d) rd = rsqrtf(block_sum<256>(ss, red) / (float)K + p.eps);
+    const float sc = p.scalar ? bf2f(p.scalar[0]) : 1.0f;
+    float hs = 0.f;
+#pragma unroll
+    for (int j = 0; j < PT; ++j) {
+      const int i = t + 256 * j;
+      if (i < K) {
+        float hn = av[j];
+        if (p.d) hn = (hn + dv[j] * rd * bf2f(p.gd[i])) * sc;
+        av[j] = hn;
+        hs += hn * hn;
+        if (p.d && p.h_out) p.h_out[(size_t)b * K + i] = hn;
+      }
+    }
+    float rh = 1.f;
+    if (p.kind == kResNorm) rh = rsqrtf(block_sum<256>(hs, red) / (float)K + p.eps);
+#pragma unroll
+    for (int j = 0; j < PT; ++j) {
+      const int i = t + 256 * j;
+      if (i < K) xs[i] = p.kind == kResNorm ? av[j] * rh * bf2f(p.gx[i]) : av[j];
+    }
+  } else {
+    for (int i = t; i < K; i += 256) {
+      const float a0 = p.a[(size_t)b * p.lda + i];
+      float v = a0;
+      if (p.kind == kGeglu) v = gelu_tanh(a0) * p.a[(size_t)b * p.lda + K + i];
+      else if (p.kind == kPleGate) v = gelu_tanh(a0) * p.pli[(size_t)b * p.pli_ld + i];
+      xs[i] = v;
+    }
+  }
+  __syncthreads();
+  for (int i = t; i < K; i += 256) {
+    const float v = xs[i];
+    const uint32_t h = f2bf(v), l = f2bf(v - bf2f(h));
+    xh[(size_t)b * K + i] = (uint16_t)h;
+    xl[(size_t)b * K + i] = (uint16_t)l;
+    xs[i] = bf2f(h) + bf2f(l);
+  }
+  __syncthreads();
+  for (int g = t; g < K / 32; g += 256) {
+    float s_ = 0.f;
+    for (int k = 0; k < 32; ++k) s_ += xs[32 * g + k];
+    xg[(size_t)b * (K / 32) + g] = s_;
+  }
+}
+
+hipError_t launch_xprep(const Prologue& p, int rows, int K, uint16_t* xh, uint16_t* xl, float* xg,
+                        hipStream_t st) {
+  if ((p.kind == kRes || p.kind == kResNorm) && K > 2048) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_xprep, dim3(rows), dim3(256), (size_t)K * sizeof(float), st, p, rows, K,
+                     xh, xl, xg);
+  return hipGetLastError();
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+template <int WQ, int TAG>
+__global__ __launch_bounds__(256) void k_gemm(Lin W, int rows, const uint16_t* __restrict__ xh,
+                                              const uint16_t* __restrict__ xl,
+                                              const float* __restrict__ xg, int KS, Epilogue epi) {
+  __shared__ __attribute__((aligned(16))) uint16_t sh_h[kMB][kKC + 8];
+  __shared__ __attribute__((aligned(16))) uint16_t sh_l[kMB][kKC + 8];
+  __shared__ float sh_g[kMB][kKC / 32];
+  __shared__ float rv[4][kMB];
+  __shared__ int ri[4][kMB];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nb = blockIdx.x, ks = blockIdx.y, mb = blockIdx.z;
+  const int K = W.K, N = W.N;
+  const int m0 = mb * kMB, mrows = min(kMB, rows - m0);
+  const int nl = nb * kNB + wave * 16 + (lane & 15);  // this lane's weight row (B column)
+  const bool nok = nl < N;
+  const int kq = lane >> 4;
+  f32x4_t acc[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int kbeg = ks * KS, kend = kbeg + KS;
+  for (int kc = kbeg; kc < kend; kc += kKC) {
+    const int KC = min(kKC, kend - kc);  // k staged in this chunk (a multiple of 32)
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < kMB * KC / 8; idx += 256) {
+      const int m = idx / (KC / 8), k8 = idx % (KC / 8);
+      uint4 vh = make_uint4(0, 0, 0, 0), vl = make_uint4(0, 0, 0, 0);
+      if (m < mrows) {
+        vh = *reinterpret_cast<const uint4*>(xh + (size_t)(m0 + m) * K + kc + 8 * k8);
+        vl = *reinterpret_cast<const uint4*>(xl + (size_t)(m0 + m) * K + kc + 8 * k8);
+      }
+      *reinterpret_cast<uint4*>(&sh_h[m][8 * k8]) = vh;
+      *reinterpret_cast<uint4*>(&sh_l[m][8 * k8]) = vl;
+    }
+    if (WQ)
+      for (int idx = threadIdx.x; idx < kMB * (KC / 32); idx += 256) {
+        const int m = idx / (KC / 32), g = idx % (KC / 32);
+        sh_g[m][g] = m < mrows ? xg[(size_t)(m0 + m) * (K / 32) + kc / 32 + g] : 0.f;
+      }
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < kKC / 32; ++s) {
+      if (32 * s >= KC) break;
+      const int k0 = kc + 32 * s;
+      uint4 bw = make_uint4(0, 0, 0, 0);
+      float scl = 0.f;
+      if (WQ) {
+        uint32_t word = 0x88888888u;  // code 8: q = 0
+        if (nok) {
+          word = W.q[(size_t)nl * (K / 8) + k0 / 8 + kq];
+          scl = bf2f(W.s[(size_t)nl * (K / 32) + k0 / 32]);
+        }
+        const uint32_t lo = word & 0x0F0F0F0Fu, hi = (word >> 4) & 0x0F0F0F0Fu;
+        const uint32_t u = __builtin_amdgcn_perm(hi, lo, 0x05010400u);  // codes 0,1,2,3 as bytes
+        const uint32_t v = __builtin_amdgcn_perm(hi, lo, 0x07030602u);  // codes 4,5,6,7
+        bw.x = __builtin_amdgcn_perm(0x43434343u, u, 0x04010400u);
+        bw.y = __builtin_amdgcn_perm(0x43434343u, u, 0x04030402u);
+        bw.z = __builtin_amdgcn_perm(0x43434343u, v, 0x04010400u);
+        bw.w = __builtin_amdgcn_perm(0x43434343u, v, 0x04030402u);
+      } else if (nok) {
+        bw = *reinterpret_cast<const uint4*>(W.w + (size_t)nl * K + k0 + 8 * kq);
+      }
+      const bf16x8_t B = as_bf16x8(bw);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const int mr = 16 * mt + (lane & 15);
+        const bf16x8_t Ah = as_bf16x8(*reinterpret_cast<const uint4*>(&sh_h[mr][32 * s + 8 * kq]));
+        const bf16x8_t Al = as_bf16x8(*reinterpret_cast<const uint4*>(&sh_l[mr][32 * s + 8 * kq]));
+        if (WQ) {
+          f32x4_t t4 = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          t4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ah, B, t4, 0, 0, 0);
+          t4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Al, B, t4, 0, 0, 0);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            acc[mt][i] += scl * (t4[i] - 136.0f * sh_g[16 * mt + 4 * kq + i][s]);
+        } else {
+          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ah, B, acc[mt], 0, 0, 0);
+          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Al, B, acc[mt], 0, 0, 0);
+        }
+      }
+    }
+  }
+  if (!epi.argmax) {
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = 16 * mt + 4 * kq + i;
+        if (m < mrows && nok) epi.y[((size_t)ks * rows + m0 + m) * N + nl] = acc[mt][i];
+      }
+    return;
+  }
+  // argmax: per row, best (value, lowest index) over this block's 64 columns
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = 16 * mt + 4 * kq + i;
+      float v = nok ? acc[mt][i] : -FLT_MAX;
+      int x = nok ? nl : 0x7FFFFFFF;
+      if (epi.logits && nok && m < mrows) epi.logits[(size_t)(m0 + m) * N + nl] = v;
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) {
+        const float ov = __shfl_xor(v, o, 64);
+        const int ox = __shfl_xor(x, o, 64);
+        if (ov > v || (ov == v && ox < x)) {
+          v = ov;
+          x = ox;
+        }
+      }
+      if ((lane & 15) == 0) {
+        rv[wave][m] = v;
+        ri[wave][m] = x;
+      }
+    }
+  __syncthreads();
+  if (threadIdx.x < mrows) {
+    const int m = threadIdx.x;
+    float v = rv[0][m];
+    int x = ri[0][m];
+    for (int w = 1; w < 4; ++w)
+      if (rv[w][m] > v || (rv[w][m] == v && ri[w][m] < x)) {
+        v = rv[w][m];
+        x = ri[w][m];
+      }
+    epi.cand_val[(size_t)(m0 + m) * gridDim.x + nb] = v;
+    epi.cand_idx[(size_t)(m0 + m) * gridDim.x + nb] = x;
+  }
+}
+
+// K slices of the batched product: only where the consumer sums partials
+int gemm_splits(int K, bool partial_ok) {
+  if (!partial_ok) return 1;
+  if (K % (6 * kKC) == 0 && K >= 6 * 2048) return 6;
+  if (K % (3 * kKC) == 0 && K >= 3 * 1024) return 3;
+  if (K % (2 * kKC) == 0 && K >= 2048) return 2;
+  return 1;
+}
+
+template <int WQ, int TAG>
+static hipError_t run_gemm(const Lin& W, int rows, const uint16_t* xh, const uint16_t* xl,
+                           const float* xg, int nks, const Epilogue& epi, int* nblk, hipStream_t st) {
+  const int nbx = (W.N + kNB - 1) / kNB;
+  if (nblk) *nblk = nbx;
+  dim3 grid(nbx, nks, (rows + kMB - 1) / kMB);
+  hipLaunchKernelGGL((k_gemm<WQ, TAG>), grid, dim3(256), 0, st, W, rows, xh, xl, xg, W.K / nks, epi);
+  return hipGetLastError();
+}
+
+template <int WQ>
+static hipError_t gemm_tag(int tag, const Lin& W, int rows, const uint16_t* xh, const uint16_t* xl,
+                           const float* xg, int nks, const Epilogue& epi, int* nblk, hipStream_t st) {
+  switch (tag) {
+    case kTagQkv: return run_gemm<WQ, kTagQkv>(W, rows, xh, xl, xg, nks, epi, nblk, st);
+    case kTagO: return run_gemm<WQ, kTagO>(W, rows, xh, xl, xg, nks, epi, nblk, st);
+    case kTagGateUp: return run_gemm<WQ, kTagGateUp>(W, rows, xh, xl, xg, nks, epi, nblk, st);
+    case kTagDown: return run_gemm<WQ, kTagDown>(W, rows, xh, xl, xg, nks, epi, nblk, st);
+    case kTagPleGate: return run_gemm<WQ, kTagPleGate>(W, rows, xh, xl, xg, nks, epi, nblk, st);
+    case kTagPleProj: return run_gemm<WQ, kTagPleProj>(W, rows, xh, xl, xg, nks, epi, nblk, st);
+    case kTagPleModel: return run_gemm<WQ, kTagPleModel>(W, rows, xh, xl, xg, nks, epi, nblk, st);
+    case kTagLmHead: return run_gemm<WQ, kTagLmHead>(W, rows, xh, xl, xg, nks, epi, nblk, st);
+    default: return run_gemm<WQ, kTagOther>(W, rows, xh, xl, xg, nks, epi, nblk, st);
+  }
+}
+
+hipError_t launch_gemm(int quant, int tag, const Lin& W, int rows, const uint16_t* xh,
+                       const uint16_t* xl, const float* xg, int nks, const Epilogue& epi,
+                       int* nblk, hipStream_t st) {
+  if (rows < 1 || nks < 1 || W.K % nks || (W.K / nks) % 32) return hipErrorInvalidValue;
+  if (epi.argmax && (quant || nks != 1)) return hipErrorInvalidValue;
+  return quant ? gemm_tag<1>(tag, W, rows, xh, xl, xg, nks, epi, nblk, st)
+               : gemm_tag<0>(tag, W, rows, xh, xl, xg, nks, epi, nblk, st);
 }
 
 // positions[r] += 1 (graph-replayed decode loops advance on the device)
