@@ -198,11 +198,11 @@ int e2b_kv_view(const e2b_model* model, int layer, int which, void** out);
  * at most 8 equal slices of width 32, 128, 256, 512, 1536 or 2048 (the first
  * that divides K among 2048, 1536; else K itself when K <= 512; else 512);
  * other K -> E2B_EINVAL.  d_ws (256-byte
- * aligned) must hold e2b_matvec_workspace_bytes(N, K, rows) bytes (0 for
+ * aligned) must hold e2b_matvec_workspace_bytes(quant, N, K, rows) bytes (0 for
  * one row with K <= 2048, else nonzero).  One row streams the weights through
  * the matvec kernel; two or more rows share one pass over the weights on the
  * matrix cores.  Asynchronous. */
-size_t e2b_matvec_workspace_bytes(int N, int K, int rows);
+size_t e2b_matvec_workspace_bytes(int quant, int N, int K, int rows);
 int e2b_matvec(int quant, const void* d_w, const uint16_t* d_scale, int N, int K,
                const float* d_x, int rows, float* d_y, void* d_ws, size_t ws_bytes,
                void* stream);

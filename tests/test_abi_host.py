@@ -146,16 +146,21 @@ def test_matvec_validation(lib):
     L = lib.load_library()
     assert L.e2b_matvec(0, 256, None, 8, 100, 256, 1, 256, None, 0, None) == lib.E2B_EINVAL
     assert L.e2b_matvec(1, 256, None, 8, 1536, 256, 1, 256, None, 0, None) == lib.E2B_EINVAL
-    assert L.e2b_matvec_workspace_bytes(1536, 12288, 1) == 6 * 1536 * 4   # six 2048-wide slices
-    assert L.e2b_matvec_workspace_bytes(1536, 1536, 1) == 0
+    assert L.e2b_matvec_workspace_bytes(0, 1536, 12288, 1) == 6 * 1536 * 4   # six 2048-wide slices
+    assert L.e2b_matvec_workspace_bytes(0, 1536, 1536, 1) == 0
     # widths with no matvec instantiation are refused by both paths
     for K in (64, 96, 160, 480, 4608 * 4):
-        assert L.e2b_matvec_workspace_bytes(64, K, 3) == 0, K
+        assert L.e2b_matvec_workspace_bytes(0, 64, K, 3) == 0, K
         assert L.e2b_matvec(0, 256, None, 8, K, 256, 3, 256, 256, 1 << 20, None) == lib.E2B_EINVAL, K
     # several rows: bf16 hi and lo rows + fp32 group sums (256-byte aligned
     # regions), then the K-slice partials of the matrix-core path
     up = lambda b: (b + 255) // 256 * 256
     prep = lambda r, K: 2 * up(2 * r * K) + up(4 * r * (K // 32))
-    assert L.e2b_matvec_workspace_bytes(1536, 1536, 3) == prep(3, 1536)
-    assert L.e2b_matvec_workspace_bytes(1536, 12288, 70) == prep(70, 12288) + 6 * 70 * 1536 * 4
-    assert L.e2b_matvec_workspace_bytes(1536, 4096, 2) == prep(2, 4096) + 2 * 2 * 1536 * 4
+    for quant in (0, 1):
+        for N, K, r in ((1536, 1536, 3), (1536, 12288, 70), (1536, 4096, 2), (24576, 1536, 64)):
+            extra = L.e2b_matvec_workspace_bytes(quant, N, K, r) - prep(r, K)
+            slices, rem = divmod(extra, r * N * 4)
+            assert rem == 0 and slices in (0, 2, 3, 4, 6, 8, 12, 16), (quant, N, K, r, extra)
+            if slices:
+                assert K % slices == 0 and (K // slices) % 32 == 0
+    assert L.e2b_matvec_workspace_bytes(2, 1536, 1536, 3) == 0   # unknown quant

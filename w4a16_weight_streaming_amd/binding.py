@@ -88,7 +88,7 @@ def load_library():
                                    ctypes.POINTER(ctypes.c_double)]
     L.e2b_kv_view.argtypes = [vp, i32, i32, ctypes.POINTER(vp)]
     L.e2b_matvec_workspace_bytes.restype = sz
-    L.e2b_matvec_workspace_bytes.argtypes = [i32, i32, i32]
+    L.e2b_matvec_workspace_bytes.argtypes = [i32, i32, i32, i32]
     L.e2b_matvec.argtypes = [i32, vp, vp, i32, i32, vp, i32, vp, vp, sz, vp]
     for f in ("e2b_config_preset", "e2b_create", "e2b_kv_share_map", "e2b_load_weights",
               "e2b_kv_alloc", "e2b_decode_step", "e2b_prefill", "e2b_check", "e2b_kv_view",
@@ -183,7 +183,7 @@ def matvec(quant: str, w, scale, x, y, ws=None):
     N = y.shape[-1]
     K = x.shape[-1]
     rows = x.numel() // K
-    need = L.e2b_matvec_workspace_bytes(N, K, rows)
+    need = L.e2b_matvec_workspace_bytes(QUANT[quant], N, K, rows)
     if need and (ws is None or ws.numel() < need):
         ws = torch.empty(need, dtype=torch.uint8, device=x.device)
     _check(L.e2b_matvec(QUANT[quant], w.data_ptr(), 0 if scale is None else scale.data_ptr(), N, K,

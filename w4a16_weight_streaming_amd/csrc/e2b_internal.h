@@ -9,6 +9,7 @@ namespace e2b {
 
 constexpr int kMaxChunks = 64;   // attention key chunks per (row, layer)
 constexpr int kMaxSplitK = 8;    // K slices of one matrix-vector product
+constexpr int kMaxGemmSplit = 16;  // K slices of one batched (matrix-core) product
 constexpr int kGemvThreads = 256;
 constexpr int kLmBlocks = 1024;  // blocks of the lm_head pass (argmax candidates)
 
@@ -53,8 +54,11 @@ struct Prologue {
   int kind = kPlain;
   const float* a = nullptr;   // kPlain: x [rows, lda]; kRes*: h [rows, K]; kGeglu: [rows, 2K]; kPleGate: [rows, K]
   int lda = 0;                // row stride of a (elements)
-  const float* d = nullptr;   // delta partials [nd][rows][K] (kRes*), may be null
+  const float* d = nullptr;   // delta partials: nd of them, d_pstride floats apart, each [rows][K]
   int nd = 0;
+  size_t d_pstride = 0;
+  int na = 1;                 // batched prep only: a is the sum of na partials a_pstride apart
+  size_t a_pstride = 0;
   const uint16_t* gd = nullptr;      // gain of rms(delta)
   const uint16_t* scalar = nullptr;  // layer scalar (bf16[1]) or null
   const uint16_t* gx = nullptr;      // gain of rms(h') (kResNorm)
@@ -87,6 +91,8 @@ struct AttnArgs {
   float* out = nullptr;         // [rows][nq * hd]
   int nq = 0, hd = 0, window = 0 /* 0: full */, chunk = 0, nchunk = 0;
   int owns = 0;                 // the layer computes K/V (raw rows hold q, k, v)
+  int qkv_parts = 1;            // qkv is the sum of this many partials
+  size_t qkv_pstride = 0;       // floats between partials
   float eps = 1e-6f;
 };
 
@@ -99,6 +105,8 @@ struct QkvPostArgs {
   uint16_t* kc = nullptr;       // this layer's cache when it owns K/V, else null
   uint16_t* vc = nullptr;
   int nq = 0, hd = 0;
+  int qkv_parts = 1;
+  size_t qkv_pstride = 0;
   float eps = 1e-6f;
 };
 
@@ -106,9 +114,10 @@ struct QkvPostArgs {
 hipError_t launch_embed(const Rows& R, const uint16_t* E, const uint16_t* Eple, int H, int LP,
                         float sqrtH, float sqrtP, float* h, float* tokple, int* err,
                         hipStream_t st);
-hipError_t launch_ple_finish(const Rows& R, const float* u, const float* tokple,
-                             const uint16_t* g, int L, int P, float inv_sqrtH, float eps,
-                             float* pli, hipStream_t st);
+// u: u_parts partials u_pstride floats apart, each [rows][L*P]
+hipError_t launch_ple_finish(const Rows& R, const float* u, int u_parts, size_t u_pstride,
+                             const float* tokple, const uint16_t* g, int L, int P,
+                             float inv_sqrtH, float eps, float* pli, hipStream_t st);
 // blocks_hint > 0 fixes the number of blocks along N (else chosen from N);
 // *blocks_out (nullable) receives it -- the argmax candidate count per row.
 hipError_t launch_gemv(int quant, int tag, const Lin& W, int rows, const Prologue& pro,
@@ -121,11 +130,15 @@ hipError_t launch_advance(int32_t* pos, int n, hipStream_t st);
 // batched rows (>= 2): prologue into bf16 hi/lo rows + group sums, then MFMA
 hipError_t launch_xprep(const Prologue& p, int rows, int K, uint16_t* xh, uint16_t* xl, float* xg,
                         hipStream_t st);
-int gemm_splits(int K, bool partial_ok);
+struct GemmPlan {
+  int nt = 1;   // 16-column tiles per wave (block covers 64 * nt columns)
+  int nks = 1;  // K slices (partials written [nks][rows][N])
+};
+GemmPlan gemm_plan(int quant, int N, int K, bool partial_ok);
 // *nblk receives the number of column blocks (argmax candidates per row)
 hipError_t launch_gemm(int quant, int tag, const Lin& W, int rows, const uint16_t* xh,
-                       const uint16_t* xl, const float* xg, int nks, const Epilogue& epi,
-                       int* nblk, hipStream_t st);
+                       const uint16_t* xl, const float* xg, const GemmPlan& plan,
+                       const Epilogue& epi, int* nblk, hipStream_t st);
 hipError_t launch_sum_partials(int nparts, size_t n, const float* parts, float* out,
                                hipStream_t st);
 hipError_t launch_argmax_final(int rows, int nblk, const float* cand_val,

@@ -257,30 +257,41 @@ Ws ws_layout(const e2b_model* m, int R) {
   };
   const size_t f = sizeof(float);
   const int hdm = std::max(m->c.head_dim, m->c.global_head_dim);
-  int Imax = 0, nko = 1, nkd = 1, Kmax = std::max(m->H, m->P);
+  // K-slice partials a product can write (matvec or matrix-core plan)
+  auto parts = [&](int N, int K) {
+    return std::max(e2b::gemv_splits(K), e2b::gemm_plan(m->quant, N, K, true).nks);
+  };
+  const int H = m->H, P = m->P, LPn = m->L * m->P;
+  int Kmax = std::max(H, P);
+  size_t qkv_f = 0, gu_f = 0, oo_f = 0, dn_f = 0, pgy_f = 0, ppo_f = 0;
   for (const LayerInfo& y : m->li) {
-    Imax = std::max(Imax, y.I);
+    const int nqkv = (m->nq + (y.src == &y - &m->li[0] ? 2 : 0)) * y.hd;
     Kmax = std::max(Kmax, std::max(y.I, m->nq * y.hd));
-    nko = std::max(nko, std::max(e2b::gemv_splits(m->nq * y.hd), e2b::gemm_splits(m->nq * y.hd, true)));
-    nkd = std::max(nkd, std::max(e2b::gemv_splits(y.I), e2b::gemm_splits(y.I, true)));
+    qkv_f = std::max(qkv_f, (size_t)parts(nqkv, H) * nqkv);
+    gu_f = std::max(gu_f, (size_t)parts(2 * y.I, H) * 2 * y.I);
+    oo_f = std::max(oo_f, (size_t)parts(H, m->nq * y.hd) * H);
+    dn_f = std::max(dn_f, (size_t)parts(H, y.I) * H);
+    pgy_f = std::max(pgy_f, (size_t)parts(P, H) * P);
+    ppo_f = std::max(ppo_f, (size_t)parts(H, P) * H);
   }
+  const size_t u_f = (size_t)parts(LPn, H) * LPn;
   w.ncand = std::max(e2b::kLmBlocks, (m->V + 63) / 64);
   const size_t LP = (size_t)m->L * m->P;
   w.err = take(64);
   w.h0 = take(f * R * m->H);
   w.h1 = take(f * R * m->H);
   w.tokple = take(f * R * LP);
-  w.u = take(f * R * LP);
+  w.u = take(f * R * u_f);
   w.pli = take(f * R * LP);
-  w.qkv = take(f * R * (m->nq + 2) * hdm);
+  w.qkv = take(f * R * qkv_f);
   w.qn = take(f * R * m->nq * hdm);
   w.part = take(f * R * m->nq * e2b::kMaxChunks * (hdm + 2));
   w.attn = take(f * R * m->nq * hdm);
-  w.oo = take(f * nko * R * m->H);
-  w.gu = take(f * R * 2 * Imax);
-  w.dn = take(f * nkd * R * m->H);
-  w.pgy = take(f * R * m->P);
-  w.ppo = take(f * R * m->H);
+  w.oo = take(f * R * oo_f);
+  w.gu = take(f * R * gu_f);
+  w.dn = take(f * R * dn_f);
+  w.pgy = take(f * R * pgy_f);
+  w.ppo = take(f * R * ppo_f);
   w.cv = take(f * R * w.ncand);
   w.ci = take(sizeof(int32_t) * R * w.ncand);
   if (R > 1) {  // batched rows go through the MFMA path
@@ -335,14 +346,17 @@ hipError_t matmul(e2b_model* m, int quant, int tag, const Lin& W, int rows, bool
   int splits = 1;
   if (!batched) {
     splits = e2b::gemv_splits(W.K);
+    // the matvec prologue reads one copy of a; it splits only K > 2048
+    if (pr.na != 1 || (splits > 1 && !partial_ok)) return hipErrorInvalidValue;
     e = e2b::launch_gemv(quant, tag, W, rows, pr, ep, 0, nblk, st);
   } else {
     uint16_t* xh = reinterpret_cast<uint16_t*>(ws + L.xh);
     uint16_t* xl = reinterpret_cast<uint16_t*>(ws + L.xl);
     float* xg = reinterpret_cast<float*>(ws + L.xg);
-    splits = e2b::gemm_splits(W.K, partial_ok);
+    const e2b::GemmPlan plan = e2b::gemm_plan(quant, W.N, W.K, partial_ok);
+    splits = plan.nks;
     e = e2b::launch_xprep(pr, rows, W.K, xh, xl, xg, st);
-    if (e == hipSuccess) e = e2b::launch_gemm(quant, tag, W, rows, xh, xl, xg, splits, ep, nblk, st);
+    if (e == hipSuccess) e = e2b::launch_gemm(quant, tag, W, rows, xh, xl, xg, plan, ep, nblk, st);
   }
   if (nd) *nd = splits;
   if (e != hipSuccess) return e;
@@ -367,6 +381,8 @@ int run_rows(e2b_model* m, const e2b::Rows& R, bool head, int head_row, float* d
   auto F = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
   int* err = reinterpret_cast<int*>(ws + W.err);
 
+  const bool bat = n > 1;  // batched pass: matrix-core products
+  int nd_u = 1;            // K-slice partials of the per-layer model projection
   CK(launch_embed(R, m->embed, m->ple, H, LP, std::sqrt((float)H), std::sqrt((float)P), F(W.h0),
                   F(W.tokple), err, st),
      "embed");
@@ -377,27 +393,30 @@ int run_rows(e2b_model* m, const e2b::Rows& R, bool head, int head_row, float* d
     pr.lda = H;
     Epilogue ep;
     ep.y = F(W.u);
-    CK(matmul(m, q, kTagPleModel, m->plmp, n, n > 1, pr, ep, false, nullptr, nullptr, ws, W, st), "per-layer model projection");
+    CK(matmul(m, q, kTagPleModel, m->plmp, n, bat, pr, ep, true, &nd_u, nullptr, ws, W, st),
+       "per-layer model projection");
   }
-  CK(launch_ple_finish(R, F(W.u), F(W.tokple), m->g_plpn, L, P, 1.0f / std::sqrt((float)H), eps,
-                       F(W.pli), st),
+  CK(launch_ple_finish(R, F(W.u), nd_u, (size_t)n * LP, F(W.tokple), m->g_plpn, L, P,
+                       1.0f / std::sqrt((float)H), eps, F(W.pli), st),
      "per-layer inputs");
 
   float* cur = F(W.h0);
   float* oth = F(W.h1);
   const float* pend = nullptr;  // per-layer projection output not yet added
+  int pend_n = 1;               // ... as this many K-slice partials
   const uint16_t *pend_g = nullptr, *pend_s = nullptr;
   for (int l = 0; l < L; ++l) {
     const LayerInfo& y = m->li[l];
     const LayerDev& d = m->ld[l];
     const bool owns = y.src == l;
-    int nd_o = 1, nd_dn = 1;  // K-slice partials of the O and down products
+    int nd_qkv = 1, nd_o = 1, nd_gu = 1, nd_dn = 1, nd_pg = 1;  // K-slice partials written
     {  // QKV with the residual update of the previous layer fused in front
       Prologue pr;
       pr.kind = kResNorm;
       pr.a = cur;
       pr.d = pend;
-      pr.nd = 1;
+      pr.nd = pend_n;
+      pr.d_pstride = (size_t)n * H;
       pr.gd = pend_g;
       pr.scalar = pend_s;
       pr.gx = d.g_in;
@@ -405,7 +424,8 @@ int run_rows(e2b_model* m, const e2b::Rows& R, bool head, int head_row, float* d
       pr.eps = eps;
       Epilogue ep;
       ep.y = F(W.qkv);
-      CK(matmul(m, q, kTagQkv, d.qkv, n, n > 1, pr, ep, false, nullptr, nullptr, ws, W, st), "qkv projection");
+      CK(matmul(m, q, kTagQkv, d.qkv, n, bat, pr, ep, true, &nd_qkv, nullptr, ws, W, st),
+         "qkv projection");
       if (pend) std::swap(cur, oth);
     }
     // decode rows are distinct sequences: the attention kernel writes the new
@@ -422,6 +442,8 @@ int run_rows(e2b_model* m, const e2b::Rows& R, bool head, int head_row, float* d
       a.vc = m->vc[l];
       a.nq = m->nq;
       a.hd = y.hd;
+      a.qkv_parts = nd_qkv;
+      a.qkv_pstride = (size_t)n * d.qkv.N;
       a.eps = eps;
       CK(launch_qkv_post(R, a, st), "k/v write");
     }
@@ -441,6 +463,8 @@ int run_rows(e2b_model* m, const e2b::Rows& R, bool head, int head_row, float* d
       a.nq = m->nq;
       a.hd = y.hd;
       a.window = y.full ? 0 : m->c.sliding_window;
+      a.qkv_parts = nd_qkv;
+      a.qkv_pstride = (size_t)n * d.qkv.N;
       a.eps = eps;
       attn_chunks(m, y.full, &a.chunk, &a.nchunk);
       CK(launch_attention(R, a, st), "attention");
@@ -452,7 +476,7 @@ int run_rows(e2b_model* m, const e2b::Rows& R, bool head, int head_row, float* d
       pr.lda = m->nq * y.hd;
       Epilogue ep;
       ep.y = F(W.oo);
-      CK(matmul(m, q, kTagO, d.o, n, n > 1, pr, ep, true, &nd_o, nullptr, ws, W, st), "o projection");
+      CK(matmul(m, q, kTagO, d.o, n, bat, pr, ep, true, &nd_o, nullptr, ws, W, st), "o projection");
     }
     {  // post-attention norm + residual, pre-FFN norm, gate/up
       Prologue pr;
@@ -460,13 +484,15 @@ int run_rows(e2b_model* m, const e2b::Rows& R, bool head, int head_row, float* d
       pr.a = cur;
       pr.d = F(W.oo);
       pr.nd = nd_o;
+      pr.d_pstride = (size_t)n * H;
       pr.gd = d.g_pa;
       pr.gx = d.g_pf;
       pr.h_out = oth;
       pr.eps = eps;
       Epilogue ep;
       ep.y = F(W.gu);
-      CK(matmul(m, q, kTagGateUp, d.gu, n, n > 1, pr, ep, false, nullptr, nullptr, ws, W, st), "gate/up projection");
+      CK(matmul(m, q, kTagGateUp, d.gu, n, bat, pr, ep, true, &nd_gu, nullptr, ws, W, st),
+         "gate/up projection");
       std::swap(cur, oth);
     }
     {  // GeGLU then down
@@ -474,9 +500,12 @@ int run_rows(e2b_model* m, const e2b::Rows& R, bool head, int head_row, float* d
       pr.kind = kGeglu;
       pr.a = F(W.gu);
       pr.lda = 2 * y.I;
+      pr.na = nd_gu;
+      pr.a_pstride = (size_t)n * 2 * y.I;
       Epilogue ep;
       ep.y = F(W.dn);
-      CK(matmul(m, q, kTagDown, d.down, n, n > 1, pr, ep, true, &nd_dn, nullptr, ws, W, st), "down projection");
+      CK(matmul(m, q, kTagDown, d.down, n, bat, pr, ep, true, &nd_dn, nullptr, ws, W, st),
+         "down projection");
     }
     {  // post-FFN norm + residual, per-layer input gate
       Prologue pr;
@@ -484,12 +513,14 @@ int run_rows(e2b_model* m, const e2b::Rows& R, bool head, int head_row, float* d
       pr.a = cur;
       pr.d = F(W.dn);
       pr.nd = nd_dn;
+      pr.d_pstride = (size_t)n * H;
       pr.gd = d.g_ff;
       pr.h_out = oth;
       pr.eps = eps;
       Epilogue ep;
       ep.y = F(W.pgy);
-      CK(matmul(m, q, kTagPleGate, d.pg, n, n > 1, pr, ep, false, nullptr, nullptr, ws, W, st), "per-layer input gate");
+      CK(matmul(m, q, kTagPleGate, d.pg, n, bat, pr, ep, true, &nd_pg, nullptr, ws, W, st),
+         "per-layer input gate");
       std::swap(cur, oth);
     }
     {  // gelu(gate) * pli[l], per-layer projection
@@ -497,11 +528,14 @@ int run_rows(e2b_model* m, const e2b::Rows& R, bool head, int head_row, float* d
       pr.kind = kPleGate;
       pr.a = F(W.pgy);
       pr.lda = P;
+      pr.na = nd_pg;
+      pr.a_pstride = (size_t)n * P;
       pr.pli = F(W.pli) + (size_t)l * P;
       pr.pli_ld = LP;
       Epilogue ep;
       ep.y = F(W.ppo);
-      CK(matmul(m, q, kTagPleProj, d.pp, n, n > 1, pr, ep, false, nullptr, nullptr, ws, W, st), "per-layer projection");
+      CK(matmul(m, q, kTagPleProj, d.pp, n, bat, pr, ep, true, &pend_n, nullptr, ws, W, st),
+         "per-layer projection");
     }
     pend = F(W.ppo);
     pend_g = d.g_pple;
@@ -518,7 +552,8 @@ int run_rows(e2b_model* m, const e2b::Rows& R, bool head, int head_row, float* d
   pr.kind = kResNorm;
   pr.a = cur + (size_t)hr * H;
   pr.d = pend + (size_t)hr * H;
-  pr.nd = 1;
+  pr.nd = pend_n;
+  pr.d_pstride = (size_t)n * H;
   pr.gd = pend_g;
   pr.scalar = pend_s;
   pr.gx = m->g_final;
@@ -530,7 +565,8 @@ int run_rows(e2b_model* m, const e2b::Rows& R, bool head, int head_row, float* d
   ep.cand_val = F(W.cv);
   ep.cand_idx = reinterpret_cast<int32_t*>(ws + W.ci);
   int nblk = 0;
-  CK(matmul(m, E2B_QUANT_BF16, kTagLmHead, E, nh, n > 1, pr, ep, false, nullptr, &nblk, ws, W, st), "lm_head");
+  CK(matmul(m, E2B_QUANT_BF16, kTagLmHead, E, nh, bat, pr, ep, false, nullptr, &nblk, ws, W, st),
+     "lm_head");
   if (nblk > W.ncand) return fail(E2B_EINVAL, "lm_head: %d candidate blocks", nblk);
   CK(launch_argmax_final(nh, nblk, ep.cand_val, ep.cand_idx, d_argmax, st), "argmax");
   return E2B_OK;
@@ -854,14 +890,14 @@ struct MvWs {
   size_t xh, xl, xg, part, total;
   int nks;
 };
-MvWs matvec_ws(int N, int K, int rows) {
+MvWs matvec_ws(int quant, int N, int K, int rows) {
   MvWs w{};
   auto up = [](size_t b) { return (b + 255) & ~(size_t)255; };
   if (rows == 1) {
     w.nks = e2b::gemv_splits(K);
     w.part = 0;
   } else {
-    w.nks = e2b::gemm_splits(K, true);
+    w.nks = e2b::gemm_plan(quant, N, K, true).nks;
     w.xh = 0;
     w.xl = up(2 * (size_t)rows * K);
     w.xg = w.xl + up(2 * (size_t)rows * K);
@@ -872,9 +908,10 @@ MvWs matvec_ws(int N, int K, int rows) {
 }
 }  // namespace
 
-size_t e2b_matvec_workspace_bytes(int N, int K, int rows) {
+size_t e2b_matvec_workspace_bytes(int quant, int N, int K, int rows) {
+  if (quant != E2B_QUANT_BF16 && quant != E2B_QUANT_W4A16) return 0;
   if (N < 1 || rows < 1 || K < 32 || K % 32 || !supported_k(K)) return 0;
-  return matvec_ws(N, K, rows).total;
+  return matvec_ws(quant, N, K, rows).total;
 }
 
 int e2b_matvec(int quant, const void* d_w, const uint16_t* d_scale, int N, int K,
@@ -887,7 +924,7 @@ int e2b_matvec(int quant, const void* d_w, const uint16_t* d_scale, int N, int K
   if (N < 1 || rows < 1 || rows > 65535 || K % 32 || !supported_k(K))
     return fail(E2B_EINVAL, "unsupported shape N=%d K=%d rows=%d", N, K, rows);
   if (reinterpret_cast<uintptr_t>(d_w) % 16) return fail(E2B_EINVAL, "weights must be 16-byte aligned");
-  const MvWs L = matvec_ws(N, K, rows);
+  const MvWs L = matvec_ws(quant, N, K, rows);
   if (L.total && (!d_ws || ws_bytes < L.total))
     return fail(E2B_ENOMEM, "workspace of %zu bytes < %zu required", ws_bytes, L.total);
   if (L.total && reinterpret_cast<uintptr_t>(d_ws) % 256)
@@ -916,7 +953,8 @@ int e2b_matvec(int quant, const void* d_w, const uint16_t* d_scale, int N, int K
     uint16_t* xl = reinterpret_cast<uint16_t*>(ws + L.xl);
     float* xg = reinterpret_cast<float*>(ws + L.xg);
     CK(e2b::launch_xprep(pr, rows, K, xh, xl, xg, st), "matvec input prep");
-    CK(e2b::launch_gemm(quant, e2b::kTagOther, W, rows, xh, xl, xg, L.nks, ep, nullptr, st),
+    CK(e2b::launch_gemm(quant, e2b::kTagOther, W, rows, xh, xl, xg,
+                        e2b::gemm_plan(quant, N, K, true), ep, nullptr, st),
        "matvec mfma");
   }
   if (L.nks > 1) CK(e2b::launch_sum_partials(L.nks, (size_t)rows * N, ep.y, d_y, st), "matvec sum");

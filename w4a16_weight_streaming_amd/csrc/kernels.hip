@@ -17,6 +17,7 @@
 #include "e2b_internal.h"
 
 #include <float.h>
+#include <type_traits>
 #include <math.h>
 
 namespace e2b {
@@ -109,24 +110,29 @@ hipError_t launch_embed(const Rows& R, const uint16_t* E, const uint16_t* Eple, 
 // ------------------------------------------------------ per-layer input finish
 // pli[r][l] = (rms(u[r][l] * H^-1/2) * g + tokple[r][l]) * 2^-1/2
 __global__ __launch_bounds__(256) void k_ple_finish(int LP, int P, const float* __restrict__ u,
+                                                    int u_parts, size_t u_pstride,
                                                     const float* __restrict__ tokple,
                                                     const uint16_t* __restrict__ g, float inv_sqrtH,
                                                     float eps, float* __restrict__ pli) {
   __shared__ float sh[4];
   const int r = blockIdx.x, l = blockIdx.y, i = threadIdx.x;
   const size_t base = (size_t)r * LP + (size_t)l * P;
-  float v = (i < P) ? u[base + i] * inv_sqrtH : 0.f;
+  float v = 0.f;
+  if (i < P) {
+    for (int q = 0; q < u_parts; ++q) v += u[(size_t)q * u_pstride + base + i];
+    v *= inv_sqrtH;
+  }
   const float ss = block_sum<256>(v * v, sh);
   const float rr = rsqrtf(ss / (float)P + eps);
   if (i < P) pli[base + i] = (v * rr * bf2f(g[i]) + tokple[base + i]) * 0.70710678118654752f;
 }
 
-hipError_t launch_ple_finish(const Rows& R, const float* u, const float* tokple,
-                             const uint16_t* g, int L, int P, float inv_sqrtH, float eps,
-                             float* pli, hipStream_t st) {
-  if (P > 256) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_ple_finish, dim3(R.n, L), dim3(256), 0, st, L * P, P, u, tokple, g,
-                     inv_sqrtH, eps, pli);
+hipError_t launch_ple_finish(const Rows& R, const float* u, int u_parts, size_t u_pstride,
+                             const float* tokple, const uint16_t* g, int L, int P,
+                             float inv_sqrtH, float eps, float* pli, hipStream_t st) {
+  if (P > 256 || u_parts < 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_ple_finish, dim3(R.n, L), dim3(256), 0, st, L * P, P, u, u_parts, u_pstride,
+                     tokple, g, inv_sqrtH, eps, pli);
   return hipGetLastError();
 }
 
@@ -178,7 +184,7 @@ struct PrologueRegs {
         if (p.d) {
 #pragma unroll
           for (int q = 0; q < kMaxSplitK; ++q)
-            if (q < p.nd) dq[j][q] = p.d[((size_t)q * rows + b) * K + i];
+            if (q < p.nd) dq[j][q] = p.d[(size_t)q * p.d_pstride + (size_t)b * K + i];
           g0[j] = bf2f(p.gd[i]);
         }
         if (p.kind == kResNorm) g1[j] = bf2f(p.gx[i]);
@@ -616,14 +622,16 @@ __device__ __forceinline__ void load_row(const uint16_t* p, float (&out)[DPL]) {
 // by lane l ^ 32.  Used for queries, and for the keys and values written to
 // the cache, by both the decode and the prefill path (identical arithmetic).
 template <int HD>
-__device__ __forceinline__ void head_vec(const float* raw, const uint16_t* gain, bool rope,
-                                         const float* cs, const float* sn, int lane, float eps,
+__device__ __forceinline__ void head_vec(const float* raw, int nparts, size_t pstride,
+                                         const uint16_t* gain, bool rope, const float* cs,
+                                         const float* sn, int lane, float eps,
                                          float (&y)[HD / 64]) {
   constexpr int DPL = HD / 64;
   float ss = 0.f;
 #pragma unroll
   for (int i = 0; i < DPL; ++i) {
     y[i] = raw[lane * DPL + i];
+    for (int q = 1; q < nparts; ++q) y[i] += raw[(size_t)q * pstride + lane * DPL + i];
     ss += y[i] * y[i];
   }
   const float rr = rsqrtf(wave_sum(ss) / (float)HD + eps);
@@ -683,7 +691,7 @@ __global__ __launch_bounds__(256) void k_attn_dec(Rows R, AttnArgs a) {
   // query heads (wave per head)
   for (int h = wave; h < nq; h += 4) {
     float y[DPL];
-    head_vec<HD>(raw + h * HD, a.gq, true, cs, sn, lane, a.eps, y);
+    head_vec<HD>(raw + h * HD, a.qkv_parts, a.qkv_pstride, a.gq, true, cs, sn, lane, a.eps, y);
 #pragma unroll
     for (int i = 0; i < DPL; ++i) qs[h * HD + lane * DPL + i] = y[i];
   }
@@ -694,7 +702,7 @@ __global__ __launch_bounds__(256) void k_attn_dec(Rows R, AttnArgs a) {
   if (a.kc_own && j1 == pos + 1 && wave < 2) {
     const bool is_v = wave == 1;
     float y[DPL];
-    head_vec<HD>(raw + (nq + wave) * HD, is_v ? nullptr : a.gk, !is_v, cs, sn, lane, a.eps, y);
+    head_vec<HD>(raw + (nq + wave) * HD, a.qkv_parts, a.qkv_pstride, is_v ? nullptr : a.gk, !is_v, cs, sn, lane, a.eps, y);
     uint16_t* dst = (is_v ? a.vc_own : a.kc_own) + ((size_t)seq * R.max_ctx + pos) * HD;
 #pragma unroll
     for (int i = 0; i < DPL; ++i) dst[lane * DPL + i] = (uint16_t)f2bf(y[i]);
@@ -870,7 +878,7 @@ __global__ __launch_bounds__(128) void k_kv_write(Rows R, QkvPostArgs a) {
   const float* raw = a.qkv + (size_t)r * (a.nq + 2) * HD + (size_t)(a.nq + wave) * HD;
   const bool is_v = wave == 1;
   float y[DPL];
-  head_vec<HD>(raw, is_v ? nullptr : a.gk, !is_v, cs, sn, lane, a.eps, y);
+  head_vec<HD>(raw, a.qkv_parts, a.qkv_pstride, is_v ? nullptr : a.gk, !is_v, cs, sn, lane, a.eps, y);
   uint16_t* dst = (is_v ? a.vc : a.kc) + ((size_t)seq * R.max_ctx + pos) * HD;
 #pragma unroll
   for (int i = 0; i < DPL; ++i) dst[lane * DPL + i] = (uint16_t)f2bf(y[i]);
@@ -907,201 +915,354 @@ hipError_t launch_attention(const Rows& R, const AttnArgs& a, hipStream_t st) {
 
 // ===================================================== batched rows: MFMA path
 // For rows >= 2 (batched decode, prefill) the input rows are prepared once by
-// k_xprep (same prologue arithmetic as the single-row matvec) as bf16 hi/lo
-// pairs [rows][K] plus per-32-group sums of hi+lo, and k_gemm streams each
-// weight row once for up to 64 rows with v_mfma_f32_16x16x32_bf16:
+// k_xprep (the same prologue arithmetic as the single-row matvec, K-slice
+// partials of the producer summed) as bf16 hi/lo pairs [rows][K] plus per-32
+// group sums of hi+lo, and k_gemm streams each weight row once for up to 64
+// rows with v_mfma_f32_16x16x32_bf16:
 //   D[m][n] += A_hi[m][k] W[n][k] + A_lo[m][k] W[n][k]
 // A (16 rows x 32 k): lane l holds row l%16, k = 8(l/16)..8(l/16)+7.
 // B (32 k x 16 cols): lane l holds col l%16, the same k range.
 // D (16 x 16): lane l holds rows 4(l/16)..4(l/16)+3 of col l%16.
-// W4A16: the B operand holds 128 + c (code c under the bf16 exponent byte);
-// each 32-wide k step is one scale group, so per group
+// W4A16: the B operand holds 128 + c (code c under the bf16 exponent byte
+// 0x43); each 32-wide k step is one scale group, so per group
 //   acc += s[n][g] * (D_group - 136 * sum_k (A_hi + A_lo)[m][k]).
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kMB = 64;   // input rows per block
-constexpr int kNB = 64;   // weight rows per block (4 waves x 16)
-constexpr int kKC = 128;  // k per LDS chunk
+__device__ __forceinline__ void ld8(const float* p, float (&v)[8]) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+__device__ __forceinline__ void ld8_bf(const uint16_t* p, float (&v)[8]) {
+  const uint4 u = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { v[2 * i] = bf2f(w[i]); v[2 * i + 1] = bf2f(w[i] >> 16); }
+}
+// sum of n partial rows (stride floats apart), 8 consecutive elements
+__device__ __forceinline__ void ld8_parts(const float* p, int n, size_t stride, float (&v)[8]) {
+  ld8(p, v);
+  for (int q = 1; q < n; ++q) {
+    float t[8];
+    ld8(p + (size_t)q * stride, t);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] += t[j];
+  }
+}
 
+// Writes x[i0 .. i0+7] as bf16 hi/lo and, from the four threads that cover
+// one 32-group (consecutive threads, all active together), its group sum.
+__device__ __forceinline__ void emit8(const float (&v)[8], uint16_t* xh, uint16_t* xl, float* xg,
+                                      int i0) {
+  uint32_t h[4], l[4];
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    split_pair(v[2 * j], v[2 * j + 1], h[j], l[j]);
+    s += (bf2f(h[j]) + bf2f(l[j])) + (bf2f(h[j] >> 16) + bf2f(l[j] >> 16));
+  }
+  *reinterpret_cast<uint4*>(xh + i0) = make_uint4(h[0], h[1], h[2], h[3]);
+  *reinterpret_cast<uint4*>(xl + i0) = make_uint4(l[0], l[1], l[2], l[3]);
+  s += __shfl_xor(s, 1, 64);
+  s += __shfl_xor(s, 2, 64);
+  if ((threadIdx.x & 3) == 0) xg[i0 / 32] = s;
+}
+
+// Block per row; thread t handles elements 8t.. (+2048 per pass).
 __global__ __launch_bounds__(256) void k_xprep(Prologue p, int rows, int K, uint16_t* __restrict__ xh,
                                                uint16_t* __restrict__ xl, float* __restrict__ xg) {
-  extern __shared__ float xs[];  // K floats
   __shared__ float red[8];
   const int b = blockIdx.x, t = threadIdx.x;
-  if (p.kind == kRes || p.kind == kResNorm) {  // K == hidden size <= 2048
-    constexpr int PT = 2048 / 256;
-    float dv[PT], av[PT], ss = 0.f;
+  uint16_t* oh = xh + (size_t)b * K;
+  uint16_t* ol = xl + (size_t)b * K;
+  float* og = xg + (size_t)b * (K / 32);
+  if (p.kind == kRes || p.kind == kResNorm) {  // K == hidden size <= 2048: one pass
+    const int i0 = 8 * t;
+    const bool on = i0 < K;
+    float av[8], dv[8];
+    float ss = 0.f;
 #pragma unroll
-    for (int j = 0; j < PT; ++j) {
-      const int i = t + 256 * j;
-      float s_ = 0.f, a_ = 0.f;
-      if (i < K) {
-        a_ = p.a[(size_t)b * K + i];
-        if (p.d)
-          for (int q = 0; q < p.nd; ++q) s_ += p.d[((size_t)q * rows + b) * K + i];
+    for (int j = 0; j < 8; ++j) av[j] = dv[j] = 0.f;
+    if (on) {
+      ld8(p.a + (size_t)b * K + i0, av);
+      if (p.d) {
+        ld8_parts(p.d + (size_t)b * K + i0, p.nd, p.d_pstride, dv);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) ss += dv[j] * dv[j];
       }
-      dv[j] = s_;
-      av[j] = a_;
-      ss += s_ * s_;
     }
     float rd = 0.f;
     if (p.d) rd = rsqrtf(block_sum<256>(ss, red) / (float)K + p.eps);
     const float sc = p.scalar ? bf2f(p.scalar[0]) : 1.0f;
     float hs = 0.f;
+    if (on) {
+      if (p.d) {
+        float g[8];
+        ld8_bf(p.gd + i0, g);
 #pragma unroll
-    for (int j = 0; j < PT; ++j) {
-      const int i = t + 256 * j;
-      if (i < K) {
-        float hn = av[j];
-        if (p.d) hn = (hn + dv[j] * rd * bf2f(p.gd[i])) * sc;
-        av[j] = hn;
-        hs += hn * hn;
-        if (p.d && p.h_out) p.h_out[(size_t)b * K + i] = hn;
+        for (int j = 0; j < 8; ++j) av[j] = (av[j] + dv[j] * rd * g[j]) * sc;
+        if (p.h_out) {
+          float* ho = p.h_out + (size_t)b * K + i0;
+          *reinterpret_cast<float4*>(ho) = make_float4(av[0], av[1], av[2], av[3]);
+          *reinterpret_cast<float4*>(ho + 4) = make_float4(av[4], av[5], av[6], av[7]);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) hs += av[j] * av[j];
+    }
+    if (p.kind == kResNorm) {
+      const float rh = rsqrtf(block_sum<256>(hs, red) / (float)K + p.eps);
+      if (on) {
+        float g[8];
+        ld8_bf(p.gx + i0, g);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) av[j] *= rh * g[j];
       }
     }
-    float rh = 1.f;
-    if (p.kind == kResNorm) rh = rsqrtf(block_sum<256>(hs, red) / (float)K + p.eps);
-#pragma unroll
-    for (int j = 0; j < PT; ++j) {
-      const int i = t + 256 * j;
-      if (i < K) xs[i] = p.kind == kResNorm ? av[j] * rh * bf2f(p.gx[i]) : av[j];
-    }
+    if (on) emit8(av, oh, ol, og, i0);
   } else {
-    for (int i = t; i < K; i += 256) {
-      const float a0 = p.a[(size_t)b * p.lda + i];
-      float v = a0;
-      if (p.kind == kGeglu) v = gelu_tanh(a0) * p.a[(size_t)b * p.lda + K + i];
-      else if (p.kind == kPleGate) v = gelu_tanh(a0) * p.pli[(size_t)b * p.pli_ld + i];
-      xs[i] = v;
+    for (int i0 = 8 * t; i0 < K; i0 += 2048) {
+      float v[8];
+      const float* src = p.a + (size_t)b * p.lda + i0;
+      ld8_parts(src, p.na, p.a_pstride, v);
+      if (p.kind == kGeglu || p.kind == kPleGate) {
+        float u[8];
+        if (p.kind == kGeglu) ld8_parts(src + K, p.na, p.a_pstride, u);
+        else ld8(p.pli + (size_t)b * p.pli_ld + i0, u);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = gelu_tanh(v[j]) * u[j];
+      }
+      emit8(v, oh, ol, og, i0);
     }
-  }
-  __syncthreads();
-  for (int i = t; i < K; i += 256) {
-    const float v = xs[i];
-    const uint32_t h = f2bf(v), l = f2bf(v - bf2f(h));
-    xh[(size_t)b * K + i] = (uint16_t)h;
-    xl[(size_t)b * K + i] = (uint16_t)l;
-    xs[i] = bf2f(h) + bf2f(l);
-  }
-  __syncthreads();
-  for (int g = t; g < K / 32; g += 256) {
-    float s_ = 0.f;
-    for (int k = 0; k < 32; ++k) s_ += xs[32 * g + k];
-    xg[(size_t)b * (K / 32) + g] = s_;
   }
 }
 
 hipError_t launch_xprep(const Prologue& p, int rows, int K, uint16_t* xh, uint16_t* xl, float* xg,
                         hipStream_t st) {
-  if ((p.kind == kRes || p.kind == kResNorm) && K > 2048) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_xprep, dim3(rows), dim3(256), (size_t)K * sizeof(float), st, p, rows, K,
-                     xh, xl, xg);
+  if (K % 32 || ((p.kind == kRes || p.kind == kResNorm) && K > 2048)) return hipErrorInvalidValue;
+  if (p.na < 1 || (p.d && p.nd < 1)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_xprep, dim3(rows), dim3(256), 0, st, p, rows, K, xh, xl, xg);
   return hipGetLastError();
 }
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
-template <int WQ, int TAG>
-__global__ __launch_bounds__(256) void k_gemm(Lin W, int rows, const uint16_t* __restrict__ xh,
-                                              const uint16_t* __restrict__ xl,
-                                              const float* __restrict__ xg, int KS, Epilogue epi) {
-  __shared__ __attribute__((aligned(16))) uint16_t sh_h[kMB][kKC + 8];
-  __shared__ __attribute__((aligned(16))) uint16_t sh_l[kMB][kKC + 8];
-  __shared__ float sh_g[kMB][kKC / 32];
+// eight int4 codes (one packed word) -> eight bf16 values 128 + c
+__device__ __forceinline__ uint4 w4_to_bf16(uint32_t word) {
+  const uint32_t lo = word & 0x0F0F0F0Fu, hi = (word >> 4) & 0x0F0F0F0Fu;
+  const uint32_t u = __builtin_amdgcn_perm(hi, lo, 0x05010400u);  // codes 0,1,2,3 as bytes
+  const uint32_t v = __builtin_amdgcn_perm(hi, lo, 0x07030602u);  // codes 4,5,6,7
+  uint4 r;
+  r.x = __builtin_amdgcn_perm(0x43434343u, u, 0x04010400u);
+  r.y = __builtin_amdgcn_perm(0x43434343u, u, 0x04030402u);
+  r.z = __builtin_amdgcn_perm(0x43434343u, v, 0x04010400u);
+  r.w = __builtin_amdgcn_perm(0x43434343u, v, 0x04030402u);
+  return r;
+}
+
+constexpr int kMB = 64;         // input rows per block (4 m-tiles)
+constexpr int kKC = 128;        // k per LDS stage (4 k-steps of 32)
+constexpr int kAP = kKC + 8;    // padded LDS row of bf16: 16-byte reads conflict-free
+
+// Block = 4 waves side by side along N; wave w owns NT column tiles of 16
+// (block covers 64*NT columns) for all 64 rows, over one K slice of KS.
+// A chunks (64 rows x 128 k, hi and lo) are double-buffered in LDS, one
+// barrier per chunk; each wave's weight fragments for the next chunk are
+// loaded into registers while the current chunk is multiplied.
+template <int WQ, int NT, int TAG>
+__global__ __launch_bounds__(256, 2) void k_gemm(Lin W, int rows, const uint16_t* __restrict__ xh,
+                                                 const uint16_t* __restrict__ xl,
+                                                 const float* __restrict__ xg, int KS, Epilogue epi) {
+  __shared__ __attribute__((aligned(16))) uint16_t sa[2][2][kMB][kAP];
+  __shared__ __attribute__((aligned(16))) float sg[2][kKC / 32][kMB];  // 136 * group sums
   __shared__ float rv[4][kMB];
   __shared__ int ri[4][kMB];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int nb = blockIdx.x, ks = blockIdx.y, mb = blockIdx.z;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6, kq = lane >> 4;
+  const int ks = blockIdx.y, m0 = blockIdx.z * kMB;
   const int K = W.K, N = W.N;
-  const int m0 = mb * kMB, mrows = min(kMB, rows - m0);
-  const int nl = nb * kNB + wave * 16 + (lane & 15);  // this lane's weight row (B column)
-  const bool nok = nl < N;
-  const int kq = lane >> 4;
-  f32x4_t acc[4];
+  const int mrows = min(kMB, rows - m0);
+  int ncol[NT];
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < NT; ++j) ncol[j] = blockIdx.x * 64 * NT + wave * 16 * NT + 16 * j + (lane & 15);
+
+  f32x4_t acc[4][NT];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int j = 0; j < NT; ++j) acc[mt][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // weight fragments of one chunk (4 k-steps)
+  uint4 bw[2][WQ ? 1 : 4][WQ ? 1 : NT];
+  uint32_t bq[2][WQ ? 4 : 1][WQ ? NT : 1];
+  float bs[2][WQ ? 4 : 1][WQ ? NT : 1];
+  // A chunk staged through registers
+  uint4 rah[4], ral[4];
+  float rg = 0.f;
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+#pragma unroll
+    for (int s = 0; s < (WQ ? 1 : 4); ++s)
+#pragma unroll
+      for (int j = 0; j < (WQ ? 1 : NT); ++j) bw[x][s][j] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int s = 0; s < (WQ ? 4 : 1); ++s)
+#pragma unroll
+      for (int j = 0; j < (WQ ? NT : 1); ++j) {
+        bq[x][s][j] = 0x88888888u;
+        bs[x][s][j] = 0.f;
+      }
+  }
+
   const int kbeg = ks * KS, kend = kbeg + KS;
-  for (int kc = kbeg; kc < kend; kc += kKC) {
-    const int KC = min(kKC, kend - kc);  // k staged in this chunk (a multiple of 32)
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < kMB * KC / 8; idx += 256) {
-      const int m = idx / (KC / 8), k8 = idx % (KC / 8);
-      uint4 vh = make_uint4(0, 0, 0, 0), vl = make_uint4(0, 0, 0, 0);
-      if (m < mrows) {
-        vh = *reinterpret_cast<const uint4*>(xh + (size_t)(m0 + m) * K + kc + 8 * k8);
-        vl = *reinterpret_cast<const uint4*>(xl + (size_t)(m0 + m) * K + kc + 8 * k8);
-      }
-      *reinterpret_cast<uint4*>(&sh_h[m][8 * k8]) = vh;
-      *reinterpret_cast<uint4*>(&sh_l[m][8 * k8]) = vl;
-    }
-    if (WQ)
-      for (int idx = threadIdx.x; idx < kMB * (KC / 32); idx += 256) {
-        const int m = idx / (KC / 32), g = idx % (KC / 32);
-        sh_g[m][g] = m < mrows ? xg[(size_t)(m0 + m) * (K / 32) + kc / 32 + g] : 0.f;
-      }
-    __syncthreads();
+  // (buffer indices are compile-time constants so the fragments stay in registers)
+  auto load_b = [&](auto BUF, int kc, int kcn) {
+    constexpr int buf = decltype(BUF)::value;
 #pragma unroll
-    for (int s = 0; s < kKC / 32; ++s) {
-      if (32 * s >= KC) break;
-      const int k0 = kc + 32 * s;
-      uint4 bw = make_uint4(0, 0, 0, 0);
-      float scl = 0.f;
-      if (WQ) {
-        uint32_t word = 0x88888888u;  // code 8: q = 0
-        if (nok) {
-          word = W.q[(size_t)nl * (K / 8) + k0 / 8 + kq];
-          scl = bf2f(W.s[(size_t)nl * (K / 32) + k0 / 32]);
+    for (int s = 0; s < 4; ++s) {
+      if (32 * s >= kcn) break;
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        // columns past N read row 0 (always valid) and are zeroed
+        const bool ok = ncol[j] < N;
+        const size_t row = ok ? (size_t)ncol[j] : 0;
+        if constexpr (WQ) {
+          const uint32_t qv = W.q[row * (K / 8) + (kc + 32 * s) / 8 + kq];
+          const float sv = bf2f(W.s[row * (K / 32) + (kc + 32 * s) / 32]);
+          bq[buf][s][j] = ok ? qv : 0x88888888u;
+          bs[buf][s][j] = ok ? sv : 0.f;
+        } else {
+          uint4 v = *reinterpret_cast<const uint4*>(W.w + row * K + kc + 32 * s + 8 * kq);
+          if (!ok) v = make_uint4(0, 0, 0, 0);
+          bw[buf][s][j] = v;
         }
-        const uint32_t lo = word & 0x0F0F0F0Fu, hi = (word >> 4) & 0x0F0F0F0Fu;
-        const uint32_t u = __builtin_amdgcn_perm(hi, lo, 0x05010400u);  // codes 0,1,2,3 as bytes
-        const uint32_t v = __builtin_amdgcn_perm(hi, lo, 0x07030602u);  // codes 4,5,6,7
-        bw.x = __builtin_amdgcn_perm(0x43434343u, u, 0x04010400u);
-        bw.y = __builtin_amdgcn_perm(0x43434343u, u, 0x04030402u);
-        bw.z = __builtin_amdgcn_perm(0x43434343u, v, 0x04010400u);
-        bw.w = __builtin_amdgcn_perm(0x43434343u, v, 0x04030402u);
-      } else if (nok) {
-        bw = *reinterpret_cast<const uint4*>(W.w + (size_t)nl * K + k0 + 8 * kq);
       }
-      const bf16x8_t B = as_bf16x8(bw);
+    }
+  };
+  auto load_a = [&](int kc, int kcn) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int idx = t + 256 * j, m = idx >> 4, k8 = idx & 15;
+      // out-of-range slots read element 0 (always valid) and are zeroed
+      const bool ok = m < mrows && 8 * k8 < kcn;
+      const size_t o = ok ? (size_t)(m0 + m) * K + kc + 8 * k8 : 0;
+      uint4 vh = *reinterpret_cast<const uint4*>(xh + o);
+      uint4 vl = *reinterpret_cast<const uint4*>(xl + o);
+      if (!ok) vh = vl = make_uint4(0, 0, 0, 0);
+      rah[j] = vh;
+      ral[j] = vl;
+    }
+    if (WQ) {
+      const int m = t >> 2, g = t & 3;
+      const bool ok = m < mrows && 32 * g < kcn;
+      const float v = xg[ok ? (size_t)(m0 + m) * (K / 32) + kc / 32 + g : 0];
+      rg = ok ? 136.0f * v : 0.f;
+    }
+  };
+  auto store_a = [&](int st) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int idx = t + 256 * j, m = idx >> 4, k8 = idx & 15;
+      *reinterpret_cast<uint4*>(&sa[st][0][m][8 * k8]) = rah[j];
+      *reinterpret_cast<uint4*>(&sa[st][1][m][8 * k8]) = ral[j];
+    }
+    if (WQ) sg[st][t & 3][t >> 2] = rg;
+  };
+
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  // one chunk: prefetch the next into the other buffers, multiply this one
+  auto chunk = [&](auto BUF, int c, int nch) {
+    constexpr int buf = decltype(BUF)::value;
+    const int kc = kbeg + c * kKC, kcn = min(kKC, kend - kc);
+    const bool more = c + 1 < nch;
+    if (more) {
+      const int kn = kc + kKC, knn = min(kKC, kend - kn);
+      load_a(kn, knn);
+      load_b(std::integral_constant<int, buf ^ 1>(), kn, knn);
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      if (32 * s >= kcn) break;
+      bf16x8_t B[NT];
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        if constexpr (WQ) B[j] = as_bf16x8(w4_to_bf16(bq[buf][s][j]));
+        else B[j] = as_bf16x8(bw[buf][s][j]);
+      }
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         const int mr = 16 * mt + (lane & 15);
-        const bf16x8_t Ah = as_bf16x8(*reinterpret_cast<const uint4*>(&sh_h[mr][32 * s + 8 * kq]));
-        const bf16x8_t Al = as_bf16x8(*reinterpret_cast<const uint4*>(&sh_l[mr][32 * s + 8 * kq]));
-        if (WQ) {
-          f32x4_t t4 = f32x4_t{0.f, 0.f, 0.f, 0.f};
-          t4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ah, B, t4, 0, 0, 0);
-          t4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Al, B, t4, 0, 0, 0);
+        const bf16x8_t Ah = as_bf16x8(*reinterpret_cast<const uint4*>(&sa[buf][0][mr][32 * s + 8 * kq]));
+        const bf16x8_t Al = as_bf16x8(*reinterpret_cast<const uint4*>(&sa[buf][1][mr][32 * s + 8 * kq]));
+        if constexpr (WQ) {
+          const float4 g4 = *reinterpret_cast<const float4*>(&sg[buf][s][16 * mt + 4 * kq]);
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            acc[mt][i] += scl * (t4[i] - 136.0f * sh_g[16 * mt + 4 * kq + i][s]);
+          for (int j = 0; j < NT; ++j) {
+            f32x4_t d = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ah, B[j], d, 0, 0, 0);
+            d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Al, B[j], d, 0, 0, 0);
+            const float sc = bs[buf][s][j];
+            acc[mt][j][0] += sc * (d[0] - g4.x);
+            acc[mt][j][1] += sc * (d[1] - g4.y);
+            acc[mt][j][2] += sc * (d[2] - g4.z);
+            acc[mt][j][3] += sc * (d[3] - g4.w);
+          }
         } else {
-          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ah, B, acc[mt], 0, 0, 0);
-          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Al, B, acc[mt], 0, 0, 0);
+#pragma unroll
+          for (int j = 0; j < NT; ++j) {
+            acc[mt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ah, B[j], acc[mt][j], 0, 0, 0);
+            acc[mt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Al, B[j], acc[mt][j], 0, 0, 0);
+          }
         }
       }
     }
+    if (more) store_a(buf ^ 1);
+    __syncthreads();
+  };
+
+  const int nch = (KS + kKC - 1) / kKC;
+  load_a(kbeg, min(kKC, KS));
+  load_b(I0(), kbeg, min(kKC, KS));
+  store_a(0);
+  __syncthreads();
+  for (int c = 0; c < nch; c += 2) {
+    chunk(I0(), c, nch);
+    if (c + 1 < nch) chunk(I1(), c + 1, nch);
   }
+
   if (!epi.argmax) {
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int m = 16 * mt + 4 * kq + i;
-        if (m < mrows && nok) epi.y[((size_t)ks * rows + m0 + m) * N + nl] = acc[mt][i];
+        if (m < mrows)
+#pragma unroll
+          for (int j = 0; j < NT; ++j)
+            if (ncol[j] < N) epi.y[((size_t)ks * rows + m0 + m) * N + ncol[j]] = acc[mt][j][i];
       }
     return;
   }
-  // argmax: per row, best (value, lowest index) over this block's 64 columns
+  // argmax: per row, best (value, lowest index) over this block's columns
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int m = 16 * mt + 4 * kq + i;
-      float v = nok ? acc[mt][i] : -FLT_MAX;
-      int x = nok ? nl : 0x7FFFFFFF;
-      if (epi.logits && nok && m < mrows) epi.logits[(size_t)(m0 + m) * N + nl] = v;
+      float v = -FLT_MAX;
+      int x = 0x7FFFFFFF;
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+        if (ncol[j] < N) {
+          const float a_ = acc[mt][j][i];
+          if (epi.logits && m < mrows) epi.logits[(size_t)(m0 + m) * N + ncol[j]] = a_;
+          if (a_ > v || (a_ == v && ncol[j] < x)) {
+            v = a_;
+            x = ncol[j];
+          }
+        }
 #pragma unroll
       for (int o = 1; o < 16; o <<= 1) {
         const float ov = __shfl_xor(v, o, 64);
@@ -1117,65 +1278,85 @@ __global__ __launch_bounds__(256) void k_gemm(Lin W, int rows, const uint16_t* _
       }
     }
   __syncthreads();
-  if (threadIdx.x < mrows) {
-    const int m = threadIdx.x;
-    float v = rv[0][m];
-    int x = ri[0][m];
+  if (t < mrows) {
+    float v = rv[0][t];
+    int x = ri[0][t];
     for (int w = 1; w < 4; ++w)
-      if (rv[w][m] > v || (rv[w][m] == v && ri[w][m] < x)) {
-        v = rv[w][m];
-        x = ri[w][m];
+      if (rv[w][t] > v || (rv[w][t] == v && ri[w][t] < x)) {
+        v = rv[w][t];
+        x = ri[w][t];
       }
-    epi.cand_val[(size_t)(m0 + m) * gridDim.x + nb] = v;
-    epi.cand_idx[(size_t)(m0 + m) * gridDim.x + nb] = x;
+    epi.cand_val[(size_t)(m0 + t) * gridDim.x + blockIdx.x] = v;
+    epi.cand_idx[(size_t)(m0 + t) * gridDim.x + blockIdx.x] = x;
   }
 }
 
-// K slices of the batched product: only where the consumer sums partials
-int gemm_splits(int K, bool partial_ok) {
-  if (!partial_ok) return 1;
-  if (K % (6 * kKC) == 0 && K >= 6 * 2048) return 6;
-  if (K % (3 * kKC) == 0 && K >= 3 * 1024) return 3;
-  if (K % (2 * kKC) == 0 && K >= 2048) return 2;
-  return 1;
+// Column tile and K slices of a batched product (independent of the row
+// count, so a row's result does not depend on how many rows share the pass).
+// Enough blocks to cover the chip: narrower column tiles first, then (where
+// the consumer sums partials) K slices of >= 256.
+GemmPlan gemm_plan(int quant, int N, int K, bool partial_ok) {
+  constexpr int kTarget = 256;
+  GemmPlan p;
+  p.nt = quant ? 4 : 2;
+  const int nt_min = quant ? 2 : 1;
+  auto cols = [&](int nt) { return (N + 64 * nt - 1) / (64 * nt); };
+  while (p.nt > nt_min && cols(p.nt) < kTarget) p.nt >>= 1;
+  p.nks = 1;
+  if (partial_ok) {
+    static const int cand[] = {2, 3, 4, 6, 8, 12, 16};
+    for (int c : cand) {
+      if (cols(p.nt) * p.nks >= kTarget) break;
+      if (K % (32 * c) == 0 && K / c >= 256) p.nks = c;
+    }
+  }
+  return p;
 }
 
-template <int WQ, int TAG>
+template <int WQ, int NT, int TAG>
 static hipError_t run_gemm(const Lin& W, int rows, const uint16_t* xh, const uint16_t* xl,
                            const float* xg, int nks, const Epilogue& epi, int* nblk, hipStream_t st) {
-  const int nbx = (W.N + kNB - 1) / kNB;
+  const int nbx = (W.N + 64 * NT - 1) / (64 * NT);
   if (nblk) *nblk = nbx;
   dim3 grid(nbx, nks, (rows + kMB - 1) / kMB);
-  hipLaunchKernelGGL((k_gemm<WQ, TAG>), grid, dim3(256), 0, st, W, rows, xh, xl, xg, W.K / nks, epi);
+  hipLaunchKernelGGL((k_gemm<WQ, NT, TAG>), grid, dim3(256), 0, st, W, rows, xh, xl, xg, W.K / nks,
+                     epi);
   return hipGetLastError();
 }
 
-template <int WQ>
+template <int WQ, int NT>
 static hipError_t gemm_tag(int tag, const Lin& W, int rows, const uint16_t* xh, const uint16_t* xl,
                            const float* xg, int nks, const Epilogue& epi, int* nblk, hipStream_t st) {
   switch (tag) {
-    case kTagQkv: return run_gemm<WQ, kTagQkv>(W, rows, xh, xl, xg, nks, epi, nblk, st);
-    case kTagO: return run_gemm<WQ, kTagO>(W, rows, xh, xl, xg, nks, epi, nblk, st);
-    case kTagGateUp: return run_gemm<WQ, kTagGateUp>(W, rows, xh, xl, xg, nks, epi, nblk, st);
-    case kTagDown: return run_gemm<WQ, kTagDown>(W, rows, xh, xl, xg, nks, epi, nblk, st);
-    case kTagPleGate: return run_gemm<WQ, kTagPleGate>(W, rows, xh, xl, xg, nks, epi, nblk, st);
-    case kTagPleProj: return run_gemm<WQ, kTagPleProj>(W, rows, xh, xl, xg, nks, epi, nblk, st);
-    case kTagPleModel: return run_gemm<WQ, kTagPleModel>(W, rows, xh, xl, xg, nks, epi, nblk, st);
-    case kTagLmHead: return run_gemm<WQ, kTagLmHead>(W, rows, xh, xl, xg, nks, epi, nblk, st);
-    default: return run_gemm<WQ, kTagOther>(W, rows, xh, xl, xg, nks, epi, nblk, st);
+    case kTagQkv: return run_gemm<WQ, NT, kTagQkv>(W, rows, xh, xl, xg, nks, epi, nblk, st);
+    case kTagO: return run_gemm<WQ, NT, kTagO>(W, rows, xh, xl, xg, nks, epi, nblk, st);
+    case kTagGateUp: return run_gemm<WQ, NT, kTagGateUp>(W, rows, xh, xl, xg, nks, epi, nblk, st);
+    case kTagDown: return run_gemm<WQ, NT, kTagDown>(W, rows, xh, xl, xg, nks, epi, nblk, st);
+    case kTagPleGate: return run_gemm<WQ, NT, kTagPleGate>(W, rows, xh, xl, xg, nks, epi, nblk, st);
+    case kTagPleProj: return run_gemm<WQ, NT, kTagPleProj>(W, rows, xh, xl, xg, nks, epi, nblk, st);
+    case kTagPleModel: return run_gemm<WQ, NT, kTagPleModel>(W, rows, xh, xl, xg, nks, epi, nblk, st);
+    case kTagLmHead: return run_gemm<WQ, NT, kTagLmHead>(W, rows, xh, xl, xg, nks, epi, nblk, st);
+    default: return run_gemm<WQ, NT, kTagOther>(W, rows, xh, xl, xg, nks, epi, nblk, st);
   }
 }
 
 hipError_t launch_gemm(int quant, int tag, const Lin& W, int rows, const uint16_t* xh,
-                       const uint16_t* xl, const float* xg, int nks, const Epilogue& epi,
-                       int* nblk, hipStream_t st) {
-  if (rows < 1 || nks < 1 || W.K % nks || (W.K / nks) % 32) return hipErrorInvalidValue;
+                       const uint16_t* xl, const float* xg, const GemmPlan& plan,
+                       const Epilogue& epi, int* nblk, hipStream_t st) {
+  const int nks = plan.nks;
+  if (rows < 1 || nks < 1 || nks > kMaxGemmSplit || W.K % nks || (W.K / nks) % 32)
+    return hipErrorInvalidValue;
   if (epi.argmax && (quant || nks != 1)) return hipErrorInvalidValue;
-  return quant ? gemm_tag<1>(tag, W, rows, xh, xl, xg, nks, epi, nblk, st)
-               : gemm_tag<0>(tag, W, rows, xh, xl, xg, nks, epi, nblk, st);
+  if (quant) {
+    if (plan.nt == 4) return gemm_tag<1, 4>(tag, W, rows, xh, xl, xg, nks, epi, nblk, st);
+    if (plan.nt == 2) return gemm_tag<1, 2>(tag, W, rows, xh, xl, xg, nks, epi, nblk, st);
+  } else {
+    if (plan.nt == 2) return gemm_tag<0, 2>(tag, W, rows, xh, xl, xg, nks, epi, nblk, st);
+    if (plan.nt == 1) return gemm_tag<0, 1>(tag, W, rows, xh, xl, xg, nks, epi, nblk, st);
+  }
+  return hipErrorInvalidValue;
 }
 
-// positions[r] += 1 (graph-replayed decode loops advance on the device)
 __global__ void k_advance(int32_t* pos, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) pos[i] += 1;
