@@ -134,7 +134,8 @@ size_t e2b_kv_bytes(const e2b_model* model, int max_batch, int max_ctx);
 /* Workspace bytes for calls that process up to max_rows rows (decode batch,
  * or prefill rows per pass).  The workspace (256-byte aligned) is scratch
  * except its first 64 bytes, the device error word: zero them once before
- * the first call; e2b_check reads and re-zeroes them. */
+ * the first call; e2b_check reads and re-zeroes them.  Calls that overlap in
+ * time must not share a workspace. */
 size_t e2b_workspace_bytes(const e2b_model* model, int max_rows);
 
 /* Copy the tensors to the caller's device arena (d_arena, arena_bytes >=
@@ -197,11 +198,11 @@ int e2b_kv_view(const e2b_model* model, int layer, int which, void** out);
  * [rows, N].  K must be one of the widths the library supports: K split into
  * at most 8 equal slices of width 32, 128, 256, 512, 1536 or 2048 (the first
  * that divides K among 2048, 1536; else K itself when K <= 512; else 512);
- * other K -> E2B_EINVAL.  d_ws (256-byte
- * aligned) must hold e2b_matvec_workspace_bytes(quant, N, K, rows) bytes (0 for
- * one row with K <= 2048, else nonzero).  One row streams the weights through
- * the matvec kernel; two or more rows share one pass over the weights on the
- * matrix cores.  Asynchronous. */
+ * other K -> E2B_EINVAL.  d_ws (256-byte aligned) must hold
+ * e2b_matvec_workspace_bytes(quant, N, K, rows) bytes: the K-slice partial
+ * sums, 0 when the product is not split.  One row streams the weights through
+ * the matvec kernel; two or more rows (x 16-byte aligned) share one pass over
+ * the weights on the matrix cores.  Asynchronous. */
 size_t e2b_matvec_workspace_bytes(int quant, int N, int K, int rows);
 int e2b_matvec(int quant, const void* d_w, const uint16_t* d_scale, int N, int K,
                const float* d_x, int rows, float* d_y, void* d_ws, size_t ws_bytes,

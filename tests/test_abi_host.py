@@ -152,13 +152,10 @@ def test_matvec_validation(lib):
     for K in (64, 96, 160, 480, 4608 * 4):
         assert L.e2b_matvec_workspace_bytes(0, 64, K, 3) == 0, K
         assert L.e2b_matvec(0, 256, None, 8, K, 256, 3, 256, 256, 1 << 20, None) == lib.E2B_EINVAL, K
-    # several rows: bf16 hi and lo rows + fp32 group sums (256-byte aligned
-    # regions), then the K-slice partials of the matrix-core path
-    up = lambda b: (b + 255) // 256 * 256
-    prep = lambda r, K: 2 * up(2 * r * K) + up(4 * r * (K // 32))
+    # several rows: only the K-slice partials of the matrix-core product
     for quant in (0, 1):
         for N, K, r in ((1536, 1536, 3), (1536, 12288, 70), (1536, 4096, 2), (24576, 1536, 64)):
-            extra = L.e2b_matvec_workspace_bytes(quant, N, K, r) - prep(r, K)
+            extra = L.e2b_matvec_workspace_bytes(quant, N, K, r)
             slices, rem = divmod(extra, r * N * 4)
             assert rem == 0 and slices in (0, 2, 3, 4, 6, 8, 12, 16), (quant, N, K, r, extra)
             if slices:

@@ -78,17 +78,28 @@ struct Epilogue {
   int32_t* cand_idx = nullptr;  // [rows][gridDim.x]
 };
 
+// Per-row RoPE cos/sin for both layer types, built once per pass by the
+// embedding kernel: row r holds [cos_s | sin_s] (hd_s/2 each) then
+// [cos_f | sin_f] (hd_f/2 each).
+struct RopeTable {
+  float* out = nullptr;
+  const double* inv_s = nullptr;  // sliding inverse frequencies [hd_s/2]
+  const double* inv_f = nullptr;  // full [hd_f/2]
+  int hd_s = 0, hd_f = 0;
+};
+
 struct AttnArgs {
   const float* qkv = nullptr;   // raw projections [rows][(nq + 2 * (kc_own != null)) * hd]
   const uint16_t* gq = nullptr; // q_norm gain
   const uint16_t* gk = nullptr; // k_norm gain (own K/V)
-  const double* inv_freq = nullptr;  // [hd/2]
   const uint16_t* kc = nullptr; // K cache read (the source layer's) [max_batch][max_ctx][hd]
   const uint16_t* vc = nullptr;
   uint16_t* kc_own = nullptr;   // decode: cache to write this position's K/V into (layer owns
   uint16_t* vc_own = nullptr;   // K/V); null when the layer shares or the K/V are already written
   float* part = nullptr;        // [rows][nq][kMaxChunks][hd + 2]
   float* out = nullptr;         // [rows][nq * hd]
+  const float* rope = nullptr;  // RoPE table rows (rope_ld floats each), this type at rope_off
+  int rope_ld = 0, rope_off = 0;
   int nq = 0, hd = 0, window = 0 /* 0: full */, chunk = 0, nchunk = 0;
   int owns = 0;                 // the layer computes K/V (raw rows hold q, k, v)
   int qkv_parts = 1;            // qkv is the sum of this many partials
@@ -100,8 +111,8 @@ struct QkvPostArgs {
   const float* qkv = nullptr;   // [rows][(nq + 2*owns) * hd] raw projections
   const uint16_t* gq = nullptr;
   const uint16_t* gk = nullptr;
-  const double* inv_freq = nullptr;  // [hd/2]
-  float* q_out = nullptr;       // [rows][nq][hd]
+  const float* rope = nullptr;  // RoPE table (see AttnArgs)
+  int rope_ld = 0, rope_off = 0;
   uint16_t* kc = nullptr;       // this layer's cache when it owns K/V, else null
   uint16_t* vc = nullptr;
   int nq = 0, hd = 0;
@@ -113,7 +124,7 @@ struct QkvPostArgs {
 // ---- launchers (kernels.hip) ----------------------------------------------
 hipError_t launch_embed(const Rows& R, const uint16_t* E, const uint16_t* Eple, int H, int LP,
                         float sqrtH, float sqrtP, float* h, float* tokple, int* err,
-                        hipStream_t st);
+                        const RopeTable& rt, hipStream_t st);
 // u: u_parts partials u_pstride floats apart, each [rows][L*P]
 hipError_t launch_ple_finish(const Rows& R, const float* u, int u_parts, size_t u_pstride,
                              const float* tokple, const uint16_t* g, int L, int P,
@@ -135,10 +146,19 @@ struct GemmPlan {
   int nks = 1;  // K slices (partials written [nks][rows][N])
 };
 GemmPlan gemm_plan(int quant, int N, int K, bool partial_ok);
+// Input rows of a batched product: either prepared by k_xprep (bf16 hi/lo
+// [rows][K] + fp32 group sums [rows][K/32]) or, for a plain input (kPlain,
+// one partial), fp32 rows [rows][lda] read and split by the product itself.
+struct GemmA {
+  const uint16_t* xh = nullptr;
+  const uint16_t* xl = nullptr;
+  const float* xg = nullptr;
+  const float* a = nullptr;  // non-null: fp32 rows
+  int kind = kPlain, lda = 0, na = 1;
+};
 // *nblk receives the number of column blocks (argmax candidates per row)
-hipError_t launch_gemm(int quant, int tag, const Lin& W, int rows, const uint16_t* xh,
-                       const uint16_t* xl, const float* xg, const GemmPlan& plan,
-                       const Epilogue& epi, int* nblk, hipStream_t st);
+hipError_t launch_gemm(int quant, int tag, const Lin& W, int rows, const GemmA& A,
+                       const GemmPlan& plan, const Epilogue& epi, int* nblk, hipStream_t st);
 hipError_t launch_sum_partials(int nparts, size_t n, const float* parts, float* out,
                                hipStream_t st);
 hipError_t launch_argmax_final(int rows, int nblk, const float* cand_val,

@@ -242,7 +242,7 @@ Lin resolve(const e2b_model* m, const LinOff& o) {
 
 // ---- workspace layout ------------------------------------------------------
 struct Ws {
-  size_t err, h0, h1, tokple, u, pli, qkv, qn, part, attn, oo, gu, dn, pgy, ppo, cv, ci, xh, xl, xg,
+  size_t err, rope, h0, h1, tokple, u, pli, qkv, part, attn, oo, gu, dn, pgy, ppo, cv, ci, xh, xl, xg,
       total;
   int ncand;  // argmax candidates per row
 };
@@ -278,13 +278,13 @@ Ws ws_layout(const e2b_model* m, int R) {
   w.ncand = std::max(e2b::kLmBlocks, (m->V + 63) / 64);
   const size_t LP = (size_t)m->L * m->P;
   w.err = take(64);
+  w.rope = take(f * R * (m->c.head_dim + m->c.global_head_dim));
   w.h0 = take(f * R * m->H);
   w.h1 = take(f * R * m->H);
   w.tokple = take(f * R * LP);
   w.u = take(f * R * u_f);
   w.pli = take(f * R * LP);
   w.qkv = take(f * R * qkv_f);
-  w.qn = take(f * R * m->nq * hdm);
   w.part = take(f * R * m->nq * e2b::kMaxChunks * (hdm + 2));
   w.attn = take(f * R * m->nq * hdm);
   w.oo = take(f * R * oo_f);
@@ -350,13 +350,21 @@ hipError_t matmul(e2b_model* m, int quant, int tag, const Lin& W, int rows, bool
     if (pr.na != 1 || (splits > 1 && !partial_ok)) return hipErrorInvalidValue;
     e = e2b::launch_gemv(quant, tag, W, rows, pr, ep, 0, nblk, st);
   } else {
-    uint16_t* xh = reinterpret_cast<uint16_t*>(ws + L.xh);
-    uint16_t* xl = reinterpret_cast<uint16_t*>(ws + L.xl);
-    float* xg = reinterpret_cast<float*>(ws + L.xg);
     const e2b::GemmPlan plan = e2b::gemm_plan(quant, W.N, W.K, partial_ok);
     splits = plan.nks;
-    e = e2b::launch_xprep(pr, rows, W.K, xh, xl, xg, st);
-    if (e == hipSuccess) e = e2b::launch_gemm(quant, tag, W, rows, xh, xl, xg, plan, ep, nblk, st);
+    e2b::GemmA A;
+    if (pr.kind == e2b::kPlain && pr.na == 1 && plan.nt <= 2) {  // read fp32 rows directly
+      A.a = pr.a;
+      A.kind = pr.kind;
+      A.lda = pr.lda;
+    } else {
+      A.xh = reinterpret_cast<uint16_t*>(ws + L.xh);
+      A.xl = reinterpret_cast<uint16_t*>(ws + L.xl);
+      A.xg = reinterpret_cast<float*>(ws + L.xg);
+      e = e2b::launch_xprep(pr, rows, W.K, const_cast<uint16_t*>(A.xh),
+                            const_cast<uint16_t*>(A.xl), const_cast<float*>(A.xg), st);
+    }
+    if (e == hipSuccess) e = e2b::launch_gemm(quant, tag, W, rows, A, plan, ep, nblk, st);
   }
   if (nd) *nd = splits;
   if (e != hipSuccess) return e;
@@ -383,8 +391,14 @@ int run_rows(e2b_model* m, const e2b::Rows& R, bool head, int head_row, float* d
 
   const bool bat = n > 1;  // batched pass: matrix-core products
   int nd_u = 1;            // K-slice partials of the per-layer model projection
+  RopeTable rt;
+  rt.out = F(W.rope);
+  rt.inv_s = m->invf[0];
+  rt.inv_f = m->invf[1];
+  rt.hd_s = m->c.head_dim;
+  rt.hd_f = m->c.global_head_dim;
   CK(launch_embed(R, m->embed, m->ple, H, LP, std::sqrt((float)H), std::sqrt((float)P), F(W.h0),
-                  F(W.tokple), err, st),
+                  F(W.tokple), err, rt, st),
      "embed");
   {
     Prologue pr;
@@ -436,8 +450,9 @@ int run_rows(e2b_model* m, const e2b::Rows& R, bool head, int head_row, float* d
       a.qkv = F(W.qkv);
       a.gq = d.g_q;
       a.gk = d.g_k;
-      a.inv_freq = m->invf[y.full];
-      a.q_out = F(W.qn);
+      a.rope = F(W.rope);
+      a.rope_ld = m->c.head_dim + m->c.global_head_dim;
+      a.rope_off = y.full ? m->c.head_dim : 0;
       a.kc = m->kc[l];
       a.vc = m->vc[l];
       a.nq = m->nq;
@@ -452,7 +467,9 @@ int run_rows(e2b_model* m, const e2b::Rows& R, bool head, int head_row, float* d
       a.qkv = F(W.qkv);
       a.gq = d.g_q;
       a.gk = d.g_k;
-      a.inv_freq = m->invf[y.full];
+      a.rope = F(W.rope);
+      a.rope_ld = m->c.head_dim + m->c.global_head_dim;
+      a.rope_off = y.full ? m->c.head_dim : 0;
       a.kc = m->kc[y.src];
       a.vc = m->vc[y.src];
       a.kc_own = (owns && fused_kv) ? m->kc[l] : nullptr;
@@ -883,27 +900,17 @@ int e2b_kv_view(const e2b_model* m, int layer, int which, void** out) {
 }
 
 namespace {
-// Workspace of e2b_matvec: one row -> the matvec kernel's K-slice partials;
-// several rows -> the MFMA path's prepared rows (bf16 hi/lo + group sums,
-// each region 256-byte aligned) then its K-slice partials.
+// Workspace of e2b_matvec: the K-slice partials of the one-row matvec
+// kernel or of the several-row matrix-core product (none when unsplit).
 struct MvWs {
-  size_t xh, xl, xg, part, total;
+  size_t part, total;
   int nks;
 };
 MvWs matvec_ws(int quant, int N, int K, int rows) {
   MvWs w{};
-  auto up = [](size_t b) { return (b + 255) & ~(size_t)255; };
-  if (rows == 1) {
-    w.nks = e2b::gemv_splits(K);
-    w.part = 0;
-  } else {
-    w.nks = e2b::gemm_plan(quant, N, K, true).nks;
-    w.xh = 0;
-    w.xl = up(2 * (size_t)rows * K);
-    w.xg = w.xl + up(2 * (size_t)rows * K);
-    w.part = w.xg + up(sizeof(float) * (size_t)rows * (K / 32));
-  }
-  w.total = w.part + (w.nks > 1 ? (size_t)w.nks * rows * N * sizeof(float) : 0);
+  w.nks = rows == 1 ? e2b::gemv_splits(K) : e2b::gemm_plan(quant, N, K, true).nks;
+  w.part = 0;
+  w.total = w.nks > 1 ? (size_t)w.nks * rows * N * sizeof(float) : 0;
   return w;
 }
 }  // namespace
@@ -924,6 +931,8 @@ int e2b_matvec(int quant, const void* d_w, const uint16_t* d_scale, int N, int K
   if (N < 1 || rows < 1 || rows > 65535 || K % 32 || !supported_k(K))
     return fail(E2B_EINVAL, "unsupported shape N=%d K=%d rows=%d", N, K, rows);
   if (reinterpret_cast<uintptr_t>(d_w) % 16) return fail(E2B_EINVAL, "weights must be 16-byte aligned");
+  if (rows > 1 && reinterpret_cast<uintptr_t>(d_x) % 16)
+    return fail(E2B_EINVAL, "x must be 16-byte aligned for several rows");
   const MvWs L = matvec_ws(quant, N, K, rows);
   if (L.total && (!d_ws || ws_bytes < L.total))
     return fail(E2B_ENOMEM, "workspace of %zu bytes < %zu required", ws_bytes, L.total);
@@ -949,12 +958,12 @@ int e2b_matvec(int quant, const void* d_w, const uint16_t* d_scale, int N, int K
   if (rows == 1) {
     CK(e2b::launch_gemv(quant, e2b::kTagOther, W, rows, pr, ep, 0, nullptr, st), "matvec");
   } else {
-    uint16_t* xh = reinterpret_cast<uint16_t*>(ws + L.xh);
-    uint16_t* xl = reinterpret_cast<uint16_t*>(ws + L.xl);
-    float* xg = reinterpret_cast<float*>(ws + L.xg);
-    CK(e2b::launch_xprep(pr, rows, K, xh, xl, xg, st), "matvec input prep");
-    CK(e2b::launch_gemm(quant, e2b::kTagOther, W, rows, xh, xl, xg,
-                        e2b::gemm_plan(quant, N, K, true), ep, nullptr, st),
+    e2b::GemmA A;
+    A.a = d_x;
+    A.kind = e2b::kPlain;
+    A.lda = K;
+    CK(e2b::launch_gemm(quant, e2b::kTagOther, W, rows, A, e2b::gemm_plan(quant, N, K, true), ep,
+                        nullptr, st),
        "matvec mfma");
   }
   if (L.nks > 1) CK(e2b::launch_sum_partials(L.nks, (size_t)rows * N, ep.y, d_y, st), "matvec sum");

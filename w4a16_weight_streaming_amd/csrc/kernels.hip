@@ -75,7 +75,7 @@ __device__ __forceinline__ int row_seq(const Rows& R, int r) { return R.seq0 + r
 __global__ __launch_bounds__(256) void k_embed(Rows R, const uint16_t* __restrict__ E,
                                                const uint16_t* __restrict__ Eple, int H, int LP,
                                                float sqrtH, float sqrtP, float* __restrict__ h,
-                                               float* __restrict__ tokple, int* err) {
+                                               float* __restrict__ tokple, int* err, RopeTable rt) {
   const int r = blockIdx.x;
   int tok = R.tokens[r];
   if (tok < 0 || tok >= R.vocab) {
@@ -97,13 +97,28 @@ __global__ __launch_bounds__(256) void k_embed(Rows R, const uint16_t* __restric
   const uint16_t* t = Eple + (size_t)tok * LP;
   for (int i = threadIdx.x; i < LP; i += blockDim.x)
     tokple[(size_t)r * LP + i] = bf2f(t[i]) * sqrtP;
+  // RoPE angles of this row's position for both layer types, from fp64
+  // (cos then sin, hd/2 each; sliding first, then full)
+  const int p = clamp_pos(R, pos);
+  float* o = rt.out + (size_t)r * (rt.hd_s + rt.hd_f);
+  for (int i = threadIdx.x; i < rt.hd_s / 2 + rt.hd_f / 2; i += blockDim.x) {
+    const bool full = i >= rt.hd_s / 2;
+    const int k = full ? i - rt.hd_s / 2 : i;
+    const int half = full ? rt.hd_f / 2 : rt.hd_s / 2;
+    float* base = full ? o + rt.hd_s : o;
+    double sd, cd;
+    sincos((double)p * (full ? rt.inv_f : rt.inv_s)[k], &sd, &cd);
+    base[k] = (float)cd;
+    base[half + k] = (float)sd;
+  }
 }
 
 hipError_t launch_embed(const Rows& R, const uint16_t* E, const uint16_t* Eple, int H, int LP,
                         float sqrtH, float sqrtP, float* h, float* tokple, int* err,
-                        hipStream_t st) {
+                        const RopeTable& rt, hipStream_t st) {
+  if (!rt.out || !rt.inv_s || !rt.inv_f) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_embed, dim3(R.n), dim3(256), 0, st, R, E, Eple, H, LP, sqrtH, sqrtP, h,
-                     tokple, err);
+                     tokple, err, rt);
   return hipGetLastError();
 }
 
@@ -647,26 +662,58 @@ __device__ __forceinline__ void head_vec(const float* raw, int nparts, size_t ps
   }
 }
 
-template <int HD>
-__device__ __forceinline__ void rope_angles(int pos, const double* inv_freq, float* cs, float* sn) {
-  for (int i = threadIdx.x; i < HD / 2; i += blockDim.x) {
-    double sd, cd;
-    sincos((double)pos * inv_freq[i], &sd, &cd);
-    cs[i] = (float)cd;
-    sn[i] = (float)sd;
+// One wave's K/V rows for a group of 4 keys, kept packed (bf16) until used.
+template <int DPL>
+struct KvGroup {
+  static constexpr int W = DPL >= 2 ? DPL / 2 : 1;  // 32-bit words per lane per row
+  uint32_t k[4][W], v[4][W];
+};
+
+template <int DPL>
+__device__ __forceinline__ void load_packed(const uint16_t* p, uint32_t (&w)[KvGroup<DPL>::W]) {
+  if constexpr (DPL == 8) {
+    const uint4 u = *reinterpret_cast<const uint4*>(p);
+    w[0] = u.x; w[1] = u.y; w[2] = u.z; w[3] = u.w;
+  } else if constexpr (DPL == 4) {
+    const uint2 u = *reinterpret_cast<const uint2*>(p);
+    w[0] = u.x; w[1] = u.y;
+  } else if constexpr (DPL == 2) {
+    w[0] = *reinterpret_cast<const uint32_t*>(p);
+  } else {
+    w[0] = *p;
   }
 }
 
+template <int DPL>
+__device__ __forceinline__ void unpack(const uint32_t (&w)[KvGroup<DPL>::W], float (&out)[DPL]) {
+  if constexpr (DPL == 1) {
+    out[0] = bf2f(w[0]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < DPL / 2; ++i) { out[2 * i] = bf2f(w[i]); out[2 * i + 1] = bf2f(w[i] >> 16); }
+  }
+}
+
+// Block (chunk c, row r): the keys j0..j1-1 of chunk c of the row's window,
+// all query heads against the single K/V head; 4 waves take groups of 4 keys,
+// the next group's K/V rows loaded while the current one is used.  Queries
+// are normed and rotated in the block (angles from the per-row table).  With
+// own K/V (decode, the layer computes K/V) the block holding the position
+// norms, rotates and stores that position's key and value (bf16) and uses
+// them from LDS.  Every block writes a (max, sum, o) partial per head;
+// k_attn_combine merges them.  (Merging in the row's last block instead needs
+// a device-scope fence per block, which writes back the L2 and costs more
+// than the extra launch.)
 template <int HD>
 __global__ __launch_bounds__(256) void k_attn_dec(Rows R, AttnArgs a) {
   constexpr int DPL = HD / 64;
   constexpr int NH = kMaxHeads;
+  using G = KvGroup<DPL>;
   __shared__ float qs[NH * HD];
-  __shared__ float cs[HD / 2], sn[HD / 2];
+  __shared__ float kv_own[2][HD];
   __shared__ float pw[4][32];
   __shared__ float cw[4][NH];
   __shared__ float wm[4][NH], wl[4][NH];
-  __shared__ float red[4];
   const int c = blockIdx.x, r = blockIdx.y, t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6, nq = a.nq;
   const int pos = clamp_pos(R, row_pos(R, r));
@@ -676,146 +723,176 @@ __global__ __launch_bounds__(256) void k_attn_dec(Rows R, AttnArgs a) {
   const int j1 = min(j0 + a.chunk, pos + 1);
   const size_t hstride = (size_t)kMaxChunks * (HD + 2);
   float* part = a.part + ((size_t)r * nq * kMaxChunks + c) * (HD + 2);
-  if (j0 >= j1) {
-    if (t < nq) {
-      part[t * hstride + HD] = -INFINITY;
-      part[t * hstride + HD + 1] = 0.f;
-    }
-    return;
-  }
-  const int nraw = nq + (a.owns ? 2 : 0);
-  const float* raw = a.qkv + (size_t)r * nraw * HD;
 
-  rope_angles<HD>(pos, a.inv_freq, cs, sn);
-  __syncthreads();
-  // query heads (wave per head)
-  for (int h = wave; h < nq; h += 4) {
-    float y[DPL];
-    head_vec<HD>(raw + h * HD, a.qkv_parts, a.qkv_pstride, a.gq, true, cs, sn, lane, a.eps, y);
+  if (j0 < j1) {
+    const bool own = a.kc_own != nullptr && j1 == pos + 1;
+    const uint16_t* kb = a.kc + (size_t)seq * R.max_ctx * HD + lane * DPL;
+    const uint16_t* vb = a.vc + (size_t)seq * R.max_ctx * HD + lane * DPL;
+    const int ngroups = (j1 - j0 + 3) / 4;
+    // K/V rows of a group (the own position and keys past the chunk read as 0)
+    auto load_group = [&](int gi, G& g) {
 #pragma unroll
-    for (int i = 0; i < DPL; ++i) qs[h * HD + lane * DPL + i] = y[i];
-  }
-  // this position's key and value, stored as bf16 (decode: the block holding
-  // the position writes them before any wave reads the cache)
-  const uint16_t* kb = a.kc + (size_t)seq * R.max_ctx * HD;
-  const uint16_t* vb = a.vc + (size_t)seq * R.max_ctx * HD;
-  if (a.kc_own && j1 == pos + 1 && wave < 2) {
-    const bool is_v = wave == 1;
-    float y[DPL];
-    head_vec<HD>(raw + (nq + wave) * HD, a.qkv_parts, a.qkv_pstride, is_v ? nullptr : a.gk, !is_v, cs, sn, lane, a.eps, y);
-    uint16_t* dst = (is_v ? a.vc_own : a.kc_own) + ((size_t)seq * R.max_ctx + pos) * HD;
+      for (int k = 0; k < 4; ++k) {
+        const int key = j0 + 4 * gi + k;
+        const bool ok = gi < ngroups && key < j1 && !(own && key == pos);
+        const size_t o = ok ? (size_t)key * HD : 0;
+        load_packed<DPL>(kb + o, g.k[k]);
+        load_packed<DPL>(vb + o, g.v[k]);
+        if (!ok)
 #pragma unroll
-    for (int i = 0; i < DPL; ++i) dst[lane * DPL + i] = (uint16_t)f2bf(y[i]);
-    __threadfence_block();
-  }
-  __syncthreads();
-
-  // this lane's query dims for every head
-  float qr[NH][DPL];
-#pragma unroll
-  for (int h = 0; h < NH; ++h)
-#pragma unroll
-    for (int i = 0; i < DPL; ++i) qr[h][i] = h < nq ? qs[h * HD + lane * DPL + i] : 0.f;
-
-  const float scale = rsqrtf((float)HD);
-  const int myh = (lane >> 1) & 7, myk = lane >> 4;  // value index lane>>1 = k*8 + h
-  float m_run = -INFINITY, l_run = 0.f;
-  float o[NH][DPL];
-#pragma unroll
-  for (int h = 0; h < NH; ++h)
-#pragma unroll
-    for (int i = 0; i < DPL; ++i) o[h][i] = 0.f;
-
-  const int ngroups = (j1 - j0 + 3) / 4;
-  for (int gi = wave; gi < ngroups; gi += 4) {
-    const int key0 = j0 + 4 * gi;
-    float kr[4][DPL], vr[4][DPL];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int key = key0 + k;
-      if (key < j1) {
-        load_row<DPL>(kb + (size_t)key * HD + lane * DPL, kr[k]);
-        load_row<DPL>(vb + (size_t)key * HD + lane * DPL, vr[k]);
-      } else {
-#pragma unroll
-        for (int i = 0; i < DPL; ++i) { kr[k][i] = 0.f; vr[k][i] = 0.f; }
+          for (int i = 0; i < G::W; ++i) g.k[k][i] = g.v[k][i] = 0u;
       }
+    };
+    G cur;
+    load_group(wave, cur);  // issued before the query work: independent of it
+
+    const int nraw = nq + (a.owns ? 2 : 0);
+    const float* raw = a.qkv + (size_t)r * nraw * HD;
+    const float* cs = a.rope + (size_t)r * a.rope_ld + a.rope_off;
+    const float* sn = cs + HD / 2;
+    for (int h = wave; h < nq; h += 4) {
+      float y[DPL];
+      head_vec<HD>(raw + h * HD, a.qkv_parts, a.qkv_pstride, a.gq, true, cs, sn, lane, a.eps, y);
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) qs[h * HD + lane * DPL + i] = y[i];
     }
-    float part32[32];
+    if (own && wave < 2) {
+      const bool is_v = wave == 1;
+      float y[DPL];
+      head_vec<HD>(raw + (nq + wave) * HD, a.qkv_parts, a.qkv_pstride, is_v ? nullptr : a.gk,
+                   !is_v, cs, sn, lane, a.eps, y);
+      uint16_t* dst = (is_v ? a.vc_own : a.kc_own) + ((size_t)seq * R.max_ctx + pos) * HD;
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
-#pragma unroll
-      for (int h = 0; h < NH; ++h) {
-        float d = 0.f;
-#pragma unroll
-        for (int i = 0; i < DPL; ++i) d += qr[h][i] * kr[k][i];
-        part32[k * NH + h] = d;
-      }
-    float sc_ = transpose_reduce32(part32, lane) * scale;
-    if (key0 + myk >= j1 || myh >= nq) sc_ = -INFINITY;
-    float mx = fmaxf(sc_, __shfl_xor(sc_, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);
-    const float pr = (m_new == -INFINITY || sc_ == -INFINITY) ? 0.f : expf(sc_ - m_new);
-    const float corr = (m_new == -INFINITY || m_run == -INFINITY) ? (m_run == -INFINITY ? 0.f : 1.f)
-                                                                   : expf(m_run - m_new);
-    float ps = pr + __shfl_xor(pr, 16, 64);
-    ps += __shfl_xor(ps, 32, 64);
-    l_run = l_run * corr + ps;
-    m_run = m_new;
-    if ((lane & 1) == 0) pw[wave][lane >> 1] = pr;
-    if (lane < 16 && (lane & 1) == 0) cw[wave][lane >> 1] = corr;
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-#pragma unroll
-    for (int h = 0; h < NH; ++h) {
-      const float cf = cw[wave][h];
-      const float p0 = pw[wave][h], p1 = pw[wave][NH + h], p2 = pw[wave][2 * NH + h],
-                  p3 = pw[wave][3 * NH + h];
-#pragma unroll
-      for (int i = 0; i < DPL; ++i)
-        o[h][i] = o[h][i] * cf + p0 * vr[0][i] + p1 * vr[1][i] + p2 * vr[2][i] + p3 * vr[3][i];
-    }
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-  }
-  // merge the four waves: per head max M, then rescale and sum
-  if (lane < 16 && (lane & 1) == 0) {
-    wm[wave][lane >> 1] = m_run;
-    wl[wave][lane >> 1] = l_run;
-  }
-  __syncthreads();
-  float* acc = qs;  // reuse: [NH][HD]
-  for (int w = 0; w < 4; ++w) {
-    if (wave == w) {
-#pragma unroll
-      for (int h = 0; h < NH; ++h) {
-        float M = wm[0][h];
-        for (int x = 1; x < 4; ++x) M = fmaxf(M, wm[x][h]);
-        const float f = (wm[w][h] == -INFINITY) ? 0.f : expf(wm[w][h] - M);
-#pragma unroll
-        for (int i = 0; i < DPL; ++i) {
-          const float v = o[h][i] * f;
-          acc[h * HD + lane * DPL + i] = (w == 0) ? v : acc[h * HD + lane * DPL + i] + v;
-        }
+      for (int i = 0; i < DPL; ++i) {
+        const uint32_t b = f2bf(y[i]);
+        dst[lane * DPL + i] = (uint16_t)b;
+        kv_own[wave][lane * DPL + i] = bf2f(b);
       }
     }
     __syncthreads();
+
+    // this lane's query dims for every head
+    float qr[NH][DPL];
+#pragma unroll
+    for (int h = 0; h < NH; ++h)
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) qr[h][i] = h < nq ? qs[h * HD + lane * DPL + i] : 0.f;
+
+    const float scale = rsqrtf((float)HD);
+    const int myh = (lane >> 1) & 7, myk = lane >> 4;  // value index lane>>1 = k*8 + h
+    float m_run = -INFINITY, l_run = 0.f;
+    float o[NH][DPL];
+#pragma unroll
+    for (int h = 0; h < NH; ++h)
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) o[h][i] = 0.f;
+
+    for (int gi = wave; gi < ngroups; gi += 4) {
+      G nxt;
+      if constexpr (DPL < 8) load_group(gi + 4, nxt);  // hd 512: registers too tight
+      const int key0 = j0 + 4 * gi;
+      // key / value row k of the group as fp32 (unpacked when used)
+      auto row_of = [&](int k, int which, float (&x)[DPL]) {
+        if (own && key0 + k == pos) {
+#pragma unroll
+          for (int i = 0; i < DPL; ++i) x[i] = kv_own[which][lane * DPL + i];
+        } else {
+          unpack<DPL>(which ? cur.v[k] : cur.k[k], x);
+        }
+      };
+      float part32[32];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        float kr[DPL];
+        row_of(k, 0, kr);
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+          float d = 0.f;
+#pragma unroll
+          for (int i = 0; i < DPL; ++i) d += qr[h][i] * kr[i];
+          part32[k * NH + h] = d;
+        }
+      }
+      float sc_ = transpose_reduce32(part32, lane) * scale;
+      if (key0 + myk >= j1 || myh >= nq) sc_ = -INFINITY;
+      float mx = fmaxf(sc_, __shfl_xor(sc_, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float m_new = fmaxf(m_run, mx);
+      const float pr = (m_new == -INFINITY || sc_ == -INFINITY) ? 0.f : expf(sc_ - m_new);
+      const float corr = (m_new == -INFINITY || m_run == -INFINITY)
+                             ? (m_run == -INFINITY ? 0.f : 1.f)
+                             : expf(m_run - m_new);
+      float ps = pr + __shfl_xor(pr, 16, 64);
+      ps += __shfl_xor(ps, 32, 64);
+      l_run = l_run * corr + ps;
+      m_run = m_new;
+      if ((lane & 1) == 0) pw[wave][lane >> 1] = pr;
+      if (lane < 16 && (lane & 1) == 0) cw[wave][lane >> 1] = corr;
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int h = 0; h < NH; ++h) {
+        const float cf = cw[wave][h];
+#pragma unroll
+        for (int i = 0; i < DPL; ++i) o[h][i] *= cf;
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        float vr[DPL];
+        row_of(k, 1, vr);
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+          const float pk = pw[wave][k * NH + h];
+#pragma unroll
+          for (int i = 0; i < DPL; ++i) o[h][i] += pk * vr[i];
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      if constexpr (DPL < 8) cur = nxt;
+      else if (gi + 4 < ngroups) load_group(gi + 4, cur);
+    }
+    // merge the four waves: per head max M, then rescale and sum
+    if (lane < 16 && (lane & 1) == 0) {
+      wm[wave][lane >> 1] = m_run;
+      wl[wave][lane >> 1] = l_run;
+    }
+    __syncthreads();
+    float* acc = qs;  // reuse: [NH][HD]
+    for (int w = 0; w < 4; ++w) {
+      if (wave == w) {
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+          float M = wm[0][h];
+          for (int x = 1; x < 4; ++x) M = fmaxf(M, wm[x][h]);
+          const float f = (wm[w][h] == -INFINITY) ? 0.f : expf(wm[w][h] - M);
+#pragma unroll
+          for (int i = 0; i < DPL; ++i) {
+            const float v = o[h][i] * f;
+            acc[h * HD + lane * DPL + i] = (w == 0) ? v : acc[h * HD + lane * DPL + i] + v;
+          }
+        }
+      }
+      __syncthreads();
+    }
+    for (int idx = t; idx < nq * HD; idx += 256) {
+      const int h = idx / HD, d = idx % HD;
+      part[h * hstride + d] = acc[idx];
+    }
+    if (t < nq) {
+      float M = wm[0][t];
+      for (int x = 1; x < 4; ++x) M = fmaxf(M, wm[x][t]);
+      float L = 0.f;
+      for (int x = 0; x < 4; ++x)
+        if (wm[x][t] != -INFINITY) L += wl[x][t] * expf(wm[x][t] - M);
+      part[t * hstride + HD] = M;
+      part[t * hstride + HD + 1] = L;
+    }
+  } else if (t < nq) {  // no keys in this chunk
+    part[t * hstride + HD] = -INFINITY;
+    part[t * hstride + HD + 1] = 0.f;
   }
-  for (int idx = t; idx < nq * HD; idx += 256) {
-    const int h = idx / HD, d = idx % HD;
-    part[h * hstride + d] = acc[idx];
-  }
-  if (t < nq) {
-    float M = wm[0][t];
-    for (int x = 1; x < 4; ++x) M = fmaxf(M, wm[x][t]);
-    float L = 0.f;
-    for (int x = 0; x < 4; ++x)
-      if (wm[x][t] != -INFINITY) L += wl[x][t] * expf(wm[x][t] - M);
-    part[t * hstride + HD] = M;
-    part[t * hstride + HD + 1] = L;
-  }
-  (void)red;
+
 }
 
 // out[r][h*hd + d] = sum_c e^(m_c - M) o_c[d] / sum_c e^(m_c - M) l_c over the
@@ -866,15 +943,17 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a) {
   }
 }
 
+// Prefill: K/V of every row written before attention.  Block per row, wave 0
+// the key (norm with gain + RoPE), wave 1 the value (norm), bf16 at slot =
+// position (the same arithmetic as the decode path's own-K/V write).
 template <int HD>
 __global__ __launch_bounds__(128) void k_kv_write(Rows R, QkvPostArgs a) {
   constexpr int DPL = HD / 64;
-  __shared__ float cs[HD / 2], sn[HD / 2];
   const int r = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int pos = clamp_pos(R, row_pos(R, r));
   const int seq = row_seq(R, r);
-  rope_angles<HD>(pos, a.inv_freq, cs, sn);
-  __syncthreads();
+  const float* cs = a.rope + (size_t)r * a.rope_ld + a.rope_off;
+  const float* sn = cs + HD / 2;
   const float* raw = a.qkv + (size_t)r * (a.nq + 2) * HD + (size_t)(a.nq + wave) * HD;
   const bool is_v = wave == 1;
   float y[DPL];
@@ -885,7 +964,7 @@ __global__ __launch_bounds__(128) void k_kv_write(Rows R, QkvPostArgs a) {
 }
 
 hipError_t launch_qkv_post(const Rows& R, const QkvPostArgs& a, hipStream_t st) {
-  if (!a.kc || !a.vc) return hipErrorInvalidValue;
+  if (!a.kc || !a.vc || !a.rope) return hipErrorInvalidValue;
   switch (a.hd) {
     case 64: hipLaunchKernelGGL(k_kv_write<64>, dim3(R.n), dim3(128), 0, st, R, a); break;
     case 128: hipLaunchKernelGGL(k_kv_write<128>, dim3(R.n), dim3(128), 0, st, R, a); break;
@@ -897,7 +976,7 @@ hipError_t launch_qkv_post(const Rows& R, const QkvPostArgs& a, hipStream_t st) 
 }
 
 hipError_t launch_attention(const Rows& R, const AttnArgs& a, hipStream_t st) {
-  if (a.nq > kMaxHeads || a.nchunk > kMaxChunks || a.nchunk < 1 || a.chunk < 1)
+  if (a.nq > kMaxHeads || a.nchunk > kMaxChunks || a.nchunk < 1 || a.chunk < 1 || !a.rope)
     return hipErrorInvalidValue;
   dim3 grid(a.nchunk, R.n);
   switch (a.hd) {
@@ -941,14 +1020,23 @@ __device__ __forceinline__ void ld8_bf(const uint16_t* p, float (&v)[8]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) { v[2 * i] = bf2f(w[i]); v[2 * i + 1] = bf2f(w[i] >> 16); }
 }
-// sum of n partial rows (stride floats apart), 8 consecutive elements
+// sum of n partial rows (stride floats apart), 8 consecutive elements; the
+// loads of up to B partials are issued together, the sum runs in order
+template <int B = 8>
 __device__ __forceinline__ void ld8_parts(const float* p, int n, size_t stride, float (&v)[8]) {
   ld8(p, v);
-  for (int q = 1; q < n; ++q) {
-    float t[8];
-    ld8(p + (size_t)q * stride, t);
+  for (int q0 = 1; q0 < n; q0 += B) {
+    float t[B][8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] += t[j];
+    for (int u = 0; u < B; ++u) {
+      const bool ok = q0 + u < n;
+      ld8(p + (ok ? (size_t)(q0 + u) * stride : 0), t[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < B; ++u)
+      if (q0 + u < n)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] += t[u][j];
   }
 }
 
@@ -981,11 +1069,13 @@ __global__ __launch_bounds__(256) void k_xprep(Prologue p, int rows, int K, uint
   if (p.kind == kRes || p.kind == kResNorm) {  // K == hidden size <= 2048: one pass
     const int i0 = 8 * t;
     const bool on = i0 < K;
-    float av[8], dv[8];
+    float av[8], dv[8], gdv[8], gxv[8];
     float ss = 0.f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) av[j] = dv[j] = 0.f;
-    if (on) {
+    for (int j = 0; j < 8; ++j) av[j] = dv[j] = gdv[j] = gxv[j] = 0.f;
+    if (on) {  // every load of the prologue issued up front
+      if (p.d) ld8_bf(p.gd + i0, gdv);
+      if (p.kind == kResNorm) ld8_bf(p.gx + i0, gxv);
       ld8(p.a + (size_t)b * K + i0, av);
       if (p.d) {
         ld8_parts(p.d + (size_t)b * K + i0, p.nd, p.d_pstride, dv);
@@ -999,10 +1089,8 @@ __global__ __launch_bounds__(256) void k_xprep(Prologue p, int rows, int K, uint
     float hs = 0.f;
     if (on) {
       if (p.d) {
-        float g[8];
-        ld8_bf(p.gd + i0, g);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) av[j] = (av[j] + dv[j] * rd * g[j]) * sc;
+        for (int j = 0; j < 8; ++j) av[j] = (av[j] + dv[j] * rd * gdv[j]) * sc;
         if (p.h_out) {
           float* ho = p.h_out + (size_t)b * K + i0;
           *reinterpret_cast<float4*>(ho) = make_float4(av[0], av[1], av[2], av[3]);
@@ -1014,12 +1102,9 @@ __global__ __launch_bounds__(256) void k_xprep(Prologue p, int rows, int K, uint
     }
     if (p.kind == kResNorm) {
       const float rh = rsqrtf(block_sum<256>(hs, red) / (float)K + p.eps);
-      if (on) {
-        float g[8];
-        ld8_bf(p.gx + i0, g);
+      if (on)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) av[j] *= rh * g[j];
-      }
+        for (int j = 0; j < 8; ++j) av[j] *= rh * gxv[j];
     }
     if (on) emit8(av, oh, ol, og, i0);
   } else {
@@ -1071,10 +1156,11 @@ constexpr int kAP = kKC + 8;    // padded LDS row of bf16: 16-byte reads conflic
 // A chunks (64 rows x 128 k, hi and lo) are double-buffered in LDS, one
 // barrier per chunk; each wave's weight fragments for the next chunk are
 // loaded into registers while the current chunk is multiplied.
-template <int WQ, int NT, int TAG>
-__global__ __launch_bounds__(256, 2) void k_gemm(Lin W, int rows, const uint16_t* __restrict__ xh,
-                                                 const uint16_t* __restrict__ xl,
-                                                 const float* __restrict__ xg, int KS, Epilogue epi) {
+template <int WQ, int NT, int FA, int TAG>
+__global__ __launch_bounds__(256, 2) void k_gemm(Lin W, int rows, GemmA A, int KS, Epilogue epi) {
+  const uint16_t* __restrict__ xh = A.xh;
+  const uint16_t* __restrict__ xl = A.xl;
+  const float* __restrict__ xg = A.xg;
   __shared__ __attribute__((aligned(16))) uint16_t sa[2][2][kMB][kAP];
   __shared__ __attribute__((aligned(16))) float sg[2][kKC / 32][kMB];  // 136 * group sums
   __shared__ float rv[4][kMB];
@@ -1094,14 +1180,17 @@ __global__ __launch_bounds__(256, 2) void k_gemm(Lin W, int rows, const uint16_t
     for (int j = 0; j < NT; ++j) acc[mt][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   // weight fragments of one chunk (4 k-steps)
-  uint4 bw[2][WQ ? 1 : 4][WQ ? 1 : NT];
-  uint32_t bq[2][WQ ? 4 : 1][WQ ? NT : 1];
-  float bs[2][WQ ? 4 : 1][WQ ? NT : 1];
+  // weight fragments: a ring of D chunks, D - 1 of them in flight ahead
+  constexpr int D = WQ ? (NT >= 4 ? 2 : 4) : (NT >= 2 ? 3 : 4);
+  uint4 bw[D][WQ ? 1 : 4][WQ ? 1 : NT];
+  uint32_t bq[D][WQ ? 4 : 1][WQ ? NT : 1];
+  float bs[D][WQ ? 4 : 1][WQ ? NT : 1];
   // A chunk staged through registers
   uint4 rah[4], ral[4];
-  float rg = 0.f;
+  float rg = 0.f, rgs[4] = {0.f, 0.f, 0.f, 0.f};
+  float raf[FA ? 4 : 1][8];  // fp32 input slots (FA)
 #pragma unroll
-  for (int x = 0; x < 2; ++x) {
+  for (int x = 0; x < D; ++x) {
 #pragma unroll
     for (int s = 0; s < (WQ ? 1 : 4); ++s)
 #pragma unroll
@@ -1141,6 +1230,18 @@ __global__ __launch_bounds__(256, 2) void k_gemm(Lin W, int rows, const uint16_t
     }
   };
   auto load_a = [&](int kc, int kcn) {
+    if constexpr (FA) {  // fp32 rows: loaded now, split when stored (after the multiply)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int idx = t + 256 * j, m = idx >> 4, k8 = idx & 15;
+        const bool ok = m < mrows && 8 * k8 < kcn;
+        ld8(A.a + (ok ? (size_t)(m0 + m) * A.lda + kc + 8 * k8 : 0), raf[j]);
+        if (!ok)
+#pragma unroll
+          for (int x = 0; x < 8; ++x) raf[j][x] = 0.f;
+      }
+      return;
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int idx = t + 256 * j, m = idx >> 4, k8 = idx & 15;
@@ -1161,26 +1262,55 @@ __global__ __launch_bounds__(256, 2) void k_gemm(Lin W, int rows, const uint16_t
     }
   };
   auto store_a = [&](int st) {
+    if constexpr (FA) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint32_t h[4], l[4];
+        float gs = 0.f;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          split_pair(raf[j][2 * x], raf[j][2 * x + 1], h[x], l[x]);
+          gs += (bf2f(h[x]) + bf2f(l[x])) + (bf2f(h[x] >> 16) + bf2f(l[x] >> 16));
+        }
+        rah[j] = make_uint4(h[0], h[1], h[2], h[3]);
+        ral[j] = make_uint4(l[0], l[1], l[2], l[3]);
+        if (WQ) {  // group of 32 = the 4 consecutive lanes with the same row
+          gs += __shfl_xor(gs, 1, 64);
+          gs += __shfl_xor(gs, 2, 64);
+          rgs[j] = 136.0f * gs;
+        }
+      }
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int idx = t + 256 * j, m = idx >> 4, k8 = idx & 15;
       *reinterpret_cast<uint4*>(&sa[st][0][m][8 * k8]) = rah[j];
       *reinterpret_cast<uint4*>(&sa[st][1][m][8 * k8]) = ral[j];
     }
-    if (WQ) sg[st][t & 3][t >> 2] = rg;
+    if constexpr (WQ && FA) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int idx = t + 256 * j, m = idx >> 4, k8 = idx & 15;
+        if ((k8 & 3) == 0) sg[st][k8 >> 2][m] = rgs[j];
+      }
+    } else if (WQ) {
+      sg[st][t & 3][t >> 2] = rg;
+    }
   };
 
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  // one chunk: prefetch the next into the other buffers, multiply this one
-  auto chunk = [&](auto BUF, int c, int nch) {
+  const int nch = (KS + kKC - 1) / kKC;
+  // one chunk: issue the weight loads of chunk c + D - 1 and the activation
+  // loads of chunk c + 1, multiply chunk c, stage chunk c + 1 in LDS
+  auto chunk = [&](auto BUF, int c) {
     constexpr int buf = decltype(BUF)::value;
-    const int kc = kbeg + c * kKC, kcn = min(kKC, kend - kc);
+    const int kc = kbeg + c * kKC, kcn = min(kKC, kend - kc), st = c & 1;
     const bool more = c + 1 < nch;
-    if (more) {
-      const int kn = kc + kKC, knn = min(kKC, kend - kn);
-      load_a(kn, knn);
-      load_b(std::integral_constant<int, buf ^ 1>(), kn, knn);
+    // (activation loads first: loads complete in issue order, and staging
+    // chunk c + 1 must not wait for the weight loads issued after it)
+    if (more) load_a(kc + kKC, min(kKC, kend - kc - kKC));
+    if (c + D - 1 < nch) {
+      const int kf = kc + (D - 1) * kKC;
+      load_b(std::integral_constant<int, (buf + D - 1) % D>(), kf, min(kKC, kend - kf));
     }
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -1194,10 +1324,10 @@ __global__ __launch_bounds__(256, 2) void k_gemm(Lin W, int rows, const uint16_t
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         const int mr = 16 * mt + (lane & 15);
-        const bf16x8_t Ah = as_bf16x8(*reinterpret_cast<const uint4*>(&sa[buf][0][mr][32 * s + 8 * kq]));
-        const bf16x8_t Al = as_bf16x8(*reinterpret_cast<const uint4*>(&sa[buf][1][mr][32 * s + 8 * kq]));
+        const bf16x8_t Ah = as_bf16x8(*reinterpret_cast<const uint4*>(&sa[st][0][mr][32 * s + 8 * kq]));
+        const bf16x8_t Al = as_bf16x8(*reinterpret_cast<const uint4*>(&sa[st][1][mr][32 * s + 8 * kq]));
         if constexpr (WQ) {
-          const float4 g4 = *reinterpret_cast<const float4*>(&sg[buf][s][16 * mt + 4 * kq]);
+          const float4 g4 = *reinterpret_cast<const float4*>(&sg[st][s][16 * mt + 4 * kq]);
 #pragma unroll
           for (int j = 0; j < NT; ++j) {
             f32x4_t d = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -1218,18 +1348,29 @@ __global__ __launch_bounds__(256, 2) void k_gemm(Lin W, int rows, const uint16_t
         }
       }
     }
-    if (more) store_a(buf ^ 1);
+    if (more) store_a(st ^ 1);
     __syncthreads();
   };
+  using C0 = std::integral_constant<int, 0>;
+  using C1 = std::integral_constant<int, 1>;
+  using C2 = std::integral_constant<int, 2>;
+  using C3 = std::integral_constant<int, 3>;
 
-  const int nch = (KS + kKC - 1) / kKC;
   load_a(kbeg, min(kKC, KS));
-  load_b(I0(), kbeg, min(kKC, KS));
+  load_b(C0(), kbeg, min(kKC, KS));
+  if constexpr (D > 2)
+    if (1 < nch) load_b(C1(), kbeg + kKC, min(kKC, KS - kKC));
+  if constexpr (D > 3)
+    if (2 < nch) load_b(C2(), kbeg + 2 * kKC, min(kKC, KS - 2 * kKC));
   store_a(0);
   __syncthreads();
-  for (int c = 0; c < nch; c += 2) {
-    chunk(I0(), c, nch);
-    if (c + 1 < nch) chunk(I1(), c + 1, nch);
+  for (int c = 0; c < nch; c += D) {
+    chunk(C0(), c);
+    if (c + 1 < nch) chunk(C1(), c + 1);
+    if constexpr (D > 2)
+      if (c + 2 < nch) chunk(C2(), c + 2);
+    if constexpr (D > 3)
+      if (c + 3 < nch) chunk(C3(), c + 3);
   }
 
   if (!epi.argmax) {
@@ -1313,46 +1454,52 @@ GemmPlan gemm_plan(int quant, int N, int K, bool partial_ok) {
   return p;
 }
 
-template <int WQ, int NT, int TAG>
-static hipError_t run_gemm(const Lin& W, int rows, const uint16_t* xh, const uint16_t* xl,
-                           const float* xg, int nks, const Epilogue& epi, int* nblk, hipStream_t st) {
+template <int WQ, int NT, int FA, int TAG>
+static hipError_t run_gemm(const Lin& W, int rows, const GemmA& A, int nks, const Epilogue& epi,
+                           int* nblk, hipStream_t st) {
   const int nbx = (W.N + 64 * NT - 1) / (64 * NT);
   if (nblk) *nblk = nbx;
   dim3 grid(nbx, nks, (rows + kMB - 1) / kMB);
-  hipLaunchKernelGGL((k_gemm<WQ, NT, TAG>), grid, dim3(256), 0, st, W, rows, xh, xl, xg, W.K / nks,
-                     epi);
+  hipLaunchKernelGGL((k_gemm<WQ, NT, FA, TAG>), grid, dim3(256), 0, st, W, rows, A, W.K / nks, epi);
   return hipGetLastError();
 }
 
 template <int WQ, int NT>
-static hipError_t gemm_tag(int tag, const Lin& W, int rows, const uint16_t* xh, const uint16_t* xl,
-                           const float* xg, int nks, const Epilogue& epi, int* nblk, hipStream_t st) {
+static hipError_t gemm_tag(int tag, const Lin& W, int rows, const GemmA& A, int nks,
+                           const Epilogue& epi, int* nblk, hipStream_t st) {
+  if (A.a) {  // fp32 input rows: the products whose input is a plain copy
+    switch (tag) {
+      case kTagO: return run_gemm<WQ, NT, 1, kTagO>(W, rows, A, nks, epi, nblk, st);
+      case kTagPleModel: return run_gemm<WQ, NT, 1, kTagPleModel>(W, rows, A, nks, epi, nblk, st);
+      default: return run_gemm<WQ, NT, 1, kTagOther>(W, rows, A, nks, epi, nblk, st);
+    }
+  }
   switch (tag) {
-    case kTagQkv: return run_gemm<WQ, NT, kTagQkv>(W, rows, xh, xl, xg, nks, epi, nblk, st);
-    case kTagO: return run_gemm<WQ, NT, kTagO>(W, rows, xh, xl, xg, nks, epi, nblk, st);
-    case kTagGateUp: return run_gemm<WQ, NT, kTagGateUp>(W, rows, xh, xl, xg, nks, epi, nblk, st);
-    case kTagDown: return run_gemm<WQ, NT, kTagDown>(W, rows, xh, xl, xg, nks, epi, nblk, st);
-    case kTagPleGate: return run_gemm<WQ, NT, kTagPleGate>(W, rows, xh, xl, xg, nks, epi, nblk, st);
-    case kTagPleProj: return run_gemm<WQ, NT, kTagPleProj>(W, rows, xh, xl, xg, nks, epi, nblk, st);
-    case kTagPleModel: return run_gemm<WQ, NT, kTagPleModel>(W, rows, xh, xl, xg, nks, epi, nblk, st);
-    case kTagLmHead: return run_gemm<WQ, NT, kTagLmHead>(W, rows, xh, xl, xg, nks, epi, nblk, st);
-    default: return run_gemm<WQ, NT, kTagOther>(W, rows, xh, xl, xg, nks, epi, nblk, st);
+    case kTagQkv: return run_gemm<WQ, NT, 0, kTagQkv>(W, rows, A, nks, epi, nblk, st);
+    case kTagGateUp: return run_gemm<WQ, NT, 0, kTagGateUp>(W, rows, A, nks, epi, nblk, st);
+    case kTagDown: return run_gemm<WQ, NT, 0, kTagDown>(W, rows, A, nks, epi, nblk, st);
+    case kTagPleGate: return run_gemm<WQ, NT, 0, kTagPleGate>(W, rows, A, nks, epi, nblk, st);
+    case kTagPleProj: return run_gemm<WQ, NT, 0, kTagPleProj>(W, rows, A, nks, epi, nblk, st);
+    case kTagLmHead: return run_gemm<WQ, NT, 0, kTagLmHead>(W, rows, A, nks, epi, nblk, st);
+    default: return run_gemm<WQ, NT, 0, kTagOther>(W, rows, A, nks, epi, nblk, st);
   }
 }
 
-hipError_t launch_gemm(int quant, int tag, const Lin& W, int rows, const uint16_t* xh,
-                       const uint16_t* xl, const float* xg, const GemmPlan& plan,
-                       const Epilogue& epi, int* nblk, hipStream_t st) {
+hipError_t launch_gemm(int quant, int tag, const Lin& W, int rows, const GemmA& A,
+                       const GemmPlan& plan, const Epilogue& epi, int* nblk, hipStream_t st) {
   const int nks = plan.nks;
   if (rows < 1 || nks < 1 || nks > kMaxGemmSplit || W.K % nks || (W.K / nks) % 32)
     return hipErrorInvalidValue;
   if (epi.argmax && (quant || nks != 1)) return hipErrorInvalidValue;
+  if (A.a ? A.kind != kPlain || A.na != 1 || A.lda % 8
+          : (!A.xh || !A.xl || (quant && !A.xg)))
+    return hipErrorInvalidValue;
   if (quant) {
-    if (plan.nt == 4) return gemm_tag<1, 4>(tag, W, rows, xh, xl, xg, nks, epi, nblk, st);
-    if (plan.nt == 2) return gemm_tag<1, 2>(tag, W, rows, xh, xl, xg, nks, epi, nblk, st);
+    if (plan.nt == 4) return gemm_tag<1, 4>(tag, W, rows, A, nks, epi, nblk, st);
+    if (plan.nt == 2) return gemm_tag<1, 2>(tag, W, rows, A, nks, epi, nblk, st);
   } else {
-    if (plan.nt == 2) return gemm_tag<0, 2>(tag, W, rows, xh, xl, xg, nks, epi, nblk, st);
-    if (plan.nt == 1) return gemm_tag<0, 1>(tag, W, rows, xh, xl, xg, nks, epi, nblk, st);
+    if (plan.nt == 2) return gemm_tag<0, 2>(tag, W, rows, A, nks, epi, nblk, st);
+    if (plan.nt == 1) return gemm_tag<0, 1>(tag, W, rows, A, nks, epi, nblk, st);
   }
   return hipErrorInvalidValue;
 }
