@@ -225,11 +225,12 @@ int e2b_graph_replay(e2b_graph* graph, void* stream);
 void e2b_graph_destroy(e2b_graph* graph);
 
 /* ---- per-kernel timing ----------------------------------------------------
- * While profiling a kind, every eager launch of that kernel kind is bracketed
- * by HIP events on its stream; e2b_profile_read synchronises them and
- * returns the launch count, summed duration (ms) and summed algorithmic bytes
- * (weights streamed once plus input and output vectors), then stops
- * profiling.  kind 0 stops without reading. */
+ * While profiling a kind, every eager launch of that kind's product kernel
+ * records HIP events at its own start and end (the dispatch's timestamps,
+ * hipExtLaunchKernel; a batched product's input-prep kernel is not included);
+ * e2b_profile_read synchronises them and returns the launch count, summed
+ * duration (ms) and summed algorithmic bytes (weights streamed once plus input
+ * and output vectors), then stops profiling.  kind 0 stops without reading. */
 enum {
   E2B_KIND_NONE = 0, E2B_KIND_QKV = 1, E2B_KIND_O = 2, E2B_KIND_GATE_UP = 3, E2B_KIND_DOWN = 4,
   E2B_KIND_PLE_GATE = 5, E2B_KIND_PLE_PROJ = 6, E2B_KIND_PLE_MODEL = 7, E2B_KIND_LM_HEAD = 8

@@ -159,6 +159,9 @@ struct GemmA {
 // *nblk receives the number of column blocks (argmax candidates per row)
 hipError_t launch_gemm(int quant, int tag, const Lin& W, int rows, const GemmA& A,
                        const GemmPlan& plan, const Epilogue& epi, int* nblk, hipStream_t st);
+// The next launch_gemv / launch_gemm on this host thread records these
+// events at its kernel's start and end.
+void set_launch_events(hipEvent_t start, hipEvent_t stop);
 hipError_t launch_sum_partials(int nparts, size_t n, const float* parts, float* out,
                                hipStream_t st);
 hipError_t launch_argmax_final(int rows, int nblk, const float* cand_val,

@@ -337,10 +337,9 @@ hipError_t matmul(e2b_model* m, int quant, int tag, const Lin& W, int rows, bool
   const bool prof = m->prof_kind == tag;
   e2b_model::Mark mk{};
   hipError_t e = hipSuccess;
-  if (prof) {
+  if (prof) {  // the product kernel itself records them (dispatch timestamps)
     e = hipEventCreate(&mk.a);
     if (e == hipSuccess) e = hipEventCreate(&mk.b);
-    if (e == hipSuccess) e = hipEventRecord(mk.a, st);
     if (e != hipSuccess) return e;
   }
   int splits = 1;
@@ -348,6 +347,7 @@ hipError_t matmul(e2b_model* m, int quant, int tag, const Lin& W, int rows, bool
     splits = e2b::gemv_splits(W.K);
     // the matvec prologue reads one copy of a; it splits only K > 2048
     if (pr.na != 1 || (splits > 1 && !partial_ok)) return hipErrorInvalidValue;
+    if (prof) e2b::set_launch_events(mk.a, mk.b);
     e = e2b::launch_gemv(quant, tag, W, rows, pr, ep, 0, nblk, st);
   } else {
     const e2b::GemmPlan plan = e2b::gemm_plan(quant, W.N, W.K, partial_ok);
@@ -364,13 +364,12 @@ hipError_t matmul(e2b_model* m, int quant, int tag, const Lin& W, int rows, bool
       e = e2b::launch_xprep(pr, rows, W.K, const_cast<uint16_t*>(A.xh),
                             const_cast<uint16_t*>(A.xl), const_cast<float*>(A.xg), st);
     }
+    if (e == hipSuccess && prof) e2b::set_launch_events(mk.a, mk.b);
     if (e == hipSuccess) e = e2b::launch_gemm(quant, tag, W, rows, A, plan, ep, nblk, st);
   }
   if (nd) *nd = splits;
   if (e != hipSuccess) return e;
   if (prof) {
-    e = hipEventRecord(mk.b, st);
-    if (e != hipSuccess) return e;
     const double wb = quant ? (double)W.N * W.K / 2 + (double)W.N * (W.K / 32) * 2
                             : (double)W.N * W.K * 2;
     mk.bytes = wb + (double)rows * (W.K + W.N) * sizeof(float);

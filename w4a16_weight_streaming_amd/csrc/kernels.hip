@@ -16,11 +16,33 @@
 // most 12 significant bits).
 #include "e2b_internal.h"
 
+#include <hip/hip_ext.h>
+
 #include <float.h>
 #include <type_traits>
 #include <math.h>
 
 namespace e2b {
+
+// Timestamps of the next matrix product launch (per host thread): when set,
+// that launch records them at its own start and end (the dispatch's
+// timestamps, not a marker queued before it), then they are cleared.
+namespace {
+thread_local hipEvent_t g_ev_start = nullptr, g_ev_stop = nullptr;
+}
+void set_launch_events(hipEvent_t start, hipEvent_t stop) {
+  g_ev_start = start;
+  g_ev_stop = stop;
+}
+#define E2B_TIMED_LAUNCH(kernel, grid, block, shm, st, ...)                                    \
+  do {                                                                                         \
+    if (g_ev_start) {                                                                          \
+      hipExtLaunchKernelGGL(kernel, grid, block, shm, st, g_ev_start, g_ev_stop, 0, __VA_ARGS__); \
+      g_ev_start = g_ev_stop = nullptr;                                                        \
+    } else {                                                                                   \
+      hipLaunchKernelGGL(kernel, grid, block, shm, st, __VA_ARGS__);                           \
+    }                                                                                          \
+  } while (0)
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
@@ -524,8 +546,8 @@ static hipError_t run_gemv(const Lin& W, int rows, const Prologue& pro, const Ep
   if (bx < 1) bx = 1;
   if (blocks_out) *blocks_out = bx;
   const size_t shm = ((size_t)KS + Packed<WQ, KS>::words + 32) * sizeof(float);
-  hipLaunchKernelGGL((k_gemv<WQ, KS, U, TAG>), dim3(bx, nks, rows), dim3(kGemvThreads), shm, st,
-                     W, rows, pro, epi);
+  E2B_TIMED_LAUNCH((k_gemv<WQ, KS, U, TAG>), dim3(bx, nks, rows), dim3(kGemvThreads), shm, st, W,
+                   rows, pro, epi);
   return hipGetLastError();
 }
 
@@ -1460,7 +1482,7 @@ static hipError_t run_gemm(const Lin& W, int rows, const GemmA& A, int nks, cons
   const int nbx = (W.N + 64 * NT - 1) / (64 * NT);
   if (nblk) *nblk = nbx;
   dim3 grid(nbx, nks, (rows + kMB - 1) / kMB);
-  hipLaunchKernelGGL((k_gemm<WQ, NT, FA, TAG>), grid, dim3(256), 0, st, W, rows, A, W.K / nks, epi);
+  E2B_TIMED_LAUNCH((k_gemm<WQ, NT, FA, TAG>), grid, dim3(256), 0, st, W, rows, A, W.K / nks, epi);
   return hipGetLastError();
 }
 

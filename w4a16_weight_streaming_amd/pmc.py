@@ -1,0 +1,87 @@
+"""HBM traffic per kernel launch from two rocprofv3 counter runs.
+
+Usage (after two runs of the same command, one with `--pmc FETCH_SIZE`, one
+with `--pmc WRITE_SIZE`, both with `--output-format csv`, the command running
+`bench.py --copy-calibration` so that a 1 GiB elementwise copy is among the
+dispatches):
+
+    python -m w4a16_weight_streaming_amd.pmc FETCH_DIR WRITE_DIR OUT.json
+
+Both counters are reported in KiB per dispatch.  Each is scaled by what it
+reads for the reference copy (1 GiB read, 1 GiB written), so the factors
+absorb any unit or sampling convention of the counters.  OUT.json records the
+mean per-dispatch values of every kernel of this library, the two factors,
+and a hash of the kernel sources, so that a reader can tell when the profile
+no longer describes the current kernels.
+"""
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+from collections import defaultdict
+
+GIB = float(1 << 30)
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def kernels_sha():
+    h = hashlib.sha1()
+    for f in ("kernels.hip", "e2b_internal.h"):
+        with open(os.path.join(HERE, "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def read_counter(d, counter):
+    """{kernel name: [per-dispatch value (KiB)]} for one counter run."""
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    per = defaultdict(lambda: defaultdict(float))  # kernel -> dispatch -> value
+    for fn in files:
+        with open(fn, newline="") as f:
+            for row in csv.DictReader(f):
+                if row.get("Counter_Name", "").strip() != counter:
+                    continue
+                name = row["Kernel_Name"].strip()
+                disp = row.get("Dispatch_Id") or row.get("Correlation_Id")
+                per[name][disp] += float(row["Counter_Value"])
+    return {k: list(v.values()) for k, v in per.items()}
+
+
+def short(name):
+    return name.split("(")[0].strip()
+
+
+def main(fetch_dir, write_dir, out):
+    fetch = read_counter(fetch_dir, "FETCH_SIZE")
+    write = read_counter(write_dir, "WRITE_SIZE")
+    copy = [k for k in fetch if "neg" in k.lower() and "e2b::" not in k]
+    if not copy:
+        raise SystemExit("reference copy kernel not found (run bench.py with --copy-calibration)")
+    big = lambda d, k: max(d.get(k, [0.0]))
+    ck = max(copy, key=lambda k: big(fetch, k))
+    f_copy, w_copy = big(fetch, ck) * 1024.0, big(write, ck) * 1024.0
+    res = {"kernels_sha": kernels_sha(), "reference_kernel": short(ck),
+           "reference_fetch_kib": f_copy / 1024.0, "reference_write_kib": w_copy / 1024.0,
+           "fetch_factor": GIB / f_copy, "write_factor": GIB / w_copy, "kernels": {}}
+    for k in sorted(set(fetch) | set(write)):
+        if "e2b::" not in k:
+            continue
+        fv, wv = fetch.get(k, []), write.get(k, [])
+        res["kernels"][short(k)] = {
+            "dispatches": max(len(fv), len(wv)),
+            "fetch_bytes": 1024.0 * sum(fv) / max(len(fv), 1),
+            "write_bytes": 1024.0 * sum(wv) / max(len(wv), 1)}
+    with open(out, "w") as f:
+        json.dump(res, f, indent=1, sort_keys=True)
+    print(f"reference {short(ck)}: fetch {f_copy / GIB:.4f} GiB, write {w_copy / GIB:.4f} GiB "
+          f"for 1 GiB each; {len(res['kernels'])} kernels -> {out}")
+
+
+if __name__ == "__main__":
+    if len(sys.argv) != 4:
+        raise SystemExit(__doc__)
+    main(*sys.argv[1:])
