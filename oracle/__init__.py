@@ -76,6 +76,8 @@ def lib():
         L.orc_kv_source.argtypes = [vp, i32]
         L.orc_kv_row.restype = ctypes.POINTER(ctypes.c_double)
         L.orc_kv_row.argtypes = [vp, i32, i32, i32, i32]
+        L.orc_kv_load.restype = i32
+        L.orc_kv_load.argtypes = [vp, i32, i32, i32, i32, vp, vp]
         L.orc_linear_apply.argtypes = [i32, vp, vp, i32, i32, i32, dp, dp]
         L.orc_decode_weight.restype = ctypes.c_double
         L.orc_decode_weight.argtypes = [i32, vp, vp, i32, i32, i32, i64, i64]
@@ -168,6 +170,14 @@ class Oracle:
     def kv_row(self, l: int, which: int, seq: int, pos: int, hd: int) -> np.ndarray:
         p = lib().orc_kv_row(self._h, l, which, seq, pos)
         return np.ctypeslib.as_array(p, shape=(hd,)).copy()
+
+    def kv_load(self, l: int, seq: int, pos0: int, k_bits: np.ndarray, v_bits: np.ndarray):
+        """Set cached positions pos0.. of a K/V-owning layer from bf16 bits [n, hd]
+        (test set-up: seeded cache contents in place of a long prefill)."""
+        k = np.ascontiguousarray(k_bits, np.uint16)
+        v = np.ascontiguousarray(v_bits, np.uint16)
+        if lib().orc_kv_load(self._h, l, seq, pos0, k.shape[0], _ptr(k), _ptr(v)) != 0:
+            raise RuntimeError("oracle: bad kv_load arguments")
 
 
 # ---- single pieces, for the pins -------------------------------------------

@@ -323,6 +323,25 @@ const double* orc_kv_row(void* p, int l, int which, int seq, int pos) {
   return base + ((size_t)seq * m->max_ctx + pos) * y->hd;
 }
 
+/* Test set-up: store n cached positions pos0 .. pos0+n-1 of sequence seq
+ * for layer l, which must own its K/V, from bf16 bit patterns ([n][hd] each
+ * for K and V).  A long context can then be given as seeded cache contents
+ * instead of a long prefill.  0, or -1 on a bad argument. */
+int orc_kv_load(void* p, int l, int seq, int pos0, int n, const uint16_t* k, const uint16_t* v) {
+  orc_model* m = (orc_model*)p;
+  if (l < 0 || l >= m->L || m->layers[l].src != l || seq < 0 || seq >= m->max_seq || pos0 < 0 ||
+      n < 0 || pos0 + n > m->max_ctx)
+    return -1;
+  const int hd = m->layers[l].hd;
+  for (int i = 0; i < n; ++i)
+    for (int d = 0; d < hd; ++d) {
+      const size_t o = ((size_t)seq * m->max_ctx + pos0 + i) * hd + d;
+      m->kc[l][o] = bf(k[(size_t)i * hd + d]);
+      m->vc[l][o] = bf(v[(size_t)i * hd + d]);
+    }
+  return 0;
+}
+
 /* ------------------------------------------------------------- the step */
 
 /* Embedding e = E[x] * sqrt(H), and the per-layer inputs pli [L, P]: the

@@ -361,3 +361,81 @@ def test_e2b_greedy_parity(torch_dev, e2b_model):
     eng = _engine(cfg, quant, w, 1, 64, 16)
     orc = oracle.Oracle(cfg, quant, w, 1, 64)
     run_greedy(torch, eng, orc, [synth.tokens(16, 1, cfg["vocab_size"])], 16, quant)
+
+
+def _seed_cache(torch, eng, cfg, T_of, orc=None, orc_rows=()):
+    """Seeded synthetic K/V (bf16 N(0, 1), like normed keys and values) at
+    positions 0 .. T_of[b]-1 of every sequence b, written into the GPU cache
+    and, for the sequences in orc_rows (oracle sequence i = orc_rows[i]), into
+    the oracle's.  Stands in for a long prefill; comes from the shared input
+    generator, not from either implementation."""
+    dev = eng.device
+    smap = eng.model.kv_share_map()
+    for l in range(cfg["num_hidden_layers"]):
+        if smap[l] != l:
+            continue
+        hd = synth.layer_head_dim(cfg, l)
+        kt, vt = eng.kv_tensor(l, 0, hd), eng.kv_tensor(l, 1, hd)
+        for b, T in enumerate(T_of):
+            kb = synth.normal_bf16((T, hd), 500 + b, f"cache.k.{l}", 0.0, 1.0)
+            vb = synth.normal_bf16((T, hd), 500 + b, f"cache.v.{l}", 0.0, 1.0)
+            kt[b, :T] = torch.from_numpy(kb.view(np.int16)).to(dev)
+            vt[b, :T] = torch.from_numpy(vb.view(np.int16)).to(dev)
+            if orc is not None and b in orc_rows:
+                orc.kv_load(l, orc_rows.index(b), 0, kb, vb)
+
+
+def _graph_decode_vs_oracle(torch, eng, orc, cfg, quant, T_of, rows, steps, seed):
+    """`steps` greedy steps of a captured decode graph (the launch the bench
+    times) from positions T_of; the sampled rows' logits against the oracle,
+    teacher-forced on the GPU's tokens."""
+    dev = eng.device
+    B, V = len(T_of), cfg["vocab_size"]
+    st = Stats(quant)
+    s = torch.cuda.Stream(dev)
+    with torch.cuda.stream(s):
+        tok = torch.from_numpy(synth.tokens(B, seed, V)).to(dev)
+        pos = torch.tensor(T_of, dtype=torch.int32, device=dev)
+        lg = torch.zeros(B, V, dtype=torch.float32, device=dev)
+        g = eng.capture(tok, pos, tok, lg, advance=True)
+        for i in range(steps):
+            fed = tok.cpu().numpy().copy()
+            g.replay()
+            s.synchronize()
+            eng.check()
+            got_l, got_t = lg.cpu().numpy(), tok.cpu().numpy()
+            for j, b in enumerate(rows):
+                _, ref, _ = orc.step(j, int(fed[b]), T_of[b] + i)
+                st.add(got_l[b], int(got_t[b]), ref, f"step {i} row {b} (position {T_of[b] + i})")
+        g.close()
+    st.finish()
+
+
+def test_e2b_batch64_graph_parity(torch_dev, e2b_model):
+    """Batched decode at full size: 64 sequences at positions 129 .. 633
+    (seeded caches), 2 steps of the captured graph, rows 0, 31 and 63 against
+    the oracle."""
+    torch, dev = torch_dev
+    cfg, quant, w = e2b_model
+    T_of = [129 + 8 * b for b in range(64)]
+    rows = [0, 31, 63]
+    eng = _engine(cfg, quant, w, 64, 640, 64)
+    orc = oracle.Oracle(cfg, quant, w, len(rows), 640)
+    _seed_cache(torch, eng, cfg, T_of, orc, rows)
+    _graph_decode_vs_oracle(torch, eng, orc, cfg, quant, T_of, rows, 2, 77)
+
+
+@pytest.mark.parametrize("B", [1, 8])
+def test_e2b_long_context_graph_parity(torch_dev, B):
+    """Long context at full size (W4A16): contexts near 8,000 (seeded
+    caches), 2 steps of the captured graph, first and last rows against the
+    oracle -- full-layer attention over ~8,000 keys, sliding layers over 512."""
+    torch, dev = torch_dev
+    cfg = synth.get_config("e2b")
+    w = synth.generate(cfg, "w4a16", seed=0)
+    T_of = [8000 - 123 * b for b in range(B)]
+    rows = sorted({0, B - 1})
+    eng = _engine(cfg, "w4a16", w, B, 8064, 64)
+    orc = oracle.Oracle(cfg, "w4a16", w, len(rows), 8064)
+    _seed_cache(torch, eng, cfg, T_of, orc, rows)
+    _graph_decode_vs_oracle(torch, eng, orc, cfg, "w4a16", T_of, rows, 2, 78)

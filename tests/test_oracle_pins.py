@@ -301,3 +301,29 @@ def test_e2b_inventory_matches_page_totals():
     for nq in (7, 9):
         other, _ = _bytes(dict(cfg, num_attention_heads=nq), "bf16")
         assert abs(other - int(g["bf16_total"])) / int(g["bf16_total"]) > 5e-3
+
+
+def test_kv_load_places_rows_where_prefill_does():
+    """kv_load stores bf16 rows at (layer, sequence, position): an oracle whose
+    cache is loaded with another oracle's prefill cache (sequence 1 into
+    sequence 0) decodes the next token bit-identically; a layer that reads
+    shared K/V refuses a load."""
+    cfg = synth.get_config("toy10")
+    V = cfg["vocab_size"]
+    w = synth.generate(cfg, "bf16", seed=3)
+    a = oracle.Oracle(cfg, "bf16", w, 2, 24)
+    b = oracle.Oracle(cfg, "bf16", w, 2, 24)
+    toks = synth.tokens(10, 4, V)
+    a.prefill(1, toks)
+    owners = [l for l in range(cfg["num_hidden_layers"]) if a.kv_source(l) == l]
+    for l in owners:
+        hd = synth.layer_head_dim(cfg, l)
+        k = np.stack([a.kv_row(l, 0, 1, p, hd) for p in range(10)]).astype(np.float32)
+        v = np.stack([a.kv_row(l, 1, 1, p, hd) for p in range(10)]).astype(np.float32)
+        b.kv_load(l, 0, 0, synth.f32_to_bf16(k), synth.f32_to_bf16(v))
+    ta, la, _ = a.step(1, 17, 10)
+    tb, lb, _ = b.step(0, 17, 10)
+    assert ta == tb and np.array_equal(la, lb)
+    shared = [l for l in range(cfg["num_hidden_layers"]) if a.kv_source(l) != l][0]
+    with pytest.raises(RuntimeError):
+        b.kv_load(shared, 0, 0, np.zeros((1, 64), np.uint16), np.zeros((1, 64), np.uint16))
