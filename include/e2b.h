@@ -133,9 +133,10 @@ size_t e2b_kv_bytes(const e2b_model* model, int max_batch, int max_ctx);
 
 /* Workspace bytes for calls that process up to max_rows rows (decode batch,
  * or prefill rows per pass).  The workspace (256-byte aligned) is scratch
- * except its first 64 bytes, the device error word: zero them once before
- * the first call; e2b_check reads and re-zeroes them.  Calls that overlap in
- * time must not share a workspace. */
+ * except its first 32 KiB of control words (the device error word, kernel
+ * counters): zero them once before the first call; the kernels leave the
+ * counters zero, and e2b_check reads and re-zeroes the error word.  Calls
+ * that overlap in time must not share a workspace. */
 size_t e2b_workspace_bytes(const e2b_model* model, int max_rows);
 
 /* Copy the tensors to the caller's device arena (d_arena, arena_bytes >=
@@ -233,7 +234,8 @@ void e2b_graph_destroy(e2b_graph* graph);
  * and output vectors), then stops profiling.  kind 0 stops without reading. */
 enum {
   E2B_KIND_NONE = 0, E2B_KIND_QKV = 1, E2B_KIND_O = 2, E2B_KIND_GATE_UP = 3, E2B_KIND_DOWN = 4,
-  E2B_KIND_PLE_GATE = 5, E2B_KIND_PLE_PROJ = 6, E2B_KIND_PLE_MODEL = 7, E2B_KIND_LM_HEAD = 8
+  E2B_KIND_PLE_GATE = 5, E2B_KIND_PLE_PROJ = 6, E2B_KIND_PLE_MODEL = 7, E2B_KIND_LM_HEAD = 8,
+  E2B_KIND_STEP = 9 /* the whole one-row decode step (one persistent kernel) */
 };
 int e2b_profile_begin(e2b_model* model, int kind);
 int e2b_profile_read(e2b_model* model, int* launches, double* total_ms, double* total_bytes);

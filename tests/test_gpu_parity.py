@@ -439,3 +439,34 @@ def test_e2b_long_context_graph_parity(torch_dev, B):
     orc = oracle.Oracle(cfg, "w4a16", w, len(rows), 8064)
     _seed_cache(torch, eng, cfg, T_of, orc, rows)
     _graph_decode_vs_oracle(torch, eng, orc, cfg, "w4a16", T_of, rows, 2, 78)
+
+
+@pytest.mark.parametrize("name,quant", [("toy10", "bf16"), ("toy10", "w4a16"), ("e2b", "bf16")])
+def test_persistent_step_parity(torch_dev, name, quant, monkeypatch):
+    """The opt-in persistent one-row step (one kernel per decode step, phases
+    separated by grid barriers): greedy parity against the oracle, and the
+    same tokens and bitwise logits as the per-phase kernels."""
+    torch, dev = torch_dev
+    cfg = synth.get_config(name)
+    w = synth.generate(cfg, quant, seed=0)
+    V = cfg["vocab_size"]
+    prompt = synth.tokens(12, 3, V)
+    steps = 12 if name == "e2b" else 24
+    monkeypatch.setenv("E2B_PERSISTENT_STEP", "1")
+    eng = _engine(cfg, quant, w, 1, 64, 16)
+    orc = oracle.Oracle(cfg, quant, w, 1, 64)
+    run_greedy(torch, eng, orc, [prompt], steps, quant)
+    # persistent vs per-phase kernels on identical inputs: the same arithmetic
+    # element by element, so the same token and the same logits bit for bit
+    monkeypatch.setenv("E2B_PERSISTENT_STEP", "0")
+    ref = _engine(cfg, quant, w, 1, 64, 16)
+    outs = []
+    for e in (eng, ref):
+        a = torch.zeros(1, dtype=torch.int32, device=dev)
+        lg = torch.zeros(1, V, dtype=torch.float32, device=dev)
+        e.prefill(0, torch.from_numpy(prompt).to(dev), 0, a)
+        e.decode_step(a.clone(), torch.tensor([12], dtype=torch.int32, device=dev), a, lg)
+        e.check()
+        outs.append((int(a.item()), lg.cpu().numpy()[0]))
+    (t0, l0), (t1, l1) = outs
+    assert t0 == t1 and np.array_equal(l0, l1)

@@ -18,7 +18,7 @@ _lib = None
 
 E2B_OK, E2B_EINVAL, E2B_ERANGE, E2B_ENOMEM, E2B_EHIP, E2B_EDEVICE, E2B_ESTATE = range(7)
 KINDS = {"qkv": 1, "o": 2, "gate_up": 3, "down": 4, "ple_gate": 5, "ple_proj": 6, "ple_model": 7,
-         "lm_head": 8}
+         "lm_head": 8, "step": 9}
 QUANT = {"bf16": 0, "w4a16": 1}
 DTYPE_BF16, DTYPE_INT32 = 0, 1
 

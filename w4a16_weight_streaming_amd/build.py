@@ -8,8 +8,9 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libe2b.so")
-SOURCES = [os.path.join(CSRC, "kernels.hip"), os.path.join(CSRC, "host.cpp")]
-HEADERS = [os.path.join(CSRC, "e2b_internal.h"), os.path.join(ROOT, "include", "e2b.h")]
+SOURCES = [os.path.join(CSRC, "kernels.hip"), os.path.join(CSRC, "step1.hip"), os.path.join(CSRC, "host.cpp")]
+HEADERS = [os.path.join(CSRC, "e2b_internal.h"), os.path.join(CSRC, "dev_common.h"),
+           os.path.join(ROOT, "include", "e2b.h")]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
@@ -27,18 +28,37 @@ def stale() -> bool:
 
 
 def build(force: bool = True, verbose: bool = False) -> str:
-    """Compile every source into libe2b.so (always when force)."""
+    """Compile every source into libe2b.so (always when force): the sources in
+    parallel to objects under _build/, then one link."""
     if not force and not stale():
         return LIB
+    from concurrent.futures import ThreadPoolExecutor
     hipcc = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc] + HIPCC_FLAGS + ["-shared", "-o", tmp] + SOURCES
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    msgs = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if "packed-fp32-ops" not in l)
+    objdir = os.path.join(ROOT, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    tag = "%d" % os.getpid()
+
+    def compile_one(src):
+        obj = os.path.join(objdir, os.path.basename(src) + "." + tag + ".o")
+        r = subprocess.run([hipcc] + HIPCC_FLAGS + ["-c", src, "-o", obj], capture_output=True, text=True)
+        return obj, r
+
+    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+        results = list(ex.map(compile_one, SOURCES))
+    msgs = []
+    for obj, r in results:
+        msgs += [l for l in (r.stdout + r.stderr).splitlines() if "packed-fp32-ops" not in l]
+        if r.returncode != 0:
+            raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
+    tmp = LIB + ".tmp" + tag
+    r = subprocess.run([hipcc, "--offload-arch=gfx950", "-shared", "-o", tmp] + [o for o, _ in results],
+                       capture_output=True, text=True)
+    for o, _ in results:
+        os.remove(o)
     if r.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + msgs)
-    if verbose and msgs.strip():
-        print(msgs)
+        raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
+    if verbose and msgs:
+        print("\n".join(msgs))
     os.replace(tmp, LIB)
     return LIB
 

@@ -14,7 +14,7 @@
 // contributes  s * (sum (128 + c_k) x_k - 136 * sum x_k) = s * sum (c_k - 8) x_k,
 // with the group scale s applied in fp32 (exact decode: (c - 8) * s needs at
 // most 12 significant bits).
-#include "e2b_internal.h"
+#include "dev_common.h"
 
 #include <hip/hip_ext.h>
 
@@ -34,6 +34,12 @@ void set_launch_events(hipEvent_t start, hipEvent_t stop) {
   g_ev_start = start;
   g_ev_stop = stop;
 }
+bool take_launch_events(hipEvent_t* start, hipEvent_t* stop) {
+  *start = g_ev_start;
+  *stop = g_ev_stop;
+  g_ev_start = g_ev_stop = nullptr;
+  return *start != nullptr;
+}
 #define E2B_TIMED_LAUNCH(kernel, grid, block, shm, st, ...)                                    \
   do {                                                                                         \
     if (g_ev_start) {                                                                          \
@@ -43,54 +49,6 @@ void set_launch_events(hipEvent_t start, hipEvent_t stop) {
       hipLaunchKernelGGL(kernel, grid, block, shm, st, __VA_ARGS__);                           \
     }                                                                                          \
   } while (0)
-
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ float bf2f(uint32_t b) { return __uint_as_float((b & 0xFFFFu) << 16); }
-
-__device__ __forceinline__ uint32_t f2bf(float f) {  // round to nearest even (finite inputs)
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
-}
-
-__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
-                                         __builtin_bit_cast(bf16x2_t, b), c, false);
-}
-
-__device__ __forceinline__ float gelu_tanh(float x) {
-  const float c = 0.7978845608028654f;  // sqrt(2/pi)
-  return 0.5f * x * (1.0f + tanhf(c * (x + 0.044715f * x * x * x)));
-}
-
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
-
-// Sum over a block of NT threads, same value returned to every thread.
-// `sh` needs NT/64 floats; the leading barrier makes back-to-back calls safe.
-template <int NT>
-__device__ float block_sum(float v, float* sh) {
-  v = wave_sum(v);
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
-  __syncthreads();
-  float s = 0.f;
-#pragma unroll
-  for (int i = 0; i < NT / 64; ++i) s += sh[i];
-  return s;
-}
-
-__device__ __forceinline__ int row_pos(const Rows& R, int r) {
-  return R.positions ? R.positions[r] : R.pos0 + r;
-}
-__device__ __forceinline__ int clamp_pos(const Rows& R, int p) {
-  return p < 0 ? 0 : (p >= R.max_ctx ? R.max_ctx - 1 : p);
-}
-__device__ __forceinline__ int row_seq(const Rows& R, int r) { return R.seq0 + r * R.seq_stride; }
 
 // ---------------------------------------------------------------- embedding
 // h[r] = E[tok] * sqrt(H);  tokple[r] = E_ple[tok] * sqrt(P)
@@ -174,163 +132,6 @@ hipError_t launch_ple_finish(const Rows& R, const float* u, int u_parts, size_t 
 }
 
 // ------------------------------------------------------- matrix-vector product
-// Lane layout for one K slice of KS elements (a 16-byte load per lane):
-//  bf16  : a lane covers 8 consecutive k per 512-wide chunk; S lanes per row.
-//  W4A16 : a lane covers whole 32-groups (16 bytes = one group); S lanes per row.
-// RPL = 64 / S rows are covered by one wave-wide load ("unit"); C loads per unit.
-template <int WQ, int KS>
-struct Lay {
-  static constexpr int G = KS / 32;
-  static constexpr int S =
-      WQ ? ((G % 64 == 0) ? 64 : ((G % 16 == 0) ? 16 : G)) : (KS / 8 < 64 ? KS / 8 : 64);
-  static constexpr int RPL = 64 / S;
-  static constexpr int C = WQ ? G / S : (KS >= 512 ? KS / 512 : 1);
-  static constexpr int NP = WQ ? C * 16 : C * 4;  // bf16 pairs of x per lane
-  static_assert(64 % S == 0, "lanes per row must divide the wave");
-};
-
-// The block's fp32 input slice xs[0..KS) for row b (K slice k0..k0+KS), in two
-// halves: load() issues every global read the prologue needs at once (one
-// round trip; the weight prefetch is issued after it), finish() does the
-// arithmetic and writes xs.
-template <int KS>
-struct PrologueRegs {
-  static constexpr int PT = (KS + kGemvThreads - 1) / kGemvThreads;
-  float a0[PT], a1[PT], g0[PT], g1[PT];
-  float dq[PT][kMaxSplitK];
-
-  __device__ __forceinline__ void load(const Prologue& p, int rows, int b, int k0, int K) {
-    const int t = threadIdx.x;
-#pragma unroll
-    for (int j = 0; j < PT; ++j) {
-      const int i = t + j * kGemvThreads;
-      a0[j] = a1[j] = g0[j] = g1[j] = 0.f;
-#pragma unroll
-      for (int q = 0; q < kMaxSplitK; ++q) dq[j][q] = 0.f;
-      if (i >= KS) continue;
-      if (p.kind == kPlain) {
-        a0[j] = p.a[(size_t)b * p.lda + k0 + i];
-      } else if (p.kind == kGeglu) {
-        a0[j] = p.a[(size_t)b * p.lda + k0 + i];
-        a1[j] = p.a[(size_t)b * p.lda + K + k0 + i];
-      } else if (p.kind == kPleGate) {
-        a0[j] = p.a[(size_t)b * p.lda + k0 + i];
-        a1[j] = p.pli[(size_t)b * p.pli_ld + k0 + i];
-      } else {  // kRes / kResNorm: KS == K == hidden size
-        a0[j] = p.a[(size_t)b * K + i];
-        if (p.d) {
-#pragma unroll
-          for (int q = 0; q < kMaxSplitK; ++q)
-            if (q < p.nd) dq[j][q] = p.d[(size_t)q * p.d_pstride + (size_t)b * K + i];
-          g0[j] = bf2f(p.gd[i]);
-        }
-        if (p.kind == kResNorm) g1[j] = bf2f(p.gx[i]);
-      }
-    }
-  }
-
-  __device__ __forceinline__ void finish(const Prologue& p, int b, int K, float* xs, float* red) {
-    const int t = threadIdx.x;
-    if (p.kind == kPlain) {
-#pragma unroll
-      for (int j = 0; j < PT; ++j)
-        if (t + j * kGemvThreads < KS) xs[t + j * kGemvThreads] = a0[j];
-    } else if (p.kind == kGeglu || p.kind == kPleGate) {
-#pragma unroll
-      for (int j = 0; j < PT; ++j)
-        if (t + j * kGemvThreads < KS) xs[t + j * kGemvThreads] = gelu_tanh(a0[j]) * a1[j];
-    } else {
-      float dv[PT], ss = 0.f;
-#pragma unroll
-      for (int j = 0; j < PT; ++j) {
-        float s = 0.f;
-#pragma unroll
-        for (int q = 0; q < kMaxSplitK; ++q) s += dq[j][q];
-        dv[j] = s;
-        ss += s * s;
-      }
-      float rd = 0.f;
-      if (p.d) rd = rsqrtf(block_sum<kGemvThreads>(ss, red) / (float)K + p.eps);
-      const float sc = p.scalar ? bf2f(p.scalar[0]) : 1.0f;
-      const bool store = p.d && p.h_out && blockIdx.x == 0 && blockIdx.y == 0;
-      float hv[PT], hs = 0.f;
-#pragma unroll
-      for (int j = 0; j < PT; ++j) {
-        const int i = t + j * kGemvThreads;
-        float hn = a0[j];
-        if (p.d) hn = (hn + dv[j] * rd * g0[j]) * sc;
-        hv[j] = hn;
-        if (i < KS) {
-          hs += hn * hn;
-          if (store) p.h_out[(size_t)b * K + i] = hn;
-        }
-      }
-      if (p.kind == kResNorm) {
-        const float rh = rsqrtf(block_sum<kGemvThreads>(hs, red) / (float)K + p.eps);
-#pragma unroll
-        for (int j = 0; j < PT; ++j)
-          if (t + j * kGemvThreads < KS) xs[t + j * kGemvThreads] = hv[j] * rh * g1[j];
-      } else {
-#pragma unroll
-        for (int j = 0; j < PT; ++j)
-          if (t + j * kGemvThreads < KS) xs[t + j * kGemvThreads] = hv[j];
-      }
-    }
-    __syncthreads();
-  }
-};
-
-// split an fp32 pair into a bf16 hi pair and a bf16 lo pair (x = hi + lo)
-__device__ __forceinline__ void split_pair(float a, float b, uint32_t& hi, uint32_t& lo) {
-  const uint32_t ha = f2bf(a), hb = f2bf(b);
-  const uint32_t la = f2bf(a - bf2f(ha)), lb = f2bf(b - bf2f(hb));
-  hi = ha | (hb << 16);
-  lo = la | (lb << 16);
-}
-
-// LDS words of the packed input: bf16 layout 8 words per (chunk, lane slot)
-// [4 hi pairs | 4 lo pairs]; W4A16 layout 36 words per 32-group
-// [16 hi pairs | 16 lo pairs | group sum | pad].
-template <int WQ, int KS>
-struct Packed {
-  static constexpr int kWordsW4 = 36;
-  static constexpr int words = WQ ? (KS / 32) * kWordsW4 : KS;
-};
-
-// xs (fp32, KS) -> xp (packed pairs in the order lanes consume them)
-template <int WQ, int KS>
-__device__ void pack_x(const float* xs, uint32_t* xp) {
-  using Y = Lay<WQ, KS>;
-  for (int p = threadIdx.x; p < KS / 2; p += kGemvThreads) {
-    uint32_t hi, lo;
-    if (WQ) {
-      const int g = p / 16, q = p % 16, j = q / 4, i = q % 4;
-      const int k = 32 * g + 8 * j + i;  // pair (k, k + 4) matches the nibble unpack
-      split_pair(xs[k], xs[k + 4], hi, lo);
-      xp[g * Packed<WQ, KS>::kWordsW4 + q] = hi;
-      xp[g * Packed<WQ, KS>::kWordsW4 + 16 + q] = lo;
-    } else {
-      const int k = 2 * p, c = k / 512, o = k % 512, ls = o / 8, j = (o % 8) / 2;
-      split_pair(xs[k], xs[k + 1], hi, lo);
-      xp[(c * Y::S + ls) * 8 + j] = hi;
-      xp[(c * Y::S + ls) * 8 + 4 + j] = lo;
-    }
-  }
-  if (WQ) {
-    __syncthreads();
-    for (int g = threadIdx.x; g < KS / 32; g += kGemvThreads) {
-      float s = 0.f;
-      for (int q = 0; q < 16; ++q) {
-        const uint32_t hi = xp[g * Packed<WQ, KS>::kWordsW4 + q];
-        const uint32_t lo = xp[g * Packed<WQ, KS>::kWordsW4 + 16 + q];
-        s += (bf2f(hi) + bf2f(lo)) + (bf2f(hi >> 16) + bf2f(lo >> 16));
-      }
-      xp[g * Packed<WQ, KS>::kWordsW4 + 32] = __float_as_uint(s);
-    }
-  }
-  __syncthreads();
-}
-
 template <int WQ, int KS, int U, int TAG>
 __global__ __launch_bounds__(kGemvThreads) void k_gemv(Lin W, int rows, Prologue pro,
                                                        Epilogue epi) {
@@ -384,7 +185,7 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv(Lin W, int rows, Prologue
   int u0 = blockIdx.x * 4 + wave;
   Batch A, Bq;
   load_batch(A, u0);                  // then the weights (independent of x)
-  pr.finish(pro, b, K, xs, red);
+  pr.finish(pro, b, K, xs, red, blockIdx.x == 0 && blockIdx.y == 0);
   pack_x<WQ, KS>(xs, xp);
 
   // this lane's x pairs (and group sums for W4A16), read once
@@ -598,371 +399,13 @@ hipError_t launch_gemv(int quant, int tag, const Lin& W, int rows, const Prologu
 // K/V is written before attention: block per row, wave 0 the key (norm with
 // gain + RoPE), wave 1 the value (norm), bf16 at slot = position.
 // ------------------------------------------------------------ decode attention
-// Block (chunk c, row r): the keys j0..j1-1 of chunk c of the row's window,
-// all query heads against the single K/V head.  The block normalises and
-// rotates the row's queries itself (q_norm with gain, rotate-half RoPE at the
-// logical position).  With own_kv (decode: every row is its own sequence) the
-// block whose chunk holds the row's position also norms, rotates and stores
-// that position's key and value (bf16) before attending, so no separate pass
-// is needed; for prefill the cache is written by k_kv_write first.
-// Lanes own hd/64 consecutive dims; each wave takes groups of 4 keys, reduces
-// the 32 (key, head) dot products with a transposing butterfly (31 shuffles),
-// and keeps an online softmax (max, sum, o) per head.  The 4 waves merge in
-// LDS and write one (max, sum, o) partial per (row, head, chunk).
-constexpr int kMaxHeads = 8;
-
-// One butterfly step of a transposing reduction: lanes whose bit `o` is set
-// keep the upper half of their values, the others the lower half; each adds
-// its partner's copy of the half it keeps.
-template <int H>
-__device__ __forceinline__ void tr_step(float* cur, int lane, int o) {
-  const bool upper = (lane & o) != 0;
-#pragma unroll
-  for (int i = 0; i < H; ++i) {
-    const float send = upper ? cur[i] : cur[i + H];
-    const float keep = upper ? cur[i + H] : cur[i];
-    cur[i] = keep + __shfl_xor(send, o, 64);
-  }
-}
-
-// 32 values per lane -> lane l ends with the full 64-lane sum of value l >> 1
-__device__ __forceinline__ float transpose_reduce32(float (&v)[32], int lane) {
-  tr_step<16>(v, lane, 32);
-  tr_step<8>(v, lane, 16);
-  tr_step<4>(v, lane, 8);
-  tr_step<2>(v, lane, 4);
-  tr_step<1>(v, lane, 2);
-  return v[0] + __shfl_xor(v[0], 1, 64);
-}
-
-template <int DPL>
-__device__ __forceinline__ void load_row(const uint16_t* p, float (&out)[DPL]) {
-  if constexpr (DPL == 8) {
-    const uint4 v = *reinterpret_cast<const uint4*>(p);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) { out[2 * i] = bf2f(w[i]); out[2 * i + 1] = bf2f(w[i] >> 16); }
-  } else if constexpr (DPL == 4) {
-    const uint2 v = *reinterpret_cast<const uint2*>(p);
-    out[0] = bf2f(v.x); out[1] = bf2f(v.x >> 16); out[2] = bf2f(v.y); out[3] = bf2f(v.y >> 16);
-  } else if constexpr (DPL == 2) {
-    const uint32_t v = *reinterpret_cast<const uint32_t*>(p);
-    out[0] = bf2f(v); out[1] = bf2f(v >> 16);
-  } else {
-    out[0] = bf2f(*p);
-  }
-}
-
-// One head vector of a row: RMS norm over hd (gain optional), then (rope)
-// rotate-half RoPE with the position's angles cs/sn [hd/2].  Lane l holds dims
-// l*DPL .. l*DPL+DPL-1; the rotation partner of dim d < hd/2 is d + hd/2, held
-// by lane l ^ 32.  Used for queries, and for the keys and values written to
-// the cache, by both the decode and the prefill path (identical arithmetic).
-template <int HD>
-__device__ __forceinline__ void head_vec(const float* raw, int nparts, size_t pstride,
-                                         const uint16_t* gain, bool rope, const float* cs,
-                                         const float* sn, int lane, float eps,
-                                         float (&y)[HD / 64]) {
-  constexpr int DPL = HD / 64;
-  float ss = 0.f;
-#pragma unroll
-  for (int i = 0; i < DPL; ++i) {
-    y[i] = raw[lane * DPL + i];
-    for (int q = 1; q < nparts; ++q) y[i] += raw[(size_t)q * pstride + lane * DPL + i];
-    ss += y[i] * y[i];
-  }
-  const float rr = rsqrtf(wave_sum(ss) / (float)HD + eps);
-#pragma unroll
-  for (int i = 0; i < DPL; ++i) y[i] = y[i] * rr * (gain ? bf2f(gain[lane * DPL + i]) : 1.0f);
-  if (rope) {
-#pragma unroll
-    for (int i = 0; i < DPL; ++i) {
-      const float other = __shfl_xor(y[i], 32, 64);
-      const int ii = (lane & 31) * DPL + i;
-      y[i] = lane < 32 ? y[i] * cs[ii] - other * sn[ii] : other * sn[ii] + y[i] * cs[ii];
-    }
-  }
-}
-
-// One wave's K/V rows for a group of 4 keys, kept packed (bf16) until used.
-template <int DPL>
-struct KvGroup {
-  static constexpr int W = DPL >= 2 ? DPL / 2 : 1;  // 32-bit words per lane per row
-  uint32_t k[4][W], v[4][W];
-};
-
-template <int DPL>
-__device__ __forceinline__ void load_packed(const uint16_t* p, uint32_t (&w)[KvGroup<DPL>::W]) {
-  if constexpr (DPL == 8) {
-    const uint4 u = *reinterpret_cast<const uint4*>(p);
-    w[0] = u.x; w[1] = u.y; w[2] = u.z; w[3] = u.w;
-  } else if constexpr (DPL == 4) {
-    const uint2 u = *reinterpret_cast<const uint2*>(p);
-    w[0] = u.x; w[1] = u.y;
-  } else if constexpr (DPL == 2) {
-    w[0] = *reinterpret_cast<const uint32_t*>(p);
-  } else {
-    w[0] = *p;
-  }
-}
-
-template <int DPL>
-__device__ __forceinline__ void unpack(const uint32_t (&w)[KvGroup<DPL>::W], float (&out)[DPL]) {
-  if constexpr (DPL == 1) {
-    out[0] = bf2f(w[0]);
-  } else {
-#pragma unroll
-    for (int i = 0; i < DPL / 2; ++i) { out[2 * i] = bf2f(w[i]); out[2 * i + 1] = bf2f(w[i] >> 16); }
-  }
-}
-
-// Block (chunk c, row r): the keys j0..j1-1 of chunk c of the row's window,
-// all query heads against the single K/V head; 4 waves take groups of 4 keys,
-// the next group's K/V rows loaded while the current one is used.  Queries
-// are normed and rotated in the block (angles from the per-row table).  With
-// own K/V (decode, the layer computes K/V) the block holding the position
-// norms, rotates and stores that position's key and value (bf16) and uses
-// them from LDS.  Every block writes a (max, sum, o) partial per head;
-// k_attn_combine merges them.  (Merging in the row's last block instead needs
-// a device-scope fence per block, which writes back the L2 and costs more
-// than the extra launch.)
 template <int HD>
 __global__ __launch_bounds__(256) void k_attn_dec(Rows R, AttnArgs a) {
-  constexpr int DPL = HD / 64;
-  constexpr int NH = kMaxHeads;
-  using G = KvGroup<DPL>;
-  __shared__ float qs[NH * HD];
-  __shared__ float kv_own[2][HD];
-  __shared__ float pw[4][32];
-  __shared__ float cw[4][NH];
-  __shared__ float wm[4][NH], wl[4][NH];
-  const int c = blockIdx.x, r = blockIdx.y, t = threadIdx.x;
-  const int lane = t & 63, wave = t >> 6, nq = a.nq;
-  const int pos = clamp_pos(R, row_pos(R, r));
-  const int seq = row_seq(R, r);
-  const int lo = a.window ? max(0, pos - a.window + 1) : 0;
-  const int j0 = lo + c * a.chunk;
-  const int j1 = min(j0 + a.chunk, pos + 1);
-  const size_t hstride = (size_t)kMaxChunks * (HD + 2);
-  float* part = a.part + ((size_t)r * nq * kMaxChunks + c) * (HD + 2);
-
-  if (j0 < j1) {
-    const bool own = a.kc_own != nullptr && j1 == pos + 1;
-    const uint16_t* kb = a.kc + (size_t)seq * R.max_ctx * HD + lane * DPL;
-    const uint16_t* vb = a.vc + (size_t)seq * R.max_ctx * HD + lane * DPL;
-    const int ngroups = (j1 - j0 + 3) / 4;
-    // K/V rows of a group (the own position and keys past the chunk read as 0)
-    auto load_group = [&](int gi, G& g) {
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int key = j0 + 4 * gi + k;
-        const bool ok = gi < ngroups && key < j1 && !(own && key == pos);
-        const size_t o = ok ? (size_t)key * HD : 0;
-        load_packed<DPL>(kb + o, g.k[k]);
-        load_packed<DPL>(vb + o, g.v[k]);
-        if (!ok)
-#pragma unroll
-          for (int i = 0; i < G::W; ++i) g.k[k][i] = g.v[k][i] = 0u;
-      }
-    };
-    G cur;
-    load_group(wave, cur);  // issued before the query work: independent of it
-
-    const int nraw = nq + (a.owns ? 2 : 0);
-    const float* raw = a.qkv + (size_t)r * nraw * HD;
-    const float* cs = a.rope + (size_t)r * a.rope_ld + a.rope_off;
-    const float* sn = cs + HD / 2;
-    for (int h = wave; h < nq; h += 4) {
-      float y[DPL];
-      head_vec<HD>(raw + h * HD, a.qkv_parts, a.qkv_pstride, a.gq, true, cs, sn, lane, a.eps, y);
-#pragma unroll
-      for (int i = 0; i < DPL; ++i) qs[h * HD + lane * DPL + i] = y[i];
-    }
-    if (own && wave < 2) {
-      const bool is_v = wave == 1;
-      float y[DPL];
-      head_vec<HD>(raw + (nq + wave) * HD, a.qkv_parts, a.qkv_pstride, is_v ? nullptr : a.gk,
-                   !is_v, cs, sn, lane, a.eps, y);
-      uint16_t* dst = (is_v ? a.vc_own : a.kc_own) + ((size_t)seq * R.max_ctx + pos) * HD;
-#pragma unroll
-      for (int i = 0; i < DPL; ++i) {
-        const uint32_t b = f2bf(y[i]);
-        dst[lane * DPL + i] = (uint16_t)b;
-        kv_own[wave][lane * DPL + i] = bf2f(b);
-      }
-    }
-    __syncthreads();
-
-    // this lane's query dims for every head
-    float qr[NH][DPL];
-#pragma unroll
-    for (int h = 0; h < NH; ++h)
-#pragma unroll
-      for (int i = 0; i < DPL; ++i) qr[h][i] = h < nq ? qs[h * HD + lane * DPL + i] : 0.f;
-
-    const float scale = rsqrtf((float)HD);
-    const int myh = (lane >> 1) & 7, myk = lane >> 4;  // value index lane>>1 = k*8 + h
-    float m_run = -INFINITY, l_run = 0.f;
-    float o[NH][DPL];
-#pragma unroll
-    for (int h = 0; h < NH; ++h)
-#pragma unroll
-      for (int i = 0; i < DPL; ++i) o[h][i] = 0.f;
-
-    for (int gi = wave; gi < ngroups; gi += 4) {
-      G nxt;
-      if constexpr (DPL < 8) load_group(gi + 4, nxt);  // hd 512: registers too tight
-      const int key0 = j0 + 4 * gi;
-      // key / value row k of the group as fp32 (unpacked when used)
-      auto row_of = [&](int k, int which, float (&x)[DPL]) {
-        if (own && key0 + k == pos) {
-#pragma unroll
-          for (int i = 0; i < DPL; ++i) x[i] = kv_own[which][lane * DPL + i];
-        } else {
-          unpack<DPL>(which ? cur.v[k] : cur.k[k], x);
-        }
-      };
-      float part32[32];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        float kr[DPL];
-        row_of(k, 0, kr);
-#pragma unroll
-        for (int h = 0; h < NH; ++h) {
-          float d = 0.f;
-#pragma unroll
-          for (int i = 0; i < DPL; ++i) d += qr[h][i] * kr[i];
-          part32[k * NH + h] = d;
-        }
-      }
-      float sc_ = transpose_reduce32(part32, lane) * scale;
-      if (key0 + myk >= j1 || myh >= nq) sc_ = -INFINITY;
-      float mx = fmaxf(sc_, __shfl_xor(sc_, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run, mx);
-      const float pr = (m_new == -INFINITY || sc_ == -INFINITY) ? 0.f : expf(sc_ - m_new);
-      const float corr = (m_new == -INFINITY || m_run == -INFINITY)
-                             ? (m_run == -INFINITY ? 0.f : 1.f)
-                             : expf(m_run - m_new);
-      float ps = pr + __shfl_xor(pr, 16, 64);
-      ps += __shfl_xor(ps, 32, 64);
-      l_run = l_run * corr + ps;
-      m_run = m_new;
-      if ((lane & 1) == 0) pw[wave][lane >> 1] = pr;
-      if (lane < 16 && (lane & 1) == 0) cw[wave][lane >> 1] = corr;
-      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-#pragma unroll
-      for (int h = 0; h < NH; ++h) {
-        const float cf = cw[wave][h];
-#pragma unroll
-        for (int i = 0; i < DPL; ++i) o[h][i] *= cf;
-      }
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        float vr[DPL];
-        row_of(k, 1, vr);
-#pragma unroll
-        for (int h = 0; h < NH; ++h) {
-          const float pk = pw[wave][k * NH + h];
-#pragma unroll
-          for (int i = 0; i < DPL; ++i) o[h][i] += pk * vr[i];
-        }
-      }
-      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      if constexpr (DPL < 8) cur = nxt;
-      else if (gi + 4 < ngroups) load_group(gi + 4, cur);
-    }
-    // merge the four waves: per head max M, then rescale and sum
-    if (lane < 16 && (lane & 1) == 0) {
-      wm[wave][lane >> 1] = m_run;
-      wl[wave][lane >> 1] = l_run;
-    }
-    __syncthreads();
-    float* acc = qs;  // reuse: [NH][HD]
-    for (int w = 0; w < 4; ++w) {
-      if (wave == w) {
-#pragma unroll
-        for (int h = 0; h < NH; ++h) {
-          float M = wm[0][h];
-          for (int x = 1; x < 4; ++x) M = fmaxf(M, wm[x][h]);
-          const float f = (wm[w][h] == -INFINITY) ? 0.f : expf(wm[w][h] - M);
-#pragma unroll
-          for (int i = 0; i < DPL; ++i) {
-            const float v = o[h][i] * f;
-            acc[h * HD + lane * DPL + i] = (w == 0) ? v : acc[h * HD + lane * DPL + i] + v;
-          }
-        }
-      }
-      __syncthreads();
-    }
-    for (int idx = t; idx < nq * HD; idx += 256) {
-      const int h = idx / HD, d = idx % HD;
-      part[h * hstride + d] = acc[idx];
-    }
-    if (t < nq) {
-      float M = wm[0][t];
-      for (int x = 1; x < 4; ++x) M = fmaxf(M, wm[x][t]);
-      float L = 0.f;
-      for (int x = 0; x < 4; ++x)
-        if (wm[x][t] != -INFINITY) L += wl[x][t] * expf(wm[x][t] - M);
-      part[t * hstride + HD] = M;
-      part[t * hstride + HD + 1] = L;
-    }
-  } else if (t < nq) {  // no keys in this chunk
-    part[t * hstride + HD] = -INFINITY;
-    part[t * hstride + HD + 1] = 0.f;
-  }
-
+  attn_chunk<HD, false>(R, a, blockIdx.x, blockIdx.y);
 }
 
-// out[r][h*hd + d] = sum_c e^(m_c - M) o_c[d] / sum_c e^(m_c - M) l_c over the
-// chunks holding keys.  Those are a prefix of the chunk list (keys are split in
-// order); empty chunks leave o unwritten, so they are never read.
 __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a) {
-  __shared__ float wn[kMaxChunks];
-  __shared__ float sh[8];
-  __shared__ int na[4];
-  const int r = blockIdx.x, h = blockIdx.y, hd = a.hd, t = threadIdx.x;
-  const size_t hstride = (size_t)kMaxChunks * (hd + 2);
-  const float* part = a.part + ((size_t)r * a.nq + h) * hstride;
-  float mc = -INFINITY, lc = 0.f;
-  if (t < a.nchunk) {
-    mc = part[(size_t)t * (hd + 2) + hd];
-    lc = part[(size_t)t * (hd + 2) + hd + 1];
-  }
-  const bool act = lc > 0.f;
-  float M = act ? mc : -INFINITY;
-  int nact = act ? t + 1 : 0;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    M = fmaxf(M, __shfl_xor(M, o, 64));
-    nact = max(nact, __shfl_xor(nact, o, 64));
-  }
-  if ((t & 63) == 0) {
-    sh[t >> 6] = M;
-    na[t >> 6] = nact;
-  }
-  __syncthreads();
-  M = fmaxf(fmaxf(sh[0], sh[1]), fmaxf(sh[2], sh[3]));
-  nact = max(max(na[0], na[1]), max(na[2], na[3]));
-  const float w = act ? expf(mc - M) : 0.f;
-  const float L = block_sum<256>(w * lc, sh + 4);
-  if (t < kMaxChunks) wn[t] = w / L;
-  __syncthreads();
-  for (int d = t; d < hd; d += 256) {
-    float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
-    int cc = 0;
-    for (; cc + 4 <= nact; cc += 4) {
-      o0 += wn[cc] * part[(size_t)cc * (hd + 2) + d];
-      o1 += wn[cc + 1] * part[(size_t)(cc + 1) * (hd + 2) + d];
-      o2 += wn[cc + 2] * part[(size_t)(cc + 2) * (hd + 2) + d];
-      o3 += wn[cc + 3] * part[(size_t)(cc + 3) * (hd + 2) + d];
-    }
-    for (; cc < nact; ++cc) o0 += wn[cc] * part[(size_t)cc * (hd + 2) + d];
-    a.out[(size_t)r * a.nq * hd + (size_t)h * hd + d] = (o0 + o1) + (o2 + o3);
-  }
+  attn_combine<false>(a, blockIdx.x, blockIdx.y);
 }
 
 // Prefill: K/V of every row written before attention.  Block per row, wave 0
