@@ -325,7 +325,7 @@ Ws ws_layout(const e2b_model* m, int R) {
 
 void attn_chunks(const e2b_model* m, bool full, int* chunk, int* nchunk) {
   const int span = full ? m->max_ctx : std::min(m->c.sliding_window, m->max_ctx);
-  int n = (span + 31) / 32;
+  int n = (span + 31) / 32;  // 32-key chunks (64 or 128 measured no better)
   if (n > e2b::kMaxChunks) n = e2b::kMaxChunks;
   if (n < 1) n = 1;
   *nchunk = n;

@@ -19,6 +19,7 @@
 #include <hip/hip_ext.h>
 
 #include <float.h>
+#include <stdlib.h>
 #include <type_traits>
 #include <math.h>
 
@@ -902,7 +903,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm(Lin W, int rows, GemmA A, int K
 // Enough blocks to cover the chip: narrower column tiles first, then (where
 // the consumer sums partials) K slices of >= 256.
 GemmPlan gemm_plan(int quant, int N, int K, bool partial_ok) {
-  constexpr int kTarget = 256;
+  constexpr int kTarget = 256;  // 512 / 1024 blocks, or 128-column minimum tiles: no better
   GemmPlan p;
   p.nt = quant ? 4 : 2;
   const int nt_min = quant ? 2 : 1;
