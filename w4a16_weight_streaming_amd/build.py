@@ -16,6 +16,9 @@ HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # keep the compiler from forming packed fp32 ops (v_pk_*_f32)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # fuse only the multiply-adds the source writes out (fmaf): the same
+    # expression then rounds the same way in every kernel it is inlined into
+    "-ffp-contract=off",
     "-I" + os.path.join(ROOT, "include"), "-I" + CSRC,
 ]
 

@@ -67,7 +67,8 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
 
 __device__ __forceinline__ float gelu_tanh(float x) {
   const float c = 0.7978845608028654f;  // sqrt(2/pi)
-  return 0.5f * x * (1.0f + tanhf(c * (x + 0.044715f * x * x * x)));
+  // (fused multiply-adds written out: the same rounding wherever it is inlined)
+  return 0.5f * x * (1.0f + tanhf(c * fmaf(0.044715f * x * x, x, x)));
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
@@ -118,41 +119,93 @@ struct Lay {
 // halves: load() issues every global read the prologue needs at once (one
 // round trip; the weight prefetch is issued after it), finish() does the
 // arithmetic and writes xs.
-template <int KS>
+// A never-written row of zeros: what an unconditional load of an absent
+// operand reads (memory written by the same kernel would not do: a plain load
+// of it can leave a stale line behind for the persistent step's coherent
+// reads).  2048 bf16 = 1024 floats, the widest row such a load covers.
+static __device__ uint16_t kZeroRow[2048];
+
+template <int KS, int PK = -1, int ND = kMaxSplitK>
 struct PrologueRegs {
   static constexpr int PT = (KS + kGemvThreads - 1) / kGemvThreads;
-  float a0[PT], a1[PT], g0[PT], g1[PT];
-  float dq[PT][kMaxSplitK];
+  static constexpr int NDX = PK >= 0 ? (ND > 0 ? ND : 1) : kMaxSplitK;
+  // PK >= 0: the kind is known at compile time and every load is
+  // unconditional (absent operands read from stand-ins and are dropped by
+  // selects later).  bf16 gains and the layer scalar stay raw until finish():
+  // a conversion next to its load (which the compiler makes out of a
+  // conditional load) waits for every load in flight, one memory round trip
+  // each.
+  float a0[PT], a1[PT];
+  uint32_t g0[PT], g1[PT], sc;
+  float dq[PT][NDX];
+  int nd;
+
+  __device__ __forceinline__ int kind(const Prologue& p) const { return PK >= 0 ? PK : p.kind; }
 
   template <bool COH = false>
   __device__ __forceinline__ void load(const Prologue& p, int rows, int b, int k0, int K) {
     const int t = threadIdx.x;
 #pragma unroll
     for (int j = 0; j < PT; ++j) {
-      const int i = t + j * kGemvThreads;
-      a0[j] = a1[j] = g0[j] = g1[j] = 0.f;
+      a0[j] = a1[j] = 0.f;
+      g0[j] = g1[j] = 0u;
 #pragma unroll
-      for (int q = 0; q < kMaxSplitK; ++q) dq[j][q] = 0.f;
-      if (i >= KS) continue;
-      if (p.kind == kPlain) {
-        a0[j] = ld32<COH>(p.a + (size_t)b * p.lda + k0 + i);
-      } else if (p.kind == kGeglu) {
-        a0[j] = ld32<COH>(p.a + (size_t)b * p.lda + k0 + i);
-        a1[j] = ld32<COH>(p.a + (size_t)b * p.lda + K + k0 + i);
-      } else if (p.kind == kPleGate) {
-        a0[j] = ld32<COH>(p.a + (size_t)b * p.lda + k0 + i);
-        a1[j] = ld32<COH>(p.pli + (size_t)b * p.pli_ld + k0 + i);
-      } else {  // kRes / kResNorm: KS == K == hidden size
-        a0[j] = ld32<COH>(p.a + (size_t)b * K + i);
-        if (p.d) {
-#pragma unroll
-          for (int q = 0; q < kMaxSplitK; ++q)
-            if (q < p.nd) dq[j][q] = ld32<COH>(p.d + (size_t)q * p.d_pstride + (size_t)b * K + i);
-          g0[j] = bf2f(p.gd[i]);
-        }
-        if (p.kind == kResNorm) g1[j] = bf2f(p.gx[i]);
-      }
+      for (int q = 0; q < NDX; ++q) dq[j][q] = 0.f;
     }
+    sc = 0u;
+    nd = 0;
+    auto ok = [&](int j) { return KS % kGemvThreads == 0 || t + j * kGemvThreads < KS; };
+    const int kd = kind(p);
+    if (kd == kPlain || kd == kGeglu || kd == kPleGate) {
+      const float* s0 = p.a + (size_t)b * p.lda + k0;
+      const float* s1 = kd == kGeglu ? s0 + K
+                        : kd == kPleGate ? p.pli + (size_t)b * p.pli_ld + k0
+                                         : nullptr;
+#pragma unroll
+      for (int j = 0; j < PT; ++j)
+        if (ok(j)) a0[j] = ld32<COH>(s0 + t + j * kGemvThreads);
+      if (PK == kGeglu || PK == kPleGate || (PK < 0 && s1))
+#pragma unroll
+        for (int j = 0; j < PT; ++j)
+          if (ok(j)) a1[j] = ld32<COH>(s1 + t + j * kGemvThreads);
+      return;
+    }
+    // kRes / kResNorm: KS == K == hidden size.  Gains absent here read the
+    // zero row and are not used
+    const float* hrow = p.a + (size_t)b * K;
+    const uint16_t* stand_in = kZeroRow;
+    const uint16_t* gx = kd == kResNorm ? p.gx : stand_in;
+    const uint16_t* gd = p.d ? p.gd : stand_in;
+#pragma unroll
+    for (int j = 0; j < PT; ++j)
+      if (ok(j)) {
+        const int i = t + j * kGemvThreads;
+        a0[j] = ld32<COH>(hrow + i);
+        g1[j] = gx[i];
+        g0[j] = gd[i];
+      }
+    nd = p.d ? p.nd : 0;
+    if constexpr (PK >= 0) {
+      // partial q (or partial 0 again past nd; h itself, read coherently like
+      // the delta, when there is none)
+      const float* dp = p.d ? p.d + (size_t)b * K : hrow;
+      const size_t ps = p.d ? p.d_pstride : 0;
+#pragma unroll
+      for (int q = 0; q < NDX; ++q) {
+        const float* src = dp + (q < nd ? (size_t)q * ps : 0);
+#pragma unroll
+        for (int j = 0; j < PT; ++j)
+          if (ok(j)) dq[j][q] = ld32<COH>(src + t + j * kGemvThreads);
+      }
+    } else if (p.d) {
+#pragma unroll
+      for (int q = 0; q < NDX; ++q)
+        if (q < nd)
+#pragma unroll
+          for (int j = 0; j < PT; ++j)
+            if (ok(j)) dq[j][q] = ld32<COH>(p.d + (size_t)q * p.d_pstride + (size_t)b * K + t + j * kGemvThreads);
+    }
+    sc = *(p.scalar ? p.scalar : stand_in);  // (1 when there is no scalar)
   }
 
   // store_h: this block writes the updated residual h' (one block per
@@ -161,11 +214,12 @@ struct PrologueRegs {
   __device__ __forceinline__ void finish(const Prologue& p, int b, int K, float* xs, float* red,
                                          bool store_h) {
     const int t = threadIdx.x;
-    if (p.kind == kPlain) {
+    const int kd = kind(p);
+    if (kd == kPlain) {
 #pragma unroll
       for (int j = 0; j < PT; ++j)
         if (t + j * kGemvThreads < KS) xs[t + j * kGemvThreads] = a0[j];
-    } else if (p.kind == kGeglu || p.kind == kPleGate) {
+    } else if (kd == kGeglu || kd == kPleGate) {
 #pragma unroll
       for (int j = 0; j < PT; ++j)
         if (t + j * kGemvThreads < KS) xs[t + j * kGemvThreads] = gelu_tanh(a0[j]) * a1[j];
@@ -175,31 +229,31 @@ struct PrologueRegs {
       for (int j = 0; j < PT; ++j) {
         float s = 0.f;
 #pragma unroll
-        for (int q = 0; q < kMaxSplitK; ++q) s += dq[j][q];
+        for (int q = 0; q < NDX; ++q) s += q < nd ? dq[j][q] : 0.f;
         dv[j] = s;
-        ss += s * s;
+        ss = fmaf(s, s, ss);
       }
       float rd = 0.f;
       if (p.d) rd = rsqrtf(block_sum<kGemvThreads>(ss, red) / (float)K + p.eps);
-      const float sc = p.scalar ? bf2f(p.scalar[0]) : 1.0f;
+      const float scv = p.scalar ? bf2f(sc) : 1.0f;
       const bool store = p.d && p.h_out && store_h;
       float hv[PT], hs = 0.f;
 #pragma unroll
       for (int j = 0; j < PT; ++j) {
         const int i = t + j * kGemvThreads;
         float hn = a0[j];
-        if (p.d) hn = (hn + dv[j] * rd * g0[j]) * sc;
+        if (p.d) hn = fmaf(dv[j] * rd, bf2f(g0[j]), hn) * scv;
         hv[j] = hn;
         if (i < KS) {
-          hs += hn * hn;
+          hs = fmaf(hn, hn, hs);
           if (store) st32<COH>(p.h_out + (size_t)b * K + i, hn);
         }
       }
-      if (p.kind == kResNorm) {
+      if (kd == kResNorm) {
         const float rh = rsqrtf(block_sum<kGemvThreads>(hs, red) / (float)K + p.eps);
 #pragma unroll
         for (int j = 0; j < PT; ++j)
-          if (t + j * kGemvThreads < KS) xs[t + j * kGemvThreads] = hv[j] * rh * g1[j];
+          if (t + j * kGemvThreads < KS) xs[t + j * kGemvThreads] = hv[j] * rh * bf2f(g1[j]);
       } else {
 #pragma unroll
         for (int j = 0; j < PT; ++j)
@@ -311,31 +365,94 @@ __device__ __forceinline__ void load_row(const uint16_t* p, float (&out)[DPL]) {
 // l*DPL .. l*DPL+DPL-1; the rotation partner of dim d < hd/2 is d + hd/2, held
 // by lane l ^ 32.  Used for queries, and for the keys and values written to
 // the cache, by both the decode and the prefill path (identical arithmetic).
+// Split in two so that a wave issues the reads of all its heads (and the gains
+// and angles) before it waits for any: head_raw sums the K-slice partials of
+// the projection, head_side reads gain and angles, head_finish does the rest.
+template <int HD, bool COH = false>
+__device__ __forceinline__ void head_raw(const float* raw, int nparts, size_t pstride, int lane,
+                                         float (&y)[HD / 64]) {
+  constexpr int DPL = HD / 64;
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) y[i] = ld32<COH>(raw + lane * DPL + i);
+  for (int q0 = 1; q0 < nparts; q0 += 4) {  // further partials, 4 in flight
+    float v[4][DPL];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float* src = raw + (size_t)(q0 + k < nparts ? q0 + k : 0) * pstride;
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) v[k][i] = ld32<COH>(src + lane * DPL + i);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) y[i] += q0 + k < nparts ? v[k][i] : 0.f;
+  }
+}
+
+template <int HD>
+struct HeadSide {
+  static constexpr int DPL = HD / 64;
+  static constexpr int GW = DPL >= 2 ? DPL / 2 : 1;
+  uint32_t g[GW];  // gain, raw bf16 pairs (split when used)
+  float c[DPL], s[DPL];
+  __device__ __forceinline__ float gain(int i) const {
+    return DPL == 1 ? bf2f(g[0]) : bf2f((i & 1) ? g[i / 2] >> 16 : g[i / 2]);
+  }
+};
+
+// gain: may be null (values: no gain); cs/sn: null when there is no rotation.
+// Absent operands read the zero row and are not used.
+template <int HD, bool COH = false>
+__device__ __forceinline__ void head_side(const uint16_t* gain, const float* cs, const float* sn,
+                                          int lane, HeadSide<HD>& hs) {
+  constexpr int DPL = HD / 64;
+  const float* zf = reinterpret_cast<const float*>(kZeroRow);
+  const uint16_t* gp = gain ? gain : kZeroRow;
+  const float* cp = cs ? cs : zf;
+  const float* sp = sn ? sn : zf;
+  if constexpr (DPL == 1) {
+    hs.g[0] = gp[lane];
+  } else {
+#pragma unroll
+    for (int w = 0; w < DPL / 2; ++w) hs.g[w] = reinterpret_cast<const uint32_t*>(gp + lane * DPL)[w];
+  }
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) {
+    const int ii = (lane & 31) * DPL + i;
+    hs.c[i] = ld32<COH>(cp + ii);
+    hs.s[i] = ld32<COH>(sp + ii);
+  }
+}
+
+template <int HD>
+__device__ __forceinline__ void head_finish(float (&y)[HD / 64], const HeadSide<HD>& hs, bool gain,
+                                            bool rope, int lane, float eps) {
+  constexpr int DPL = HD / 64;
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) ss = fmaf(y[i], y[i], ss);
+  const float rr = rsqrtf(wave_sum(ss) / (float)HD + eps);
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) y[i] = y[i] * rr * (gain ? hs.gain(i) : 1.0f);
+  if (rope) {
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) {
+      const float other = __shfl_xor(y[i], 32, 64);
+      const float os = other * hs.s[i];
+      y[i] = fmaf(y[i], hs.c[i], lane < 32 ? -os : os);
+    }
+  }
+}
+
 template <int HD, bool COH = false>
 __device__ __forceinline__ void head_vec(const float* raw, int nparts, size_t pstride,
                                          const uint16_t* gain, bool rope, const float* cs,
                                          const float* sn, int lane, float eps,
                                          float (&y)[HD / 64]) {
-  constexpr int DPL = HD / 64;
-  float ss = 0.f;
-#pragma unroll
-  for (int i = 0; i < DPL; ++i) {
-    y[i] = ld32<COH>(raw + lane * DPL + i);
-    for (int q = 1; q < nparts; ++q) y[i] += ld32<COH>(raw + (size_t)q * pstride + lane * DPL + i);
-    ss += y[i] * y[i];
-  }
-  const float rr = rsqrtf(wave_sum(ss) / (float)HD + eps);
-#pragma unroll
-  for (int i = 0; i < DPL; ++i) y[i] = y[i] * rr * (gain ? bf2f(gain[lane * DPL + i]) : 1.0f);
-  if (rope) {
-#pragma unroll
-    for (int i = 0; i < DPL; ++i) {
-      const float other = __shfl_xor(y[i], 32, 64);
-      const int ii = (lane & 31) * DPL + i;
-      const float c_ = ld32<COH>(cs + ii), s_ = ld32<COH>(sn + ii);
-      y[i] = lane < 32 ? y[i] * c_ - other * s_ : other * s_ + y[i] * c_;
-    }
-  }
+  HeadSide<HD> hs;
+  head_side<HD, COH>(gain, rope ? cs : nullptr, rope ? sn : nullptr, lane, hs);
+  head_raw<HD, COH>(raw, nparts, pstride, lane, y);
+  head_finish<HD>(y, hs, gain != nullptr, rope, lane, eps);
 }
 
 // One wave's K/V rows for a group of 4 keys, kept packed (bf16) until used.
@@ -416,31 +533,32 @@ __device__ void attn_chunk(const Rows& R, const AttnArgs& a, int c, int r) {
     const uint16_t* kb = a.kc + (size_t)seq * R.max_ctx * HD + lane * DPL;
     const uint16_t* vb = a.vc + (size_t)seq * R.max_ctx * HD + lane * DPL;
     const int ngroups = (j1 - j0 + 3) / 4;
-    // K/V rows of a group (the own position and keys past the chunk read as 0)
+    // K/V rows of a group.  Keys past the chunk, and the own position (which
+    // this block writes), read the zero row instead (loads are unconditional:
+    // a select right after a load would wait for it); row_of takes the own
+    // position from the block's own K/V
     auto load_group = [&](int gi, G& g) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const int key = j0 + 4 * gi + k;
         const bool ok = gi < ngroups && key < j1 && !(own && key == pos);
-        const size_t o = ok ? (size_t)key * HD : 0;
+        const uint16_t* kr = ok ? kb + (size_t)key * HD : kZeroRow + lane * DPL;
+        const uint16_t* vr = ok ? vb + (size_t)key * HD : kZeroRow + lane * DPL;
         if (COH && ok && key == pos) {  // written earlier in this kernel by the source layer
 #pragma unroll
           for (int i = 0; i < G::W; ++i) {
             if constexpr (DPL == 1) {
-              g.k[k][i] = ldu16<true>(kb + o);
-              g.v[k][i] = ldu16<true>(vb + o);
+              g.k[k][i] = ldu16<true>(kr);
+              g.v[k][i] = ldu16<true>(vr);
             } else {
-              g.k[k][i] = ldu32<true>(reinterpret_cast<const uint32_t*>(kb + o) + i);
-              g.v[k][i] = ldu32<true>(reinterpret_cast<const uint32_t*>(vb + o) + i);
+              g.k[k][i] = ldu32<true>(reinterpret_cast<const uint32_t*>(kr) + i);
+              g.v[k][i] = ldu32<true>(reinterpret_cast<const uint32_t*>(vr) + i);
             }
           }
         } else {
-          load_packed<DPL>(kb + o, g.k[k]);
-          load_packed<DPL>(vb + o, g.v[k]);
+          load_packed<DPL>(kr, g.k[k]);
+          load_packed<DPL>(vr, g.v[k]);
         }
-        if (!ok)
-#pragma unroll
-          for (int i = 0; i < G::W; ++i) g.k[k][i] = g.v[k][i] = 0u;
       }
     };
     G cur;
@@ -450,21 +568,37 @@ __device__ void attn_chunk(const Rows& R, const AttnArgs& a, int c, int r) {
     const float* raw = a.qkv + (size_t)r * nraw * HD;
     const float* cs = a.rope + (size_t)r * a.rope_ld + a.rope_off;
     const float* sn = cs + HD / 2;
-    for (int h = wave; h < nq; h += 4) {
-      float y[DPL];
-      head_vec<HD, COH>(raw + h * HD, a.qkv_parts, a.qkv_pstride, a.gq, true, cs, sn, lane, a.eps, y);
+    // reads first (every head of this wave, its own K/V, gains, angles), then
+    // the arithmetic: one round trip instead of one per head
+    constexpr int HW = (kMaxHeads + 3) / 4;  // query heads per wave
+    const bool own_kv = own && wave < 2;
+    // (all unconditional: heads past nq and K/V rows a block does not own read
+    // head 0 and are not used)
+    HeadSide<HD> sq, sk;
+    head_side<HD, COH>(a.gq, cs, sn, lane, sq);
+    head_side<HD, COH>(own_kv && wave == 0 ? a.gk : nullptr, cs, sn, lane, sk);
+    float yq[HW][DPL], yk[DPL];
 #pragma unroll
-      for (int i = 0; i < DPL; ++i) qs[h * HD + lane * DPL + i] = y[i];
+    for (int x = 0; x < HW; ++x)
+      head_raw<HD, COH>(raw + (wave + 4 * x < nq ? wave + 4 * x : 0) * HD, a.qkv_parts, a.qkv_pstride,
+                        lane, yq[x]);
+    head_raw<HD, COH>(raw + (own_kv ? nq + wave : 0) * HD, a.qkv_parts, a.qkv_pstride, lane, yk);
+#pragma unroll
+    for (int x = 0; x < HW; ++x) {
+      const int h = wave + 4 * x;
+      if (h < nq) {
+        head_finish<HD>(yq[x], sq, a.gq != nullptr, true, lane, a.eps);
+#pragma unroll
+        for (int i = 0; i < DPL; ++i) qs[h * HD + lane * DPL + i] = yq[x][i];
+      }
     }
-    if (own && wave < 2) {
+    if (own_kv) {
       const bool is_v = wave == 1;
-      float y[DPL];
-      head_vec<HD, COH>(raw + (nq + wave) * HD, a.qkv_parts, a.qkv_pstride, is_v ? nullptr : a.gk,
-                   !is_v, cs, sn, lane, a.eps, y);
+      head_finish<HD>(yk, sk, !is_v && a.gk != nullptr, !is_v, lane, a.eps);
       uint16_t* dst = (is_v ? a.vc_own : a.kc_own) + ((size_t)seq * R.max_ctx + pos) * HD;
 #pragma unroll
       for (int i = 0; i < DPL; ++i) {
-        const uint32_t b = f2bf(y[i]);
+        const uint32_t b = f2bf(yk[i]);
         st16<COH>(dst + lane * DPL + i, (uint16_t)b);
         kv_own[wave][lane * DPL + i] = bf2f(b);
       }
@@ -509,7 +643,7 @@ __device__ void attn_chunk(const Rows& R, const AttnArgs& a, int c, int r) {
         for (int h = 0; h < NH; ++h) {
           float d = 0.f;
 #pragma unroll
-          for (int i = 0; i < DPL; ++i) d += qr[h][i] * kr[i];
+          for (int i = 0; i < DPL; ++i) d = fmaf(qr[h][i], kr[i], d);
           part32[k * NH + h] = d;
         }
       }
@@ -524,7 +658,7 @@ __device__ void attn_chunk(const Rows& R, const AttnArgs& a, int c, int r) {
                              : expf(m_run - m_new);
       float ps = pr + __shfl_xor(pr, 16, 64);
       ps += __shfl_xor(ps, 32, 64);
-      l_run = l_run * corr + ps;
+      l_run = fmaf(l_run, corr, ps);
       m_run = m_new;
       if ((lane & 1) == 0) pw[wave][lane >> 1] = pr;
       if (lane < 16 && (lane & 1) == 0) cw[wave][lane >> 1] = corr;
@@ -544,7 +678,7 @@ __device__ void attn_chunk(const Rows& R, const AttnArgs& a, int c, int r) {
         for (int h = 0; h < NH; ++h) {
           const float pk = pw[wave][k * NH + h];
 #pragma unroll
-          for (int i = 0; i < DPL; ++i) o[h][i] += pk * vr[i];
+          for (int i = 0; i < DPL; ++i) o[h][i] = fmaf(pk, vr[i], o[h][i]);
         }
       }
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
@@ -568,8 +702,8 @@ __device__ void attn_chunk(const Rows& R, const AttnArgs& a, int c, int r) {
           const float f = (wm[w][h] == -INFINITY) ? 0.f : expf(wm[w][h] - M);
 #pragma unroll
           for (int i = 0; i < DPL; ++i) {
-            const float v = o[h][i] * f;
-            acc[h * HD + lane * DPL + i] = (w == 0) ? v : acc[h * HD + lane * DPL + i] + v;
+            float& a_ = acc[h * HD + lane * DPL + i];
+            a_ = (w == 0) ? o[h][i] * f : fmaf(o[h][i], f, a_);
           }
         }
       }
@@ -584,7 +718,7 @@ __device__ void attn_chunk(const Rows& R, const AttnArgs& a, int c, int r) {
       for (int x = 1; x < 4; ++x) M = fmaxf(M, wm[x][t]);
       float L = 0.f;
       for (int x = 0; x < 4; ++x)
-        if (wm[x][t] != -INFINITY) L += wl[x][t] * expf(wm[x][t] - M);
+        if (wm[x][t] != -INFINITY) L = fmaf(wl[x][t], expf(wm[x][t] - M), L);
       st32<COH>(part + t * hstride + HD, M);
       st32<COH>(part + t * hstride + HD + 1, L);
     }
@@ -605,6 +739,18 @@ __device__ void attn_combine(const AttnArgs& a, int r, int h) {
   const int hd = a.hd, t = threadIdx.x;
   const size_t hstride = (size_t)kMaxChunks * (hd + 2);
   const float* part = a.part + ((size_t)r * a.nq + h) * hstride;
+  // the o values of the first kPre chunks are read together with (m, l), before
+  // the weights are known (slots past the last written chunk hold stale
+  // values: dropped by a select, never multiplied)
+  constexpr int kPre = 16, kDt = 2;  // hd <= 512 = kDt * 256
+  float pv[kDt][kPre];
+#pragma unroll
+  for (int it = 0; it < kDt; ++it) {
+    const int d = t + 256 * it < hd ? t + 256 * it : 0;
+#pragma unroll
+    for (int c = 0; c < kPre; ++c)
+      pv[it][c] = ld32<COH>(part + (size_t)(c < a.nchunk ? c : 0) * (hd + 2) + d);
+  }
   float mc = -INFINITY, lc = 0.f;
   if (t < a.nchunk) {
     mc = ld32<COH>(part + (size_t)t * (hd + 2) + hd);
@@ -629,16 +775,27 @@ __device__ void attn_combine(const AttnArgs& a, int r, int h) {
   const float L = block_sum<256>(w * lc, sh + 4);
   if (t < kMaxChunks) wn[t] = w / L;
   __syncthreads();
-  for (int d = t; d < hd; d += 256) {
+#pragma unroll
+  for (int it = 0; it < kDt; ++it) {
+    const int d = t + 256 * it;
+    if (d >= hd) break;
     float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
-    int cc = 0;
-    for (; cc + 4 <= nact; cc += 4) {
-      o0 += wn[cc] * ld32<COH>(part + (size_t)cc * (hd + 2) + d);
-      o1 += wn[cc + 1] * ld32<COH>(part + (size_t)(cc + 1) * (hd + 2) + d);
-      o2 += wn[cc + 2] * ld32<COH>(part + (size_t)(cc + 2) * (hd + 2) + d);
-      o3 += wn[cc + 3] * ld32<COH>(part + (size_t)(cc + 3) * (hd + 2) + d);
+#pragma unroll
+    // (explicit fma: the same rounding in every instantiation)
+    for (int c = 0; c < kPre; c += 4) {
+      o0 = c < nact ? fmaf(wn[c], pv[it][c], o0) : o0;
+      o1 = c + 1 < nact ? fmaf(wn[c + 1], pv[it][c + 1], o1) : o1;
+      o2 = c + 2 < nact ? fmaf(wn[c + 2], pv[it][c + 2], o2) : o2;
+      o3 = c + 3 < nact ? fmaf(wn[c + 3], pv[it][c + 3], o3) : o3;
     }
-    for (; cc < nact; ++cc) o0 += wn[cc] * ld32<COH>(part + (size_t)cc * (hd + 2) + d);
+    int cc = kPre;
+    for (; cc + 4 <= nact; cc += 4) {
+      o0 = fmaf(wn[cc], ld32<COH>(part + (size_t)cc * (hd + 2) + d), o0);
+      o1 = fmaf(wn[cc + 1], ld32<COH>(part + (size_t)(cc + 1) * (hd + 2) + d), o1);
+      o2 = fmaf(wn[cc + 2], ld32<COH>(part + (size_t)(cc + 2) * (hd + 2) + d), o2);
+      o3 = fmaf(wn[cc + 3], ld32<COH>(part + (size_t)(cc + 3) * (hd + 2) + d), o3);
+    }
+    for (; cc < nact; ++cc) o0 = fmaf(wn[cc], ld32<COH>(part + (size_t)cc * (hd + 2) + d), o0);
     st32<COH>(a.out + (size_t)r * a.nq * hd + (size_t)h * hd + d, (o0 + o1) + (o2 + o3));
   }
 }

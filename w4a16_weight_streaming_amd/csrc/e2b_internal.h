@@ -50,6 +50,21 @@ enum PrologueKind : int {
   kPleGate = 4   // x = gelu_tanh(a[row][k]) * pli[row][k]
 };
 
+// The prologue of each product of the decode step is fixed by its kind
+// (tag): the matrix-vector kernel is specialised on it.  -1: read at run time.
+// tag_nd: most K-slice partials of the residual delta that prologue sums.
+__host__ __device__ constexpr int tag_kind(int tag) {
+  return tag == kTagQkv || tag == kTagGateUp || tag == kTagLmHead ? kResNorm
+         : tag == kTagPleGate                                   ? kRes
+         : tag == kTagO || tag == kTagPleModel                  ? kPlain
+         : tag == kTagDown                                      ? kGeglu
+         : tag == kTagPleProj                                   ? kPleGate
+                                                                : -1;
+}
+__host__ __device__ constexpr int tag_nd(int tag) {
+  return tag == kTagPleGate ? kMaxSplitK : tag == kTagQkv || tag == kTagGateUp || tag == kTagLmHead ? 2 : 0;
+}
+
 struct Prologue {
   int kind = kPlain;
   const float* a = nullptr;   // kPlain: x [rows, lda]; kRes*: h [rows, K]; kGeglu: [rows, 2K]; kPleGate: [rows, K]

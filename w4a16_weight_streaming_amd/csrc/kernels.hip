@@ -153,35 +153,32 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv(Lin W, int rows, Prologue
   // buffered: batch i+1 is requested before batch i is reduced.
   struct Batch {
     uint4 wv[U][Y::C];
-    float sc[U][Y::C];
+    uint32_t sc[U][Y::C];  // W4A16 scales, raw bf16 (converted when used)
     int n[U];
   };
+  // every load is unconditional (units past the end read row 0 and are never
+  // stored), so no value is touched before the batch is reduced
   auto load_batch = [&](Batch& B, int u0) {
 #pragma unroll
     for (int uu = 0; uu < U; ++uu) {
       const int u = u0 + uu * stride;
       B.n[uu] = u * Y::RPL + rsub;
-      const bool ok = (u < NU) && (B.n[uu] < N);
+      const size_t row = (u < NU) && (B.n[uu] < N) ? (size_t)B.n[uu] : 0;
 #pragma unroll
       for (int c = 0; c < Y::C; ++c) {
-        B.wv[uu][c] = make_uint4(0, 0, 0, 0);
-        B.sc[uu][c] = 0.f;
-        if (ok) {
-          if (WQ) {
-            const int g = ls + Y::S * c;
-            B.wv[uu][c] = *reinterpret_cast<const uint4*>(W.q + (size_t)B.n[uu] * ldq +
-                                                          (size_t)ks * (KS / 8) + 4 * g);
-            B.sc[uu][c] = bf2f(W.s[(size_t)B.n[uu] * lds + (size_t)ks * Y::G + g]);
-          } else {
-            B.wv[uu][c] = *reinterpret_cast<const uint4*>(W.w + (size_t)B.n[uu] * K +
-                                                          (size_t)ks * KS + 512 * c + 8 * ls);
-          }
+        if (WQ) {
+          const int g = ls + Y::S * c;
+          B.wv[uu][c] = *reinterpret_cast<const uint4*>(W.q + row * ldq + (size_t)ks * (KS / 8) + 4 * g);
+          B.sc[uu][c] = W.s[row * lds + (size_t)ks * Y::G + g];
+        } else {
+          B.wv[uu][c] = *reinterpret_cast<const uint4*>(W.w + row * K + (size_t)ks * KS + 512 * c + 8 * ls);
+          B.sc[uu][c] = 0u;
         }
       }
     }
   };
 
-  PrologueRegs<KS> pr;
+  PrologueRegs<KS, tag_kind(TAG), tag_nd(TAG)> pr;
   pr.load(pro, rows, b, ks * KS, K);  // input reads first: they gate the compute
   int u0 = blockIdx.x * 4 + wave;
   Batch A, Bq;
@@ -243,7 +240,7 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv(Lin W, int rows, Prologue
             a = dot2(p3, xh[c * 16 + j * 4 + 3], a);
             a = dot2(p3, xl[c * 16 + j * 4 + 3], a);
           }
-          acc += B.sc[uu][c] * (a - 136.0f * gsum[c]);
+          acc = fmaf(bf2f(B.sc[uu][c]), fmaf(-136.0f, gsum[c], a), acc);  // (fmas written out)
         } else {
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
@@ -390,6 +387,13 @@ hipError_t launch_gemv(int quant, int tag, const Lin& W, int rows, const Prologu
     return hipErrorInvalidValue;
   if (epi.argmax && gemv_splits(W.K) != 1) return hipErrorInvalidValue;
   if (epi.argmax && quant) return hipErrorInvalidValue;  // the tied lm_head is bf16
+  // the kernel is specialised on the product's prologue (argmax: the lm_head's)
+  const int tk = epi.argmax ? kTagLmHead : tag;
+  if (tag_kind(tk) >= 0 && pro.kind != tag_kind(tk)) return hipErrorInvalidValue;
+  if ((pro.kind == kRes || pro.kind == kResNorm) && pro.d) {
+    const int ndmax = tag_kind(tk) >= 0 ? tag_nd(tk) : kMaxSplitK;
+    if (pro.nd < 1 || pro.nd > ndmax) return hipErrorInvalidValue;
+  }
   if (epi.argmax) return dispatch_gemv<0, kTagLmHead>(W, rows, pro, epi, blocks_hint, blocks_out, st);
   return quant ? dispatch_tag<1>(tag, W, rows, pro, epi, blocks_hint, blocks_out, st)
                : dispatch_tag<0>(tag, W, rows, pro, epi, blocks_hint, blocks_out, st);
@@ -800,10 +804,10 @@ __global__ __launch_bounds__(256, 2) void k_gemm(Lin W, int rows, GemmA A, int K
             d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ah, B[j], d, 0, 0, 0);
             d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Al, B[j], d, 0, 0, 0);
             const float sc = bs[buf][s][j];
-            acc[mt][j][0] += sc * (d[0] - g4.x);
-            acc[mt][j][1] += sc * (d[1] - g4.y);
-            acc[mt][j][2] += sc * (d[2] - g4.z);
-            acc[mt][j][3] += sc * (d[3] - g4.w);
+            acc[mt][j][0] = fmaf(sc, d[0] - g4.x, acc[mt][j][0]);
+            acc[mt][j][1] = fmaf(sc, d[1] - g4.y, acc[mt][j][1]);
+            acc[mt][j][2] = fmaf(sc, d[2] - g4.z, acc[mt][j][2]);
+            acc[mt][j][3] = fmaf(sc, d[3] - g4.w, acc[mt][j][3]);
           }
         } else {
 #pragma unroll

@@ -243,7 +243,7 @@ __device__ void gemv_step(const Lin& W, const Prologue& pro, const VB& v, const 
             s_ = dot2(p3, xh[c * 16 + j * 4 + 3], s_);
             s_ = dot2(p3, xl[c * 16 + j * 4 + 3], s_);
           }
-          acc += B.sc[uu][c] * (s_ - 136.0f * gsum[c]);
+          acc = fmaf(B.sc[uu][c], fmaf(-136.0f, gsum[c], s_), acc);  // as the per-phase kernel
         } else {
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
