@@ -120,10 +120,13 @@ struct Lay {
 // round trip; the weight prefetch is issued after it), finish() does the
 // arithmetic and writes xs.
 // A never-written row of zeros: what an unconditional load of an absent
-// operand reads (memory written by the same kernel would not do: a plain load
-// of it can leave a stale line behind for the persistent step's coherent
-// reads).  2048 bf16 = 1024 floats, the widest row such a load covers.
-static __device__ uint16_t kZeroRow[2048];
+// operand reads.  (Memory written by the same kernel would not do: a plain
+// load of it can leave a stale line behind for the persistent step's coherent
+// reads.  Nor would repeating a real operand's address: the compiler then
+// copies that load's register, which waits for it.)  4096 bf16 = 2048 floats,
+// the widest row such a load covers.
+static __device__ __align__(16) uint16_t kZeroRow[4096];
+__device__ __forceinline__ const float* zero_f() { return reinterpret_cast<const float*>(kZeroRow); }
 
 template <int KS, int PK = -1, int ND = kMaxSplitK>
 struct PrologueRegs {
@@ -186,13 +189,11 @@ struct PrologueRegs {
       }
     nd = p.d ? p.nd : 0;
     if constexpr (PK >= 0) {
-      // partial q (or partial 0 again past nd; h itself, read coherently like
-      // the delta, when there is none)
-      const float* dp = p.d ? p.d + (size_t)b * K : hrow;
-      const size_t ps = p.d ? p.d_pstride : 0;
+      // partial q, or the zero row past nd
+      const float* dp = p.d ? p.d + (size_t)b * K : zero_f();
 #pragma unroll
       for (int q = 0; q < NDX; ++q) {
-        const float* src = dp + (q < nd ? (size_t)q * ps : 0);
+        const float* src = q < nd ? dp + (size_t)q * p.d_pstride : zero_f();
 #pragma unroll
         for (int j = 0; j < PT; ++j)
           if (ok(j)) dq[j][q] = ld32<COH>(src + t + j * kGemvThreads);
@@ -378,7 +379,7 @@ __device__ __forceinline__ void head_raw(const float* raw, int nparts, size_t ps
     float v[4][DPL];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const float* src = raw + (size_t)(q0 + k < nparts ? q0 + k : 0) * pstride;
+      const float* src = q0 + k < nparts ? raw + (size_t)(q0 + k) * pstride : zero_f();
 #pragma unroll
       for (int i = 0; i < DPL; ++i) v[k][i] = ld32<COH>(src + lane * DPL + i);
     }
@@ -741,7 +742,8 @@ __device__ void attn_combine(const AttnArgs& a, int r, int h) {
   const float* part = a.part + ((size_t)r * a.nq + h) * hstride;
   // the o values of the first kPre chunks are read together with (m, l), before
   // the weights are known (slots past the last written chunk hold stale
-  // values: dropped by a select, never multiplied)
+  // values, and chunks past nchunk read the zero row: dropped by a select,
+  // never multiplied)
   constexpr int kPre = 16, kDt = 2;  // hd <= 512 = kDt * 256
   float pv[kDt][kPre];
 #pragma unroll
@@ -749,7 +751,7 @@ __device__ void attn_combine(const AttnArgs& a, int r, int h) {
     const int d = t + 256 * it < hd ? t + 256 * it : 0;
 #pragma unroll
     for (int c = 0; c < kPre; ++c)
-      pv[it][c] = ld32<COH>(part + (size_t)(c < a.nchunk ? c : 0) * (hd + 2) + d);
+      pv[it][c] = c < a.nchunk ? ld32<COH>(part + (size_t)c * (hd + 2) + d) : ld32<COH>(zero_f() + d);
   }
   float mc = -INFINITY, lc = 0.f;
   if (t < a.nchunk) {

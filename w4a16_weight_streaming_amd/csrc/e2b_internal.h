@@ -182,7 +182,8 @@ bool take_launch_events(hipEvent_t* start, hipEvent_t* stop);
 hipError_t launch_sum_partials(int nparts, size_t n, const float* parts, float* out,
                                hipStream_t st);
 hipError_t launch_argmax_final(int rows, int nblk, const float* cand_val,
-                               const int32_t* cand_idx, int32_t* out, hipStream_t st);
+                               const int32_t* cand_idx, int32_t* out, int32_t* adv,
+                               hipStream_t st);
 
 // ---- persistent one-row decode step (step1.hip) ---------------------------
 // One kernel per decode step of one sequence: every phase of the step runs

@@ -567,7 +567,7 @@ int run_step1(e2b_model* m, const int32_t* d_tokens, const int32_t* d_positions,
 // One pass over R.n rows: all layers, then (if head) the final norm, lm_head
 // and argmax for every row (head_row < 0) or for row head_row only.
 int run_rows(e2b_model* m, const e2b::Rows& R, bool head, int head_row, float* d_logits,
-             int32_t* d_argmax, char* ws, const Ws& W, hipStream_t st) {
+             int32_t* d_argmax, char* ws, const Ws& W, hipStream_t st, int32_t* adv_pos = nullptr) {
   using namespace e2b;
   const int n = R.n, H = m->H, P = m->P, L = m->L, LP = L * P, q = m->quant;
   const float eps = m->c.rms_eps;
@@ -770,7 +770,7 @@ int run_rows(e2b_model* m, const e2b::Rows& R, bool head, int head_row, float* d
   CK(matmul(m, E2B_QUANT_BF16, kTagLmHead, E, nh, bat, pr, ep, false, nullptr, &nblk, ws, W, st),
      "lm_head");
   if (nblk > W.ncand) return fail(E2B_EINVAL, "lm_head: %d candidate blocks", nblk);
-  CK(launch_argmax_final(nh, nblk, ep.cand_val, ep.cand_idx, d_argmax, st), "argmax");
+  CK(launch_argmax_final(nh, nblk, ep.cand_val, ep.cand_idx, d_argmax, adv_pos, st), "argmax");
   return E2B_OK;
 }
 
@@ -1029,9 +1029,15 @@ int e2b_kv_alloc(e2b_model* m, void* d_kv, size_t bytes, int max_batch, int max_
   return upload_step_plan(m);
 }
 
-int e2b_decode_step(e2b_model* m, const int32_t* d_tokens, const int32_t* d_positions, int batch,
-                    float* d_logits, int32_t* d_argmax, void* d_ws, size_t ws_bytes,
-                    void* stream) {
+}  // extern "C"
+
+namespace {
+// adv_pos (graph capture): also advance the positions, by the final argmax
+// kernel of the per-phase path (*advanced set) or not at all
+int decode_impl(e2b_model* m, const int32_t* d_tokens, const int32_t* d_positions, int batch,
+                float* d_logits, int32_t* d_argmax, void* d_ws, size_t ws_bytes, void* stream,
+                int32_t* adv_pos, bool* advanced) {
+  if (advanced) *advanced = false;
   if (!m || !d_tokens || !d_positions || !d_argmax || !d_ws)
     return fail(E2B_EINVAL, "null argument");
   if (!m->loaded) return fail(E2B_ESTATE, "weights not loaded");
@@ -1054,8 +1060,19 @@ int e2b_decode_step(e2b_model* m, const int32_t* d_tokens, const int32_t* d_posi
   R.n = batch;
   R.max_ctx = m->max_ctx;
   R.vocab = m->V;
-  return run_rows(m, R, true, -1, d_logits, d_argmax, reinterpret_cast<char*>(d_ws), W,
-                  reinterpret_cast<hipStream_t>(stream));
+  const int rc = run_rows(m, R, true, -1, d_logits, d_argmax, reinterpret_cast<char*>(d_ws), W,
+                         reinterpret_cast<hipStream_t>(stream), adv_pos);
+  if (rc == E2B_OK && advanced) *advanced = adv_pos != nullptr;
+  return rc;
+}
+}  // namespace
+
+extern "C" {
+int e2b_decode_step(e2b_model* m, const int32_t* d_tokens, const int32_t* d_positions, int batch,
+                    float* d_logits, int32_t* d_argmax, void* d_ws, size_t ws_bytes,
+                    void* stream) {
+  return decode_impl(m, d_tokens, d_positions, batch, d_logits, d_argmax, d_ws, ws_bytes, stream,
+                     nullptr, nullptr);
 }
 
 int e2b_prefill(e2b_model* m, int seq, const int32_t* d_tokens, int n_tokens, int pos0,
@@ -1190,9 +1207,10 @@ int e2b_graph_capture(e2b_model* m, const int32_t* d_tokens, int32_t* d_position
     delete g;
     return hip_fail(e, "begin capture");
   }
-  int rc = e2b_decode_step(m, d_tokens, d_positions, batch, d_logits, d_argmax, d_ws, ws_bytes,
-                           stream);
-  if (rc == E2B_OK && advance_positions) {
+  bool advanced = false;
+  int rc = decode_impl(m, d_tokens, d_positions, batch, d_logits, d_argmax, d_ws, ws_bytes, stream,
+                       advance_positions ? d_positions : nullptr, &advanced);
+  if (rc == E2B_OK && advance_positions && !advanced) {
     hipError_t ea = e2b::launch_advance(d_positions, batch, st);
     if (ea != hipSuccess) rc = hip_fail(ea, "advance positions");
   }

@@ -73,11 +73,36 @@ __global__ __launch_bounds__(256) void k_embed(Rows R, const uint16_t* __restric
     atomicExch(err + 2, pos);
     atomicExch(err + 3, r);
   }
+  // 8 values per item (H and LP are multiples of 8), the loads of up to 8
+  // items per thread issued before any store
   const uint16_t* e = E + (size_t)tok * H;
-  for (int i = threadIdx.x; i < H; i += blockDim.x) h[(size_t)r * H + i] = bf2f(e[i]) * sqrtH;
   const uint16_t* t = Eple + (size_t)tok * LP;
-  for (int i = threadIdx.x; i < LP; i += blockDim.x)
-    tokple[(size_t)r * LP + i] = bf2f(t[i]) * sqrtP;
+  const int nh = H / 8, nw = nh + LP / 8;
+  for (int b0 = 0; b0 < nw; b0 += 8 * 256) {
+    uint4 v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      int w = b0 + threadIdx.x + 256 * k;
+      w = w < nw ? w : nw - 1;
+      v[k] = *reinterpret_cast<const uint4*>(w < nh ? e + 8 * w : t + 8 * (w - nh));
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int w = b0 + threadIdx.x + 256 * k;
+      if (w >= nw) break;
+      const bool is_h = w < nh;
+      const float sc = is_h ? sqrtH : sqrtP;
+      float* dst = is_h ? h + (size_t)r * H + 8 * w : tokple + (size_t)r * LP + 8 * (w - nh);
+      const uint32_t q[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+      float4 lo, hi;
+      lo.x = bf2f(q[0]) * sc; lo.y = bf2f(q[0] >> 16) * sc;
+      lo.z = bf2f(q[1]) * sc; lo.w = bf2f(q[1] >> 16) * sc;
+      hi.x = bf2f(q[2]) * sc; hi.y = bf2f(q[2] >> 16) * sc;
+      hi.z = bf2f(q[3]) * sc; hi.w = bf2f(q[3] >> 16) * sc;
+      reinterpret_cast<float4*>(dst)[0] = lo;
+      reinterpret_cast<float4*>(dst)[1] = hi;
+    }
+  }
   // RoPE angles of this row's position for both layer types, from fp64
   // (cos then sin, hd/2 each; sliding first, then full)
   const int p = clamp_pos(R, pos);
@@ -98,6 +123,7 @@ hipError_t launch_embed(const Rows& R, const uint16_t* E, const uint16_t* Eple, 
                         float sqrtH, float sqrtP, float* h, float* tokple, int* err,
                         const RopeTable& rt, hipStream_t st) {
   if (!rt.out || !rt.inv_s || !rt.inv_f) return hipErrorInvalidValue;
+  if (H % 8 || LP % 8 || H + LP < 8) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_embed, dim3(R.n), dim3(256), 0, st, R, E, Eple, H, LP, sqrtH, sqrtP, h,
                      tokple, err, rt);
   return hipGetLastError();
@@ -113,14 +139,15 @@ __global__ __launch_bounds__(256) void k_ple_finish(int LP, int P, const float* 
   __shared__ float sh[4];
   const int r = blockIdx.x, l = blockIdx.y, i = threadIdx.x;
   const size_t base = (size_t)r * LP + (size_t)l * P;
+  const int ic = i < P ? i : 0;
+  const uint32_t gi = g[ic];          // read with u, used after the reduction
+  const float tp = tokple[base + ic];
   float v = 0.f;
-  if (i < P) {
-    for (int q = 0; q < u_parts; ++q) v += u[(size_t)q * u_pstride + base + i];
-    v *= inv_sqrtH;
-  }
+  for (int q = 0; q < u_parts; ++q) v += u[(size_t)q * u_pstride + base + ic];
+  v = i < P ? v * inv_sqrtH : 0.f;
   const float ss = block_sum<256>(v * v, sh);
   const float rr = rsqrtf(ss / (float)P + eps);
-  if (i < P) pli[base + i] = (v * rr * bf2f(g[i]) + tokple[base + i]) * 0.70710678118654752f;
+  if (i < P) pli[base + i] = fmaf(v * rr, bf2f(gi), tp) * 0.70710678118654752f;
 }
 
 hipError_t launch_ple_finish(const Rows& R, const float* u, int u_parts, size_t u_pstride,
@@ -494,14 +521,23 @@ __device__ __forceinline__ void ld8_bf(const uint16_t* p, float (&v)[8]) {
 // loads of up to B partials are issued together, the sum runs in order
 template <int B = 8>
 __device__ __forceinline__ void ld8_parts(const float* p, int n, size_t stride, float (&v)[8]) {
-  ld8(p, v);
-  for (int q0 = 1; q0 < n; q0 += B) {
+  // the first 4 partials are read unconditionally (the zero row past n),
+  // with no use in between: a loop entered with a read pending would wait
+  // for it first
+  float t0[4][8];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) ld8(k < n ? p + (size_t)k * stride : zero_f(), t0[k]);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = t0[0][j];
+#pragma unroll
+  for (int k = 1; k < 4; ++k)
+    if (k < n)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] += t0[k][j];
+  for (int q0 = 4; q0 < n; q0 += B) {
     float t[B][8];
 #pragma unroll
-    for (int u = 0; u < B; ++u) {
-      const bool ok = q0 + u < n;
-      ld8(p + (ok ? (size_t)(q0 + u) * stride : 0), t[u]);
-    }
+    for (int u = 0; u < B; ++u) ld8(q0 + u < n ? p + (size_t)(q0 + u) * stride : zero_f(), t[u]);
 #pragma unroll
     for (int u = 0; u < B; ++u)
       if (q0 + u < n)
@@ -528,7 +564,60 @@ __device__ __forceinline__ void emit8(const float (&v)[8], uint16_t* xh, uint16_
   if ((threadIdx.x & 3) == 0) xg[i0 / 32] = s;
 }
 
-// Block per row; thread t handles elements 8t.. (+2048 per pass).
+// Two operands (the second optional) with their partials, all reads in
+// flight together (the first 4 partials of each unconditionally, as above)
+__device__ __forceinline__ void ld8_parts2(const float* p0, const float* p1, bool two, int n,
+                                           size_t stride, float (&v)[8], float (&u)[8]) {
+  if (!two) {
+    ld8_parts(p0, n, stride, v);
+    return;
+  }
+  float t0[4][8], t1[4][8];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    ld8(k < n ? p0 + (size_t)k * stride : zero_f(), t0[k]);
+    ld8(k < n ? p1 + (size_t)k * stride : zero_f(), t1[k]);
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    v[j] = t0[0][j];
+    u[j] = t1[0][j];
+  }
+#pragma unroll
+  for (int k = 1; k < 4; ++k)
+    if (k < n)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        v[j] += t0[k][j];
+        u[j] += t1[k][j];
+      }
+  for (int q0 = 4; q0 < n; q0 += 4) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      ld8(q0 + k < n ? p0 + (size_t)(q0 + k) * stride : zero_f(), t0[k]);
+      ld8(q0 + k < n ? p1 + (size_t)(q0 + k) * stride : zero_f(), t1[k]);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (q0 + k < n)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          v[j] += t0[k][j];
+          u[j] += t1[k][j];
+        }
+  }
+}
+
+__device__ __forceinline__ void unpack8(uint4 w, float (&v)[8]) {
+  const uint32_t q[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { v[2 * i] = bf2f(q[i]); v[2 * i + 1] = bf2f(q[i] >> 16); }
+}
+
+// Thread t handles elements 8t.. of the row's slice.  kRes / kResNorm: block
+// per row (K <= 2048, row reductions); the other kinds: block per (row,
+// 2048-slice).  Every read is issued before the first value is used (absent
+// gains read the zero row); bf16 gains stay packed until then.
 __global__ __launch_bounds__(256) void k_xprep(Prologue p, int rows, int K, uint16_t* __restrict__ xh,
                                                uint16_t* __restrict__ xl, float* __restrict__ xg) {
   __shared__ float red[8];
@@ -536,69 +625,71 @@ __global__ __launch_bounds__(256) void k_xprep(Prologue p, int rows, int K, uint
   uint16_t* oh = xh + (size_t)b * K;
   uint16_t* ol = xl + (size_t)b * K;
   float* og = xg + (size_t)b * (K / 32);
-  if (p.kind == kRes || p.kind == kResNorm) {  // K == hidden size <= 2048: one pass
+  if (p.kind == kRes || p.kind == kResNorm) {
     const int i0 = 8 * t;
     const bool on = i0 < K;
-    float av[8], dv[8], gdv[8], gxv[8];
+    const int ic = on ? i0 : 0;
+    const uint16_t* gdp = p.d ? p.gd : kZeroRow;
+    const uint16_t* gxp = p.kind == kResNorm ? p.gx : kZeroRow;
+    const uint4 gdw = *reinterpret_cast<const uint4*>(gdp + ic);
+    const uint4 gxw = *reinterpret_cast<const uint4*>(gxp + ic);
+    const uint32_t scw = *(p.scalar ? p.scalar : kZeroRow);
+    float av[8], dv[8];
+    ld8(p.a + (size_t)b * K + ic, av);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) dv[j] = 0.f;
+    if (p.d) ld8_parts<8>(p.d + (size_t)b * K + ic, p.nd, p.d_pstride, dv);
     float ss = 0.f;
+    if (on)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) av[j] = dv[j] = gdv[j] = gxv[j] = 0.f;
-    if (on) {  // every load of the prologue issued up front
-      if (p.d) ld8_bf(p.gd + i0, gdv);
-      if (p.kind == kResNorm) ld8_bf(p.gx + i0, gxv);
-      ld8(p.a + (size_t)b * K + i0, av);
-      if (p.d) {
-        ld8_parts(p.d + (size_t)b * K + i0, p.nd, p.d_pstride, dv);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) ss += dv[j] * dv[j];
-      }
-    }
+      for (int j = 0; j < 8; ++j) ss = fmaf(dv[j], dv[j], ss);
     float rd = 0.f;
     if (p.d) rd = rsqrtf(block_sum<256>(ss, red) / (float)K + p.eps);
-    const float sc = p.scalar ? bf2f(p.scalar[0]) : 1.0f;
+    const float sc = p.scalar ? bf2f(scw) : 1.0f;
+    float gdv[8], gxv[8];
+    unpack8(gdw, gdv);
+    unpack8(gxw, gxv);
     float hs = 0.f;
-    if (on) {
-      if (p.d) {
+    if (p.d) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) av[j] = (av[j] + dv[j] * rd * gdv[j]) * sc;
-        if (p.h_out) {
-          float* ho = p.h_out + (size_t)b * K + i0;
-          *reinterpret_cast<float4*>(ho) = make_float4(av[0], av[1], av[2], av[3]);
-          *reinterpret_cast<float4*>(ho + 4) = make_float4(av[4], av[5], av[6], av[7]);
-        }
+      for (int j = 0; j < 8; ++j) av[j] = fmaf(dv[j] * rd, gdv[j], av[j]) * sc;
+      if (p.h_out && on) {
+        float* ho = p.h_out + (size_t)b * K + i0;
+        *reinterpret_cast<float4*>(ho) = make_float4(av[0], av[1], av[2], av[3]);
+        *reinterpret_cast<float4*>(ho + 4) = make_float4(av[4], av[5], av[6], av[7]);
       }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) hs += av[j] * av[j];
     }
+    if (on)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) hs = fmaf(av[j], av[j], hs);
     if (p.kind == kResNorm) {
       const float rh = rsqrtf(block_sum<256>(hs, red) / (float)K + p.eps);
-      if (on)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) av[j] *= rh * gxv[j];
+      for (int j = 0; j < 8; ++j) av[j] = av[j] * rh * gxv[j];
     }
     if (on) emit8(av, oh, ol, og, i0);
   } else {
-    for (int i0 = 8 * t; i0 < K; i0 += 2048) {
-      float v[8];
-      const float* src = p.a + (size_t)b * p.lda + i0;
-      ld8_parts(src, p.na, p.a_pstride, v);
-      if (p.kind == kGeglu || p.kind == kPleGate) {
-        float u[8];
-        if (p.kind == kGeglu) ld8_parts(src + K, p.na, p.a_pstride, u);
-        else ld8(p.pli + (size_t)b * p.pli_ld + i0, u);
+    const int i0 = blockIdx.y * 2048 + 8 * t;
+    if (i0 >= K) return;  // whole 32-groups: the four threads of a group go together
+    const float* src = p.a + (size_t)b * p.lda + i0;
+    float v[8], u[8];
+    const bool two = p.kind == kGeglu;
+    if (p.kind == kPleGate) ld8(p.pli + (size_t)b * p.pli_ld + i0, u);
+    ld8_parts2(src, src + K, two, p.na, p.a_pstride, v, u);
+    if (p.kind == kGeglu || p.kind == kPleGate)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = gelu_tanh(v[j]) * u[j];
-      }
-      emit8(v, oh, ol, og, i0);
-    }
+      for (int j = 0; j < 8; ++j) v[j] = gelu_tanh(v[j]) * u[j];
+    emit8(v, oh, ol, og, i0);
   }
 }
 
 hipError_t launch_xprep(const Prologue& p, int rows, int K, uint16_t* xh, uint16_t* xl, float* xg,
                         hipStream_t st) {
-  if (K % 32 || ((p.kind == kRes || p.kind == kResNorm) && K > 2048)) return hipErrorInvalidValue;
+  const bool res = p.kind == kRes || p.kind == kResNorm;
+  if (K % 32 || (res && K > 2048)) return hipErrorInvalidValue;
   if (p.na < 1 || (p.d && p.nd < 1)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_xprep, dim3(rows), dim3(256), 0, st, p, rows, K, xh, xl, xg);
+  hipLaunchKernelGGL(k_xprep, dim3(rows, res ? 1 : (K + 2047) / 2048), dim3(256), 0, st, p, rows, K,
+                     xh, xl, xg);
   return hipGetLastError();
 }
 
@@ -1006,9 +1097,12 @@ hipError_t launch_sum_partials(int nparts, size_t n, const float* parts, float* 
 }
 
 // ------------------------------------------------------------- argmax, pass 2
+// adv (optional): the row's position, advanced by one once the token is out
+// (a captured step that advances its positions needs no kernel of its own)
 __global__ __launch_bounds__(256) void k_argmax_final(int nblk, const float* __restrict__ cv,
                                                       const int32_t* __restrict__ ci,
-                                                      int32_t* __restrict__ out) {
+                                                      int32_t* __restrict__ out,
+                                                      int32_t* __restrict__ adv) {
   __shared__ float sv[4];
   __shared__ int si[4];
   const int r = blockIdx.x, t = threadIdx.x;
@@ -1043,12 +1137,15 @@ __global__ __launch_bounds__(256) void k_argmax_final(int nblk, const float* __r
         bi = si[w];
       }
     out[r] = bi == 0x7FFFFFFF ? 0 : bi;
+    if (adv) adv[r] += 1;
   }
 }
 
 hipError_t launch_argmax_final(int rows, int nblk, const float* cand_val,
-                               const int32_t* cand_idx, int32_t* out, hipStream_t st) {
-  hipLaunchKernelGGL(k_argmax_final, dim3(rows), dim3(256), 0, st, nblk, cand_val, cand_idx, out);
+                               const int32_t* cand_idx, int32_t* out, int32_t* adv,
+                               hipStream_t st) {
+  hipLaunchKernelGGL(k_argmax_final, dim3(rows), dim3(256), 0, st, nblk, cand_val, cand_idx, out,
+                     adv);
   return hipGetLastError();
 }
 

@@ -452,7 +452,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step1(StepArgs a) {
       const float rr = rsqrtf(block_sum<kStepThreads>(v * v, sh) / (float)P + a.eps);
       if (t < P)
         st32<true>(S + a.pli + (size_t)ls * P + t,
-                   (v * rr * bf2f(a.g_plpn[t]) + ld32<true>(S + a.tokple + (size_t)ls * P + t)) *
+                   fmaf(v * rr, bf2f(a.g_plpn[t]), ld32<true>(S + a.tokple + (size_t)ls * P + t)) *
                        0.70710678118654752f);
     }
     if (y.full) prefetch<WQ, KOF>(y.o, pf);
