@@ -687,32 +687,27 @@ __device__ void attn_chunk(const Rows& R, const AttnArgs& a, int c, int r) {
       if constexpr (DPL < 8) cur = nxt;
       else if (gi + 4 < ngroups) load_group(gi + 4, cur);
     }
-    // merge the four waves: per head max M, then rescale and sum
+    // merge the four waves: per head max M, then rescale and sum.  Each wave
+    // parks its o in LDS (wave 0 in qs, whose queries are in registers); the
+    // factors are formed once per (wave, head); every element then sums the
+    // four in wave order (the same arithmetic as folding them in one by one)
+    __shared__ float op[3][NH * HD];
+    __shared__ float fw[4][NH];
     if (lane < 16 && (lane & 1) == 0) {
       wm[wave][lane >> 1] = m_run;
       wl[wave][lane >> 1] = l_run;
     }
+    float* mine = wave == 0 ? qs : op[wave - 1];
+#pragma unroll
+    for (int h = 0; h < NH; ++h)
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) mine[h * HD + lane * DPL + i] = o[h][i];
     __syncthreads();
-    float* acc = qs;  // reuse: [NH][HD]
-    for (int w = 0; w < 4; ++w) {
-      if (wave == w) {
-#pragma unroll
-        for (int h = 0; h < NH; ++h) {
-          float M = wm[0][h];
-          for (int x = 1; x < 4; ++x) M = fmaxf(M, wm[x][h]);
-          const float f = (wm[w][h] == -INFINITY) ? 0.f : expf(wm[w][h] - M);
-#pragma unroll
-          for (int i = 0; i < DPL; ++i) {
-            float& a_ = acc[h * HD + lane * DPL + i];
-            a_ = (w == 0) ? o[h][i] * f : fmaf(o[h][i], f, a_);
-          }
-        }
-      }
-      __syncthreads();
-    }
-    for (int idx = t; idx < nq * HD; idx += 256) {
-      const int h = idx / HD, d = idx % HD;
-      st32<COH>(part + h * hstride + d, acc[idx]);
+    if (t < 4 * NH) {
+      const int w = t / NH, h = t % NH;
+      float M = wm[0][h];
+      for (int x = 1; x < 4; ++x) M = fmaxf(M, wm[x][h]);
+      fw[w][h] = (wm[w][h] == -INFINITY) ? 0.f : expf(wm[w][h] - M);
     }
     if (t < nq) {
       float M = wm[0][t];
@@ -722,6 +717,15 @@ __device__ void attn_chunk(const Rows& R, const AttnArgs& a, int c, int r) {
         if (wm[x][t] != -INFINITY) L = fmaf(wl[x][t], expf(wm[x][t] - M), L);
       st32<COH>(part + t * hstride + HD, M);
       st32<COH>(part + t * hstride + HD + 1, L);
+    }
+    __syncthreads();
+    for (int idx = t; idx < nq * HD; idx += 256) {
+      const int h = idx / HD, d = idx % HD;
+      float a_ = qs[idx] * fw[0][h];
+      a_ = fmaf(op[0][idx], fw[1][h], a_);
+      a_ = fmaf(op[1][idx], fw[2][h], a_);
+      a_ = fmaf(op[2][idx], fw[3][h], a_);
+      st32<COH>(part + h * hstride + d, a_);
     }
   } else if (t < nq) {  // no keys in this chunk
     st32<COH>(part + t * hstride + HD, -INFINITY);
@@ -744,7 +748,7 @@ __device__ void attn_combine(const AttnArgs& a, int r, int h) {
   // the weights are known (slots past the last written chunk hold stale
   // values, and chunks past nchunk read the zero row: dropped by a select,
   // never multiplied)
-  constexpr int kPre = 16, kDt = 2;  // hd <= 512 = kDt * 256
+  constexpr int kPre = 32, kDt = 2;  // hd <= 512 = kDt * 256
   float pv[kDt][kPre];
 #pragma unroll
   for (int it = 0; it < kDt; ++it) {

@@ -323,9 +323,13 @@ Ws ws_layout(const e2b_model* m, int R) {
   return w;
 }
 
-void attn_chunks(const e2b_model* m, bool full, int* chunk, int* nchunk) {
+// Keys per attention block: 16 for a single row (each wave then takes one
+// group of 4 keys: the shortest chain, and the chip has room for the blocks),
+// else 32 (64 or 128 measured no better)
+void attn_chunks(const e2b_model* m, bool full, int rows, int* chunk, int* nchunk) {
   const int span = full ? m->max_ctx : std::min(m->c.sliding_window, m->max_ctx);
-  int n = (span + 31) / 32;  // 32-key chunks (64 or 128 measured no better)
+  const int w = rows == 1 ? 16 : 32;
+  int n = (span + w - 1) / w;
   if (n > e2b::kMaxChunks) n = e2b::kMaxChunks;
   if (n < 1) n = 1;
   *nchunk = n;
@@ -434,7 +438,7 @@ void plan_slab(e2b_model* m) {
   m->slab_floats = cur;
 }
 
-void attn_chunks(const e2b_model* m, bool full, int* chunk, int* nchunk);
+void attn_chunks(const e2b_model* m, bool full, int rows, int* chunk, int* nchunk);
 
 // Fill the persistent step's plan in the arena (synchronous copy); needs the
 // weights loaded and the K/V cache bound.  Disables the step when the device
@@ -477,7 +481,7 @@ int upload_step_plan(e2b_model* m) {
     p.hd = y.hd;
     p.full = y.full;
     p.I = y.I;
-    attn_chunks(m, y.full, &p.chunk, &p.nchunk);
+    attn_chunks(m, y.full, 1, &p.chunk, &p.nchunk);
     p.hq = s.hq;
     p.qkv_out = s.qkv_out;
     p.part = s.part;
@@ -668,7 +672,7 @@ int run_rows(e2b_model* m, const e2b::Rows& R, bool head, int head_row, float* d
       a.qkv_parts = nd_qkv;
       a.qkv_pstride = (size_t)n * d.qkv.N;
       a.eps = eps;
-      attn_chunks(m, y.full, &a.chunk, &a.nchunk);
+      attn_chunks(m, y.full, n, &a.chunk, &a.nchunk);
       CK(launch_attention(R, a, st), "attention");
     }
     {
