@@ -71,11 +71,58 @@ __device__ __forceinline__ float gelu_tanh(float x) {
   return 0.5f * x * (1.0f + tanhf(c * fmaf(0.044715f * x * x, x, x)));
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+// Cross-lane exchange.  A shuffle through the LDS crossbar (ds_bpermute)
+// costs a round trip per step; inside a row of 16 lanes the partner lane^o,
+// o = 1, 2, 4, 8, is reached by DPP moves (VALU): quad permutes for 1 and 2,
+// half-row mirror then quad reverse for 4, row mirror then half-row mirror
+// for 8.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+template <int O>
+__device__ __forceinline__ float xor_lane(float v) {  // v of lane ^ O, O < 16
+  static_assert(O == 1 || O == 2 || O == 4 || O == 8, "DPP xor partner within a row");
+  if constexpr (O == 1) return dpp_mov<0xB1>(v);                  // quad_perm [1,0,3,2]
+  else if constexpr (O == 2) return dpp_mov<0x4E>(v);             // quad_perm [2,3,0,1]
+  else if constexpr (O == 4) return dpp_mov<0x1B>(dpp_mov<0x141>(v));  // half mirror, quad reverse
+  else return dpp_mov<0x141>(dpp_mov<0x140>(v));                  // row mirror, half mirror
+}
+
+// Sum over aligned groups of S lanes (S <= 16): every lane of a group gets
+// the group's sum, the same value (and rounding) as the xor butterfly.  Once
+// a quad (8-group) holds one value, a mirror pairs it with the neighbouring
+// quad (8-group) exactly as xor 4 (8) would.
+template <int S>
+__device__ __forceinline__ float group_sum(float v) {
+  static_assert(S == 1 || S == 2 || S == 4 || S == 8 || S == 16, "group of at most one row");
+  if constexpr (S >= 2) v += dpp_mov<0xB1>(v);
+  if constexpr (S >= 4) v += dpp_mov<0x4E>(v);
+  if constexpr (S >= 8) v += dpp_mov<0x141>(v);
+  if constexpr (S >= 16) v += dpp_mov<0x140>(v);
   return v;
 }
+
+__device__ __forceinline__ float lane_value(float v, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+
+// Sum over groups of S lanes for any S up to 64 (S = 32: two halves): the
+// row sums by DPP, then the xor-16 / xor-32 steps on the four row sums read
+// out of lanes 0, 16, 32, 48 ((r0 + r1) + (r2 + r3), the butterfly's order).
+template <int S>
+__device__ __forceinline__ float lanes_sum(float v) {
+  if constexpr (S <= 16) {
+    return group_sum<S>(v);
+  } else {
+    v = group_sum<16>(v);
+    const float a = lane_value(v, 0) + lane_value(v, 16), b = lane_value(v, 32) + lane_value(v, 48);
+    if constexpr (S == 64) return a + b;
+    else return (threadIdx.x & 32) ? b : a;
+  }
+}
+
+__device__ __forceinline__ float wave_sum(float v) { return lanes_sum<64>(v); }
 
 // Sum over a block of NT threads, same value returned to every thread.
 // `sh` needs NT/64 floats; the leading barrier makes back-to-back calls safe.
@@ -289,28 +336,20 @@ __device__ void pack_x(const float* xs, uint32_t* xp) {
   for (int p = threadIdx.x; p < KS / 2; p += kGemvThreads) {
     uint32_t hi, lo;
     if (WQ) {
+      // 16 consecutive threads hold the 16 pairs of group g: its sum of
+      // hi + lo is a 16-lane butterfly
       const int g = p / 16, q = p % 16, j = q / 4, i = q % 4;
       const int k = 32 * g + 8 * j + i;  // pair (k, k + 4) matches the nibble unpack
       split_pair(xs[k], xs[k + 4], hi, lo);
       xp[g * Packed<WQ, KS>::kWordsW4 + q] = hi;
       xp[g * Packed<WQ, KS>::kWordsW4 + 16 + q] = lo;
+      const float s = group_sum<16>((bf2f(hi) + bf2f(lo)) + (bf2f(hi >> 16) + bf2f(lo >> 16)));
+      if (q == 0) xp[g * Packed<WQ, KS>::kWordsW4 + 32] = __float_as_uint(s);
     } else {
       const int k = 2 * p, c = k / 512, o = k % 512, ls = o / 8, j = (o % 8) / 2;
       split_pair(xs[k], xs[k + 1], hi, lo);
       xp[(c * Y::S + ls) * 8 + j] = hi;
       xp[(c * Y::S + ls) * 8 + 4 + j] = lo;
-    }
-  }
-  if (WQ) {
-    __syncthreads();
-    for (int g = threadIdx.x; g < KS / 32; g += kGemvThreads) {
-      float s = 0.f;
-      for (int q = 0; q < 16; ++q) {
-        const uint32_t hi = xp[g * Packed<WQ, KS>::kWordsW4 + q];
-        const uint32_t lo = xp[g * Packed<WQ, KS>::kWordsW4 + 16 + q];
-        s += (bf2f(hi) + bf2f(lo)) + (bf2f(hi >> 16) + bf2f(lo >> 16));
-      }
-      xp[g * Packed<WQ, KS>::kWordsW4 + 32] = __float_as_uint(s);
     }
   }
   __syncthreads();
@@ -333,14 +372,32 @@ __device__ __forceinline__ void tr_step(float* cur, int lane, int o) {
   }
 }
 
-// 32 values per lane -> lane l ends with the full 64-lane sum of value l >> 1
+template <int H, int O>
+__device__ __forceinline__ void tr_step_dpp(float* cur, int lane) {
+  const bool upper = (lane & O) != 0;
+#pragma unroll
+  for (int i = 0; i < H; ++i) {
+    const float send = upper ? cur[i] : cur[i + H];
+    const float keep = upper ? cur[i + H] : cur[i];
+    cur[i] = keep + xor_lane<O>(send);
+  }
+}
+
+// 32 values per lane -> every lane ends with the full 64-lane sum of value
+// tr_index(lane).  The wide steps (16 exchanges, then 8, 4, 2) run on the
+// DPP partners 1, 2, 4, 8; only the last two (16, then the pair sum over 32)
+// go through the crossbar.  Each step's partner decides one index bit, so
+// value bit 4 - i comes from lane bit i (i < 5).
+__device__ __forceinline__ int tr_index(int lane) {
+  return ((lane & 1) << 4) | ((lane & 2) << 2) | (lane & 4) | ((lane & 8) >> 2) | ((lane & 16) >> 4);
+}
 __device__ __forceinline__ float transpose_reduce32(float (&v)[32], int lane) {
-  tr_step<16>(v, lane, 32);
-  tr_step<8>(v, lane, 16);
-  tr_step<4>(v, lane, 8);
-  tr_step<2>(v, lane, 4);
-  tr_step<1>(v, lane, 2);
-  return v[0] + __shfl_xor(v[0], 1, 64);
+  tr_step_dpp<16, 1>(v, lane);
+  tr_step_dpp<8, 2>(v, lane);
+  tr_step_dpp<4, 4>(v, lane);
+  tr_step_dpp<2, 8>(v, lane);
+  tr_step<1>(v, lane, 16);
+  return v[0] + __shfl_xor(v[0], 32, 64);
 }
 
 template <int DPL>
@@ -614,7 +671,9 @@ __device__ void attn_chunk(const Rows& R, const AttnArgs& a, int c, int r) {
       for (int i = 0; i < DPL; ++i) qr[h][i] = h < nq ? qs[h * HD + lane * DPL + i] : 0.f;
 
     const float scale = rsqrtf((float)HD);
-    const int myh = (lane >> 1) & 7, myk = lane >> 4;  // value index lane>>1 = k*8 + h
+    // value index k * 8 + h of this lane after the transposing reduction: the
+    // 4 keys of a head sit in lane bits 0-1 (DPP partners 1 and 2)
+    const int vidx = tr_index(lane), myh = vidx & 7, myk = vidx >> 3;
     float m_run = -INFINITY, l_run = 0.f;
     float o[NH][DPL];
 #pragma unroll
@@ -650,19 +709,19 @@ __device__ void attn_chunk(const Rows& R, const AttnArgs& a, int c, int r) {
       }
       float sc_ = transpose_reduce32(part32, lane) * scale;
       if (key0 + myk >= j1 || myh >= nq) sc_ = -INFINITY;
-      float mx = fmaxf(sc_, __shfl_xor(sc_, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      float mx = fmaxf(sc_, xor_lane<1>(sc_));
+      mx = fmaxf(mx, xor_lane<2>(mx));
       const float m_new = fmaxf(m_run, mx);
       const float pr = (m_new == -INFINITY || sc_ == -INFINITY) ? 0.f : expf(sc_ - m_new);
       const float corr = (m_new == -INFINITY || m_run == -INFINITY)
                              ? (m_run == -INFINITY ? 0.f : 1.f)
                              : expf(m_run - m_new);
-      float ps = pr + __shfl_xor(pr, 16, 64);
-      ps += __shfl_xor(ps, 32, 64);
+      float ps = pr + xor_lane<1>(pr);
+      ps += xor_lane<2>(ps);
       l_run = fmaf(l_run, corr, ps);
       m_run = m_new;
-      if ((lane & 1) == 0) pw[wave][lane >> 1] = pr;
-      if (lane < 16 && (lane & 1) == 0) cw[wave][lane >> 1] = corr;
+      if (lane < 32) pw[wave][vidx] = pr;
+      if (lane < 32 && myk == 0) cw[wave][myh] = corr;
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
       __builtin_amdgcn_wave_barrier();
 #pragma unroll
@@ -693,9 +752,9 @@ __device__ void attn_chunk(const Rows& R, const AttnArgs& a, int c, int r) {
     // four in wave order (the same arithmetic as folding them in one by one)
     __shared__ float op[3][NH * HD];
     __shared__ float fw[4][NH];
-    if (lane < 16 && (lane & 1) == 0) {
-      wm[wave][lane >> 1] = m_run;
-      wl[wave][lane >> 1] = l_run;
+    if (lane < 32 && myk == 0) {
+      wm[wave][myh] = m_run;
+      wl[wave][myh] = l_run;
     }
     float* mine = wave == 0 ? qs : op[wave - 1];
 #pragma unroll

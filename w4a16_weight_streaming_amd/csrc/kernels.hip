@@ -207,6 +207,9 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv(Lin W, int rows, Prologue
 
   PrologueRegs<KS, tag_kind(TAG), tag_nd(TAG)> pr;
   pr.load(pro, rows, b, ks * KS, K);  // input reads first: they gate the compute
+  // every wave's input reads enter the memory pipeline before the block's
+  // weight reads (otherwise they queue behind the other waves' weights)
+  __syncthreads();
   int u0 = blockIdx.x * 4 + wave;
   Batch A, Bq;
   load_batch(A, u0);                  // then the weights (independent of x)
@@ -276,8 +279,7 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv(Lin W, int rows, Prologue
           }
         }
       }
-#pragma unroll
-      for (int o = Y::S / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+      acc = lanes_sum<Y::S>(acc);
       const int u = ub + uu * stride;
       const int nn = B.n[uu];
       if (ls == 0 && u < NU && nn < N) {
@@ -559,8 +561,7 @@ __device__ __forceinline__ void emit8(const float (&v)[8], uint16_t* xh, uint16_
   }
   *reinterpret_cast<uint4*>(xh + i0) = make_uint4(h[0], h[1], h[2], h[3]);
   *reinterpret_cast<uint4*>(xl + i0) = make_uint4(l[0], l[1], l[2], l[3]);
-  s += __shfl_xor(s, 1, 64);
-  s += __shfl_xor(s, 2, 64);
+  s = group_sum<4>(s);
   if ((threadIdx.x & 3) == 0) xg[i0 / 32] = s;
 }
 
@@ -836,8 +837,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm(Lin W, int rows, GemmA A, int K
         rah[j] = make_uint4(h[0], h[1], h[2], h[3]);
         ral[j] = make_uint4(l[0], l[1], l[2], l[3]);
         if (WQ) {  // group of 32 = the 4 consecutive lanes with the same row
-          gs += __shfl_xor(gs, 1, 64);
-          gs += __shfl_xor(gs, 2, 64);
+          gs = group_sum<4>(gs);
           rgs[j] = 136.0f * gs;
         }
       }

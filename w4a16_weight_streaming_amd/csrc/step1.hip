@@ -252,8 +252,7 @@ __device__ void gemv_step(const Lin& W, const Prologue& pro, const VB& v, const 
           }
         }
       }
-#pragma unroll
-      for (int o = Y::S / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+      acc = lanes_sum<Y::S>(acc);
       const int u = ub + uu * stride;
       const int nn = B.n[uu];
       if (ls == 0 && u < NU && nn < N) {
