@@ -124,6 +124,57 @@ __device__ __forceinline__ float lanes_sum(float v) {
 
 __device__ __forceinline__ float wave_sum(float v) { return lanes_sum<64>(v); }
 
+template <int O>
+__device__ __forceinline__ int xor_lane_i(int v) {
+  return __builtin_bit_cast(int, xor_lane<O>(__builtin_bit_cast(float, v)));
+}
+
+// Maximum over the wave, every lane gets it (row maxima by DPP, then the
+// four rows read out)
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_mov<0xB1>(v));
+  v = fmaxf(v, dpp_mov<0x4E>(v));
+  v = fmaxf(v, dpp_mov<0x141>(v));
+  v = fmaxf(v, dpp_mov<0x140>(v));
+  return fmaxf(fmaxf(lane_value(v, 0), lane_value(v, 16)), fmaxf(lane_value(v, 32), lane_value(v, 48)));
+}
+__device__ __forceinline__ int wave_max_i(int v) {
+  v = max(v, xor_lane_i<1>(v));
+  v = max(v, xor_lane_i<2>(v));
+  v = max(v, __builtin_bit_cast(int, dpp_mov<0x141>(__builtin_bit_cast(float, v))));
+  v = max(v, __builtin_bit_cast(int, dpp_mov<0x140>(__builtin_bit_cast(float, v))));
+  return max(max(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+             max(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+}
+
+// (value, index) maximum with the lowest index among equal values; the
+// result does not depend on the order of the comparisons
+__device__ __forceinline__ void arg_better(float ov, int oi, float& v, int& i) {
+  if (ov > v || (ov == v && oi < i)) {
+    v = ov;
+    i = oi;
+  }
+}
+template <int O>
+__device__ __forceinline__ void argmax_xor(float& v, int& i) {
+  arg_better(xor_lane<O>(v), xor_lane_i<O>(i), v, i);
+}
+// over groups of S lanes (S <= 16) by DPP, or the whole wave (S = 64)
+template <int S>
+__device__ __forceinline__ void argmax_lanes(float& v, int& i) {
+  if constexpr (S >= 2) argmax_xor<1>(v, i);
+  if constexpr (S >= 4) argmax_xor<2>(v, i);
+  if constexpr (S >= 8) argmax_xor<4>(v, i);
+  if constexpr (S >= 16) argmax_xor<8>(v, i);
+  if constexpr (S == 64) {  // each lane folds in the four row results
+    const float v0 = v;
+    const int i0 = i;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      arg_better(lane_value(v0, 16 * r), __builtin_amdgcn_readlane(i0, 16 * r), v, i);
+  }
+}
+
 // Sum over a block of NT threads, same value returned to every thread.
 // `sh` needs NT/64 floats; the leading barrier makes back-to-back calls safe.
 template <int NT>
@@ -824,11 +875,8 @@ __device__ void attn_combine(const AttnArgs& a, int r, int h) {
   const bool act = lc > 0.f;
   float M = act ? mc : -INFINITY;
   int nact = act ? t + 1 : 0;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    M = fmaxf(M, __shfl_xor(M, o, 64));
-    nact = max(nact, __shfl_xor(nact, o, 64));
-  }
+  M = wave_max(M);
+  nact = wave_max_i(nact);
   if ((t & 63) == 0) {
     sh[t >> 6] = M;
     na[t >> 6] = nact;

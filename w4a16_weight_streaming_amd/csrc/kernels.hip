@@ -308,15 +308,7 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv(Lin W, int rows, Prologue
 
   if (epi.argmax) {
     // wave reduce (max value, lowest index), then across the 4 waves
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(best, o, 64);
-      const int oi = __shfl_xor(bidx, o, 64);
-      if (ov > best || (ov == best && oi < bidx)) {
-        best = ov;
-        bidx = oi;
-      }
-    }
+    argmax_lanes<64>(best, bidx);
     int* redi = reinterpret_cast<int*>(red + 8);
     __syncthreads();
     if (lane == 0) {
@@ -965,15 +957,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm(Lin W, int rows, GemmA A, int K
             x = ncol[j];
           }
         }
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) {
-        const float ov = __shfl_xor(v, o, 64);
-        const int ox = __shfl_xor(x, o, 64);
-        if (ov > v || (ov == v && ox < x)) {
-          v = ov;
-          x = ox;
-        }
-      }
+      argmax_lanes<16>(v, x);
       if ((lane & 15) == 0) {
         rv[wave][m] = v;
         ri[wave][m] = x;
@@ -1116,15 +1100,7 @@ __global__ __launch_bounds__(256) void k_argmax_final(int nblk, const float* __r
       bi = x;
     }
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const float ov = __shfl_xor(best, o, 64);
-    const int oi = __shfl_xor(bi, o, 64);
-    if (ov > best || (ov == best && oi < bi)) {
-      best = ov;
-      bi = oi;
-    }
-  }
+  argmax_lanes<64>(best, bi);
   if ((t & 63) == 0) {
     sv[t >> 6] = best;
     si[t >> 6] = bi;

@@ -280,15 +280,7 @@ __device__ void gemv_step(const Lin& W, const Prologue& pro, const VB& v, const 
   }
 
   if (ARGMAX) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(best, o, 64);
-      const int oi = __shfl_xor(bidx, o, 64);
-      if (ov > best || (ov == best && oi < bidx)) {
-        best = ov;
-        bidx = oi;
-      }
-    }
+    argmax_lanes<64>(best, bidx);
     int* redi = reinterpret_cast<int*>(red + 8);
     __syncthreads();
     if (lane == 0) {
@@ -568,15 +560,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step1(StepArgs a) {
         bi = xi;
       }
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(best, o, 64);
-      const int oi = __shfl_xor(bi, o, 64);
-      if (ov > best || (ov == best && oi < bi)) {
-        best = ov;
-        bi = oi;
-      }
-    }
+    argmax_lanes<64>(best, bi);
     if ((t & 63) == 0) {
       sv[t >> 6] = best;
       si[t >> 6] = bi;
