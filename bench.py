@@ -53,7 +53,7 @@ def log(*a):
 
 def kernels_sha():
     h = hashlib.sha1()
-    for f in ("kernels.hip", "e2b_internal.h"):
+    for f in ("kernels.hip", "step1.hip", "dev_common.h", "e2b_internal.h"):
         with open(os.path.join(ROOT, "w4a16_weight_streaming_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
