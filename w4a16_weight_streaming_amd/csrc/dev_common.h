@@ -363,6 +363,73 @@ struct PrologueRegs {
   }
 };
 
+// Input slice of the one-row O product: the attention output of one head.
+// The block's K slice is head h = k0 / KS (KS = hd, K = nq * hd), and its
+// input is merged here from the (max m_c, sum l_c, unnormalised o_c) partials
+// that the attention chunks wrote for (row b, head h), instead of in a kernel
+// of its own: o = sum_c e^(m_c - M) o_c / sum_c e^(m_c - M) l_c over the chunks
+// that hold keys (M their largest m_c).  Lane c of every wave reads chunk c's
+// (m_c, l_c), so each wave forms M, the sum and the weights itself; the o
+// values of the first CB chunks are requested together with them.  Chunks
+// without keys (l_c = 0) and slots past nchunk hold stale values: they get no
+// weight and are skipped by a select, never multiplied.
+template <int KS>
+struct MergeRegs {
+  static constexpr int PT = (KS + kGemvThreads - 1) / kGemvThreads;
+  static constexpr int CB = 32 / PT;  // chunks per batch of reads
+  static_assert(kMaxChunks <= 64, "one chunk per lane");
+  float v[CB][PT];
+  float mc, lc;
+  const float* base;
+  int nchunk;
+
+  __device__ __forceinline__ void issue(int c0) {
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int c = 0; c < CB; ++c)
+#pragma unroll
+      for (int j = 0; j < PT; ++j) {
+        const int d = t + j * kGemvThreads < KS ? t + j * kGemvThreads : 0;
+        v[c][j] = c0 + c < nchunk ? base[(size_t)(c0 + c) * (KS + 2) + d] : zero_f()[d];
+      }
+  }
+
+  __device__ __forceinline__ void load(const Prologue& p, int rows, int b, int k0, int K) {
+    const int lane = threadIdx.x & 63, nq = K / KS, h = k0 / KS;
+    nchunk = p.nchunk;
+    base = p.a + (size_t)(b * nq + h) * kMaxChunks * (KS + 2);
+    const float* ml = lane < nchunk ? base + (size_t)lane * (KS + 2) + KS : zero_f();
+    mc = ml[0];
+    lc = ml[1];
+    issue(0);
+  }
+
+  __device__ __forceinline__ void finish(const Prologue&, int, int, float* xs, float*, bool) {
+    const int t = threadIdx.x, lane = t & 63;
+    const bool act = lane < nchunk && lc > 0.f;
+    const float M = wave_max(act ? mc : -INFINITY);
+    const float w = act ? expf(mc - M) : 0.f;
+    const float L = wave_sum(w * lc);
+    const float wn = L > 0.f ? w / L : 0.f;  // this lane's chunk weight
+    float o[PT];
+#pragma unroll
+    for (int j = 0; j < PT; ++j) o[j] = 0.f;
+    for (int c0 = 0; c0 < nchunk; c0 += CB) {
+      if (c0 > 0) issue(c0);
+#pragma unroll
+      for (int c = 0; c < CB; ++c) {
+        const float wc = lane_value(wn, (c0 + c) & 63);  // 0 past nchunk (lane >= nchunk)
+#pragma unroll
+        for (int j = 0; j < PT; ++j) o[j] = wc != 0.f ? fmaf(wc, v[c][j], o[j]) : o[j];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < PT; ++j)
+      if (t + j * kGemvThreads < KS) xs[t + j * kGemvThreads] = o[j];
+    __syncthreads();
+  }
+};
+
 // split an fp32 pair into a bf16 hi pair and a bf16 lo pair (x = hi + lo)
 __device__ __forceinline__ void split_pair(float a, float b, uint32_t& hi, uint32_t& lo) {
   const uint32_t ha = f2bf(a), hb = f2bf(b);

@@ -47,7 +47,9 @@ enum PrologueKind : int {
   kResNorm = 1,  // h' = (a + rms(sum_s d[s]) * gd) * scalar; x = rms(h') * gx; block 0 stores h'
   kRes = 2,      // same h', x = h'
   kGeglu = 3,    // x = gelu_tanh(a[row][k]) * a[row][I + k]   (I = K)
-  kPleGate = 4   // x = gelu_tanh(a[row][k]) * pli[row][k]
+  kPleGate = 4,  // x = gelu_tanh(a[row][k]) * pli[row][k]
+  kAttnMerge = 5 // x = attention output of head k0 / K-slice, merged from the
+                 // per-chunk partials a = AttnArgs::part (one-row O product)
 };
 
 // The prologue of each product of the decode step is fixed by its kind
@@ -56,13 +58,15 @@ enum PrologueKind : int {
 __host__ __device__ constexpr int tag_kind(int tag) {
   return tag == kTagQkv || tag == kTagGateUp || tag == kTagLmHead ? kResNorm
          : tag == kTagPleGate                                   ? kRes
-         : tag == kTagO || tag == kTagPleModel                  ? kPlain
+         : tag == kTagO                                         ? kAttnMerge
+         : tag == kTagPleModel                                  ? kPlain
          : tag == kTagDown                                      ? kGeglu
          : tag == kTagPleProj                                   ? kPleGate
                                                                 : -1;
 }
 __host__ __device__ constexpr int tag_nd(int tag) {
-  return tag == kTagPleGate ? kMaxSplitK : tag == kTagQkv || tag == kTagGateUp || tag == kTagLmHead ? 2 : 0;
+  // (gate/up: the one-row O product writes one partial per query head)
+  return tag == kTagPleGate || tag == kTagGateUp ? kMaxSplitK : tag == kTagQkv || tag == kTagLmHead ? 2 : 0;
 }
 
 struct Prologue {
@@ -80,6 +84,8 @@ struct Prologue {
   float* h_out = nullptr;            // [rows, K] (kRes*), written when d != null
   const float* pli = nullptr;        // kPleGate: row stride pli_ld
   int pli_ld = 0;
+  int nchunk = 0;                    // kAttnMerge: attention chunks written per head
+  int slice = 0;                     // kAttnMerge: head dim (the K slice of one head)
   float eps = 1e-6f;
 };
 
@@ -117,6 +123,7 @@ struct AttnArgs {
   int rope_ld = 0, rope_off = 0;
   int nq = 0, hd = 0, window = 0 /* 0: full */, chunk = 0, nchunk = 0;
   int owns = 0;                 // the layer computes K/V (raw rows hold q, k, v)
+  int combine = 1;              // merge the chunk partials into out (else the O product does)
   int qkv_parts = 1;            // qkv is the sum of this many partials
   size_t qkv_pstride = 0;       // floats between partials
   float eps = 1e-6f;

@@ -289,6 +289,8 @@ Ws ws_layout(const e2b_model* m, int R) {
     pgy_f = std::max(pgy_f, (size_t)parts(P, H) * P);
     ppo_f = std::max(ppo_f, (size_t)parts(H, P) * H);
   }
+  // the one-row O product writes one partial per head
+  oo_f = std::max(oo_f, (size_t)m->nq * H);
   const size_t u_f = (size_t)parts(LPn, H) * LPn;
   w.ncand = std::max(e2b::kLmBlocks, (m->V + 63) / 64);
   const size_t LP = (size_t)m->L * m->P;
@@ -366,7 +368,8 @@ hipError_t matmul(e2b_model* m, int quant, int tag, const Lin& W, int rows, bool
   }
   int splits = 1;
   if (!batched) {
-    splits = e2b::gemv_splits(W.K);
+    // the merged attention input comes one head (K slice) at a time
+    splits = pr.kind == e2b::kAttnMerge ? (pr.slice > 0 ? W.K / pr.slice : -1) : e2b::gemv_splits(W.K);
     // the matvec prologue reads one copy of a; it splits only K > 2048
     if (pr.na != 1 || (splits > 1 && !partial_ok)) return hipErrorInvalidValue;
     if (prof) e2b::set_launch_events(mk.a, mk.b);
@@ -613,6 +616,7 @@ int run_rows(e2b_model* m, const e2b::Rows& R, bool head, int head_row, float* d
     const LayerDev& d = m->ld[l];
     const bool owns = y.src == l;
     int nd_qkv = 1, nd_o = 1, nd_gu = 1, nd_dn = 1, nd_pg = 1;  // K-slice partials written
+    int nchunk = 0;                                             // attention chunks per head
     {  // QKV with the residual update of the previous layer fused in front
       Prologue pr;
       pr.kind = kResNorm;
@@ -673,13 +677,23 @@ int run_rows(e2b_model* m, const e2b::Rows& R, bool head, int head_row, float* d
       a.qkv_pstride = (size_t)n * d.qkv.N;
       a.eps = eps;
       attn_chunks(m, y.full, n, &a.chunk, &a.nchunk);
+      // one row: the O product merges the chunk partials itself
+      a.combine = bat ? 1 : 0;
+      nchunk = a.nchunk;
       CK(launch_attention(R, a, st), "attention");
     }
     {
       Prologue pr;
-      pr.kind = kPlain;
-      pr.a = F(W.attn);
-      pr.lda = m->nq * y.hd;
+      if (bat) {
+        pr.kind = kPlain;
+        pr.a = F(W.attn);
+        pr.lda = m->nq * y.hd;
+      } else {
+        pr.kind = kAttnMerge;
+        pr.a = F(W.part);
+        pr.nchunk = nchunk;
+        pr.slice = y.hd;
+      }
       Epilogue ep;
       ep.y = F(W.oo);
       CK(matmul(m, q, kTagO, d.o, n, bat, pr, ep, true, &nd_o, nullptr, ws, W, st), "o projection");

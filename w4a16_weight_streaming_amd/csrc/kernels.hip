@@ -205,7 +205,8 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv(Lin W, int rows, Prologue
     }
   };
 
-  PrologueRegs<KS, tag_kind(TAG), tag_nd(TAG)> pr;
+  typename std::conditional<tag_kind(TAG) == kAttnMerge, MergeRegs<KS>,
+                            PrologueRegs<KS, tag_kind(TAG), tag_nd(TAG)>>::type pr;
   pr.load(pro, rows, b, ks * KS, K);  // input reads first: they gate the compute
   // every wave's input reads enter the memory pipeline before the block's
   // weight reads (otherwise they queue behind the other waves' weights)
@@ -374,7 +375,11 @@ static hipError_t run_gemv(const Lin& W, int rows, const Prologue& pro, const Ep
 template <int WQ, int TAG>
 static hipError_t dispatch_gemv(const Lin& W, int rows, const Prologue& pro,
                                 const Epilogue& epi, int blocks_hint, int* bo, hipStream_t st) {
-  switch (gemv_slice(W.K)) {
+  // the merged attention input comes one head per K slice
+  switch (pro.kind == kAttnMerge ? pro.slice : gemv_slice(W.K)) {
+    case 64:
+      if (pro.kind != kAttnMerge) return hipErrorInvalidValue;
+      return run_gemv<WQ, 64, 4, TAG>(W, rows, pro, epi, blocks_hint, bo, st);
     case 32: return run_gemv<WQ, 32, 4, TAG>(W, rows, pro, epi, blocks_hint, bo, st);
     case 128: return run_gemv<WQ, 128, 4, TAG>(W, rows, pro, epi, blocks_hint, bo, st);
     case 256: return run_gemv<WQ, 256, 4, TAG>(W, rows, pro, epi, blocks_hint, bo, st);
@@ -405,6 +410,10 @@ hipError_t launch_gemv(int quant, int tag, const Lin& W, int rows, const Prologu
                        const Epilogue& epi, int blocks_hint, int* blocks_out, hipStream_t st) {
   if (rows < 1 || rows > 65535) return hipErrorInvalidValue;
   if ((pro.kind == kRes || pro.kind == kResNorm) && gemv_slice(W.K) != W.K)
+    return hipErrorInvalidValue;
+  if (pro.kind == kAttnMerge &&
+      (tag != kTagO || !pro.a || pro.slice < 64 || W.K % pro.slice != 0 || W.K / pro.slice > kMaxHeads ||
+       pro.nchunk < 1 || pro.nchunk > kMaxChunks))
     return hipErrorInvalidValue;
   if (epi.argmax && gemv_splits(W.K) != 1) return hipErrorInvalidValue;
   if (epi.argmax && quant) return hipErrorInvalidValue;  // the tied lm_head is bf16
@@ -478,7 +487,7 @@ hipError_t launch_attention(const Rows& R, const AttnArgs& a, hipStream_t st) {
     default: return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || !a.combine) return e;
   hipLaunchKernelGGL(k_attn_combine, dim3(R.n, a.nq), dim3(256), 0, st, a);
   return hipGetLastError();
 }
