@@ -65,8 +65,11 @@ __host__ __device__ constexpr int tag_kind(int tag) {
                                                                 : -1;
 }
 __host__ __device__ constexpr int tag_nd(int tag) {
-  // (gate/up: the one-row O product writes one partial per query head)
-  return tag == kTagPleGate || tag == kTagGateUp ? kMaxSplitK : tag == kTagQkv || tag == kTagLmHead ? 2 : 0;
+  // (gate/up: the one-row O product writes one partial per query head; PLE
+  // gate: the down product of a batched pass writes up to kMaxGemmSplit)
+  return tag == kTagPleGate ? kMaxGemmSplit
+         : tag == kTagGateUp ? kMaxSplitK
+         : tag == kTagQkv || tag == kTagLmHead ? 2 : 0;
 }
 
 struct Prologue {

@@ -367,6 +367,12 @@ hipError_t matmul(e2b_model* m, int quant, int tag, const Lin& W, int rows, bool
     if (e != hipSuccess) return e;
   }
   int splits = 1;
+  // The per-layer input gate and projection (256 x H and H x 256, under 1 MB)
+  // run through the matvec kernel for any number of rows: each row re-reads
+  // the weights from L2, which costs less than the input-prep kernel and the
+  // fixed cost of a matrix-core pass; a row's result still does not depend on
+  // the other rows of its pass.
+  if (tag == e2b::kTagPleGate || tag == e2b::kTagPleProj) batched = false;
   if (!batched) {
     // the merged attention input comes one head (K slice) at a time
     splits = pr.kind == e2b::kAttnMerge ? (pr.slice > 0 ? W.K / pr.slice : -1) : e2b::gemv_splits(W.K);
