@@ -16,7 +16,8 @@ constexpr int kLmBlocks = 1024;  // blocks of the lm_head pass (argmax candidate
 // Matrix kinds; each gets its own kernel symbol so profiles tell them apart.
 enum : int {
   kTagOther = 0, kTagQkv, kTagO, kTagGateUp, kTagDown, kTagPleGate, kTagPleProj, kTagPleModel,
-  kTagLmHead
+  kTagLmHead,
+  kTagPleGateRows = 10  // the PLE gate of a batched pass (matvec per row; more input partials)
 };
 
 // Device error word bits (first 16 bytes of the workspace).
@@ -57,7 +58,7 @@ enum PrologueKind : int {
 // tag_nd: most K-slice partials of the residual delta that prologue sums.
 __host__ __device__ constexpr int tag_kind(int tag) {
   return tag == kTagQkv || tag == kTagGateUp || tag == kTagLmHead ? kResNorm
-         : tag == kTagPleGate                                   ? kRes
+         : tag == kTagPleGate || tag == kTagPleGateRows         ? kRes
          : tag == kTagO                                         ? kAttnMerge
          : tag == kTagPleModel                                  ? kPlain
          : tag == kTagDown                                      ? kGeglu
@@ -65,10 +66,12 @@ __host__ __device__ constexpr int tag_kind(int tag) {
                                                                 : -1;
 }
 __host__ __device__ constexpr int tag_nd(int tag) {
-  // (gate/up: the one-row O product writes one partial per query head; PLE
-  // gate: the down product of a batched pass writes up to kMaxGemmSplit)
-  return tag == kTagPleGate ? kMaxGemmSplit
-         : tag == kTagGateUp ? kMaxSplitK
+  // (gate/up: the one-row O product writes one partial per query head; the
+  // PLE gate of a batched pass: the matrix-core down product's partials.  A
+  // specialised prologue reads every slot, so each kind gets only as many as
+  // its producer writes)
+  return tag == kTagPleGateRows ? kMaxGemmSplit
+         : tag == kTagPleGate || tag == kTagGateUp ? kMaxSplitK
          : tag == kTagQkv || tag == kTagLmHead ? 2 : 0;
 }
 

@@ -372,14 +372,18 @@ hipError_t matmul(e2b_model* m, int quant, int tag, const Lin& W, int rows, bool
   // the weights from L2, which costs less than the input-prep kernel and the
   // fixed cost of a matrix-core pass; a row's result still does not depend on
   // the other rows of its pass.
-  if (tag == e2b::kTagPleGate || tag == e2b::kTagPleProj) batched = false;
+  int gemv_tag = tag;
+  if (tag == e2b::kTagPleGate || tag == e2b::kTagPleProj) {
+    if (batched && tag == e2b::kTagPleGate) gemv_tag = e2b::kTagPleGateRows;
+    batched = false;
+  }
   if (!batched) {
     // the merged attention input comes one head (K slice) at a time
     splits = pr.kind == e2b::kAttnMerge ? (pr.slice > 0 ? W.K / pr.slice : -1) : e2b::gemv_splits(W.K);
     // the matvec prologue reads one copy of a; it splits only K > 2048
     if (pr.na != 1 || (splits > 1 && !partial_ok)) return hipErrorInvalidValue;
     if (prof) e2b::set_launch_events(mk.a, mk.b);
-    e = e2b::launch_gemv(quant, tag, W, rows, pr, ep, 0, nblk, st);
+    e = e2b::launch_gemv(quant, gemv_tag, W, rows, pr, ep, 0, nblk, st);
   } else {
     const e2b::GemmPlan plan = e2b::gemm_plan(quant, W.N, W.K, partial_ok);
     splits = plan.nks;

@@ -399,6 +399,7 @@ static hipError_t dispatch_tag(int tag, const Lin& W, int rows, const Prologue& 
     case kTagGateUp: return dispatch_gemv<WQ, kTagGateUp>(W, rows, pro, epi, blocks_hint, bo, st);
     case kTagDown: return dispatch_gemv<WQ, kTagDown>(W, rows, pro, epi, blocks_hint, bo, st);
     case kTagPleGate: return dispatch_gemv<WQ, kTagPleGate>(W, rows, pro, epi, blocks_hint, bo, st);
+    case kTagPleGateRows: return dispatch_gemv<WQ, kTagPleGateRows>(W, rows, pro, epi, blocks_hint, bo, st);
     case kTagPleProj: return dispatch_gemv<WQ, kTagPleProj>(W, rows, pro, epi, blocks_hint, bo, st);
     case kTagPleModel: return dispatch_gemv<WQ, kTagPleModel>(W, rows, pro, epi, blocks_hint, bo, st);
     case kTagLmHead: return dispatch_gemv<WQ, kTagLmHead>(W, rows, pro, epi, blocks_hint, bo, st);
