@@ -24,11 +24,15 @@ enum : int {
 enum : int { kErrToken = 1, kErrPos = 2, kErrSync = 4 };
 
 // One linear layer resident in the weight arena.  bf16: w [N, K].
-// W4A16: q [N, K/8] packed int4 codes, s [N, K/32] bf16 group scales.
+// W4A16: q [N, K/8] packed int4 codes, s [N, K/32] bf16 group scales, and
+// optionally the same words and scales in matrix-core fragment order (tq, ts:
+// see launch_tile_w4), which the batched products read.
 struct Lin {
   const uint16_t* w = nullptr;
   const uint32_t* q = nullptr;
   const uint16_t* s = nullptr;
+  const uint32_t* tq = nullptr;
+  const uint16_t* ts = nullptr;
   int N = 0, K = 0;
 };
 
@@ -163,6 +167,13 @@ hipError_t launch_gemv(int quant, int tag, const Lin& W, int rows, const Prologu
                        const Epilogue& epi, int blocks_hint, int* blocks_out, hipStream_t st);
 int gemv_splits(int K);
 bool gemv_supported(int K);  // K is one of the widths the matvec kernel handles
+// W4A16 words and scales in the order the matrix-core product consumes
+// them (N % 16 == 0): for column tile t (columns 16t .. 16t+15) and 32-group
+// g, the 64 words tq[(t * K/32 + g) * 64 + l] = q[16t + l % 16][4g + l / 16]
+// (the B fragment of one MFMA step, lane l) and the 16 scales
+// ts[(t * K/32 + g) * 16 + c] = s[16t + c][g].  A wave's weight reads are
+// then 256 contiguous bytes per step instead of 16 pieces of 16 bytes.
+hipError_t launch_tile_w4(const Lin& W, uint32_t* tq, uint16_t* ts, hipStream_t st);
 hipError_t launch_qkv_post(const Rows& R, const QkvPostArgs& a, hipStream_t st);
 hipError_t launch_attention(const Rows& R, const AttnArgs& a, hipStream_t st);
 hipError_t launch_advance(int32_t* pos, int n, hipStream_t st);

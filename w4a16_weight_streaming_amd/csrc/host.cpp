@@ -46,6 +46,8 @@ struct LayerInfo {
 
 struct LinOff {  // a linear layer as offsets into the arena
   size_t w = 0, q = 0, s = 0;
+  bool tiled = false;   // W4A16: a copy tiled for the matrix cores at tq, ts
+  size_t tq = 0, ts = 0;
   int N = 0, K = 0;
 };
 
@@ -160,8 +162,10 @@ struct Planner {
     copy(name, E2B_DTYPE_BF16, 2, r, c, o, r * c * 2);
     return o;
   }
-  // linears stacked along N into one matrix [sum N, K]
-  LinOff lin(const std::vector<std::string>& names, const std::vector<int>& Ns, int K) {
+  // linears stacked along N into one matrix [sum N, K]; tiled: W4A16 also
+  // keeps a copy in the matrix-core fragment order (batched passes)
+  LinOff lin(const std::vector<std::string>& names, const std::vector<int>& Ns, int K,
+             bool tiled = true) {
     LinOff L;
     int N = 0;
     for (int n : Ns) N += n;
@@ -177,6 +181,11 @@ struct Planner {
     } else {
       L.q = alloc((size_t)N * K / 2);
       L.s = alloc((size_t)N * (K / 32) * 2);
+      if (tiled && N % 16 == 0) {
+        L.tiled = true;
+        L.tq = alloc((size_t)N * K / 2);
+        L.ts = alloc((size_t)N * (K / 32) * 2);
+      }
       size_t r = 0;
       for (size_t i = 0; i < names.size(); ++i) {
         copy(names[i] + "_packed", E2B_DTYPE_INT32, 2, Ns[i], K / 8, L.q + r * K / 2,
@@ -218,8 +227,9 @@ int build_plan(e2b_model* m) {
     o.gu = p.lin({pre + "mlp.gate_proj.weight", pre + "mlp.up_proj.weight"}, {y.I, y.I}, H);
     o.down = p.lin({pre + "mlp.down_proj.weight"}, {H}, y.I);
     o.g_ff = p.vec(pre + "post_feedforward_layernorm.weight", H);
-    o.pg = p.lin({pre + "per_layer_input_gate.weight"}, {P}, H);
-    o.pp = p.lin({pre + "per_layer_projection.weight"}, {H}, P);
+    // (the per-layer input gate and projection always run on the matvec kernel)
+    o.pg = p.lin({pre + "per_layer_input_gate.weight"}, {P}, H, false);
+    o.pp = p.lin({pre + "per_layer_projection.weight"}, {H}, P, false);
     o.g_pple = p.vec(pre + "post_per_layer_input_norm.weight", H);
     o.scalar = p.vec(pre + "layer_scalar", 1);
   }
@@ -251,6 +261,10 @@ Lin resolve(const e2b_model* m, const LinOff& o) {
   } else {
     L.q = reinterpret_cast<const uint32_t*>(m->arena + o.q);
     L.s = reinterpret_cast<const uint16_t*>(m->arena + o.s);
+    if (o.tiled) {
+      L.tq = reinterpret_cast<const uint32_t*>(m->arena + o.tq);
+      L.ts = reinterpret_cast<const uint16_t*>(m->arena + o.ts);
+    }
   }
   return L;
 }
@@ -1025,6 +1039,19 @@ int e2b_load_weights(e2b_model* m, const e2b_tensor* t, int n, void* d_arena, si
     d.g_pple = U(o.g_pple);
     d.scalar = U(o.scalar);
   }
+  // the matrix-core copies of the W4A16 linears, tiled on the device
+  auto tile = [&](const LinOff& o) -> hipError_t {
+    if (!o.tiled) return hipSuccess;
+    const Lin W = resolve(m, o);
+    return e2b::launch_tile_w4(W, reinterpret_cast<uint32_t*>(A + o.tq),
+                               reinterpret_cast<uint16_t*>(A + o.ts), st);
+  };
+  CK(tile(m->plmp_off), "weight tiling");
+  for (int l = 0; l < m->L; ++l) {
+    const LayerOff& o = m->lo[l];
+    for (const LinOff* x : {&o.qkv, &o.o, &o.gu, &o.down, &o.pg, &o.pp}) CK(tile(*x), "weight tiling");
+  }
+  CK(hipStreamSynchronize(st), "weight tiling sync");
   m->loaded = true;
   return upload_step_plan(m);
 }

@@ -493,6 +493,26 @@ hipError_t launch_attention(const Rows& R, const AttnArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+__global__ __launch_bounds__(256) void k_tile_w4(const uint32_t* __restrict__ q,
+                                                 const uint16_t* __restrict__ s, int N, int K,
+                                                 uint32_t* __restrict__ tq, uint16_t* __restrict__ ts) {
+  const size_t G = K / 32, n_words = (size_t)N * K / 8;
+  for (size_t i = blockIdx.x * (size_t)256 + threadIdx.x; i < n_words; i += (size_t)gridDim.x * 256) {
+    const size_t l = i % 64, tg = i / 64, t = tg / G, g = tg % G;
+    tq[i] = q[(16 * t + l % 16) * (K / 8) + 4 * g + l / 16];
+    if (l < 16) ts[tg * 16 + l] = s[(16 * t + l) * G + g];
+  }
+}
+
+hipError_t launch_tile_w4(const Lin& W, uint32_t* tq, uint16_t* ts, hipStream_t st) {
+  if (!W.q || !W.s || !tq || !ts || W.N % 16 || W.K % 32 || W.N < 16) return hipErrorInvalidValue;
+  const size_t n_words = (size_t)W.N * W.K / 8;
+  size_t blocks = (n_words + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  hipLaunchKernelGGL(k_tile_w4, dim3((unsigned)blocks), dim3(256), 0, st, W.q, W.s, W.N, W.K, tq, ts);
+  return hipGetLastError();
+}
+
 // ===================================================== batched rows: MFMA path
 // For rows >= 2 (batched decode, prefill) the input rows are prepared once by
 // k_xprep (the same prologue arithmetic as the single-row matvec, K-slice
@@ -781,8 +801,13 @@ __global__ __launch_bounds__(256, 2) void k_gemm(Lin W, int rows, GemmA A, int K
         const bool ok = ncol[j] < N;
         const size_t row = ok ? (size_t)ncol[j] : 0;
         if constexpr (WQ) {
-          const uint32_t qv = W.q[row * (K / 8) + (kc + 32 * s) / 8 + kq];
-          const float sv = bf2f(W.s[row * (K / 32) + (kc + 32 * s) / 32]);
+          // (the tiled copy when there is one: the same word, 256 contiguous
+          // bytes per wave; the address is selected, the load is not)
+          const size_t g = (size_t)(kc + 32 * s) / 32, tile = row / 16;
+          const uint32_t* qp = W.tq ? W.tq + (tile * (K / 32) + g) * 64 + lane : W.q + row * (K / 8) + 4 * g + kq;
+          const uint16_t* sp = W.ts ? W.ts + (tile * (K / 32) + g) * 16 + (lane & 15) : W.s + row * (K / 32) + g;
+          const uint32_t qv = *qp;
+          const float sv = bf2f(*sp);
           bq[buf][s][j] = ok ? qv : 0x88888888u;
           bs[buf][s][j] = ok ? sv : 0.f;
         } else {
