@@ -319,7 +319,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=512)
     ap.add_argument("--warmup", type=int, default=8)
-    ap.add_argument("--quant", choices=["bf16", "w4a16"], default="bf16")
+    ap.add_argument("--quant", choices=["bf16", "w4a16"], default=None,
+                    help="weights (default bf16; w4a16 with --long)")
     ap.add_argument("--batch", type=int, default=1)
     ap.add_argument("--prompt", type=int, default=128)
     ap.add_argument("--eager", action="store_true", help="launch kernels per step instead of a graph")
@@ -347,6 +348,8 @@ def main():
         torch.cuda.synchronize()
         log("copy calibration: 1 GiB read + 1 GiB written by one elementwise kernel")
         del src, dst
+    if args.quant is None:
+        args.quant = "w4a16" if args.long else "bf16"
     if args.long:
         long_context(args)
         return
