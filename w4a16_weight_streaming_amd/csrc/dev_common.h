@@ -976,7 +976,19 @@ __device__ void attn_combine(const AttnArgs& a, int r, int h) {
       o3 = fmaf(wn[cc + 3], ld32<COH>(part + (size_t)(cc + 3) * (hd + 2) + d), o3);
     }
     for (; cc < nact; ++cc) o0 = fmaf(wn[cc], ld32<COH>(part + (size_t)cc * (hd + 2) + d), o0);
-    st32<COH>(a.out + (size_t)r * a.nq * hd + (size_t)h * hd + d, (o0 + o1) + (o2 + o3));
+    const float v = (o0 + o1) + (o2 + o3);
+    if (a.xh) {  // the O product's prepared input: hi + lo = v, group sums of 32
+      const size_t K = (size_t)a.nq * hd, i = (size_t)r * K + (size_t)h * hd + d;
+      const uint32_t hb = f2bf(v), lb = f2bf(v - bf2f(hb));
+      a.xh[i] = (uint16_t)hb;
+      a.xl[i] = (uint16_t)lb;
+      // (32 consecutive d are the lanes of one half wave: hd is a multiple of
+      // 64, so a wave is either whole in this loop or has left it)
+      const float gs = lanes_sum<32>(bf2f(hb) + bf2f(lb));
+      if ((d & 31) == 0) a.xg[i / 32] = gs;
+    } else {
+      st32<COH>(a.out + (size_t)r * a.nq * hd + (size_t)h * hd + d, v);
+    }
   }
 }
 

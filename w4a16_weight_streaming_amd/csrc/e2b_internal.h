@@ -53,8 +53,10 @@ enum PrologueKind : int {
   kRes = 2,      // same h', x = h'
   kGeglu = 3,    // x = gelu_tanh(a[row][k]) * a[row][I + k]   (I = K)
   kPleGate = 4,  // x = gelu_tanh(a[row][k]) * pli[row][k]
-  kAttnMerge = 5 // x = attention output of head k0 / K-slice, merged from the
-                 // per-chunk partials a = AttnArgs::part (one-row O product)
+  kAttnMerge = 5, // x = attention output of head k0 / K-slice, merged from the
+                  // per-chunk partials a = AttnArgs::part (one-row O product)
+  kPrepared = 6   // batched products only: the input rows are already in the
+                  // workspace's prepared form (bf16 hi/lo + group sums)
 };
 
 // The prologue of each product of the decode step is fixed by its kind
@@ -129,6 +131,9 @@ struct AttnArgs {
   uint16_t* vc_own = nullptr;   // K/V); null when the layer shares or the K/V are already written
   float* part = nullptr;        // [rows][nq][kMaxChunks][hd + 2]
   float* out = nullptr;         // [rows][nq * hd]
+  uint16_t* xh = nullptr;       // non-null: the merge writes its output as the O product's
+  uint16_t* xl = nullptr;       // prepared input instead (bf16 hi/lo [rows][nq * hd],
+  float* xg = nullptr;          // sums of hi + lo per 32-group [rows][nq * hd / 32])
   const float* rope = nullptr;  // RoPE table rows (rope_ld floats each), this type at rope_off
   int rope_ld = 0, rope_off = 0;
   int nq = 0, hd = 0, window = 0 /* 0: full */, chunk = 0, nchunk = 0;

@@ -406,6 +406,10 @@ hipError_t matmul(e2b_model* m, int quant, int tag, const Lin& W, int rows, bool
       A.a = pr.a;
       A.kind = pr.kind;
       A.lda = pr.lda;
+    } else if (pr.kind == e2b::kPrepared) {  // written in prepared form by the producer
+      A.xh = reinterpret_cast<uint16_t*>(ws + L.xh);
+      A.xl = reinterpret_cast<uint16_t*>(ws + L.xl);
+      A.xg = reinterpret_cast<float*>(ws + L.xg);
     } else {
       A.xh = reinterpret_cast<uint16_t*>(ws + L.xh);
       A.xl = reinterpret_cast<uint16_t*>(ws + L.xl);
@@ -701,17 +705,21 @@ int run_rows(e2b_model* m, const e2b::Rows& R, bool head, int head_row, float* d
       a.qkv_pstride = (size_t)n * d.qkv.N;
       a.eps = eps;
       attn_chunks(m, y.full, n, &a.chunk, &a.nchunk);
-      // one row: the O product merges the chunk partials itself
+      // one row: the O product merges the chunk partials itself; batched: the
+      // merge writes the O product's prepared input
       a.combine = bat ? 1 : 0;
+      if (bat) {
+        a.xh = reinterpret_cast<uint16_t*>(ws + W.xh);
+        a.xl = reinterpret_cast<uint16_t*>(ws + W.xl);
+        a.xg = F(W.xg);
+      }
       nchunk = a.nchunk;
       CK(launch_attention(R, a, st), "attention");
     }
     {
       Prologue pr;
       if (bat) {
-        pr.kind = kPlain;
-        pr.a = F(W.attn);
-        pr.lda = m->nq * y.hd;
+        pr.kind = kPrepared;
       } else {
         pr.kind = kAttnMerge;
         pr.a = F(W.part);

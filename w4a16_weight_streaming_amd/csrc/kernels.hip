@@ -1055,6 +1055,7 @@ static hipError_t gemm_tag(int tag, const Lin& W, int rows, const GemmA& A, int 
     }
   }
   switch (tag) {
+    case kTagO: return run_gemm<WQ, NT, 0, kTagO>(W, rows, A, nks, epi, nblk, st);
     case kTagQkv: return run_gemm<WQ, NT, 0, kTagQkv>(W, rows, A, nks, epi, nblk, st);
     case kTagGateUp: return run_gemm<WQ, NT, 0, kTagGateUp>(W, rows, A, nks, epi, nblk, st);
     case kTagDown: return run_gemm<WQ, NT, 0, kTagDown>(W, rows, A, nks, epi, nblk, st);
