@@ -108,12 +108,16 @@ def pmc_traffic(kernel_symbol):
 
 
 # kernel symbol (as rocprof names it) of each kind, by quant and batch path
+# (one row: o is one K slice per head, the sliding layers' 256 named here)
 def kernel_symbol(kind, quant, batch):
     tag = {"qkv": 1, "o": 2, "gate_up": 3, "down": 4, "lm_head": 8}[kind]
     if batch == 1:
         wq = 0 if kind == "lm_head" else int(quant == "w4a16")
-        ks = {"o": 2048, "down": 2048}.get(kind, 1536)
-        u = 2 if (wq and ks == 1536) or ks == 2048 else 4
+        ks = {"o": 256, "down": 2048}.get(kind, 1536)
+        if ks == 1536:
+            u = (3 if kind == "gate_up" else 2) if wq else 4
+        else:
+            u = 2 if ks == 2048 else 4
         return f"void e2b::k_gemv<{wq}, {ks}, {u}, {tag}>"
     return None
 

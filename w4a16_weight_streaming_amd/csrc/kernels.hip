@@ -384,7 +384,9 @@ static hipError_t dispatch_gemv(const Lin& W, int rows, const Prologue& pro,
     case 128: return run_gemv<WQ, 128, 4, TAG>(W, rows, pro, epi, blocks_hint, bo, st);
     case 256: return run_gemv<WQ, 256, 4, TAG>(W, rows, pro, epi, blocks_hint, bo, st);
     case 512: return run_gemv<WQ, 512, 4, TAG>(W, rows, pro, epi, blocks_hint, bo, st);
-    case 1536: return run_gemv<WQ, 1536, WQ ? 2 : 4, TAG>(W, rows, pro, epi, blocks_hint, bo, st);
+    // (W4A16 gate/up: the double-width layers give each wave three units, one
+    // batch of three instead of two dependent round trips)
+    case 1536: return run_gemv<WQ, 1536, WQ ? (TAG == kTagGateUp ? 3 : 2) : 4, TAG>(W, rows, pro, epi, blocks_hint, bo, st);
     case 2048: return run_gemv<WQ, 2048, 2, TAG>(W, rows, pro, epi, blocks_hint, bo, st);
     default: return hipErrorInvalidValue;
   }
