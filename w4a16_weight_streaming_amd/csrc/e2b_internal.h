@@ -24,11 +24,12 @@ enum : int {
 enum : int { kErrToken = 1, kErrPos = 2, kErrSync = 4 };
 
 // One linear layer resident in the weight arena.  bf16: w [N, K].
-// W4A16: q [N, K/8] packed int4 codes, s [N, K/32] bf16 group scales, and
-// optionally the same words and scales in matrix-core fragment order (tq, ts:
-// see launch_tile_w4), which the batched products read.
+// W4A16: q [N, K/8] packed int4 codes, s [N, K/32] bf16 group scales.  Both
+// optionally also in matrix-core fragment order (tw, or tq and ts: see
+// launch_tile_bf16 / launch_tile_w4), which the batched products read.
 struct Lin {
   const uint16_t* w = nullptr;
+  const uint16_t* tw = nullptr;
   const uint32_t* q = nullptr;
   const uint16_t* s = nullptr;
   const uint32_t* tq = nullptr;
@@ -179,6 +180,10 @@ bool gemv_supported(int K);  // K is one of the widths the matvec kernel handles
 // ts[(t * K/32 + g) * 16 + c] = s[16t + c][g].  A wave's weight reads are
 // then 256 contiguous bytes per step instead of 16 pieces of 16 bytes.
 hipError_t launch_tile_w4(const Lin& W, uint32_t* tq, uint16_t* ts, hipStream_t st);
+// The same for bf16 weights (N % 16 == 0): for column tile t and 32-step g,
+// the 64 lanes' 16-byte B fragments tw[((t * K/32 + g) * 64 + l) * 8 + e] =
+// w[16t + l % 16][32g + 8 (l / 16) + e], one contiguous kilobyte per step.
+hipError_t launch_tile_bf16(const Lin& W, uint16_t* tw, hipStream_t st);
 hipError_t launch_qkv_post(const Rows& R, const QkvPostArgs& a, hipStream_t st);
 hipError_t launch_attention(const Rows& R, const AttnArgs& a, hipStream_t st);
 hipError_t launch_advance(int32_t* pos, int n, hipStream_t st);

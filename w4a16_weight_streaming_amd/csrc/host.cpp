@@ -46,8 +46,8 @@ struct LayerInfo {
 
 struct LinOff {  // a linear layer as offsets into the arena
   size_t w = 0, q = 0, s = 0;
-  bool tiled = false;   // W4A16: a copy tiled for the matrix cores at tq, ts
-  size_t tq = 0, ts = 0;
+  bool tiled = false;   // a copy tiled for the matrix cores: tw (bf16) or tq, ts (W4A16)
+  size_t tw = 0, tq = 0, ts = 0;
   int N = 0, K = 0;
 };
 
@@ -80,12 +80,14 @@ struct e2b_model {
   std::vector<Copy> plan;
   size_t arena_bytes = 0, weight_bytes = 0;
   size_t off_embed = 0, off_ple = 0, off_plpn = 0, off_final = 0, off_invf[2] = {0, 0};
+  size_t off_embed_t = 0;  // the tied embedding tiled for the batched lm_head (0: none)
   LinOff plmp_off;
   std::vector<LayerOff> lo;
   // device views (valid after load)
   char* arena = nullptr;
   bool loaded = false;
   const uint16_t *embed = nullptr, *ple = nullptr, *g_plpn = nullptr, *g_final = nullptr;
+  const uint16_t* embed_t = nullptr;
   const double* invf[2] = {nullptr, nullptr};
   Lin plmp;
   std::vector<LayerDev> ld;
@@ -162,8 +164,8 @@ struct Planner {
     copy(name, E2B_DTYPE_BF16, 2, r, c, o, r * c * 2);
     return o;
   }
-  // linears stacked along N into one matrix [sum N, K]; tiled: W4A16 also
-  // keeps a copy in the matrix-core fragment order (batched passes)
+  // linears stacked along N into one matrix [sum N, K]; tiled: also keep a
+  // copy in the matrix-core fragment order (batched passes)
   LinOff lin(const std::vector<std::string>& names, const std::vector<int>& Ns, int K,
              bool tiled = true) {
     LinOff L;
@@ -173,6 +175,10 @@ struct Planner {
     L.K = K;
     if (m->quant == E2B_QUANT_BF16) {
       L.w = alloc((size_t)N * K * 2);
+      if (tiled && N % 16 == 0) {
+        L.tiled = true;
+        L.tw = alloc((size_t)N * K * 2);
+      }
       size_t r = 0;
       for (size_t i = 0; i < names.size(); ++i) {
         copy(names[i], E2B_DTYPE_BF16, 2, Ns[i], K, L.w + r * K * 2, (size_t)Ns[i] * K * 2);
@@ -203,6 +209,7 @@ int build_plan(e2b_model* m) {
   Planner p{m};
   const int L = m->L, H = m->H, P = m->P, V = m->V, nq = m->nq;
   m->off_embed = p.mat("model.embed_tokens.weight", V, H);
+  if (V % 16 == 0) m->off_embed_t = p.alloc((size_t)V * H * 2);
   m->off_ple = p.mat("model.embed_tokens_per_layer.weight", V, (int64_t)L * P);
   m->plmp_off = p.lin({"model.per_layer_model_projection.weight"}, {L * P}, H);
   m->off_plpn = p.vec("model.per_layer_projection_norm.weight", P);
@@ -258,6 +265,7 @@ Lin resolve(const e2b_model* m, const LinOff& o) {
   L.K = o.K;
   if (m->quant == E2B_QUANT_BF16) {
     L.w = reinterpret_cast<const uint16_t*>(m->arena + o.w);
+    if (o.tiled) L.tw = reinterpret_cast<const uint16_t*>(m->arena + o.tw);
   } else {
     L.q = reinterpret_cast<const uint32_t*>(m->arena + o.q);
     L.s = reinterpret_cast<const uint16_t*>(m->arena + o.s);
@@ -798,6 +806,7 @@ int run_rows(e2b_model* m, const e2b::Rows& R, bool head, int head_row, float* d
   const int nh = head_row < 0 ? n : 1;
   Lin E;
   E.w = m->embed;
+  E.tw = m->embed_t;
   E.N = m->V;
   E.K = H;
   Prologue pr;
@@ -1047,14 +1056,25 @@ int e2b_load_weights(e2b_model* m, const e2b_tensor* t, int n, void* d_arena, si
     d.g_pple = U(o.g_pple);
     d.scalar = U(o.scalar);
   }
-  // the matrix-core copies of the W4A16 linears, tiled on the device
+  // the matrix-core copies of the linears (and of the tied embedding, for the
+  // batched lm_head), tiled on the device
   auto tile = [&](const LinOff& o) -> hipError_t {
     if (!o.tiled) return hipSuccess;
     const Lin W = resolve(m, o);
+    if (m->quant == E2B_QUANT_BF16) return e2b::launch_tile_bf16(W, reinterpret_cast<uint16_t*>(A + o.tw), st);
     return e2b::launch_tile_w4(W, reinterpret_cast<uint32_t*>(A + o.tq),
                                reinterpret_cast<uint16_t*>(A + o.ts), st);
   };
   CK(tile(m->plmp_off), "weight tiling");
+  m->embed_t = nullptr;
+  if (m->off_embed_t) {
+    Lin E;
+    E.w = m->embed;
+    E.N = m->V;
+    E.K = m->H;
+    CK(e2b::launch_tile_bf16(E, reinterpret_cast<uint16_t*>(A + m->off_embed_t), st), "embedding tiling");
+    m->embed_t = U(m->off_embed_t);
+  }
   for (int l = 0; l < m->L; ++l) {
     const LayerOff& o = m->lo[l];
     for (const LinOff* x : {&o.qkv, &o.o, &o.gu, &o.down, &o.pg, &o.pp}) CK(tile(*x), "weight tiling");

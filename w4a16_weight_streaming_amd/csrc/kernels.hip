@@ -506,6 +506,25 @@ __global__ __launch_bounds__(256) void k_tile_w4(const uint32_t* __restrict__ q,
   }
 }
 
+__global__ __launch_bounds__(256) void k_tile_bf16(const uint4* __restrict__ w, int N, int K,
+                                                   uint4* __restrict__ tw) {
+  const size_t G = K / 32, n = (size_t)N * K / 8;  // 16-byte pieces
+  for (size_t i = blockIdx.x * (size_t)256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
+    const size_t l = i % 64, tg = i / 64, t = tg / G, g = tg % G;
+    tw[i] = w[(16 * t + l % 16) * (K / 8) + 4 * g + l / 16];
+  }
+}
+
+hipError_t launch_tile_bf16(const Lin& W, uint16_t* tw, hipStream_t st) {
+  if (!W.w || !tw || W.N % 16 || W.K % 32 || W.N < 16) return hipErrorInvalidValue;
+  const size_t n = (size_t)W.N * W.K / 8;
+  size_t blocks = (n + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  hipLaunchKernelGGL(k_tile_bf16, dim3((unsigned)blocks), dim3(256), 0, st,
+                     reinterpret_cast<const uint4*>(W.w), W.N, W.K, reinterpret_cast<uint4*>(tw));
+  return hipGetLastError();
+}
+
 hipError_t launch_tile_w4(const Lin& W, uint32_t* tq, uint16_t* ts, hipStream_t st) {
   if (!W.q || !W.s || !tq || !ts || W.N % 16 || W.K % 32 || W.N < 16) return hipErrorInvalidValue;
   const size_t n_words = (size_t)W.N * W.K / 8;
@@ -813,7 +832,10 @@ __global__ __launch_bounds__(256, 2) void k_gemm(Lin W, int rows, GemmA A, int K
           bq[buf][s][j] = ok ? qv : 0x88888888u;
           bs[buf][s][j] = ok ? sv : 0.f;
         } else {
-          uint4 v = *reinterpret_cast<const uint4*>(W.w + row * K + kc + 32 * s + 8 * kq);
+          // (the tiled copy when there is one: one contiguous kilobyte per wave)
+          const size_t g = (size_t)(kc + 32 * s) / 32, tile = row / 16;
+          const uint16_t* wp = W.tw ? W.tw + ((tile * (K / 32) + g) * 64 + lane) * 8 : W.w + row * K + kc + 32 * s + 8 * kq;
+          uint4 v = *reinterpret_cast<const uint4*>(wp);
           if (!ok) v = make_uint4(0, 0, 0, 0);
           bw[buf][s][j] = v;
         }
@@ -1019,11 +1041,18 @@ __global__ __launch_bounds__(256, 2) void k_gemm(Lin W, int rows, GemmA A, int K
 // Enough blocks to cover the chip: narrower column tiles first, then (where
 // the consumer sums partials) K slices of >= 256.
 GemmPlan gemm_plan(int quant, int N, int K, bool partial_ok) {
-  constexpr int kTarget = 256;  // 512 / 1024 blocks, or 128-column minimum tiles: no better
+  constexpr int kTarget = 256;  // (512 or 1024 target blocks: no better)
   GemmPlan p;
-  p.nt = quant ? 4 : 2;
-  const int nt_min = quant ? 2 : 1;
   auto cols = [&](int nt) { return (N + 64 * nt - 1) / (64 * nt); };
+  // Two column tiles per wave where the product still fills the chip with
+  // its K split (each activation fragment read from LDS then feeds two
+  // products, half the LDS traffic per weight byte); bf16 products too narrow
+  // for that (q/k/v, the sliding layers' O) keep one.
+  int kmax = 1;
+  for (int c : {2, 3, 4, 6, 8, 12, 16})
+    if (K % (32 * c) == 0 && K / c >= 256) kmax = c;
+  p.nt = quant ? 4 : 2;
+  const int nt_min = quant || cols(2) * (partial_ok ? kmax : 1) >= 192 ? 2 : 1;
   while (p.nt > nt_min && cols(p.nt) < kTarget) p.nt >>= 1;
   p.nks = 1;
   if (partial_ok) {
