@@ -123,10 +123,10 @@ int e2b_kv_share_map(const e2b_model* model, int32_t* out);
 size_t e2b_weight_bytes(const e2b_model* model);
 
 /* Device bytes e2b_load_weights needs in its arena: the parameters plus
- * alignment padding, small derived tables (RoPE frequencies) and, for W4A16,
- * a second copy of the packed words and scales of every linear the batched
- * (matrix-core) products read, in their fragment order (built on the device
- * at load time). */
+ * alignment padding, small derived tables (RoPE frequencies) and a second
+ * copy of every matrix the batched (matrix-core) products read, in their
+ * fragment order (bf16 weights or W4A16 words and scales; for bf16 also the
+ * tied embedding), built on the device at load time. */
 size_t e2b_arena_bytes(const e2b_model* model);
 
 /* K/V cache bytes for max_batch sequences of max_ctx positions: bf16 K and V
