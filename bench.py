@@ -42,8 +42,6 @@ sys.path.insert(0, ROOT)
 HBM_PEAK = 8.0e12  # MI355X HBM3E, bytes/s
 METRIC = "decode tok/s at batch 1 and 64 (E2B shape, bf16 & W4A16); % of HBM roofline"
 KINDS = ["gate_up", "down", "lm_head", "qkv", "o"]
-STEP_SYMBOL = {"bf16": "void e2b::k_step1<0, 1536, 2048, 2048, 2048, 256, 256, 512>",
-               "w4a16": "void e2b::k_step1<1, 1536, 2048, 2048, 2048, 256, 256, 512>"}
 PMC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
 
 
@@ -53,7 +51,7 @@ def log(*a):
 
 def kernels_sha():
     h = hashlib.sha1()
-    for f in ("kernels.hip", "step1.hip", "dev_common.h", "e2b_internal.h"):
+    for f in ("kernels.hip", "dev_common.h", "e2b_internal.h"):
         with open(os.path.join(ROOT, "w4a16_weight_streaming_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
@@ -179,17 +177,8 @@ def measure(cfg, quant, B, P, K, W, prof_steps, eager=False, cpu_steps=0, label=
 
     # per-kernel timing: eager steps at the same positions, each queued behind
     # a spin kernel; each launch of one kind records its own start and end.
-    # One row runs as one persistent kernel per step ("step"); else per kind.
     prof, gpu_tokens = {}, []
     kinds = KINDS
-    if prof_steps and B == 1:
-        with torch.cuda.stream(stream):
-            pos.fill_(P)
-            tok.copy_(tok0)
-            eng.profile_begin("step")
-            eng.decode_step(tok, pos, tok)
-            if eng.profile_read()[0] > 0:
-                kinds = ["step"]
     with torch.cuda.stream(stream):
         for i, kind in enumerate(kinds if prof_steps else []):
             pos.fill_(P)
@@ -202,8 +191,6 @@ def measure(cfg, quant, B, P, K, W, prof_steps, eager=False, cpu_steps=0, label=
                 if i == 0 and s < cpu_steps:
                     gpu_tokens.append(tok.cpu().numpy().copy())
             n, tms, tby = eng.profile_read()
-            if kind == "step":  # the whole step: weights + K/V read and written + gathers
-                tby = n * step_bytes(cfg, quant, B, list(range(P, P + prof_steps)))[0]
             prof[kind] = dict(launches=n, ms=tms / max(n, 1), bytes=tby / max(n, 1))
     res = {"value": B * K / (ms / 1e3), "ms_per_step": ms_step, "step_bytes": sb, "weight_bytes": wbytes,
            "kinds": prof, "graph": graph is not None}
@@ -240,7 +227,7 @@ def roofline_of(res, quant, B):
     dom = max(prof, key=lambda k: prof[k]["ms"] * prof[k]["launches"])
     d = prof[dom]
     achieved = d["bytes"] / (d["ms"] / 1e3)
-    sym = STEP_SYMBOL[quant] if dom == "step" else kernel_symbol(dom, quant, B)
+    sym = kernel_symbol(dom, quant, B)
     traffic = pmc_traffic(sym) if sym else None
     return {"bound": "hbm", "kernel": dom, "symbol": sym, "achieved": round(achieved / 1e9, 1),
             "peak": HBM_PEAK / 1e9, "unit": "GB/s", "frac": round(achieved / HBM_PEAK, 4),

@@ -136,10 +136,9 @@ size_t e2b_kv_bytes(const e2b_model* model, int max_batch, int max_ctx);
 
 /* Workspace bytes for calls that process up to max_rows rows (decode batch,
  * or prefill rows per pass).  The workspace (256-byte aligned) is scratch
- * except its first 32 KiB of control words (the device error word, kernel
- * counters): zero them once before the first call; the kernels leave the
- * counters zero, and e2b_check reads and re-zeroes the error word.  Calls
- * that overlap in time must not share a workspace. */
+ * except its first 256 bytes, the device error word: zero them once before
+ * the first call; e2b_check reads and re-zeroes it.  Calls that overlap in
+ * time must not share a workspace. */
 size_t e2b_workspace_bytes(const e2b_model* model, int max_rows);
 
 /* Copy the tensors to the caller's device arena (d_arena, arena_bytes >=
@@ -161,15 +160,20 @@ int e2b_kv_alloc(e2b_model* model, void* d_kv, size_t bytes, int max_batch, int 
 
 /* One greedy decode step for `batch` sequences b = 0..batch-1 (sequence b
  * uses cache slot row b): token d_tokens[b] at position d_positions[b]
- * (int32 device arrays).  Writes K/V of position d_positions[b] in place,
- * attends over positions <= it (window on sliding layers), and writes the
- * greedy next token to d_argmax[b] (lowest index on ties) and, if d_logits is
- * not NULL, fp32 logits [batch, vocab].  d_argmax may alias d_tokens.
- * Allocates nothing and does not synchronise.  E2B_ERANGE if batch exceeds
- * the bound max_batch or the workspace rows; E2B_ENOMEM if ws_bytes <
- * e2b_workspace_bytes(model, batch).  Tokens >= vocab or positions outside
- * [0, max_ctx) are not read or written; they set the device error word
- * reported by e2b_check. */
+ * (int32 device arrays).  The step is the decoder pass the pages define:
+ * embedding and per-layer inputs, then per layer the attention block over the
+ * cache of the layer's K/V source, the GeGLU MLP (double width from the first
+ * shared layer on) and the per-layer-input mix, then the final norm, the tied
+ * lm_head and the greedy choice ([P3] Steps 1 and 3-5; [P5] The engine:
+ * kv_share_map, RoPE at the logical position, the cache updated in place).
+ * Writes K/V of position d_positions[b] in place, attends over positions <= it
+ * (window on sliding layers), and writes the greedy next token to d_argmax[b]
+ * (lowest index on ties) and, if d_logits is not NULL, fp32 logits [batch,
+ * vocab].  d_argmax may alias d_tokens.  Allocates nothing and does not
+ * synchronise.  E2B_ERANGE if batch exceeds the bound max_batch or the
+ * workspace rows; E2B_ENOMEM if ws_bytes < e2b_workspace_bytes(model, batch).
+ * Tokens >= vocab or positions outside [0, max_ctx) are not read or written;
+ * they set the device error word reported by e2b_check. */
 int e2b_decode_step(e2b_model* model, const int32_t* d_tokens, const int32_t* d_positions,
                     int batch, float* d_logits, int32_t* d_argmax, void* d_ws, size_t ws_bytes,
                     void* stream);
@@ -204,13 +208,25 @@ int e2b_kv_view(const e2b_model* model, int layer, int which, void** out);
  * that divides K among 2048, 1536; else K itself when K <= 512; else 512);
  * other K -> E2B_EINVAL.  d_ws (256-byte aligned) must hold
  * e2b_matvec_workspace_bytes(quant, N, K, rows) bytes: the K-slice partial
- * sums, 0 when the product is not split.  One row streams the weights through
- * the matvec kernel; two or more rows (x 16-byte aligned) share one pass over
- * the weights on the matrix cores.  Asynchronous. */
+ * sums (none when the product is not split) and, for two or more rows with
+ * N % 16 == 0, a copy of the weights tiled in the matrix-core fragment order
+ * that batched decode reads (built by the call).  One row streams the
+ * weights through the matvec kernel; two or more rows (x 16-byte aligned)
+ * share one pass over the weights on the matrix cores.  Asynchronous. */
 size_t e2b_matvec_workspace_bytes(int quant, int N, int K, int rows);
 int e2b_matvec(int quant, const void* d_w, const uint16_t* d_scale, int N, int K,
                const float* d_x, int rows, float* d_y, void* d_ws, size_t ws_bytes,
                void* stream);
+
+/* The embedding gathers of the step for n tokens, on their own: d_h[r][i] =
+ * E[t_r][i] * sqrt(H) (the tied table, [P4] cell 2.2) and d_tokple[r][j] =
+ * E_ple[t_r][j] * sqrt(P) for j < L * P (the per-layer table, [P3] Step 3),
+ * fp32 row-major, each a widened bf16 table value times the fp32-rounded
+ * constant (one rounding), exactly what the decode step consumes.  The
+ * workspace must hold e2b_workspace_bytes(model, n).  Tokens outside the
+ * vocabulary read row 0 and set the device error word.  Asynchronous. */
+int e2b_embed(e2b_model* model, const int32_t* d_tokens, int n, float* d_h, float* d_tokple,
+              void* d_ws, size_t ws_bytes, void* stream);
 
 /* ---- HIP graph of one decode step -------------------------------------
  * Capture exactly what e2b_decode_step enqueues for these arguments into a
@@ -237,8 +253,7 @@ void e2b_graph_destroy(e2b_graph* graph);
  * and output vectors), then stops profiling.  kind 0 stops without reading. */
 enum {
   E2B_KIND_NONE = 0, E2B_KIND_QKV = 1, E2B_KIND_O = 2, E2B_KIND_GATE_UP = 3, E2B_KIND_DOWN = 4,
-  E2B_KIND_PLE_GATE = 5, E2B_KIND_PLE_PROJ = 6, E2B_KIND_PLE_MODEL = 7, E2B_KIND_LM_HEAD = 8,
-  E2B_KIND_STEP = 9 /* the whole one-row decode step (one persistent kernel) */
+  E2B_KIND_PLE_GATE = 5, E2B_KIND_PLE_PROJ = 6, E2B_KIND_PLE_MODEL = 7, E2B_KIND_LM_HEAD = 8
 };
 int e2b_profile_begin(e2b_model* model, int kind);
 int e2b_profile_read(e2b_model* model, int* launches, double* total_ms, double* total_bytes);

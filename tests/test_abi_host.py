@@ -152,12 +152,20 @@ def test_matvec_validation(lib):
     for K in (64, 96, 160, 480, 4608 * 4):
         assert L.e2b_matvec_workspace_bytes(0, 64, K, 3) == 0, K
         assert L.e2b_matvec(0, 256, None, 8, K, 256, 3, 256, 256, 1 << 20, None) == lib.E2B_EINVAL, K
-    # several rows: only the K-slice partials of the matrix-core product
+    # several rows: the K-slice partials of the matrix-core product, then (N %
+    # 16 == 0) the weights tiled in fragment order
+    up = lambda x: (x + 255) // 256 * 256
     for quant in (0, 1):
-        for N, K, r in ((1536, 1536, 3), (1536, 12288, 70), (1536, 4096, 2), (24576, 1536, 64)):
-            extra = L.e2b_matvec_workspace_bytes(quant, N, K, r)
-            slices, rem = divmod(extra, r * N * 4)
-            assert rem == 0 and slices in (0, 2, 3, 4, 6, 8, 12, 16), (quant, N, K, r, extra)
+        for N, K, r in ((1536, 1536, 3), (1536, 12288, 70), (1536, 4096, 2), (24576, 1536, 64),
+                        (40, 1536, 3)):
+            total = L.e2b_matvec_workspace_bytes(quant, N, K, r)
+            tiled = 0
+            if N % 16 == 0:
+                tiled = up(N * K // 2) + up(N * (K // 32) * 2) if quant else up(N * K * 2)
+            part = total - tiled
+            slices = part // (r * N * 4)
+            assert part >= 0 and slices in (0, 2, 3, 4, 6, 8, 12, 16), (quant, N, K, r, total)
+            assert part == (up(slices * r * N * 4) if slices else 0), (quant, N, K, r, total)
             if slices:
                 assert K % slices == 0 and (K // slices) % 32 == 0
     assert L.e2b_matvec_workspace_bytes(2, 1536, 1536, 3) == 0   # unknown quant

@@ -18,7 +18,7 @@ _lib = None
 
 E2B_OK, E2B_EINVAL, E2B_ERANGE, E2B_ENOMEM, E2B_EHIP, E2B_EDEVICE, E2B_ESTATE = range(7)
 KINDS = {"qkv": 1, "o": 2, "gate_up": 3, "down": 4, "ple_gate": 5, "ple_proj": 6, "ple_model": 7,
-         "lm_head": 8, "step": 9}
+         "lm_head": 8}
 QUANT = {"bf16": 0, "w4a16": 1}
 DTYPE_BF16, DTYPE_INT32 = 0, 1
 
@@ -90,9 +90,10 @@ def load_library():
     L.e2b_matvec_workspace_bytes.restype = sz
     L.e2b_matvec_workspace_bytes.argtypes = [i32, i32, i32, i32]
     L.e2b_matvec.argtypes = [i32, vp, vp, i32, i32, vp, i32, vp, vp, sz, vp]
+    L.e2b_embed.argtypes = [vp, vp, i32, vp, vp, vp, sz, vp]
     for f in ("e2b_config_preset", "e2b_create", "e2b_kv_share_map", "e2b_load_weights",
               "e2b_kv_alloc", "e2b_decode_step", "e2b_prefill", "e2b_check", "e2b_kv_view",
-              "e2b_matvec", "e2b_graph_capture", "e2b_graph_replay", "e2b_profile_begin",
+              "e2b_matvec", "e2b_embed", "e2b_graph_capture", "e2b_graph_replay", "e2b_profile_begin",
               "e2b_profile_read"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
@@ -255,6 +256,18 @@ class Engine:
         _check(self.model._lib.e2b_prefill(
             self.model.handle, seq, tokens.data_ptr(), tokens.numel(), pos0, self._ptr(logits_out),
             argmax_out.data_ptr(), self.ws.data_ptr(), self.ws.numel(), self._stream()))
+
+    def embed(self, tokens, h_out, tokple_out):
+        """The step's embedding gathers alone: h_out float32 [n, H] = E[t] * sqrt(H),
+        tokple_out float32 [n, L*P] = E_ple[t] * sqrt(P).  Asynchronous; n must not
+        exceed max_rows."""
+        n = tokens.numel()
+        assert tokens.dtype == self.torch.int32 and h_out.dtype == tokple_out.dtype == self.torch.float32
+        assert h_out.numel() >= n * self.cfg.hidden_size
+        assert tokple_out.numel() >= n * self.cfg.num_hidden_layers * self.cfg.hidden_size_per_layer_input
+        _check(self.model._lib.e2b_embed(self.model.handle, tokens.data_ptr(), n, h_out.data_ptr(),
+                                         tokple_out.data_ptr(), self.ws.data_ptr(), self.ws.numel(),
+                                         self._stream()))
 
     def kv_view(self, layer: int, which: int) -> int:
         """Device address of the K (0) / V (1) region layer `layer` reads."""

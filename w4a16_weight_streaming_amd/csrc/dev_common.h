@@ -1,5 +1,5 @@
-// Device helpers shared by the kernels of libe2b (kernels.hip: one kernel per
-// phase of the step; step1.hip: the persistent one-row decode step).
+// Device helpers of the kernels of libe2b (kernels.hip: one kernel per phase
+// of the step).
 #pragma once
 
 #include "e2b_internal.h"
@@ -9,46 +9,10 @@
 
 namespace e2b {
 
-// Stores of data that other blocks read later in the same kernel (the
-// persistent step): agent-scope relaxed atomic stores write through to the
-// device-coherent level; elsewhere plain stores.
-template <bool COH>
-__device__ __forceinline__ void st32(float* p, float v) {
-  if constexpr (COH) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  else *p = v;
-}
-// Loads of data another block wrote earlier in the same kernel: agent-scope
-// relaxed atomic loads (device-coherent); elsewhere plain loads.
-template <bool COH>
-__device__ __forceinline__ float ld32(const float* p) {
-  if constexpr (COH) return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  else return *p;
-}
-template <bool COH>
-__device__ __forceinline__ int ld32i(const int* p) {
-  if constexpr (COH) return __hip_atomic_load(const_cast<int*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  else return *p;
-}
-template <bool COH>
-__device__ __forceinline__ uint32_t ldu32(const uint32_t* p) {
-  if constexpr (COH) return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  else return *p;
-}
-template <bool COH>
-__device__ __forceinline__ uint16_t ldu16(const uint16_t* p) {
-  if constexpr (COH) return __hip_atomic_load(const_cast<uint16_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  else return *p;
-}
-template <bool COH>
-__device__ __forceinline__ void st32i(int* p, int v) {
-  if constexpr (COH) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  else *p = v;
-}
-template <bool COH>
-__device__ __forceinline__ void st16(uint16_t* p, uint16_t v) {
-  if constexpr (COH) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  else *p = v;
-}
+// Plain accessors (one place to change how activations cross kernels).
+__device__ __forceinline__ void st32(float* p, float v) { *p = v; }
+__device__ __forceinline__ float ld32(const float* p) { return *p; }
+__device__ __forceinline__ void st16(uint16_t* p, uint16_t v) { *p = v; }
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
@@ -218,10 +182,9 @@ struct Lay {
 // round trip; the weight prefetch is issued after it), finish() does the
 // arithmetic and writes xs.
 // A never-written row of zeros: what an unconditional load of an absent
-// operand reads.  (Memory written by the same kernel would not do: a plain
-// load of it can leave a stale line behind for the persistent step's coherent
-// reads.  Nor would repeating a real operand's address: the compiler then
-// copies that load's register, which waits for it.)  4096 bf16 = 2048 floats,
+// operand reads.  (Repeating a real operand's address would not do: the
+// compiler then copies that load's register, which waits for it.)  4096 bf16
+// = 2048 floats,
 // the widest row such a load covers.
 static __device__ __align__(16) uint16_t kZeroRow[4096];
 __device__ __forceinline__ const float* zero_f() { return reinterpret_cast<const float*>(kZeroRow); }
@@ -243,7 +206,6 @@ struct PrologueRegs {
 
   __device__ __forceinline__ int kind(const Prologue& p) const { return PK >= 0 ? PK : p.kind; }
 
-  template <bool COH = false>
   __device__ __forceinline__ void load(const Prologue& p, int rows, int b, int k0, int K) {
     const int t = threadIdx.x;
 #pragma unroll
@@ -264,11 +226,11 @@ struct PrologueRegs {
                                          : nullptr;
 #pragma unroll
       for (int j = 0; j < PT; ++j)
-        if (ok(j)) a0[j] = ld32<COH>(s0 + t + j * kGemvThreads);
+        if (ok(j)) a0[j] = ld32(s0 + t + j * kGemvThreads);
       if (PK == kGeglu || PK == kPleGate || (PK < 0 && s1))
 #pragma unroll
         for (int j = 0; j < PT; ++j)
-          if (ok(j)) a1[j] = ld32<COH>(s1 + t + j * kGemvThreads);
+          if (ok(j)) a1[j] = ld32(s1 + t + j * kGemvThreads);
       return;
     }
     // kRes / kResNorm: KS == K == hidden size.  Gains absent here read the
@@ -281,7 +243,7 @@ struct PrologueRegs {
     for (int j = 0; j < PT; ++j)
       if (ok(j)) {
         const int i = t + j * kGemvThreads;
-        a0[j] = ld32<COH>(hrow + i);
+        a0[j] = ld32(hrow + i);
         g1[j] = gx[i];
         g0[j] = gd[i];
       }
@@ -294,7 +256,7 @@ struct PrologueRegs {
         const float* src = q < nd ? dp + (size_t)q * p.d_pstride : zero_f();
 #pragma unroll
         for (int j = 0; j < PT; ++j)
-          if (ok(j)) dq[j][q] = ld32<COH>(src + t + j * kGemvThreads);
+          if (ok(j)) dq[j][q] = ld32(src + t + j * kGemvThreads);
       }
     } else if (p.d) {
 #pragma unroll
@@ -302,14 +264,13 @@ struct PrologueRegs {
         if (q < nd)
 #pragma unroll
           for (int j = 0; j < PT; ++j)
-            if (ok(j)) dq[j][q] = ld32<COH>(p.d + (size_t)q * p.d_pstride + (size_t)b * K + t + j * kGemvThreads);
+            if (ok(j)) dq[j][q] = ld32(p.d + (size_t)q * p.d_pstride + (size_t)b * K + t + j * kGemvThreads);
     }
     sc = *(p.scalar ? p.scalar : stand_in);  // (1 when there is no scalar)
   }
 
   // store_h: this block writes the updated residual h' (one block per
-  // product); COH: with agent-coherent stores (the persistent step)
-  template <bool COH = false>
+  // product)
   __device__ __forceinline__ void finish(const Prologue& p, int b, int K, float* xs, float* red,
                                          bool store_h) {
     const int t = threadIdx.x;
@@ -345,7 +306,7 @@ struct PrologueRegs {
         hv[j] = hn;
         if (i < KS) {
           hs = fmaf(hn, hn, hs);
-          if (store) st32<COH>(p.h_out + (size_t)b * K + i, hn);
+          if (store) st32(p.h_out + (size_t)b * K + i, hn);
         }
       }
       if (kd == kResNorm) {
@@ -544,19 +505,19 @@ __device__ __forceinline__ void load_row(const uint16_t* p, float (&out)[DPL]) {
 // Split in two so that a wave issues the reads of all its heads (and the gains
 // and angles) before it waits for any: head_raw sums the K-slice partials of
 // the projection, head_side reads gain and angles, head_finish does the rest.
-template <int HD, bool COH = false>
+template <int HD>
 __device__ __forceinline__ void head_raw(const float* raw, int nparts, size_t pstride, int lane,
                                          float (&y)[HD / 64]) {
   constexpr int DPL = HD / 64;
 #pragma unroll
-  for (int i = 0; i < DPL; ++i) y[i] = ld32<COH>(raw + lane * DPL + i);
+  for (int i = 0; i < DPL; ++i) y[i] = ld32(raw + lane * DPL + i);
   for (int q0 = 1; q0 < nparts; q0 += 4) {  // further partials, 4 in flight
     float v[4][DPL];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const float* src = q0 + k < nparts ? raw + (size_t)(q0 + k) * pstride : zero_f();
 #pragma unroll
-      for (int i = 0; i < DPL; ++i) v[k][i] = ld32<COH>(src + lane * DPL + i);
+      for (int i = 0; i < DPL; ++i) v[k][i] = ld32(src + lane * DPL + i);
     }
 #pragma unroll
     for (int k = 0; k < 4; ++k)
@@ -578,7 +539,7 @@ struct HeadSide {
 
 // gain: may be null (values: no gain); cs/sn: null when there is no rotation.
 // Absent operands read the zero row and are not used.
-template <int HD, bool COH = false>
+template <int HD>
 __device__ __forceinline__ void head_side(const uint16_t* gain, const float* cs, const float* sn,
                                           int lane, HeadSide<HD>& hs) {
   constexpr int DPL = HD / 64;
@@ -595,8 +556,8 @@ __device__ __forceinline__ void head_side(const uint16_t* gain, const float* cs,
 #pragma unroll
   for (int i = 0; i < DPL; ++i) {
     const int ii = (lane & 31) * DPL + i;
-    hs.c[i] = ld32<COH>(cp + ii);
-    hs.s[i] = ld32<COH>(sp + ii);
+    hs.c[i] = ld32(cp + ii);
+    hs.s[i] = ld32(sp + ii);
   }
 }
 
@@ -620,14 +581,14 @@ __device__ __forceinline__ void head_finish(float (&y)[HD / 64], const HeadSide<
   }
 }
 
-template <int HD, bool COH = false>
+template <int HD>
 __device__ __forceinline__ void head_vec(const float* raw, int nparts, size_t pstride,
                                          const uint16_t* gain, bool rope, const float* cs,
                                          const float* sn, int lane, float eps,
                                          float (&y)[HD / 64]) {
   HeadSide<HD> hs;
-  head_side<HD, COH>(gain, rope ? cs : nullptr, rope ? sn : nullptr, lane, hs);
-  head_raw<HD, COH>(raw, nparts, pstride, lane, y);
+  head_side<HD>(gain, rope ? cs : nullptr, rope ? sn : nullptr, lane, hs);
+  head_raw<HD>(raw, nparts, pstride, lane, y);
   head_finish<HD>(y, hs, gain != nullptr, rope, lane, eps);
 }
 
@@ -684,7 +645,7 @@ __device__ __forceinline__ void unpack(const uint32_t (&w)[KvGroup<DPL>::W], flo
 // k_attn_combine merges them.  (Merging in the row's last block instead needs
 // a device-scope fence per block, which writes back the L2 and costs more
 // than the extra launch.)
-template <int HD, bool COH>
+template <int HD>
 __device__ void attn_chunk(const Rows& R, const AttnArgs& a, int c, int r) {
   constexpr int DPL = HD / 64;
   constexpr int NH = kMaxHeads;
@@ -720,21 +681,8 @@ __device__ void attn_chunk(const Rows& R, const AttnArgs& a, int c, int r) {
         const bool ok = gi < ngroups && key < j1 && !(own && key == pos);
         const uint16_t* kr = ok ? kb + (size_t)key * HD : kZeroRow + lane * DPL;
         const uint16_t* vr = ok ? vb + (size_t)key * HD : kZeroRow + lane * DPL;
-        if (COH && ok && key == pos) {  // written earlier in this kernel by the source layer
-#pragma unroll
-          for (int i = 0; i < G::W; ++i) {
-            if constexpr (DPL == 1) {
-              g.k[k][i] = ldu16<true>(kr);
-              g.v[k][i] = ldu16<true>(vr);
-            } else {
-              g.k[k][i] = ldu32<true>(reinterpret_cast<const uint32_t*>(kr) + i);
-              g.v[k][i] = ldu32<true>(reinterpret_cast<const uint32_t*>(vr) + i);
-            }
-          }
-        } else {
-          load_packed<DPL>(kr, g.k[k]);
-          load_packed<DPL>(vr, g.v[k]);
-        }
+        load_packed<DPL>(kr, g.k[k]);
+        load_packed<DPL>(vr, g.v[k]);
       }
     };
     G cur;
@@ -751,14 +699,14 @@ __device__ void attn_chunk(const Rows& R, const AttnArgs& a, int c, int r) {
     // (all unconditional: heads past nq and K/V rows a block does not own read
     // head 0 and are not used)
     HeadSide<HD> sq, sk;
-    head_side<HD, COH>(a.gq, cs, sn, lane, sq);
-    head_side<HD, COH>(own_kv && wave == 0 ? a.gk : nullptr, cs, sn, lane, sk);
+    head_side<HD>(a.gq, cs, sn, lane, sq);
+    head_side<HD>(own_kv && wave == 0 ? a.gk : nullptr, cs, sn, lane, sk);
     float yq[HW][DPL], yk[DPL];
 #pragma unroll
     for (int x = 0; x < HW; ++x)
-      head_raw<HD, COH>(raw + (wave + 4 * x < nq ? wave + 4 * x : 0) * HD, a.qkv_parts, a.qkv_pstride,
+      head_raw<HD>(raw + (wave + 4 * x < nq ? wave + 4 * x : 0) * HD, a.qkv_parts, a.qkv_pstride,
                         lane, yq[x]);
-    head_raw<HD, COH>(raw + (own_kv ? nq + wave : 0) * HD, a.qkv_parts, a.qkv_pstride, lane, yk);
+    head_raw<HD>(raw + (own_kv ? nq + wave : 0) * HD, a.qkv_parts, a.qkv_pstride, lane, yk);
 #pragma unroll
     for (int x = 0; x < HW; ++x) {
       const int h = wave + 4 * x;
@@ -775,7 +723,7 @@ __device__ void attn_chunk(const Rows& R, const AttnArgs& a, int c, int r) {
 #pragma unroll
       for (int i = 0; i < DPL; ++i) {
         const uint32_t b = f2bf(yk[i]);
-        st16<COH>(dst + lane * DPL + i, (uint16_t)b);
+        st16(dst + lane * DPL + i, (uint16_t)b);
         kv_own[wave][lane * DPL + i] = bf2f(b);
       }
     }
@@ -892,8 +840,8 @@ __device__ void attn_chunk(const Rows& R, const AttnArgs& a, int c, int r) {
       float L = 0.f;
       for (int x = 0; x < 4; ++x)
         if (wm[x][t] != -INFINITY) L = fmaf(wl[x][t], expf(wm[x][t] - M), L);
-      st32<COH>(part + t * hstride + HD, M);
-      st32<COH>(part + t * hstride + HD + 1, L);
+      st32(part + t * hstride + HD, M);
+      st32(part + t * hstride + HD + 1, L);
     }
     __syncthreads();
     for (int idx = t; idx < nq * HD; idx += 256) {
@@ -902,18 +850,17 @@ __device__ void attn_chunk(const Rows& R, const AttnArgs& a, int c, int r) {
       a_ = fmaf(op[0][idx], fw[1][h], a_);
       a_ = fmaf(op[1][idx], fw[2][h], a_);
       a_ = fmaf(op[2][idx], fw[3][h], a_);
-      st32<COH>(part + h * hstride + d, a_);
+      st32(part + h * hstride + d, a_);
     }
   } else if (t < nq) {  // no keys in this chunk
-    st32<COH>(part + t * hstride + HD, -INFINITY);
-    st32<COH>(part + t * hstride + HD + 1, 0.f);
+    st32(part + t * hstride + HD, -INFINITY);
+    st32(part + t * hstride + HD + 1, 0.f);
   }
 }
 
 // out[r][h*hd + d] = sum_c e^(m_c - M) o_c[d] / sum_c e^(m_c - M) l_c over the
 // chunks holding keys.  Those are a prefix of the chunk list (keys are split in
 // order); empty chunks leave o unwritten, so they are never read.
-template <bool COH>
 __device__ void attn_combine(const AttnArgs& a, int r, int h) {
   __shared__ float wn[kMaxChunks];
   __shared__ float sh[8];
@@ -932,12 +879,12 @@ __device__ void attn_combine(const AttnArgs& a, int r, int h) {
     const int d = t + 256 * it < hd ? t + 256 * it : 0;
 #pragma unroll
     for (int c = 0; c < kPre; ++c)
-      pv[it][c] = c < a.nchunk ? ld32<COH>(part + (size_t)c * (hd + 2) + d) : ld32<COH>(zero_f() + d);
+      pv[it][c] = c < a.nchunk ? ld32(part + (size_t)c * (hd + 2) + d) : ld32(zero_f() + d);
   }
   float mc = -INFINITY, lc = 0.f;
   if (t < a.nchunk) {
-    mc = ld32<COH>(part + (size_t)t * (hd + 2) + hd);
-    lc = ld32<COH>(part + (size_t)t * (hd + 2) + hd + 1);
+    mc = ld32(part + (size_t)t * (hd + 2) + hd);
+    lc = ld32(part + (size_t)t * (hd + 2) + hd + 1);
   }
   const bool act = lc > 0.f;
   float M = act ? mc : -INFINITY;
@@ -970,12 +917,12 @@ __device__ void attn_combine(const AttnArgs& a, int r, int h) {
     }
     int cc = kPre;
     for (; cc + 4 <= nact; cc += 4) {
-      o0 = fmaf(wn[cc], ld32<COH>(part + (size_t)cc * (hd + 2) + d), o0);
-      o1 = fmaf(wn[cc + 1], ld32<COH>(part + (size_t)(cc + 1) * (hd + 2) + d), o1);
-      o2 = fmaf(wn[cc + 2], ld32<COH>(part + (size_t)(cc + 2) * (hd + 2) + d), o2);
-      o3 = fmaf(wn[cc + 3], ld32<COH>(part + (size_t)(cc + 3) * (hd + 2) + d), o3);
+      o0 = fmaf(wn[cc], ld32(part + (size_t)cc * (hd + 2) + d), o0);
+      o1 = fmaf(wn[cc + 1], ld32(part + (size_t)(cc + 1) * (hd + 2) + d), o1);
+      o2 = fmaf(wn[cc + 2], ld32(part + (size_t)(cc + 2) * (hd + 2) + d), o2);
+      o3 = fmaf(wn[cc + 3], ld32(part + (size_t)(cc + 3) * (hd + 2) + d), o3);
     }
-    for (; cc < nact; ++cc) o0 = fmaf(wn[cc], ld32<COH>(part + (size_t)cc * (hd + 2) + d), o0);
+    for (; cc < nact; ++cc) o0 = fmaf(wn[cc], ld32(part + (size_t)cc * (hd + 2) + d), o0);
     const float v = (o0 + o1) + (o2 + o3);
     if (a.xh) {  // the O product's prepared input: hi + lo = v, group sums of 32
       const size_t K = (size_t)a.nq * hd, i = (size_t)r * K + (size_t)h * hd + d;
@@ -987,7 +934,7 @@ __device__ void attn_combine(const AttnArgs& a, int r, int h) {
       const float gs = lanes_sum<32>(bf2f(hb) + bf2f(lb));
       if ((d & 31) == 0) a.xg[i / 32] = gs;
     } else {
-      st32<COH>(a.out + (size_t)r * a.nq * hd + (size_t)h * hd + d, v);
+      st32(a.out + (size_t)r * a.nq * hd + (size_t)h * hd + d, v);
     }
   }
 }

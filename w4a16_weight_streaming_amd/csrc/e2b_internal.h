@@ -21,7 +21,7 @@ enum : int {
 };
 
 // Device error word bits (first 16 bytes of the workspace).
-enum : int { kErrToken = 1, kErrPos = 2, kErrSync = 4 };
+enum : int { kErrToken = 1, kErrPos = 2 };
 
 // One linear layer resident in the weight arena.  bf16: w [N, K].
 // W4A16: q [N, K/8] packed int4 codes, s [N, K/32] bf16 group scales.  Both
@@ -218,52 +218,5 @@ hipError_t launch_sum_partials(int nparts, size_t n, const float* parts, float* 
 hipError_t launch_argmax_final(int rows, int nblk, const float* cand_val,
                                const int32_t* cand_idx, int32_t* out, int32_t* adv,
                                hipStream_t st);
-
-// ---- persistent one-row decode step (step1.hip) ---------------------------
-// One kernel per decode step of one sequence: every phase of the step runs
-// in one persistent grid (one block per compute unit), phases separated by a
-// grid barrier.  Data one block writes and another reads later in the same
-// launch lives in a write-once slab (each region written once per launch,
-// read only after the barrier that follows its writes) and is stored with
-// agent-coherent stores, so plain loads never see stale cache lines.
-
-// Per-layer plan (device memory, in the weight arena).  Activation regions
-// are float offsets into the slab.
-struct StepLayer {
-  Lin qkv, o, gu, down, pg, pp;
-  const uint16_t *g_in, *g_q, *g_k, *g_pa, *g_pf, *g_ff, *g_pple, *scalar;
-  const uint16_t *kc, *vc;    // cache the layer reads (its source's region)
-  uint16_t *kc_own, *vc_own;  // its own region when it computes K/V, else null
-  int hd, full, I, nchunk, chunk, owns;
-  size_t hq, qkv_out, part, attn, oo, h1, gu_out, dn, h2, pg_out, ppo;
-};
-
-struct StepArgs {
-  const StepLayer* layers;     // [L]
-  float* slab;                 // write-once activations of this step
-  unsigned long long* bar;     // grid barrier counters (monotonic, 64-bit)
-  int* err;                    // device error word
-  const int32_t* tokens;       // [1]
-  const int32_t* positions;    // [1]
-  float* logits;               // [V] or null
-  int32_t* argmax;             // [1]
-  const uint16_t *embed, *ple, *g_plpn, *g_final;
-  const double *inv_s, *inv_f;
-  Lin plmp, lm;
-  size_t e, tokple, rope, u, pli, hfin, cand_v, cand_i;  // slab offsets
-  int L, H, P, V, nq, hd_s, hd_f, window, max_ctx;
-  float eps, sqrtH, sqrtP, inv_sqrtH;
-  unsigned long long* trace;   // optional: block 0's clock (100 MHz) at each phase end
-};
-
-// Which compiled variant of the step fits this configuration (slice widths
-// of its products), or -1.  Variants: 0 = E2B widths, 1 = toy widths.
-int step1_variant(int H, int P, int nq, int hd_s, int hd_f, int I0, int I1);
-// Blocks of the persistent grid (one per compute unit) if every block fits
-// on the device at once, else 0.
-int step1_grid(int variant, int quant);
-size_t step1_barrier_bytes();
-// *nblk_lm: argmax candidates the lm_head phase writes (the grid size)
-hipError_t launch_step1(int variant, int quant, const StepArgs& a, int grid, hipStream_t st);
 
 }  // namespace e2b

@@ -95,18 +95,6 @@ struct e2b_model {
   char* kv = nullptr;
   int max_batch = 0, max_ctx = 0;
   std::vector<uint16_t*> kc, vc;
-  // persistent one-row decode step (step1.hip)
-  int step_variant = -1, step_grid = 0;
-  bool step_trace = false;  // record phase clocks (workspace bytes 1024..5119)
-  bool step_ready = false;  // plan uploaded (weights loaded and K/V bound)
-  size_t off_step = 0;      // arena offset of the per-layer plan
-  struct SlabLayer {
-    size_t hq, qkv_out, part, attn, oo, h1, gu_out, dn, h2, pg_out, ppo;
-  };
-  std::vector<SlabLayer> slab;
-  size_t s_e = 0, s_tokple = 0, s_rope = 0, s_u = 0, s_pli = 0, s_hfin = 0, s_cv = 0, s_ci = 0;
-  size_t slab_floats = 0;
-  double step_bytes = 0;  // weights streamed per step (profiling)
   // per-kernel timing
   int prof_kind = 0;
   struct Mark {
@@ -243,8 +231,6 @@ int build_plan(e2b_model* m) {
   // RoPE inverse frequencies theta^(-2i/hd), double, per attention type
   m->off_invf[0] = p.alloc(sizeof(double) * m->c.head_dim / 2);
   m->off_invf[1] = p.alloc(sizeof(double) * m->c.global_head_dim / 2);
-  // the persistent step's per-layer plan (pointers, filled once K/V are bound)
-  m->off_step = p.alloc(sizeof(e2b::StepLayer) * L);
   m->arena_bytes = p.cur;
   return E2B_OK;
 }
@@ -279,7 +265,7 @@ Lin resolve(const e2b_model* m, const LinOff& o) {
 
 // ---- workspace layout ------------------------------------------------------
 struct Ws {
-  size_t err, bar, trace, slab, rope, h0, h1, tokple, u, pli, qkv, part, attn, oo, gu, dn, pgy, ppo, cv, ci, xh, xl, xg,
+  size_t err, rope, h0, h1, tokple, u, pli, qkv, part, attn, oo, gu, dn, pgy, ppo, cv, ci, xh, xl, xg,
       total;
   int ncand;  // argmax candidates per row
 };
@@ -317,8 +303,6 @@ Ws ws_layout(const e2b_model* m, int R) {
   w.ncand = std::max(e2b::kLmBlocks, (m->V + 63) / 64);
   const size_t LP = (size_t)m->L * m->P;
   w.err = take(64);
-  w.bar = take(e2b::step1_barrier_bytes());  // fixed offset: counters persist across calls
-  w.trace = take(4096);                       // fixed offset: optional phase clock of the step
   w.rope = take(f * R * (m->c.head_dim + m->c.global_head_dim));
   w.h0 = take(f * R * m->H);
   w.h1 = take(f * R * m->H);
@@ -342,7 +326,6 @@ Ws ws_layout(const e2b_model* m, int R) {
   } else {
     w.xh = w.xl = w.xg = 0;
   }
-  w.slab = m->step_variant >= 0 ? take(f * m->slab_floats) : 0;
   w.total = cur;
   return w;
 }
@@ -437,174 +420,6 @@ hipError_t matmul(e2b_model* m, int quant, int tag, const Lin& W, int rows, bool
     m->marks.push_back(mk);
   }
   return hipSuccess;
-}
-
-// Write-once activation slab of the persistent step: every region starts on
-// its own 256-byte boundary (no cache line holds two regions).
-void plan_slab(e2b_model* m) {
-  size_t cur = 0;
-  auto take = [&](size_t floats) {
-    const size_t o = cur;
-    cur = (cur + floats + 63) / 64 * 64;
-    return o;
-  };
-  const int H = m->H, P = m->P, L = m->L, nq = m->nq;
-  m->s_e = take(H);
-  m->s_tokple = take((size_t)L * P);
-  m->s_rope = take(m->c.head_dim + m->c.global_head_dim);
-  m->s_u = take((size_t)L * P);
-  m->s_pli = take((size_t)L * P);
-  m->slab.resize(L);
-  for (int l = 0; l < L; ++l) {
-    const LayerInfo& y = m->li[l];
-    e2b_model::SlabLayer& s = m->slab[l];
-    const int nqkv = (nq + (y.src == l ? 2 : 0)) * y.hd;
-    s.hq = take(H);
-    s.qkv_out = take(nqkv);
-    s.part = take((size_t)nq * e2b::kMaxChunks * (y.hd + 2));
-    s.attn = take((size_t)nq * y.hd);
-    s.oo = take((size_t)e2b::kMaxSplitK * H);
-    s.h1 = take(H);
-    s.gu_out = take(2 * (size_t)y.I);
-    s.dn = take((size_t)e2b::kMaxSplitK * H);
-    s.h2 = take(H);
-    s.pg_out = take(P);
-    s.ppo = take(H);
-  }
-  m->s_hfin = take(H);
-  m->s_cv = take(4096);
-  m->s_ci = take(4096);
-  m->slab_floats = cur;
-}
-
-void attn_chunks(const e2b_model* m, bool full, int rows, int* chunk, int* nchunk);
-
-// Fill the persistent step's plan in the arena (synchronous copy); needs the
-// weights loaded and the K/V cache bound.  Disables the step when the device
-// cannot hold the whole grid at once or a phase would not fit it.
-int upload_step_plan(e2b_model* m) {
-  m->step_ready = false;
-  if (m->step_variant < 0 || !m->loaded || !m->kv) return E2B_OK;
-  m->step_grid = e2b::step1_grid(m->step_variant, m->quant);
-  const int G = m->step_grid;
-  if (G < 1) return E2B_OK;
-  std::vector<e2b::StepLayer> plan(m->L);
-  double bytes = 0;
-  auto lin_bytes = [&](const Lin& W) {
-    return m->quant ? (double)W.N * W.K / 2 + (double)W.N * (W.K / 32) * 2 : (double)W.N * W.K * 2;
-  };
-  for (int l = 0; l < m->L; ++l) {
-    const LayerInfo& y = m->li[l];
-    const LayerDev& d = m->ld[l];
-    const e2b_model::SlabLayer& s = m->slab[l];
-    e2b::StepLayer& p = plan[l];
-    p.qkv = d.qkv;
-    p.o = d.o;
-    p.gu = d.gu;
-    p.down = d.down;
-    p.pg = d.pg;
-    p.pp = d.pp;
-    p.g_in = d.g_in;
-    p.g_q = d.g_q;
-    p.g_k = d.g_k;
-    p.g_pa = d.g_pa;
-    p.g_pf = d.g_pf;
-    p.g_ff = d.g_ff;
-    p.g_pple = d.g_pple;
-    p.scalar = d.scalar;
-    p.kc = m->kc[y.src];
-    p.vc = m->vc[y.src];
-    p.owns = y.src == l;
-    p.kc_own = p.owns ? m->kc[l] : nullptr;
-    p.vc_own = p.owns ? m->vc[l] : nullptr;
-    p.hd = y.hd;
-    p.full = y.full;
-    p.I = y.I;
-    attn_chunks(m, y.full, 1, &p.chunk, &p.nchunk);
-    p.hq = s.hq;
-    p.qkv_out = s.qkv_out;
-    p.part = s.part;
-    p.attn = s.attn;
-    p.oo = s.oo;
-    p.h1 = s.h1;
-    p.gu_out = s.gu_out;
-    p.dn = s.dn;
-    p.h2 = s.h2;
-    p.pg_out = s.pg_out;
-    p.ppo = s.ppo;
-    // every phase must fit the grid: attention chunks (+ the per-layer input
-    // slices in layer 0), combine heads, K slices of each product
-    if (p.nchunk + (l == 0 ? m->L : 0) > G || m->nq > G) return E2B_OK;
-    for (const Lin* W : {&d.qkv, &d.o, &d.gu, &d.down, &d.pg, &d.pp})
-      if (e2b::gemv_splits(W->K) > G) return E2B_OK;
-    bytes += lin_bytes(d.qkv) + lin_bytes(d.o) + lin_bytes(d.gu) + lin_bytes(d.down) +
-             lin_bytes(d.pg) + lin_bytes(d.pp);
-  }
-  if (G > 4096) return E2B_OK;  // argmax candidate region
-  CK(hipMemcpy(m->arena + m->off_step, plan.data(), sizeof(e2b::StepLayer) * plan.size(),
-               hipMemcpyHostToDevice),
-     "step plan upload");
-  m->step_bytes = bytes + lin_bytes(m->plmp) + 2.0 * m->V * m->H;
-  m->step_ready = true;
-  return E2B_OK;
-}
-
-int run_step1(e2b_model* m, const int32_t* d_tokens, const int32_t* d_positions, float* d_logits,
-              int32_t* d_argmax, char* ws, const Ws& W, hipStream_t st) {
-  e2b::StepArgs a;
-  a.layers = reinterpret_cast<const e2b::StepLayer*>(m->arena + m->off_step);
-  a.slab = reinterpret_cast<float*>(ws + W.slab);
-  a.bar = reinterpret_cast<unsigned long long*>(ws + W.bar);
-  a.err = reinterpret_cast<int*>(ws + W.err);
-  a.tokens = d_tokens;
-  a.positions = d_positions;
-  a.logits = d_logits;
-  a.argmax = d_argmax;
-  a.embed = m->embed;
-  a.ple = m->ple;
-  a.g_plpn = m->g_plpn;
-  a.g_final = m->g_final;
-  a.inv_s = m->invf[0];
-  a.inv_f = m->invf[1];
-  a.plmp = m->plmp;
-  a.lm.w = m->embed;
-  a.lm.N = m->V;
-  a.lm.K = m->H;
-  a.e = m->s_e;
-  a.tokple = m->s_tokple;
-  a.rope = m->s_rope;
-  a.u = m->s_u;
-  a.pli = m->s_pli;
-  a.hfin = m->s_hfin;
-  a.cand_v = m->s_cv;
-  a.cand_i = m->s_ci;
-  a.L = m->L;
-  a.H = m->H;
-  a.P = m->P;
-  a.V = m->V;
-  a.nq = m->nq;
-  a.hd_s = m->c.head_dim;
-  a.hd_f = m->c.global_head_dim;
-  a.window = m->c.sliding_window;
-  a.max_ctx = m->max_ctx;
-  a.eps = m->c.rms_eps;
-  a.sqrtH = std::sqrt((float)m->H);
-  a.sqrtP = std::sqrt((float)m->P);
-  a.inv_sqrtH = 1.0f / std::sqrt((float)m->H);
-  a.trace = m->step_trace ? reinterpret_cast<unsigned long long*>(ws + W.trace) : nullptr;
-  const bool prof = m->prof_kind == E2B_KIND_STEP;
-  e2b_model::Mark mk{};
-  if (prof) {
-    CK(hipEventCreate(&mk.a), "profile event");
-    CK(hipEventCreate(&mk.b), "profile event");
-    e2b::set_launch_events(mk.a, mk.b);
-  }
-  CK(e2b::launch_step1(m->step_variant, m->quant, a, m->step_grid, st), "decode step");
-  if (prof) {
-    mk.bytes = m->step_bytes;
-    m->marks.push_back(mk);
-  }
-  return E2B_OK;
 }
 
 // One pass over R.n rows: all layers, then (if head) the final norm, lm_head
@@ -939,18 +754,6 @@ int e2b_create(const e2b_config* cfg, e2b_model** out) {
     return fail(E2B_EINVAL, "hidden_size %d must be a single slice (<=512, 1536 or 2048)", m->H);
   }
   build_plan(m);
-  {
-    const int I0 = c.intermediate_size, I1 = I0 * (c.use_double_wide_mlp ? 2 : 1);
-    // the persistent one-row step is opt-in: on MI355X its grid barrier plus
-    // coherent hand-off costs about as much per phase as a kernel boundary in
-    // a graph, so the per-phase kernels stay the default
-    const char* env = getenv("E2B_PERSISTENT_STEP");
-    if (env && env[0] == '1')
-      m->step_variant = e2b::step1_variant(m->H, m->P, m->nq, c.head_dim, c.global_head_dim, I0, I1);
-    if (m->step_variant >= 0) plan_slab(m);
-    const char* tr = getenv("E2B_STEP_TRACE");
-    m->step_trace = tr && tr[0] == '1';
-  }
   *out = m;
   return E2B_OK;
 }
@@ -1081,7 +884,7 @@ int e2b_load_weights(e2b_model* m, const e2b_tensor* t, int n, void* d_arena, si
   }
   CK(hipStreamSynchronize(st), "weight tiling sync");
   m->loaded = true;
-  return upload_step_plan(m);
+  return E2B_OK;
 }
 
 int e2b_kv_alloc(e2b_model* m, void* d_kv, size_t bytes, int max_batch, int max_ctx) {
@@ -1109,7 +912,7 @@ int e2b_kv_alloc(e2b_model* m, void* d_kv, size_t bytes, int max_batch, int max_
       m->kc[l] = m->kc[m->li[l].src];
       m->vc[l] = m->vc[m->li[l].src];
     }
-  return upload_step_plan(m);
+  return E2B_OK;
 }
 
 }  // extern "C"
@@ -1132,9 +935,6 @@ int decode_impl(e2b_model* m, const int32_t* d_tokens, const int32_t* d_position
     return fail(E2B_ENOMEM, "workspace of %zu bytes < %zu required", ws_bytes, W.total);
   if (reinterpret_cast<uintptr_t>(d_ws) % kAlign)
     return fail(E2B_EINVAL, "workspace must be %zu-byte aligned", kAlign);
-  if (batch == 1 && m->step_ready && (m->prof_kind == 0 || m->prof_kind == E2B_KIND_STEP))
-    return run_step1(m, d_tokens, d_positions, d_logits, d_argmax, reinterpret_cast<char*>(d_ws), W,
-                     reinterpret_cast<hipStream_t>(stream));
   e2b::Rows R;
   R.tokens = d_tokens;
   R.positions = d_positions;
@@ -1206,17 +1006,32 @@ int e2b_kv_view(const e2b_model* m, int layer, int which, void** out) {
 }
 
 namespace {
-// Workspace of e2b_matvec: the K-slice partials of the one-row matvec
-// kernel or of the several-row matrix-core product (none when unsplit).
+// Workspace of e2b_matvec: the K-slice partials of the one-row matvec kernel
+// or of the several-row matrix-core product (none when unsplit), then, for
+// several rows with N % 16 == 0, the copy of the weights tiled in the
+// matrix-core fragment order that batched decode reads (the arena holds one
+// per linear; here it is built in the workspace).
 struct MvWs {
-  size_t part, total;
+  size_t part, tq, ts, total;
   int nks;
+  bool tiled;
 };
 MvWs matvec_ws(int quant, int N, int K, int rows) {
   MvWs w{};
   w.nks = rows == 1 ? e2b::gemv_splits(K) : e2b::gemm_plan(quant, N, K, true).nks;
+  size_t cur = 0;
   w.part = 0;
-  w.total = w.nks > 1 ? (size_t)w.nks * rows * N * sizeof(float) : 0;
+  if (w.nks > 1) cur = align_up((size_t)w.nks * rows * N * sizeof(float));
+  w.tiled = rows > 1 && N % 16 == 0;
+  if (w.tiled) {
+    w.tq = cur;
+    cur = align_up(cur + (quant ? (size_t)N * K / 2 : (size_t)N * K * 2));
+    if (quant) {
+      w.ts = cur;
+      cur = align_up(cur + (size_t)N * (K / 32) * 2);
+    }
+  }
+  w.total = cur;
   return w;
 }
 }  // namespace
@@ -1255,6 +1070,19 @@ int e2b_matvec(int quant, const void* d_w, const uint16_t* d_scale, int N, int K
     W.q = reinterpret_cast<const uint32_t*>(d_w);
     W.s = d_scale;
   }
+  if (L.tiled) {
+    if (quant == E2B_QUANT_BF16) {
+      uint16_t* tw = reinterpret_cast<uint16_t*>(ws + L.tq);
+      CK(e2b::launch_tile_bf16(W, tw, st), "matvec tiling");
+      W.tw = tw;
+    } else {
+      uint32_t* tq = reinterpret_cast<uint32_t*>(ws + L.tq);
+      uint16_t* ts = reinterpret_cast<uint16_t*>(ws + L.ts);
+      CK(e2b::launch_tile_w4(W, tq, ts, st), "matvec tiling");
+      W.tq = tq;
+      W.ts = ts;
+    }
+  }
   e2b::Prologue pr;
   pr.kind = e2b::kPlain;
   pr.a = d_x;
@@ -1273,6 +1101,39 @@ int e2b_matvec(int quant, const void* d_w, const uint16_t* d_scale, int N, int K
        "matvec mfma");
   }
   if (L.nks > 1) CK(e2b::launch_sum_partials(L.nks, (size_t)rows * N, ep.y, d_y, st), "matvec sum");
+  return E2B_OK;
+}
+
+int e2b_embed(e2b_model* m, const int32_t* d_tokens, int n, float* d_h, float* d_tokple, void* d_ws,
+              size_t ws_bytes, void* stream) {
+  if (!m || !d_tokens || !d_h || !d_tokple || !d_ws) return fail(E2B_EINVAL, "null argument");
+  if (!m->loaded) return fail(E2B_ESTATE, "weights not loaded");
+  if (n < 1 || n > kMaxCtlRows) return fail(E2B_ERANGE, "n %d outside [1, %d]", n, kMaxCtlRows);
+  const Ws W = ws_layout(m, n);
+  if (ws_bytes < W.total)
+    return fail(E2B_ENOMEM, "workspace of %zu bytes < %zu required", ws_bytes, W.total);
+  if (reinterpret_cast<uintptr_t>(d_ws) % kAlign)
+    return fail(E2B_EINVAL, "workspace must be %zu-byte aligned", kAlign);
+  if (reinterpret_cast<uintptr_t>(d_h) % 16 || reinterpret_cast<uintptr_t>(d_tokple) % 16)
+    return fail(E2B_EINVAL, "outputs must be 16-byte aligned");
+  char* ws = reinterpret_cast<char*>(d_ws);
+  e2b::Rows R;
+  R.tokens = d_tokens;
+  R.positions = nullptr;  // rows at positions 0..n-1 (the RoPE angles go to the workspace)
+  R.pos0 = 0;
+  R.n = n;
+  R.max_ctx = n;
+  R.vocab = m->V;
+  e2b::RopeTable rt;
+  rt.out = reinterpret_cast<float*>(ws + W.rope);
+  rt.inv_s = m->invf[0];
+  rt.inv_f = m->invf[1];
+  rt.hd_s = m->c.head_dim;
+  rt.hd_f = m->c.global_head_dim;
+  CK(e2b::launch_embed(R, m->embed, m->ple, m->H, m->L * m->P, std::sqrt((float)m->H),
+                       std::sqrt((float)m->P), d_h, d_tokple, reinterpret_cast<int*>(ws + W.err), rt,
+                       reinterpret_cast<hipStream_t>(stream)),
+     "embed");
   return E2B_OK;
 }
 
@@ -1342,7 +1203,7 @@ static void drop_marks(e2b_model* m) {
 
 int e2b_profile_begin(e2b_model* m, int kind) {
   if (!m) return fail(E2B_EINVAL, "null argument");
-  if (kind < E2B_KIND_NONE || kind > E2B_KIND_STEP) return fail(E2B_EINVAL, "bad kind %d", kind);
+  if (kind < E2B_KIND_NONE || kind > E2B_KIND_LM_HEAD) return fail(E2B_EINVAL, "bad kind %d", kind);
   drop_marks(m);
   m->prof_kind = kind;
   return E2B_OK;
@@ -1380,17 +1241,9 @@ int e2b_check(e2b_model* m, void* d_ws, void* stream) {
   if (!w[0]) return E2B_OK;
   const int zero[4] = {0, 0, 0, 0};
   CK(hipMemcpy(d_ws, zero, sizeof zero, hipMemcpyHostToDevice), "check: clear error word");
-  if (w[0] & e2b::kErrSync) {  // the persistent step gave up at a barrier: restart its counters
-    const Ws W = ws_layout(m, 1);
-    std::vector<char> z(e2b::step1_barrier_bytes(), 0);
-    CK(hipMemcpy(reinterpret_cast<char*>(d_ws) + W.bar, z.data(), z.size(), hipMemcpyHostToDevice),
-       "check: reset barrier");
-  }
-  return fail(E2B_EDEVICE, "device flagged%s%s%s (token %d, position %d, row %d)",
+  return fail(E2B_EDEVICE, "device flagged%s%s (token %d, position %d, row %d)",
               (w[0] & e2b::kErrToken) ? " a token outside the vocabulary" : "",
-              (w[0] & e2b::kErrPos) ? " a position outside [0, max_ctx)" : "",
-              (w[0] & e2b::kErrSync) ? " a grid barrier of the persistent step timed out" : "", w[1],
-              w[2], w[3]);
+              (w[0] & e2b::kErrPos) ? " a position outside [0, max_ctx)" : "", w[1], w[2], w[3]);
 }
 
 }  // extern "C"

@@ -439,11 +439,11 @@ hipError_t launch_gemv(int quant, int tag, const Lin& W, int rows, const Prologu
 // ------------------------------------------------------------ decode attention
 template <int HD>
 __global__ __launch_bounds__(256) void k_attn_dec(Rows R, AttnArgs a) {
-  attn_chunk<HD, false>(R, a, blockIdx.x, blockIdx.y);
+  attn_chunk<HD>(R, a, blockIdx.x, blockIdx.y);
 }
 
 __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a) {
-  attn_combine<false>(a, blockIdx.x, blockIdx.y);
+  attn_combine(a, blockIdx.x, blockIdx.y);
 }
 
 // Prefill: K/V of every row written before attention.  Block per row, wave 0

@@ -28,7 +28,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 
 def kernels_sha():
     h = hashlib.sha1()
-    for f in ("kernels.hip", "step1.hip", "dev_common.h", "e2b_internal.h"):
+    for f in ("kernels.hip", "dev_common.h", "e2b_internal.h"):
         with open(os.path.join(HERE, "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
