@@ -218,6 +218,23 @@ int e2b_matvec(int quant, const void* d_w, const uint16_t* d_scale, int N, int K
                const float* d_x, int rows, float* d_y, void* d_ws, size_t ws_bytes,
                void* stream);
 
+/* e2b_matvec for callers that cannot allocate device memory or pass a
+ * workspace: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation.  Same arguments, arithmetic and results as
+ * e2b_matvec, without d_ws: the K-slice partial sums go to a scratch array
+ * of e2b_matvec_noalloc_max_bytes() bytes (16 MiB) that the library holds on
+ * each device it runs on until the process ends; several rows read the
+ * row-major weights directly (no tiled copy is built).  E2B_ENOMEM if the
+ * product's partials (slices x rows x N x 4 bytes, the plan e2b_matvec uses)
+ * exceed the scratch.  Calls no allocating routine.  Every call on a device
+ * shares that device's scratch, so calls that overlap in time on one device
+ * (on different streams or threads) race and must be serialised by the
+ * caller; nothing in the scratch needs to start at zero (each call writes
+ * every partial it reads).  Asynchronous. */
+size_t e2b_matvec_noalloc_max_bytes(void);
+int e2b_matvec_noalloc(int quant, const void* d_w, const uint16_t* d_scale, int N, int K,
+                       const float* d_x, int rows, float* d_y, void* stream);
+
 /* The embedding gathers of the step for n tokens, on their own: d_h[r][i] =
  * E[t_r][i] * sqrt(H) (the tied table, [P4] cell 2.2) and d_tokple[r][j] =
  * E_ple[t_r][j] * sqrt(P) for j < L * P (the per-layer table, [P3] Step 3),

@@ -91,9 +91,12 @@ def load_library():
     L.e2b_matvec_workspace_bytes.argtypes = [i32, i32, i32, i32]
     L.e2b_matvec.argtypes = [i32, vp, vp, i32, i32, vp, i32, vp, vp, sz, vp]
     L.e2b_embed.argtypes = [vp, vp, i32, vp, vp, vp, sz, vp]
+    L.e2b_matvec_noalloc_max_bytes.restype = sz
+    L.e2b_matvec_noalloc_max_bytes.argtypes = []
+    L.e2b_matvec_noalloc.argtypes = [i32, vp, vp, i32, i32, vp, i32, vp, vp]
     for f in ("e2b_config_preset", "e2b_create", "e2b_kv_share_map", "e2b_load_weights",
               "e2b_kv_alloc", "e2b_decode_step", "e2b_prefill", "e2b_check", "e2b_kv_view",
-              "e2b_matvec", "e2b_embed", "e2b_graph_capture", "e2b_graph_replay", "e2b_profile_begin",
+              "e2b_matvec", "e2b_matvec_noalloc", "e2b_embed", "e2b_graph_capture", "e2b_graph_replay", "e2b_profile_begin",
               "e2b_profile_read"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L

@@ -9,6 +9,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -1101,6 +1102,96 @@ int e2b_matvec(int quant, const void* d_w, const uint16_t* d_scale, int N, int K
        "matvec mfma");
   }
   if (L.nks > 1) CK(e2b::launch_sum_partials(L.nks, (size_t)rows * N, ep.y, d_y, st), "matvec sum");
+  return E2B_OK;
+}
+
+}  // extern "C"
+
+// ---- allocation-free matrix-vector product --------------------------------
+// The K-slice partials of e2b_matvec_noalloc live in this array, one copy per
+// device, held until the process ends.  In host code `scratch` is only a
+// host-side stand-in for the symbol: its device address on each device comes
+// from hipGetSymbolAddress (resolved once per device, with that device
+// current) and only that address is handed to kernels.
+namespace {
+constexpr size_t kScratchBytes = size_t(16) << 20;
+}
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+std::vector<void*> g_scratch_dev;  // device address of `scratch`, by device ordinal
+
+int scratch_address(void** out) {
+  int dev = -1;
+  CK(hipGetDevice(&dev), "noalloc: current device");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if ((int)g_scratch_dev.size() <= dev) g_scratch_dev.resize(dev + 1, nullptr);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    CK(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "noalloc: scratch address");
+    if (!p) return fail(E2B_EHIP, "noalloc: scratch address is null");
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return E2B_OK;
+}
+}  // namespace
+
+extern "C" {
+
+size_t e2b_matvec_noalloc_max_bytes(void) { return kScratchBytes; }
+
+int e2b_matvec_noalloc(int quant, const void* d_w, const uint16_t* d_scale, int N, int K,
+                       const float* d_x, int rows, float* d_y, void* stream) {
+  if (!d_w || !d_x || !d_y || (quant == E2B_QUANT_W4A16 && !d_scale))
+    return fail(E2B_EINVAL, "null argument");
+  if (quant != E2B_QUANT_BF16 && quant != E2B_QUANT_W4A16)
+    return fail(E2B_EINVAL, "unknown quant mode %d", quant);
+  if (N < 1 || rows < 1 || rows > 65535 || K % 32 || !supported_k(K))
+    return fail(E2B_EINVAL, "unsupported shape N=%d K=%d rows=%d", N, K, rows);
+  if (reinterpret_cast<uintptr_t>(d_w) % 16) return fail(E2B_EINVAL, "weights must be 16-byte aligned");
+  if (rows > 1 && reinterpret_cast<uintptr_t>(d_x) % 16)
+    return fail(E2B_EINVAL, "x must be 16-byte aligned for several rows");
+  // the same product plan as e2b_matvec; only its K-slice partials need room
+  const int nks = rows == 1 ? e2b::gemv_splits(K) : e2b::gemm_plan(quant, N, K, true).nks;
+  const size_t need = nks > 1 ? (size_t)nks * rows * N * sizeof(float) : 0;
+  if (need > kScratchBytes)
+    return fail(E2B_ENOMEM, "noalloc: %zu bytes of K-slice partials exceed the %zu-byte scratch", need,
+                kScratchBytes);
+  void* sp = nullptr;
+  if (need) {
+    const int rc = scratch_address(&sp);
+    if (rc) return rc;
+  }
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  Lin W;
+  W.N = N;
+  W.K = K;
+  if (quant == E2B_QUANT_BF16) {
+    W.w = reinterpret_cast<const uint16_t*>(d_w);
+  } else {
+    W.q = reinterpret_cast<const uint32_t*>(d_w);
+    W.s = d_scale;
+  }
+  e2b::Prologue pr;
+  pr.kind = e2b::kPlain;
+  pr.a = d_x;
+  pr.lda = K;
+  e2b::Epilogue ep;
+  ep.y = need ? reinterpret_cast<float*>(sp) : d_y;
+  if (rows == 1) {
+    CK(e2b::launch_gemv(quant, e2b::kTagOther, W, rows, pr, ep, 0, nullptr, st), "matvec");
+  } else {
+    e2b::GemmA A;
+    A.a = d_x;
+    A.kind = e2b::kPlain;
+    A.lda = K;
+    CK(e2b::launch_gemm(quant, e2b::kTagOther, W, rows, A, e2b::gemm_plan(quant, N, K, true), ep,
+                        nullptr, st),
+       "matvec mfma");
+  }
+  if (need) CK(e2b::launch_sum_partials(nks, (size_t)rows * N, ep.y, d_y, st), "matvec sum");
   return E2B_OK;
 }
 
