@@ -4,35 +4,45 @@
 One "step" is one greedy decode step of the whole path (embedding and
 per-layer inputs, 35 layers, tied lm_head, argmax) for every sequence of the
 batch.  Default workload: E2B shape, bf16 weights (random init N(0, 0.02),
-seed 0), batch 1, a 128-token random prompt, then 512 greedy steps (KV length
-129..640).  The prompt is prefilled before timing; warm-up steps are run and
-then the positions and tokens are reset, so the timed steps cover exactly
-positions 128..128+K-1.  Each step is one replay of a HIP graph captured by
-the library (one graph launch per step; tokens and positions advance on the
-device).
+seed 0), batch 1, a 128-token random prompt, then K greedy steps (KV length
+129..128+K).  The prompt is prefilled before timing; warm-up steps are run and
+then the positions and tokens are reset, so every timed loop covers exactly
+positions 128..128+K-1.  Each step is one replay of a HIP graph captured by the
+library (one graph launch per step; tokens and positions advance on the
+device).  The loop of K steps is timed --repeats times (HIP events on the
+stream, synchronised on both sides); value is the median.
 
 Prints one JSON line on stdout (progress goes to stderr):
-  value      tok/s = batch * K / (timed seconds) of the headline workload
-  roofline   the kernel kind with the largest share of step time: algorithmic
-             bytes per launch / mean launch duration (HIP events around each
-             launch of that kind on its stream, eager steps queued behind a
-             spin kernel so the host never starves the GPU) vs 8 TB/s;
+  value      tok/s = batch * K / (median timed seconds) of the headline workload
+  repeats    every repeat's loop time, median and interquartile range
+  roofline   the dominant kernel (the kind with the largest share of step
+             time): algorithmic bytes per launch / mean launch duration (the
+             dispatch's own timestamps, eager steps queued behind a spin
+             kernel) vs 8 TB/s, and vs the calibrated streaming read;
              traffic = HBM bytes per launch from the committed PMC profile of
-             the same kernels (null if the kernel source changed since)
+             the same kernels (null if the kernel sources changed since)
   step_roofline  algorithmic bytes of the whole step (weights streamed once +
-             unique K/V read + K/V write + gathers) / step time vs 8 TB/s
-  cpu_baseline   the fp64 oracle on this host's cores, teacher-forced on the
-             GPU's tokens, over a bounded sample of the same workload
-  also       the same measurement for W4A16 and for batch 64 (unless --no-aux)
+             unique K/V read + K/V write + gathers) / step time, vs 8 TB/s and
+             vs the calibrated streaming read
+  calibration    a plain streaming reduction over 4 GiB: the read bandwidth
+             this device sustains (best of 5)
+  kernel_kinds   per-launch time and achieved GB/s of every profiled kind
+             (attention: unique and logical K/V bytes)
+  prefill    the 128-token prompt through e2b_prefill (one 128-row pass): ms
+  cpu_baseline   the fp64 oracle on this host's cores (and on one core),
+             teacher-forced on the GPU's tokens, over a bounded sample
+  also       W4A16 B=1, bf16 and W4A16 B=64, and the long-context workload
+             (W4A16, B=1 and 8, contexts 500 / 4,000 / 8,000) unless --no-aux
 
---long: the long-context workload instead (W4A16, batch 1 or 8 via --batch,
+--long: the long-context workload alone (W4A16, batch 1 or 8 via --batch,
 context grown 500 -> 8,000 by 500-token prefill chunks, 64 timed decode
 steps at each length, decoded positions rolled back before the next chunk).
 """
 import argparse
-import hashlib
 import json
 import os
+import re
+import statistics
 import sys
 import time
 
@@ -41,20 +51,13 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK = 8.0e12  # MI355X HBM3E, bytes/s
 METRIC = "decode tok/s at batch 1 and 64 (E2B shape, bf16 & W4A16); % of HBM roofline"
-KINDS = ["gate_up", "down", "lm_head", "qkv", "o"]
+KINDS = ["gate_up", "down", "lm_head", "qkv", "o", "attn"]
 PMC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+TAGS = {"qkv": 1, "o": 2, "gate_up": 3, "down": 4, "lm_head": 8}
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
-
-
-def kernels_sha():
-    h = hashlib.sha1()
-    for f in ("kernels.hip", "dev_common.h", "e2b_internal.h"):
-        with open(os.path.join(ROOT, "w4a16_weight_streaming_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()
 
 
 def step_bytes(cfg, quant, batch, positions):
@@ -75,49 +78,62 @@ def step_bytes(cfg, quant, batch, positions):
         elif s.kind in ("gain", "scalar"):
             gain += 2 * n
     weights = lin + 2 * V * H + gain
+    kv_read = sum(kv_bytes(cfg, p, unique=True) for p in positions) / len(positions)
     first = L - cfg["num_kv_shared_layers"]
-    kv_read = 0
-    for p in positions:
-        T = p + 1
-        for l in range(first):
-            hd = synth.layer_head_dim(cfg, l)
-            t = T if synth.layer_is_full(cfg, l) else min(T, cfg["sliding_window"])
-            kv_read += 2 * 2 * hd * t
     kv_write = 2 * 2 * sum(synth.layer_head_dim(cfg, l) for l in range(first))
     gathers = 2 * H + 2 * L * P
-    per_step = weights + (kv_read / len(positions)) * batch + batch * (kv_write + gathers)
+    per_step = weights + kv_read * batch + batch * (kv_write + gathers)
     return per_step, weights
 
 
-def pmc_traffic(kernel_symbol):
-    """HBM bytes per launch of a kernel from the committed PMC profile, or None
-    if there is none or the kernel sources changed since it was taken."""
+def kv_bytes(cfg, pos, unique):
+    """K/V bytes one sequence's attention reads at position pos: every layer
+    that owns K/V (unique) or every layer (logical: sharing layers re-read
+    their source's cache)."""
+    import synth
+    L = cfg["num_hidden_layers"]
+    first = L - cfg["num_kv_shared_layers"]
+    T, tot = pos + 1, 0
+    for l in range(first if unique else L):
+        hd = synth.layer_head_dim(cfg, l)
+        t = T if synth.layer_is_full(cfg, l) else min(T, cfg["sliding_window"])
+        tot += 2 * 2 * hd * t
+    return tot
+
+
+def pmc_traffic(pattern):
+    """HBM bytes per launch (dispatch-weighted mean over the kernels whose
+    symbol matches `pattern`) from the committed PMC profile, or None if there
+    is none or the kernel sources changed since it was taken."""
     try:
         with open(PMC_FILE) as f:
             d = json.load(f)
     except (OSError, ValueError):
         return None
+    from w4a16_weight_streaming_amd.pmc import kernels_sha
     if d.get("kernels_sha") != kernels_sha():
         return None
-    k = d.get("kernels", {}).get(kernel_symbol)
-    if not k:
+    rx = re.compile(pattern)
+    hits = [k for name, k in d.get("kernels", {}).items() if rx.fullmatch(name)]
+    n = sum(k["dispatches"] for k in hits)
+    if not n:
         return None
-    return k["fetch_bytes"] * d["fetch_factor"] + k["write_bytes"] * d["write_factor"]
+    return sum((k["fetch_bytes"] * d["fetch_factor"] + k["write_bytes"] * d["write_factor"]) * k["dispatches"]
+               for k in hits) / n
 
 
-# kernel symbol (as rocprof names it) of each kind, by quant and batch path
-# (one row: o is one K slice per head, the sliding layers' 256 named here)
-def kernel_symbol(kind, quant, batch):
-    tag = {"qkv": 1, "o": 2, "gate_up": 3, "down": 4, "lm_head": 8}[kind]
+def kernel_pattern(kind, quant, batch):
+    """Regular expression of the kernel symbols (as rocprof names them) that
+    run this kind at this batch: the one-row matvec, or the matrix-core
+    product with its m-tiles per block."""
+    if kind not in TAGS:
+        return None
+    tag = TAGS[kind]
+    wq = 0 if kind == "lm_head" else int(quant == "w4a16")
     if batch == 1:
-        wq = 0 if kind == "lm_head" else int(quant == "w4a16")
-        ks = {"o": 256, "down": 2048}.get(kind, 1536)
-        if ks == 1536:
-            u = (3 if kind == "gate_up" else 2) if wq else 4
-        else:
-            u = 2 if ks == 2048 else 4
-        return f"void e2b::k_gemv<{wq}, {ks}, {u}, {tag}>"
-    return None
+        return rf"void e2b::k_gemv<{wq}, \d+, \d+, {tag}>"
+    mt = 1 if batch <= 16 else (2 if batch <= 32 else 4)
+    return rf"void e2b::k_gemm<{wq}, \d+, {mt}, \d+, {tag}>"
 
 
 def spin(torch, ms):
@@ -126,7 +142,47 @@ def spin(torch, ms):
         torch.cuda._sleep(int(ms * 2.4e6))
 
 
-def measure(cfg, quant, B, P, K, W, prof_steps, eager=False, cpu_steps=0, label=""):
+def calibrate(torch):
+    """Best of 5 streaming reductions over 4 GiB (the read bandwidth a plain
+    stream sustains on this device), bytes/s."""
+    from w4a16_weight_streaming_amd import binding
+    L = binding.load_library()
+    buf = torch.ones(1 << 30, dtype=torch.float32, device="cuda:0")
+    out = torch.zeros(L.e2b_stream_reduce_blocks(), dtype=torch.float32, device="cuda:0")
+    binding.stream_reduce(buf, out)
+    best = 0.0
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        binding.stream_reduce(buf, out)
+        e1.record()
+        torch.cuda.synchronize()
+        best = max(best, buf.numel() * 4 / (e0.elapsed_time(e1) / 1e3))
+    total = float(out.double().sum())
+    assert abs(total - buf.numel()) < 1e-3 * buf.numel(), total   # the read covered every word
+    del buf, out
+    torch.cuda.empty_cache()
+    log(f"calibration: streaming reduction over 4 GiB at {best / 1e9:.0f} GB/s")
+    return best
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def quantiles(xs):
+    q = statistics.quantiles(xs, n=4) if len(xs) >= 2 else [xs[0]] * 3
+    return q[0], statistics.median(xs), q[2]
+
+
+def measure(cfg, quant, B, P, K, W, prof_steps, repeats, eager=False, cpu_steps=0, label=""):
     import numpy as np
     import torch
 
@@ -136,7 +192,7 @@ def measure(cfg, quant, B, P, K, W, prof_steps, eager=False, cpu_steps=0, label=
     V = cfg["vocab_size"]
     t0 = time.time()
     w = synth.generate(cfg, quant, seed=0)
-    max_ctx = P + max(K, W, prof_steps)
+    max_ctx = P + max(K, W, prof_steps) + 8
     eng = Engine(cfg, quant, w, max_batch=B, max_ctx=max_ctx, max_rows=min(128, max(B, P)))
     dev = eng.device
     log(f"[{label}] engine loaded ({eng.model.arena_bytes() / 1e9:.3f} GB arena) in {time.time() - t0:.1f}s")
@@ -144,8 +200,17 @@ def measure(cfg, quant, B, P, K, W, prof_steps, eager=False, cpu_steps=0, label=
     prompts = [synth.tokens(P, 1 + b, V) for b in range(B)]
     with torch.cuda.stream(stream):
         tok = torch.zeros(B, dtype=torch.int32, device=dev)
+        pdev = [torch.from_numpy(p).to(dev) for p in prompts]
+        eng.prefill(0, pdev[0], 0, tok[0:1])       # untimed first pass
+        stream.synchronize()
+        pre_ms = []
         for b in range(B):
-            eng.prefill(b, torch.from_numpy(prompts[b]).to(dev), 0, tok[b:b + 1])
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            eng.prefill(b, pdev[b], 0, tok[b:b + 1])
+            e1.record(stream)
+            e1.synchronize()
+            pre_ms.append(e0.elapsed_time(e1))
         eng.check()
         tok0 = tok.clone()
         pos = torch.full((B,), P, dtype=torch.int32, device=dev)
@@ -161,26 +226,29 @@ def measure(cfg, quant, B, P, K, W, prof_steps, eager=False, cpu_steps=0, label=
 
         run(W)
         stream.synchronize()
-        pos.fill_(P)
-        tok.copy_(tok0)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        run(K)
-        e1.record(stream)
-        torch.cuda.synchronize()
+        loops = []
+        for _ in range(repeats):
+            pos.fill_(P)
+            tok.copy_(tok0)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            run(K)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            loops.append(e0.elapsed_time(e1))
         eng.check()
-        ms = e0.elapsed_time(e1)
-    log(f"[{label}] timed {K} steps: {ms:.2f} ms")
+    q1, ms, q3 = quantiles(loops)
+    log(f"[{label}] {repeats} x {K} steps: median {ms:.2f} ms (IQR {q1:.2f}-{q3:.2f}); "
+        f"prefill {statistics.median(pre_ms):.2f} ms")
     ms_step = ms / K
     sb, wbytes = step_bytes(cfg, quant, B, list(range(P, P + K)))
 
     # per-kernel timing: eager steps at the same positions, each queued behind
-    # a spin kernel; each launch of one kind records its own start and end.
+    # a spin kernel; each launch of one kind records its own start and end
     prof, gpu_tokens = {}, []
-    kinds = KINDS
     with torch.cuda.stream(stream):
-        for i, kind in enumerate(kinds if prof_steps else []):
+        for i, kind in enumerate(KINDS if prof_steps else []):
             pos.fill_(P)
             tok.copy_(tok0)
             eng.profile_begin(kind)
@@ -191,9 +259,18 @@ def measure(cfg, quant, B, P, K, W, prof_steps, eager=False, cpu_steps=0, label=
                 if i == 0 and s < cpu_steps:
                     gpu_tokens.append(tok.cpu().numpy().copy())
             n, tms, tby = eng.profile_read()
-            prof[kind] = dict(launches=n, ms=tms / max(n, 1), bytes=tby / max(n, 1))
+            d = dict(launches=n, ms=tms / max(n, 1), bytes=tby / max(n, 1))
+            if kind == "attn":   # K/V bytes from the positions the steps covered
+                per = [B * kv_bytes(cfg, P + s, u) for s in range(prof_steps) for u in (True, False)]
+                d["bytes"] = sum(per[0::2]) / max(n, 1)          # unique, per launch
+                d["logical_bytes"] = sum(per[1::2]) / max(n, 1)
+            prof[kind] = d
     res = {"value": B * K / (ms / 1e3), "ms_per_step": ms_step, "step_bytes": sb, "weight_bytes": wbytes,
-           "kinds": prof, "graph": graph is not None}
+           "kinds": prof, "graph": graph is not None,
+           "repeats": {"n": repeats, "loop_ms": [round(x, 3) for x in loops], "median_ms": round(ms, 3),
+                       "iqr_ms": [round(q1, 3), round(q3, 3)]},
+           "prefill": {"tokens": P, "rows_per_pass": min(128, P), "ms_median": round(statistics.median(pre_ms), 3),
+                       "ms_min": round(min(pre_ms), 3), "sequences": B}}
     if prof:
         log(f"[{label}] kernel kinds: " + ", ".join(
             f"{k}: {v['ms'] * 1e3:.1f} us x{v['launches'] // prof_steps} = {v['bytes'] / (v['ms'] / 1e3) / 1e9:.0f} GB/s"
@@ -201,7 +278,7 @@ def measure(cfg, quant, B, P, K, W, prof_steps, eager=False, cpu_steps=0, label=
 
     if cpu_steps > 0:
         import oracle
-        threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
+        threads = oracle.get_threads()
         orc = oracle.Oracle(cfg, quant, w, 1, max_ctx)
         tpf = time.time()
         orc.prefill(0, prompts[0], logits=False)
@@ -211,10 +288,22 @@ def measure(cfg, quant, B, P, K, W, prof_steps, eager=False, cpu_steps=0, label=
         for i, t in enumerate(feed):
             orc.step(0, t, P + i)
         dt = time.time() - tc
+        # one core: a few further steps on the same cache
+        one = min(4, len(feed))
+        oracle.set_threads(1)
+        t1 = time.time()
+        for i in range(one):
+            orc.step(0, feed[i], P + len(feed) + i)
+        dt1 = time.time() - t1
+        oracle.set_threads(threads)
+        log(f"[{label}] oracle: {len(feed) / dt:.2f} tok/s on {threads} threads, {one / dt1:.3f} on 1")
         res["cpu_baseline"] = {
             "value": round(len(feed) / dt, 4), "unit": "tok/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(), "precision": "fp64",
+            "value_1_core": round(one / dt1, 4),
             "sample": f"sequence 0: {len(feed)} teacher-forced decode steps at positions "
-                      f"{P}..{P + len(feed) - 1} after an untimed {P}-token prefill, fp64"}
+                      f"{P}..{P + len(feed) - 1} after an untimed {P}-token prefill, fp64, on {threads} "
+                      f"threads; then {one} steps at positions {P + len(feed)}.. on 1 thread"}
         orc.close()
     del eng, graph
     torch.cuda.synchronize()
@@ -222,37 +311,50 @@ def measure(cfg, quant, B, P, K, W, prof_steps, eager=False, cpu_steps=0, label=
     return res
 
 
-def roofline_of(res, quant, B):
-    prof = res["kinds"]
+def roofline_of(res, quant, B, calib):
+    prof = {k: v for k, v in res["kinds"].items()}
     dom = max(prof, key=lambda k: prof[k]["ms"] * prof[k]["launches"])
     d = prof[dom]
     achieved = d["bytes"] / (d["ms"] / 1e3)
-    sym = kernel_symbol(dom, quant, B)
-    traffic = pmc_traffic(sym) if sym else None
-    return {"bound": "hbm", "kernel": dom, "symbol": sym, "achieved": round(achieved / 1e9, 1),
-            "peak": HBM_PEAK / 1e9, "unit": "GB/s", "frac": round(achieved / HBM_PEAK, 4),
+    pat = kernel_pattern(dom, quant, B)
+    traffic = pmc_traffic(pat) if pat else None
+    return {"scope": "dominant kernel", "bound": "hbm", "kernel": dom, "symbols": pat,
+            "achieved": round(achieved / 1e9, 1), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK, 4),
+            "frac_calibrated": round(achieved / calib, 4) if calib else None,
             "traffic": None if traffic is None else int(traffic),
             "bytes_per_launch": int(d["bytes"]), "mean_launch_us": round(d["ms"] * 1e3, 2)}
 
 
-def step_roofline(res):
+def step_roofline(res, calib):
     ms = res["ms_per_step"]
+    a = res["step_bytes"] / (ms / 1e3)
     return {"bytes_per_step": int(res["step_bytes"]), "weight_bytes": int(res["weight_bytes"]),
-            "achieved": round(res["step_bytes"] / (ms / 1e3) / 1e9, 1), "peak": HBM_PEAK / 1e9,
-            "unit": "GB/s", "frac": round(res["step_bytes"] / (ms / 1e3) / HBM_PEAK, 4)}
+            "achieved": round(a / 1e9, 1), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+            "frac": round(a / HBM_PEAK, 4), "frac_calibrated": round(a / calib, 4) if calib else None}
 
 
-def long_context(args):
-    """Context 500 -> 8,000 in 500-token prefill chunks; 64 timed decode steps
-    per length, then the decoded positions are rolled back."""
-    import numpy as np
+def kinds_summary(res, steps):
+    out = {}
+    for k, v in res["kinds"].items():
+        e = {"mean_us": round(v["ms"] * 1e3, 2), "per_step": v["launches"] // max(steps, 1),
+             "GBps": round(v["bytes"] / (v["ms"] / 1e3) / 1e9, 1) if v["ms"] else None}
+        if "logical_bytes" in v and v["ms"]:
+            e["GBps_logical"] = round(v["logical_bytes"] / (v["ms"] / 1e3) / 1e9, 1)
+        out[k] = e
+    return out
+
+
+def long_context(quant, B, lengths=None, steps=64, chunk=500, top=8000):
+    """Context 500 -> 8,000 in 500-token prefill chunks; `steps` timed decode
+    steps at each measured length, then the decoded positions are rolled back.
+    Returns per-length rows (tok/s, step fraction, prefill ms of the chunk)."""
     import torch
 
     import synth
     from w4a16_weight_streaming_amd import Engine
 
     cfg = synth.get_config("e2b")
-    quant, B, chunk, steps, top = args.quant, args.batch, 500, 64, 8000
     V = cfg["vocab_size"]
     w = synth.generate(cfg, quant, seed=0)
     eng = Engine(cfg, quant, w, max_batch=B, max_ctx=top + steps, max_rows=128)
@@ -265,11 +367,18 @@ def long_context(args):
         graph = eng.capture(tok, pos, tok, advance=True)
         for c in range(top // chunk):
             L0 = c * chunk
-            for b in range(B):
-                t = synth.tokens(chunk, 1 + b, V, stream=f"chunk{c}")
-                eng.prefill(b, torch.from_numpy(t).to(dev), L0, tok[b:b + 1])
-            eng.check()
             L = L0 + chunk
+            chunks = [torch.from_numpy(synth.tokens(chunk, 1 + b, V, stream=f"chunk{c}")).to(dev)
+                      for b in range(B)]
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for b in range(B):
+                eng.prefill(b, chunks[b], L0, tok[b:b + 1])
+            e1.record(stream)
+            eng.check()
+            pre_ms = e0.elapsed_time(e1) / B
+            if lengths is not None and L not in lengths:
+                continue
             tok_ctx = tok.clone()
             for _ in range(2):  # warm-up replays, then roll back
                 pos.fill_(L)
@@ -288,21 +397,16 @@ def long_context(args):
             ms = e0.elapsed_time(e1) / steps
             sb, _ = step_bytes(cfg, quant, B, list(range(L, L + steps)))
             rows.append({"context": L, "tok_s": round(B / (ms / 1e3), 2), "ms_per_step": round(ms, 4),
-                         "step_bytes": int(sb), "frac": round(sb / (ms / 1e3) / HBM_PEAK, 4)})
-            log(f"context {L}: {rows[-1]['tok_s']} tok/s, {ms:.3f} ms/step")
+                         "step_bytes": int(sb), "frac": round(sb / (ms / 1e3) / HBM_PEAK, 4),
+                         "prefill_chunk_ms": round(pre_ms, 3)})
+            log(f"[long {quant} B={B}] context {L}: {rows[-1]['tok_s']} tok/s, {ms:.3f} ms/step, "
+                f"{chunk}-token chunk prefill {pre_ms:.2f} ms per sequence")
             tok.copy_(tok_ctx)
-    mean = sum(r["tok_s"] for r in rows) / len(rows)
-    ms_mean = sum(r["ms_per_step"] for r in rows) / len(rows)
-    out = {"metric": METRIC, "value": round(mean, 2), "unit": "tok/s", "n_gpus": 1,
-           "steps": steps * len(rows), "warmup": 2 * len(rows), "ms_per_step": round(ms_mean, 4),
-           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": quant,
-           "data": "synthetic",
-           "config": {"workload": f"E2B shape, {quant} weights, long-context decode: batch {B}, context "
-                                  f"grown 500 -> 8,000 by 500-token random prefill chunks, {steps} greedy "
-                                  f"decode steps timed at each length (mean over lengths)",
-                      "quant": quant, "batch": B},
-           "per_length": rows}
-    print(json.dumps(out), flush=True)
+    graph.close()
+    del eng
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return rows
 
 
 def main():
@@ -310,6 +414,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=512)
     ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--repeats", type=int, default=5, help="timed loops of K steps (median reported)")
     ap.add_argument("--quant", choices=["bf16", "w4a16"], default=None,
                     help="weights (default bf16; w4a16 with --long)")
     ap.add_argument("--batch", type=int, default=1)
@@ -317,8 +422,9 @@ def main():
     ap.add_argument("--eager", action="store_true", help="launch kernels per step instead of a graph")
     ap.add_argument("--cpu-steps", type=int, default=24, help="oracle decode steps timed (0: skip)")
     ap.add_argument("--profile-steps", type=int, default=32)
-    ap.add_argument("--no-aux", action="store_true", help="skip the W4A16 / batch-64 measurements")
-    ap.add_argument("--long", action="store_true", help="long-context workload (see above)")
+    ap.add_argument("--no-aux", action="store_true", help="skip the W4A16 / batch-64 / long-context lines")
+    ap.add_argument("--no-long", action="store_true", help="skip the long-context lines")
+    ap.add_argument("--long", action="store_true", help="long-context workload alone (see above)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a 1 GiB device copy (reference kernel for PMC byte counters)")
     args = ap.parse_args()
@@ -342,22 +448,43 @@ def main():
     if args.quant is None:
         args.quant = "w4a16" if args.long else "bf16"
     if args.long:
-        long_context(args)
+        rows = long_context(args.quant, args.batch)
+        cfg = synth.get_config("e2b")
+        mean = sum(r["tok_s"] for r in rows) / len(rows)
+        ms_mean = sum(r["ms_per_step"] for r in rows) / len(rows)
+        out = {"metric": METRIC, "value": round(mean, 2), "unit": "tok/s", "n_gpus": 1,
+               "steps": 64 * len(rows), "warmup": 2 * len(rows), "ms_per_step": round(ms_mean, 4),
+               "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": args.quant,
+               "data": "synthetic",
+               "config": {"workload": f"E2B shape, {args.quant} weights, long-context decode: batch "
+                                      f"{args.batch}, context grown 500 -> 8,000 by 500-token random "
+                                      f"prefill chunks, 64 greedy decode steps timed at each length "
+                                      f"(mean over lengths)", "quant": args.quant, "batch": args.batch},
+               "per_length": rows}
+        print(json.dumps(out), flush=True)
         return
 
+    calib = calibrate(torch)
     cfg = synth.get_config("e2b")
-    B, P, K, W = args.batch, args.prompt, args.steps, args.warmup
-    head = measure(cfg, args.quant, B, P, K, W, args.profile_steps, args.eager, args.cpu_steps,
+    B, P, K, W, R = args.batch, args.prompt, args.steps, args.warmup, max(1, args.repeats)
+    head = measure(cfg, args.quant, B, P, K, W, args.profile_steps, R, args.eager, args.cpu_steps,
                    f"{args.quant} B={B}")
     also = []
     if not args.no_aux:
         for q, b in (("w4a16", 1), ("bf16", 64), ("w4a16", 64)):
             if (q, b) == (args.quant, B):
                 continue
-            r = measure(cfg, q, b, P, K, W, 8, False, 0, f"{q} B={b}")
+            r = measure(cfg, q, b, P, K, W, 8, R, False, 0, f"{q} B={b}")
             also.append({"quant": q, "batch": b, "tok_s": round(r["value"], 2),
-                         "ms_per_step": round(r["ms_per_step"], 4), "step_roofline": step_roofline(r),
-                         "roofline": roofline_of(r, q, b)})
+                         "ms_per_step": round(r["ms_per_step"], 4), "repeats": r["repeats"],
+                         "step_roofline": step_roofline(r, calib), "roofline": roofline_of(r, q, b, calib),
+                         "kernel_kinds": kinds_summary(r, 8), "prefill": r["prefill"]})
+        if not args.no_long:
+            for b in (1, 8):
+                rows = long_context("w4a16", b, lengths=(500, 4000, 8000))
+                also.append({"workload": f"long context, w4a16, batch {b}: context grown by 500-token "
+                                         f"prefill chunks, 64 graph-replayed steps timed at each listed length",
+                             "quant": "w4a16", "batch": b, "per_length": rows})
     wl = (f"E2B shape ({cfg['num_hidden_layers']} layers, hidden {cfg['hidden_size']}, vocab "
           f"{cfg['vocab_size']}), {args.quant} weights, batch {B}, {P}-token random prompt then {K} greedy "
           f"decode steps (KV length {P + 1}..{P + K})")
@@ -367,11 +494,13 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": args.quant, "data": "synthetic",
         "config": {"workload": wl, "quant": args.quant, "batch": B, "prompt": P, "decode_steps": K,
                    "graph": head["graph"]},
-        "roofline": roofline_of(head, args.quant, B) if head["kinds"] else None,
-        "step_roofline": step_roofline(head),
-        "kernel_kinds": {k: {"mean_us": round(v["ms"] * 1e3, 2), "per_step": v["launches"] // max(args.profile_steps, 1),
-                             "GBps": round(v["bytes"] / (v["ms"] / 1e3) / 1e9, 1) if v["ms"] else None}
-                         for k, v in head["kinds"].items()},
+        "repeats": head["repeats"],
+        "roofline": roofline_of(head, args.quant, B, calib) if head["kinds"] else None,
+        "step_roofline": step_roofline(head, calib),
+        "calibration": {"method": "streaming reduction over 4 GiB (e2b_stream_reduce), best of 5",
+                        "read_GBps": round(calib / 1e9, 1)},
+        "kernel_kinds": kinds_summary(head, args.profile_steps),
+        "prefill": head["prefill"],
         "cpu_baseline": head.get("cpu_baseline"),
         "also": also,
     }

@@ -270,10 +270,24 @@ void e2b_graph_destroy(e2b_graph* graph);
  * and output vectors), then stops profiling.  kind 0 stops without reading. */
 enum {
   E2B_KIND_NONE = 0, E2B_KIND_QKV = 1, E2B_KIND_O = 2, E2B_KIND_GATE_UP = 3, E2B_KIND_DOWN = 4,
-  E2B_KIND_PLE_GATE = 5, E2B_KIND_PLE_PROJ = 6, E2B_KIND_PLE_MODEL = 7, E2B_KIND_LM_HEAD = 8
+  E2B_KIND_PLE_GATE = 5, E2B_KIND_PLE_PROJ = 6, E2B_KIND_PLE_MODEL = 7, E2B_KIND_LM_HEAD = 8,
+  E2B_KIND_ATTN = 9 /* the decode attention kernel (bytes reported as 0: the K/V
+                       span it reads depends on device-side positions) */
 };
 int e2b_profile_begin(e2b_model* model, int kind);
 int e2b_profile_read(e2b_model* model, int* launches, double* total_ms, double* total_bytes);
+
+/* ---- bandwidth calibration -------------------------------------------------
+ * A plain streaming reduction over `bytes` of device memory (every byte read
+ * once, 16 bytes per lane per load): d_out (fp32, e2b_stream_reduce_blocks()
+ * entries) receives one partial sum per block of the buffer's 32-bit words
+ * read as fp32.  Timed by the caller, its rate is the read bandwidth a plain
+ * stream sustains on this device, the denominator of a calibrated roofline
+ * ([P5] Measured: the calibrated streaming reduction the decode step's KV
+ * read is compared with).  bytes and d_buf must be multiples of 16.
+ * Asynchronous. */
+int e2b_stream_reduce(const void* d_buf, size_t bytes, float* d_out, void* stream);
+int e2b_stream_reduce_blocks(void);
 
 /* Synchronise `stream`, then read and clear the device error word in d_ws.
  * E2B_EDEVICE (message names the first bad token or position) if a kernel

@@ -90,6 +90,8 @@ def lib():
         L.orc_argmax.argtypes = [dp, i32]
         L.orc_debug_inputs.restype = i32
         L.orc_debug_inputs.argtypes = [vp, i32, dp, dp]
+        L.orc_set_threads.argtypes = [i32]
+        L.orc_get_threads.restype = i32
         _lib = L
     return _lib
 
@@ -178,6 +180,15 @@ class Oracle:
         v = np.ascontiguousarray(v_bits, np.uint16)
         if lib().orc_kv_load(self._h, l, seq, pos0, k.shape[0], _ptr(k), _ptr(v)) != 0:
             raise RuntimeError("oracle: bad kv_load arguments")
+
+
+def set_threads(n: int) -> None:
+    """OpenMP threads of the oracle's products (process-wide)."""
+    lib().orc_set_threads(int(n))
+
+
+def get_threads() -> int:
+    return lib().orc_get_threads()
 
 
 # ---- single pieces, for the pins -------------------------------------------

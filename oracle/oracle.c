@@ -34,6 +34,7 @@
  * source owning its K/V) are listed in the design notes of the repository.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -94,6 +95,11 @@ static double round_bf16(double x) {
   memcpy(&f, &u, 4);
   return (double)f;
 }
+
+/* OpenMP threads the products use (the CPU baseline is timed on all host
+ * cores and on one) */
+void orc_set_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
+int orc_get_threads(void) { return omp_get_max_threads(); }
 
 /* ---------------------------------------------------------------- pieces */
 

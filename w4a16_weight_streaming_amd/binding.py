@@ -18,7 +18,7 @@ _lib = None
 
 E2B_OK, E2B_EINVAL, E2B_ERANGE, E2B_ENOMEM, E2B_EHIP, E2B_EDEVICE, E2B_ESTATE = range(7)
 KINDS = {"qkv": 1, "o": 2, "gate_up": 3, "down": 4, "ple_gate": 5, "ple_proj": 6, "ple_model": 7,
-         "lm_head": 8}
+         "lm_head": 8, "attn": 9}
 QUANT = {"bf16": 0, "w4a16": 1}
 DTYPE_BF16, DTYPE_INT32 = 0, 1
 
@@ -94,9 +94,12 @@ def load_library():
     L.e2b_matvec_noalloc_max_bytes.restype = sz
     L.e2b_matvec_noalloc_max_bytes.argtypes = []
     L.e2b_matvec_noalloc.argtypes = [i32, vp, vp, i32, i32, vp, i32, vp, vp]
+    L.e2b_stream_reduce.argtypes = [vp, sz, vp, vp]
+    L.e2b_stream_reduce_blocks.argtypes = []
     for f in ("e2b_config_preset", "e2b_create", "e2b_kv_share_map", "e2b_load_weights",
               "e2b_kv_alloc", "e2b_decode_step", "e2b_prefill", "e2b_check", "e2b_kv_view",
-              "e2b_matvec", "e2b_matvec_noalloc", "e2b_embed", "e2b_graph_capture", "e2b_graph_replay", "e2b_profile_begin",
+              "e2b_matvec", "e2b_matvec_noalloc", "e2b_embed", "e2b_stream_reduce",
+              "e2b_stream_reduce_blocks", "e2b_graph_capture", "e2b_graph_replay", "e2b_profile_begin",
               "e2b_profile_read"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
@@ -194,6 +197,17 @@ def matvec(quant: str, w, scale, x, y, ws=None):
                         x.data_ptr(), rows, y.data_ptr(), 0 if ws is None else ws.data_ptr(),
                         0 if ws is None else ws.numel(), torch.cuda.current_stream(x.device).cuda_stream))
     return y
+
+
+def stream_reduce(buf, out):
+    """The calibration read: one pass over the bytes of device tensor `buf`
+    (a multiple of 16 bytes), per-block sums into `out` (float32, at least
+    e2b_stream_reduce_blocks() entries).  Asynchronous on the current stream."""
+    import torch
+    L = load_library()
+    assert out.dtype == torch.float32 and out.numel() >= L.e2b_stream_reduce_blocks()
+    _check(L.e2b_stream_reduce(buf.data_ptr(), buf.numel() * buf.element_size(), out.data_ptr(),
+                               torch.cuda.current_stream(buf.device).cuda_stream))
 
 
 class Engine:

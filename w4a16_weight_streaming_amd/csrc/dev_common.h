@@ -4,10 +4,23 @@
 
 #include "e2b_internal.h"
 
+#include <hip/hip_ext.h>
+
 #include <float.h>
 #include <math.h>
 
 namespace e2b {
+
+// Launch a kernel; when the host thread has pending profiling events (see
+// set_launch_events), the launch records them at its own start and end.
+#define E2B_TIMED_LAUNCH(kernel, grid, block, shm, st, ...)                                       \
+  do {                                                                                            \
+    hipEvent_t ev_a_, ev_b_;                                                                      \
+    if (take_launch_events(&ev_a_, &ev_b_))                                                       \
+      hipExtLaunchKernelGGL(kernel, grid, block, shm, st, ev_a_, ev_b_, 0, __VA_ARGS__);           \
+    else                                                                                          \
+      hipLaunchKernelGGL(kernel, grid, block, shm, st, __VA_ARGS__);                              \
+  } while (0)
 
 // Plain accessors (one place to change how activations cross kernels).
 __device__ __forceinline__ void st32(float* p, float v) { *p = v; }
@@ -160,6 +173,14 @@ __device__ __forceinline__ int clamp_pos(const Rows& R, int p) {
   return p < 0 ? 0 : (p >= R.max_ctx ? R.max_ctx - 1 : p);
 }
 __device__ __forceinline__ int row_seq(const Rows& R, int r) { return R.seq0 + r * R.seq_stride; }
+
+// eight consecutive fp32 values (16-byte aligned)
+__device__ __forceinline__ void ld8(const float* p, float (&v)[8]) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
 
 // ------------------------------------------------------- matrix-vector product
 // Lane layout for one K slice of KS elements (a 16-byte load per lane):
@@ -660,8 +681,12 @@ __device__ void attn_chunk(const Rows& R, const AttnArgs& a, int c, int r) {
   const int pos = clamp_pos(R, row_pos(R, r));
   const int seq = row_seq(R, r);
   const int lo = a.window ? max(0, pos - a.window + 1) : 0;
-  const int j0 = lo + c * a.chunk;
-  const int j1 = min(j0 + a.chunk, pos + 1);
+  // the row's live span split over the grid's chunks, at least a.chunk keys
+  // each: the chunks that hold keys are a prefix of the grid
+  const int span = pos + 1 - lo;
+  const int chunk = max(a.chunk, (span + a.nchunk - 1) / a.nchunk);
+  const int j0 = lo + c * chunk;
+  const int j1 = min(j0 + chunk, pos + 1);
   const size_t hstride = (size_t)kMaxChunks * (HD + 2);
   float* part = a.part + ((size_t)r * nq * kMaxChunks + c) * (HD + 2);
 

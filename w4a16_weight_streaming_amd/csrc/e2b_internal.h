@@ -12,6 +12,7 @@ constexpr int kMaxSplitK = 8;    // K slices of one matrix-vector product
 constexpr int kMaxGemmSplit = 16;  // K slices of one batched (matrix-core) product
 constexpr int kGemvThreads = 256;
 constexpr int kLmBlocks = 1024;  // blocks of the lm_head pass (argmax candidates)
+constexpr int kStreamBlocks = 1024;  // blocks of the streaming-read calibration
 
 // Matrix kinds; each gets its own kernel symbol so profiles tell them apart.
 enum : int {
@@ -137,7 +138,9 @@ struct AttnArgs {
   float* xg = nullptr;          // sums of hi + lo per 32-group [rows][nq * hd / 32])
   const float* rope = nullptr;  // RoPE table rows (rope_ld floats each), this type at rope_off
   int rope_ld = 0, rope_off = 0;
-  int nq = 0, hd = 0, window = 0 /* 0: full */, chunk = 0, nchunk = 0;
+  int nq = 0, hd = 0, window = 0 /* 0: full */;
+  int chunk = 0;   // fewest keys per block; a row's live span is split over
+  int nchunk = 0;  // nchunk blocks of max(chunk, ceil(span / nchunk)) keys
   int owns = 0;                 // the layer computes K/V (raw rows hold q, k, v)
   int combine = 1;              // merge the chunk partials into out (else the O product does)
   int qkv_parts = 1;            // qkv is the sum of this many partials
@@ -187,6 +190,7 @@ hipError_t launch_tile_bf16(const Lin& W, uint16_t* tw, hipStream_t st);
 hipError_t launch_qkv_post(const Rows& R, const QkvPostArgs& a, hipStream_t st);
 hipError_t launch_attention(const Rows& R, const AttnArgs& a, hipStream_t st);
 hipError_t launch_advance(int32_t* pos, int n, hipStream_t st);
+hipError_t launch_stream_reduce(const void* buf, size_t bytes, float* out, hipStream_t st);
 // batched rows (>= 2): prologue into bf16 hi/lo rows + group sums, then MFMA
 hipError_t launch_xprep(const Prologue& p, int rows, int K, uint16_t* xh, uint16_t* xl, float* xg,
                         hipStream_t st);
@@ -208,6 +212,11 @@ struct GemmA {
 // *nblk receives the number of column blocks (argmax candidates per row)
 hipError_t launch_gemm(int quant, int tag, const Lin& W, int rows, const GemmA& A,
                        const GemmPlan& plan, const Epilogue& epi, int* nblk, hipStream_t st);
+// (launch_gemm, by weight format: gemm_bf16.hip, gemm_w4.hip)
+hipError_t launch_gemm_bf16(int tag, const Lin& W, int rows, const GemmA& A, const GemmPlan& plan,
+                            const Epilogue& epi, int* nblk, hipStream_t st);
+hipError_t launch_gemm_w4(int tag, const Lin& W, int rows, const GemmA& A, const GemmPlan& plan,
+                          const Epilogue& epi, int* nblk, hipStream_t st);
 // The next launch_gemv / launch_gemm on this host thread records these
 // events at its kernel's start and end.
 void set_launch_events(hipEvent_t start, hipEvent_t stop);

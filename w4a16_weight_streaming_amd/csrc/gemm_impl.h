@@ -1,0 +1,374 @@
+// The batched (matrix-core) product of libe2b for CDNA4 (gfx950): the kernel
+// template and its launch dispatch, compiled once per weight format
+// (gemm_bf16.hip, gemm_w4.hip) so the two sets of instantiations build in
+// parallel.
+#pragma once
+
+#include "dev_common.h"
+
+#include <float.h>
+#include <type_traits>
+
+namespace e2b {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// eight int4 codes (one packed word) -> eight bf16 values 128 + c
+__device__ __forceinline__ uint4 w4_to_bf16(uint32_t word) {
+  const uint32_t lo = word & 0x0F0F0F0Fu, hi = (word >> 4) & 0x0F0F0F0Fu;
+  const uint32_t u = __builtin_amdgcn_perm(hi, lo, 0x05010400u);  // codes 0,1,2,3 as bytes
+  const uint32_t v = __builtin_amdgcn_perm(hi, lo, 0x07030602u);  // codes 4,5,6,7
+  uint4 r;
+  r.x = __builtin_amdgcn_perm(0x43434343u, u, 0x04010400u);
+  r.y = __builtin_amdgcn_perm(0x43434343u, u, 0x04030402u);
+  r.z = __builtin_amdgcn_perm(0x43434343u, v, 0x04010400u);
+  r.w = __builtin_amdgcn_perm(0x43434343u, v, 0x04030402u);
+  return r;
+}
+
+// input rows per block: 16 * MT (MT m-tiles of 16 rows; 1, 2 or 4, chosen
+// from the row count so that 2-16 rows do not pay for 64)
+constexpr int kKC = 128;        // k per LDS stage (4 k-steps of 32)
+constexpr int kAP = kKC + 8;    // padded LDS row of bf16: 16-byte reads conflict-free
+
+// Block = 4 waves side by side along N; wave w owns NT column tiles of 16
+// (block covers 64*NT columns) for all 16*MT rows, over one K slice of KS.
+// A chunks (16*MT rows x 128 k, hi and lo) are double-buffered in LDS, one
+// barrier per chunk; each wave's weight fragments for the next chunk are
+// loaded into registers while the current chunk is multiplied.
+template <int WQ, int NT, int MT, int FA, int TAG>
+__global__ __launch_bounds__(256, 2) void k_gemm(Lin W, int rows, GemmA A, int KS, Epilogue epi) {
+  constexpr int MB = 16 * MT;
+  const uint16_t* __restrict__ xh = A.xh;
+  const uint16_t* __restrict__ xl = A.xl;
+  const float* __restrict__ xg = A.xg;
+  __shared__ __attribute__((aligned(16))) uint16_t sa[2][2][MB][kAP];
+  __shared__ __attribute__((aligned(16))) float sg[2][kKC / 32][MB];  // 136 * group sums
+  __shared__ float rv[4][MB];
+  __shared__ int ri[4][MB];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6, kq = lane >> 4;
+  const int ks = blockIdx.y, m0 = blockIdx.z * MB;
+  const int K = W.K, N = W.N;
+  const int mrows = min(MB, rows - m0);
+  int ncol[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) ncol[j] = blockIdx.x * 64 * NT + wave * 16 * NT + 16 * j + (lane & 15);
+
+  f32x4_t acc[MT][NT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int j = 0; j < NT; ++j) acc[mt][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // weight fragments of one chunk (4 k-steps)
+  // weight fragments: a ring of D chunks, D - 1 of them in flight ahead
+  constexpr int D = WQ ? (NT >= 4 ? 2 : 4) : (NT >= 2 ? 3 : 4);
+  uint4 bw[D][WQ ? 1 : 4][WQ ? 1 : NT];
+  uint32_t bq[D][WQ ? 4 : 1][WQ ? NT : 1];
+  float bs[D][WQ ? 4 : 1][WQ ? NT : 1];
+  // A chunk staged through registers
+  uint4 rah[MT], ral[MT];
+  float rg = 0.f, rgs[MT];
+#pragma unroll
+  for (int j = 0; j < MT; ++j) rgs[j] = 0.f;
+  float raf[FA ? MT : 1][8];  // fp32 input slots (FA)
+#pragma unroll
+  for (int x = 0; x < D; ++x) {
+#pragma unroll
+    for (int s = 0; s < (WQ ? 1 : 4); ++s)
+#pragma unroll
+      for (int j = 0; j < (WQ ? 1 : NT); ++j) bw[x][s][j] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int s = 0; s < (WQ ? 4 : 1); ++s)
+#pragma unroll
+      for (int j = 0; j < (WQ ? NT : 1); ++j) {
+        bq[x][s][j] = 0x88888888u;
+        bs[x][s][j] = 0.f;
+      }
+  }
+
+  const int kbeg = ks * KS, kend = kbeg + KS;
+  // (buffer indices are compile-time constants so the fragments stay in registers)
+  auto load_b = [&](auto BUF, int kc, int kcn) {
+    constexpr int buf = decltype(BUF)::value;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      if (32 * s >= kcn) break;
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        // columns past N read row 0 (always valid) and are zeroed
+        const bool ok = ncol[j] < N;
+        const size_t row = ok ? (size_t)ncol[j] : 0;
+        if constexpr (WQ) {
+          // (the tiled copy when there is one: the same word, 256 contiguous
+          // bytes per wave; the address is selected, the load is not)
+          const size_t g = (size_t)(kc + 32 * s) / 32, tile = row / 16;
+          const uint32_t* qp = W.tq ? W.tq + (tile * (K / 32) + g) * 64 + lane : W.q + row * (K / 8) + 4 * g + kq;
+          const uint16_t* sp = W.ts ? W.ts + (tile * (K / 32) + g) * 16 + (lane & 15) : W.s + row * (K / 32) + g;
+          const uint32_t qv = *qp;
+          const float sv = bf2f(*sp);
+          bq[buf][s][j] = ok ? qv : 0x88888888u;
+          bs[buf][s][j] = ok ? sv : 0.f;
+        } else {
+          // (the tiled copy when there is one: one contiguous kilobyte per wave)
+          const size_t g = (size_t)(kc + 32 * s) / 32, tile = row / 16;
+          const uint16_t* wp = W.tw ? W.tw + ((tile * (K / 32) + g) * 64 + lane) * 8 : W.w + row * K + kc + 32 * s + 8 * kq;
+          uint4 v = *reinterpret_cast<const uint4*>(wp);
+          if (!ok) v = make_uint4(0, 0, 0, 0);
+          bw[buf][s][j] = v;
+        }
+      }
+    }
+  };
+  auto load_a = [&](int kc, int kcn) {
+    if constexpr (FA) {  // fp32 rows: loaded now, split when stored (after the multiply)
+#pragma unroll
+      for (int j = 0; j < MT; ++j) {
+        const int idx = t + 256 * j, m = idx >> 4, k8 = idx & 15;
+        const bool ok = m < mrows && 8 * k8 < kcn;
+        ld8(A.a + (ok ? (size_t)(m0 + m) * A.lda + kc + 8 * k8 : 0), raf[j]);
+        if (!ok)
+#pragma unroll
+          for (int x = 0; x < 8; ++x) raf[j][x] = 0.f;
+      }
+      return;
+    }
+#pragma unroll
+    for (int j = 0; j < MT; ++j) {
+      const int idx = t + 256 * j, m = idx >> 4, k8 = idx & 15;
+      // out-of-range slots read element 0 (always valid) and are zeroed
+      const bool ok = m < mrows && 8 * k8 < kcn;
+      const size_t o = ok ? (size_t)(m0 + m) * K + kc + 8 * k8 : 0;
+      uint4 vh = *reinterpret_cast<const uint4*>(xh + o);
+      uint4 vl = *reinterpret_cast<const uint4*>(xl + o);
+      if (!ok) vh = vl = make_uint4(0, 0, 0, 0);
+      rah[j] = vh;
+      ral[j] = vl;
+    }
+    if (WQ) {
+      const int m = t >> 2, g = t & 3;
+      const bool ok = m < mrows && 32 * g < kcn;
+      const float v = xg[ok ? (size_t)(m0 + m) * (K / 32) + kc / 32 + g : 0];
+      rg = ok ? 136.0f * v : 0.f;
+    }
+  };
+  auto store_a = [&](int st) {
+    if constexpr (FA) {
+#pragma unroll
+      for (int j = 0; j < MT; ++j) {
+        uint32_t h[4], l[4];
+        float gs = 0.f;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          split_pair(raf[j][2 * x], raf[j][2 * x + 1], h[x], l[x]);
+          gs += (bf2f(h[x]) + bf2f(l[x])) + (bf2f(h[x] >> 16) + bf2f(l[x] >> 16));
+        }
+        rah[j] = make_uint4(h[0], h[1], h[2], h[3]);
+        ral[j] = make_uint4(l[0], l[1], l[2], l[3]);
+        if (WQ) {  // group of 32 = the 4 consecutive lanes with the same row
+          gs = group_sum<4>(gs);
+          rgs[j] = 136.0f * gs;
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < MT; ++j) {
+      const int idx = t + 256 * j, m = idx >> 4, k8 = idx & 15;
+      *reinterpret_cast<uint4*>(&sa[st][0][m][8 * k8]) = rah[j];
+      *reinterpret_cast<uint4*>(&sa[st][1][m][8 * k8]) = ral[j];
+    }
+    if constexpr (WQ && FA) {
+#pragma unroll
+      for (int j = 0; j < MT; ++j) {
+        const int idx = t + 256 * j, m = idx >> 4, k8 = idx & 15;
+        if ((k8 & 3) == 0) sg[st][k8 >> 2][m] = rgs[j];
+      }
+    } else if (WQ) {
+      if ((t >> 2) < MB) sg[st][t & 3][t >> 2] = rg;
+    }
+  };
+
+  const int nch = (KS + kKC - 1) / kKC;
+  // one chunk: issue the weight loads of chunk c + D - 1 and the activation
+  // loads of chunk c + 1, multiply chunk c, stage chunk c + 1 in LDS
+  auto chunk = [&](auto BUF, int c) {
+    constexpr int buf = decltype(BUF)::value;
+    const int kc = kbeg + c * kKC, kcn = min(kKC, kend - kc), st = c & 1;
+    const bool more = c + 1 < nch;
+    // (activation loads first: loads complete in issue order, and staging
+    // chunk c + 1 must not wait for the weight loads issued after it)
+    if (more) load_a(kc + kKC, min(kKC, kend - kc - kKC));
+    if (c + D - 1 < nch) {
+      const int kf = kc + (D - 1) * kKC;
+      load_b(std::integral_constant<int, (buf + D - 1) % D>(), kf, min(kKC, kend - kf));
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      if (32 * s >= kcn) break;
+      bf16x8_t B[NT];
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        if constexpr (WQ) B[j] = as_bf16x8(w4_to_bf16(bq[buf][s][j]));
+        else B[j] = as_bf16x8(bw[buf][s][j]);
+      }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int mr = 16 * mt + (lane & 15);
+        const bf16x8_t Ah = as_bf16x8(*reinterpret_cast<const uint4*>(&sa[st][0][mr][32 * s + 8 * kq]));
+        const bf16x8_t Al = as_bf16x8(*reinterpret_cast<const uint4*>(&sa[st][1][mr][32 * s + 8 * kq]));
+        if constexpr (WQ) {
+          const float4 g4 = *reinterpret_cast<const float4*>(&sg[st][s][16 * mt + 4 * kq]);
+#pragma unroll
+          for (int j = 0; j < NT; ++j) {
+            f32x4_t d = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ah, B[j], d, 0, 0, 0);
+            d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Al, B[j], d, 0, 0, 0);
+            const float sc = bs[buf][s][j];
+            acc[mt][j][0] = fmaf(sc, d[0] - g4.x, acc[mt][j][0]);
+            acc[mt][j][1] = fmaf(sc, d[1] - g4.y, acc[mt][j][1]);
+            acc[mt][j][2] = fmaf(sc, d[2] - g4.z, acc[mt][j][2]);
+            acc[mt][j][3] = fmaf(sc, d[3] - g4.w, acc[mt][j][3]);
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < NT; ++j) {
+            acc[mt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ah, B[j], acc[mt][j], 0, 0, 0);
+            acc[mt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Al, B[j], acc[mt][j], 0, 0, 0);
+          }
+        }
+      }
+    }
+    if (more) store_a(st ^ 1);
+    __syncthreads();
+  };
+  using C0 = std::integral_constant<int, 0>;
+  using C1 = std::integral_constant<int, 1>;
+  using C2 = std::integral_constant<int, 2>;
+  using C3 = std::integral_constant<int, 3>;
+
+  load_a(kbeg, min(kKC, KS));
+  load_b(C0(), kbeg, min(kKC, KS));
+  if constexpr (D > 2)
+    if (1 < nch) load_b(C1(), kbeg + kKC, min(kKC, KS - kKC));
+  if constexpr (D > 3)
+    if (2 < nch) load_b(C2(), kbeg + 2 * kKC, min(kKC, KS - 2 * kKC));
+  store_a(0);
+  __syncthreads();
+  for (int c = 0; c < nch; c += D) {
+    chunk(C0(), c);
+    if (c + 1 < nch) chunk(C1(), c + 1);
+    if constexpr (D > 2)
+      if (c + 2 < nch) chunk(C2(), c + 2);
+    if constexpr (D > 3)
+      if (c + 3 < nch) chunk(C3(), c + 3);
+  }
+
+  if (!epi.argmax) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = 16 * mt + 4 * kq + i;
+        if (m < mrows)
+#pragma unroll
+          for (int j = 0; j < NT; ++j)
+            if (ncol[j] < N) epi.y[((size_t)ks * rows + m0 + m) * N + ncol[j]] = acc[mt][j][i];
+      }
+    return;
+  }
+  // argmax: per row, best (value, lowest index) over this block's columns
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = 16 * mt + 4 * kq + i;
+      float v = -FLT_MAX;
+      int x = 0x7FFFFFFF;
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+        if (ncol[j] < N) {
+          const float a_ = acc[mt][j][i];
+          if (epi.logits && m < mrows) epi.logits[(size_t)(m0 + m) * N + ncol[j]] = a_;
+          if (a_ > v || (a_ == v && ncol[j] < x)) {
+            v = a_;
+            x = ncol[j];
+          }
+        }
+      argmax_lanes<16>(v, x);
+      if ((lane & 15) == 0) {
+        rv[wave][m] = v;
+        ri[wave][m] = x;
+      }
+    }
+  __syncthreads();
+  if (t < mrows) {
+    float v = rv[0][t];
+    int x = ri[0][t];
+    for (int w = 1; w < 4; ++w)
+      if (rv[w][t] > v || (rv[w][t] == v && ri[w][t] < x)) {
+        v = rv[w][t];
+        x = ri[w][t];
+      }
+    epi.cand_val[(size_t)(m0 + t) * gridDim.x + blockIdx.x] = v;
+    epi.cand_idx[(size_t)(m0 + t) * gridDim.x + blockIdx.x] = x;
+  }
+}
+
+template <int WQ, int NT, int FA, int TAG>
+static hipError_t run_gemm(const Lin& W, int rows, const GemmA& A, int nks, const Epilogue& epi,
+                           int* nblk, hipStream_t st) {
+  const int nbx = (W.N + 64 * NT - 1) / (64 * NT);
+  if (nblk) *nblk = nbx;
+  // m-tiles per block from the row count (a row's arithmetic does not depend
+  // on which rows share its block)
+  const int mt = rows <= 16 ? 1 : (rows <= 32 ? 2 : 4);
+  dim3 grid(nbx, nks, (rows + 16 * mt - 1) / (16 * mt));
+  if (mt == 1)
+    E2B_TIMED_LAUNCH((k_gemm<WQ, NT, 1, FA, TAG>), grid, dim3(256), 0, st, W, rows, A, W.K / nks, epi);
+  else if (mt == 2)
+    E2B_TIMED_LAUNCH((k_gemm<WQ, NT, 2, FA, TAG>), grid, dim3(256), 0, st, W, rows, A, W.K / nks, epi);
+  else
+    E2B_TIMED_LAUNCH((k_gemm<WQ, NT, 4, FA, TAG>), grid, dim3(256), 0, st, W, rows, A, W.K / nks, epi);
+  return hipGetLastError();
+}
+
+template <int WQ, int NT>
+static hipError_t gemm_tag(int tag, const Lin& W, int rows, const GemmA& A, int nks,
+                           const Epilogue& epi, int* nblk, hipStream_t st) {
+  if (A.a) {  // fp32 input rows: the products whose input is a plain copy
+    switch (tag) {
+      case kTagO: return run_gemm<WQ, NT, 1, kTagO>(W, rows, A, nks, epi, nblk, st);
+      case kTagPleModel: return run_gemm<WQ, NT, 1, kTagPleModel>(W, rows, A, nks, epi, nblk, st);
+      default: return run_gemm<WQ, NT, 1, kTagOther>(W, rows, A, nks, epi, nblk, st);
+    }
+  }
+  switch (tag) {
+    case kTagO: return run_gemm<WQ, NT, 0, kTagO>(W, rows, A, nks, epi, nblk, st);
+    case kTagQkv: return run_gemm<WQ, NT, 0, kTagQkv>(W, rows, A, nks, epi, nblk, st);
+    case kTagGateUp: return run_gemm<WQ, NT, 0, kTagGateUp>(W, rows, A, nks, epi, nblk, st);
+    case kTagDown: return run_gemm<WQ, NT, 0, kTagDown>(W, rows, A, nks, epi, nblk, st);
+    case kTagPleGate: return run_gemm<WQ, NT, 0, kTagPleGate>(W, rows, A, nks, epi, nblk, st);
+    case kTagPleProj: return run_gemm<WQ, NT, 0, kTagPleProj>(W, rows, A, nks, epi, nblk, st);
+    case kTagLmHead: return run_gemm<WQ, NT, 0, kTagLmHead>(W, rows, A, nks, epi, nblk, st);
+    default: return run_gemm<WQ, NT, 0, kTagOther>(W, rows, A, nks, epi, nblk, st);
+  }
+}
+
+template <int WQ>
+hipError_t launch_gemm_q(int tag, const Lin& W, int rows, const GemmA& A, const GemmPlan& plan,
+                         const Epilogue& epi, int* nblk, hipStream_t st) {
+  const int nks = plan.nks;
+  if constexpr (WQ) {
+    if (plan.nt == 4) return gemm_tag<1, 4>(tag, W, rows, A, nks, epi, nblk, st);
+    if (plan.nt == 2) return gemm_tag<1, 2>(tag, W, rows, A, nks, epi, nblk, st);
+  } else {
+    if (plan.nt == 2) return gemm_tag<0, 2>(tag, W, rows, A, nks, epi, nblk, st);
+    if (plan.nt == 1) return gemm_tag<0, 1>(tag, W, rows, A, nks, epi, nblk, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace e2b

@@ -331,9 +331,12 @@ Ws ws_layout(const e2b_model* m, int R) {
   return w;
 }
 
-// Keys per attention block: 16 for a single row (each wave then takes one
-// group of 4 keys: the shortest chain, and the chip has room for the blocks),
-// else 32 (64 or 128 measured no better)
+// Attention blocks per (row, layer) and the fewest keys per block: 16 for a
+// single row (each wave then takes one group of 4 keys: the shortest chain,
+// and the chip has room for the blocks), else 32 (64 or 128 measured no
+// better).  The grid covers the longest span max_ctx allows (at most
+// kMaxChunks blocks); each row splits its live span over those blocks on the
+// device, so a short context is not left to a few long blocks.
 void attn_chunks(const e2b_model* m, bool full, int rows, int* chunk, int* nchunk) {
   const int span = full ? m->max_ctx : std::min(m->c.sliding_window, m->max_ctx);
   const int w = rows == 1 ? 16 : 32;
@@ -341,7 +344,7 @@ void attn_chunks(const e2b_model* m, bool full, int rows, int* chunk, int* nchun
   if (n > e2b::kMaxChunks) n = e2b::kMaxChunks;
   if (n < 1) n = 1;
   *nchunk = n;
-  *chunk = (span + n - 1) / n;
+  *chunk = w;
 }
 
 // One product of a linear layer with `rows` input rows built by `pr`:
@@ -538,7 +541,15 @@ int run_rows(e2b_model* m, const e2b::Rows& R, bool head, int head_row, float* d
         a.xg = F(W.xg);
       }
       nchunk = a.nchunk;
+      e2b_model::Mark mk{};
+      const bool prof = m->prof_kind == E2B_KIND_ATTN;
+      if (prof) {  // the attention kernel's own dispatch timestamps (bytes: the caller's)
+        CK(hipEventCreate(&mk.a), "profile event");
+        CK(hipEventCreate(&mk.b), "profile event");
+        set_launch_events(mk.a, mk.b);
+      }
       CK(launch_attention(R, a, st), "attention");
+      if (prof) m->marks.push_back(mk);
     }
     {
       Prologue pr;
@@ -1195,6 +1206,17 @@ int e2b_matvec_noalloc(int quant, const void* d_w, const uint16_t* d_scale, int 
   return E2B_OK;
 }
 
+int e2b_stream_reduce(const void* d_buf, size_t bytes, float* d_out, void* stream) {
+  if (!d_buf || !d_out) return fail(E2B_EINVAL, "null argument");
+  if (bytes % 16 || reinterpret_cast<uintptr_t>(d_buf) % 16)
+    return fail(E2B_EINVAL, "buffer and byte count must be multiples of 16");
+  CK(e2b::launch_stream_reduce(d_buf, bytes, d_out, reinterpret_cast<hipStream_t>(stream)),
+     "stream reduce");
+  return E2B_OK;
+}
+
+int e2b_stream_reduce_blocks(void) { return e2b::kStreamBlocks; }
+
 int e2b_embed(e2b_model* m, const int32_t* d_tokens, int n, float* d_h, float* d_tokple, void* d_ws,
               size_t ws_bytes, void* stream) {
   if (!m || !d_tokens || !d_h || !d_tokple || !d_ws) return fail(E2B_EINVAL, "null argument");
@@ -1294,7 +1316,7 @@ static void drop_marks(e2b_model* m) {
 
 int e2b_profile_begin(e2b_model* m, int kind) {
   if (!m) return fail(E2B_EINVAL, "null argument");
-  if (kind < E2B_KIND_NONE || kind > E2B_KIND_LM_HEAD) return fail(E2B_EINVAL, "bad kind %d", kind);
+  if (kind < E2B_KIND_NONE || kind > E2B_KIND_ATTN) return fail(E2B_EINVAL, "bad kind %d", kind);
   drop_marks(m);
   m->prof_kind = kind;
   return E2B_OK;

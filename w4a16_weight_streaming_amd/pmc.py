@@ -26,9 +26,15 @@ GIB = float(1 << 30)
 HERE = os.path.dirname(os.path.abspath(__file__))
 
 
+KERNEL_SOURCES = ("kernels.hip", "gemm_impl.h", "gemm_bf16.hip", "gemm_w4.hip", "dev_common.h",
+                  "e2b_internal.h")
+
+
 def kernels_sha():
+    """Hash of every device source, to tell whether a profile still describes
+    the current kernels."""
     h = hashlib.sha1()
-    for f in ("kernels.hip", "dev_common.h", "e2b_internal.h"):
+    for f in KERNEL_SOURCES:
         with open(os.path.join(HERE, "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
