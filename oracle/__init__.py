@@ -41,7 +41,7 @@ class OrcConfig(ctypes.Structure):
         "layer_pattern_period", "intermediate_size", "use_double_wide_mlp",
         "hidden_size_per_layer_input", "vocab_size", "quant", "group_size")] + \
         [(n, ctypes.c_double) for n in ("rms_eps", "rope_theta_sliding", "rope_theta_full")] + \
-        [("kv_bf16", ctypes.c_int)]
+        [("kv_bf16", ctypes.c_int), ("embed_quant", ctypes.c_int)]
 
 
 def build(force: bool = False) -> str:
@@ -100,13 +100,15 @@ def _ptr(a: np.ndarray) -> int:
     return a.ctypes.data
 
 
-def make_config(cfg: dict, quant: str, kv_bf16: bool = True) -> OrcConfig:
+def make_config(cfg: dict, quant: str, kv_bf16: bool = True, embed_quant: str = "bf16") -> OrcConfig:
     c = OrcConfig()
     for name, _ in OrcConfig._fields_:
         if name == "quant":
             c.quant = 1 if quant == "w4a16" else 0
         elif name == "kv_bf16":
             c.kv_bf16 = 1 if kv_bf16 else 0
+        elif name == "embed_quant":
+            c.embed_quant = 1 if embed_quant == "w4a16" else 0
         else:
             setattr(c, name, cfg[name])
     return c
@@ -116,14 +118,17 @@ class Oracle:
     """The C reference over one synthetic model (tensors from ``synth``)."""
 
     def __init__(self, cfg: dict, quant: str, tensors: Dict[str, np.ndarray], max_seq: int,
-                 max_ctx: int, kv_bf16: bool = True):
+                 max_ctx: int, kv_bf16: bool = True, embed_quant: str = None):
         self.cfg, self.quant = cfg, quant
         self.V, self.H = cfg["vocab_size"], cfg["hidden_size"]
         self._keep = {k: np.ascontiguousarray(v) for k, v in tensors.items()}
         names = list(self._keep)
         self._names = (ctypes.c_char_p * len(names))(*[n.encode() for n in names])
         self._ptrs = (ctypes.c_void_p * len(names))(*[_ptr(self._keep[n]) for n in names])
-        self._cfg = make_config(cfg, quant, kv_bf16)
+        if embed_quant is None:   # the vocabulary tables' format, read off the tensors
+            embed_quant = "w4a16" if "model.embed_tokens.weight_packed" in tensors else "bf16"
+        self.embed_quant = embed_quant
+        self._cfg = make_config(cfg, quant, kv_bf16, embed_quant)
         self.max_seq, self.max_ctx = max_seq, max_ctx
         h = lib().orc_create(ctypes.byref(self._cfg), len(names), self._names, self._ptrs,
                              max_seq, max_ctx)

@@ -74,8 +74,10 @@ class Naive:
         self.nq, self.V = c["num_attention_heads"], c["vocab_size"]
         self.first = self.L - c["num_kv_shared_layers"]
         t = tensors
-        self.E = _bf(t["model.embed_tokens.weight"])
-        self.Eple = _bf(t["model.embed_tokens_per_layer.weight"])
+        # the vocabulary tables: bf16, or int4 codes with group scales
+        eq = "w4a16" if "model.embed_tokens.weight_packed" in t else "bf16"
+        self.E = _dense(t, "model.embed_tokens.weight", eq)
+        self.Eple = _dense(t, "model.embed_tokens_per_layer.weight", eq)
         self.Wplmp = _dense(t, "model.per_layer_model_projection.weight", quant)
         self.g_plpn = _bf(t["model.per_layer_projection_norm.weight"])
         self.g_f = _bf(t["model.norm.weight"])

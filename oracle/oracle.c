@@ -47,6 +47,7 @@ typedef struct {
       hidden_size_per_layer_input, vocab_size, quant /* 0 bf16, 1 w4a16 */, group_size;
   double rms_eps, rope_theta_sliding, rope_theta_full;
   int kv_bf16; /* 1: K/V stored in the cache rounded to bf16 (the pages' cache dtype) */
+  int embed_quant; /* 0: bf16 vocabulary tables; 1: W4A16 (int4 codes, bf16 group scales) */
 } orc_config;
 
 typedef struct {
@@ -66,7 +67,9 @@ typedef struct {
 typedef struct {
   orc_config c;
   int L, H, P, V, nq, first_shared;
-  const uint16_t *embed, *ple, *g_plpn, *g_final;
+  const uint16_t *g_plpn, *g_final;
+  orc_lin embed; /* tied token embedding / lm_head [V, H] */
+  orc_lin ple;   /* per-layer table [V, L*P] */
   orc_lin plmp;
   orc_layer* layers;
   int max_seq, max_ctx;
@@ -217,11 +220,11 @@ static const void* find(const tab_t* t, const char* name) {
   return NULL;
 }
 
-static int get_lin(const tab_t* t, const orc_config* c, const char* name, int N, int K, orc_lin* L) {
+static int get_lin_q(const tab_t* t, int quant, int G, const char* name, int N, int K, orc_lin* L) {
   char buf[256];
-  L->quant = c->quant; L->N = N; L->K = K; L->G = c->group_size;
+  L->quant = quant; L->N = N; L->K = K; L->G = G;
   L->w = NULL; L->packed = NULL; L->scale = NULL;
-  if (c->quant == 0) {
+  if (quant == 0) {
     L->w = (const uint16_t*)find(t, name);
     return L->w != NULL;
   }
@@ -230,6 +233,10 @@ static int get_lin(const tab_t* t, const orc_config* c, const char* name, int N,
   snprintf(buf, sizeof buf, "%s_scale", name);
   L->scale = (const uint16_t*)find(t, buf);
   return L->packed && L->scale;
+}
+
+static int get_lin(const tab_t* t, const orc_config* c, const char* name, int N, int K, orc_lin* L) {
+  return get_lin_q(t, c->quant, c->group_size, name, N, K, L);
 }
 
 void orc_destroy(void* p);
@@ -246,8 +253,10 @@ void* orc_create(const orc_config* c, int n, const char** names, const void** pt
   m->max_seq = max_seq; m->max_ctx = max_ctx;
   int L = m->L, H = m->H, P = m->P;
   int ok = 1;
-  ok &= (m->embed = (const uint16_t*)find(&t, "model.embed_tokens.weight")) != NULL;
-  ok &= (m->ple = (const uint16_t*)find(&t, "model.embed_tokens_per_layer.weight")) != NULL;
+  /* the vocabulary tables: bf16, or (embed_quant) the W4A16 format of the linears */
+  ok &= get_lin_q(&t, c->embed_quant, c->group_size, "model.embed_tokens.weight", m->V, H, &m->embed);
+  ok &= get_lin_q(&t, c->embed_quant, c->group_size, "model.embed_tokens_per_layer.weight", m->V,
+                  L * P, &m->ple);
   ok &= (m->g_plpn = (const uint16_t*)find(&t, "model.per_layer_projection_norm.weight")) != NULL;
   ok &= (m->g_final = (const uint16_t*)find(&t, "model.norm.weight")) != NULL;
   ok &= get_lin(&t, c, "model.per_layer_model_projection.weight", L * P, H, &m->plmp);
@@ -356,8 +365,8 @@ int orc_kv_load(void* p, int l, int seq, int pos0, int n, const uint16_t* k, con
  * ("Porting Gemma 4 E2B to SGLang-JAX", Step 3). */
 static void orc_inputs(orc_model* m, int x, double* e, double* pli) {
   const int L = m->L, H = m->H, P = m->P;
-  for (int i = 0; i < H; ++i) e[i] = bf(m->embed[(int64_t)x * H + i]) * sqrt((double)H);
-  for (int i = 0; i < L * P; ++i) m->tok[i] = bf(m->ple[(int64_t)x * L * P + i]) * sqrt((double)P);
+  for (int i = 0; i < H; ++i) e[i] = lin_w(&m->embed, x, i) * sqrt((double)H);
+  for (int i = 0; i < L * P; ++i) m->tok[i] = lin_w(&m->ple, x, i) * sqrt((double)P);
   linear(&m->plmp, e, m->u);
   for (int i = 0; i < L * P; ++i) m->u[i] *= 1.0 / sqrt((double)H);
   for (int l = 0; l < L; ++l) orc_rmsnorm(m->u + l * P, P, m->g_plpn, m->c.rms_eps, m->u + l * P);
@@ -440,10 +449,7 @@ int orc_step_ex(void* p, int seq, int x, int pos, int head, double* logits, doub
   if (!head) return 0;
   /* tied lm_head and greedy choice */
   double* lg = logits ? logits : (double*)malloc(sizeof(double) * m->V);
-  {
-    orc_lin E = {0, m->V, H, c->group_size, m->embed, NULL, NULL};
-    linear(&E, m->y, lg);
-  }
+  linear(&m->embed, m->y, lg);
   int best = orc_argmax(lg, m->V);
   if (!logits) free(lg);
   return best;

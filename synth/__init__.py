@@ -201,22 +201,31 @@ def tokens(n: int, seed: int, vocab: int, stream: str = "prompt") -> np.ndarray:
 
 
 def generate(cfg: dict, quant: str = "bf16", seed: int = 0, kv_all_layers: bool = True,
-             scale_lo: float = None, scale_hi: float = None) -> Dict[str, np.ndarray]:
+             scale_lo: float = None, scale_hi: float = None,
+             embed_quant: str = "bf16") -> Dict[str, np.ndarray]:
     """All tensors of one synthetic model, keyed by canonical name.
 
     quant "bf16": linears are ``<name>`` bf16 [N, K].
     quant "w4a16": linears are ``<name>_packed`` int32 [N, K/8] plus
     ``<name>_scale`` bf16 [N, K/32] (name ends in ``.weight`` so the keys are
     ``...weight_packed`` / ``...weight_scale``).
+    embed_quant "w4a16": the two vocabulary tables (the tied token embedding
+    and the per-layer table) in that same format too, codes uniform and group
+    scales from the workload's W4A16 range (the int4 vocabulary tables of the
+    pages' "text-emb4" build); "bf16": N(0, 0.02) bf16 tables.
     """
-    assert quant in ("bf16", "w4a16")
+    assert quant in ("bf16", "w4a16") and embed_quant in ("bf16", "w4a16")
     G = cfg["group_size"]
     lo, hi = cfg.get("w4a16_scale", (0.002, 0.02))
     scale_lo = lo if scale_lo is None else scale_lo
     scale_hi = hi if scale_hi is None else scale_hi
     out: Dict[str, np.ndarray] = {}
     for s in tensor_specs(cfg, kv_all_layers=kv_all_layers):
-        if s.kind == "embed":
+        if s.kind == "embed" and embed_quant == "w4a16":
+            N, K = s.shape
+            out[s.name + "_packed"] = bits32((N, K // 8), seed, s.name + "_packed")
+            out[s.name + "_scale"] = uniform_bf16((N, K // G), seed, s.name + "_scale", scale_lo, scale_hi)
+        elif s.kind == "embed":
             out[s.name] = normal_bf16(s.shape, seed, s.name)
         elif s.kind == "gain":
             out[s.name] = normal_bf16(s.shape, seed, s.name, 1.0, 0.02)

@@ -240,13 +240,14 @@ def test_per_layer_inputs_closed_forms():
 
 # ---------------------------------------------------------------- cached vs brute force
 @pytest.mark.parametrize("name", ["toy", "toy10"])
-@pytest.mark.parametrize("quant", ["bf16", "w4a16"])
+@pytest.mark.parametrize("quant,embed_quant", [("bf16", "bf16"), ("w4a16", "bf16"), ("w4a16", "w4a16")])
 @pytest.mark.parametrize("kv_bf16", [True, False])
-def test_cached_oracle_matches_bruteforce(name, quant, kv_bf16):
+def test_cached_oracle_matches_bruteforce(name, quant, embed_quant, kv_bf16):
     """Cached decode == re-running the whole sequence (tolerance: fp64 roundoff),
     across the sliding-window edge (sequence 26 > window 16), with the cache
-    in bf16 and in fp64."""
-    cfg, w = _small(name, quant)
+    in bf16 and in fp64, and with the vocabulary tables in bf16 or int4."""
+    cfg = synth.get_config(name)
+    w = synth.generate(cfg, quant, embed_quant=embed_quant)
     o = oracle.Oracle(cfg, quant, w, 2, 40, kv_bf16=kv_bf16)
     nv = Naive(cfg, quant, w, kv_bf16=kv_bf16)
     toks = list(synth.tokens(26, 11, cfg["vocab_size"]))
@@ -255,6 +256,45 @@ def test_cached_oracle_matches_bruteforce(name, quant, kv_bf16):
         r, lg, _ = o.step(1, t, p)
         assert np.max(np.abs(lg - ref[p])) < 1e-11 * max(1.0, np.abs(ref[p]).max())
         assert r == int(np.argmax(ref[p]))
+
+
+def _unpack_codes(packed):
+    """int4 codes of packed words, natural order (element 8j+i in bits 4i..4i+3)."""
+    u = packed.view(np.uint32)
+    return np.stack([(u >> np.uint32(4 * i)) & np.uint32(15) for i in range(8)], axis=-1).reshape(
+        u.shape[0], u.shape[1] * 8).astype(np.int64)
+
+
+@pytest.mark.parametrize("name", ["toy", "toy10"])
+def test_int4_vocabulary_tables_reduce_to_bf16_tables(name):
+    """Special case: with power-of-two group scales every decoded value
+    (c - 8) * 2^-e has at most four significant bits, so it is a bf16 number.
+    A model whose two vocabulary tables are int4 must then give exactly the
+    logits of the same model with those values stored as bf16 tables: the
+    embedding gather, the per-layer table gather and the tied lm_head all read
+    the int4 tables ("Six Serving Engines on One Cloud TPU v5e Chip", What
+    Changes and What Stays: the vocabulary tables in int4; Step 3: an int4
+    lm_head).  A wrong nibble order or scale index breaks the equality."""
+    cfg = synth.get_config(name)
+    w4 = synth.generate(cfg, "w4a16", seed=5, embed_quant="w4a16")
+    rng = np.random.default_rng(0)
+    wb = {k: v for k, v in w4.items() if not k.startswith("model.embed_tokens")}
+    for t in ("model.embed_tokens.weight", "model.embed_tokens_per_layer.weight"):
+        sc = w4[t + "_scale"]
+        pw = rng.integers(-9, -5, size=sc.shape)                      # scales 2^-9 .. 2^-6
+        w4[t + "_scale"] = synth.f32_to_bf16(np.ldexp(np.ones(sc.shape, np.float32), pw))
+        vals = (_unpack_codes(w4[t + "_packed"]) - 8) * np.repeat(np.ldexp(1.0, pw), 32, axis=1)
+        bits = synth.f32_to_bf16(vals.astype(np.float32))
+        assert np.array_equal(synth.bf16_to_f32(bits).astype(np.float64), vals)   # exact in bf16
+        wb[t] = bits
+    toks = synth.tokens(10, 3, cfg["vocab_size"])
+    o4 = oracle.Oracle(cfg, "w4a16", w4, 1, 16)
+    ob = oracle.Oracle(cfg, "w4a16", wb, 1, 16)
+    assert o4.embed_quant == "w4a16" and ob.embed_quant == "bf16"
+    for p, t in enumerate(toks):
+        r4, l4, _ = o4.step(0, int(t), p)
+        rb, lb, _ = ob.step(0, int(t), p)
+        assert np.array_equal(l4, lb) and r4 == rb, p
 
 
 def test_greedy_prefill_then_decode_matches_bruteforce():
