@@ -60,12 +60,14 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def step_bytes(cfg, quant, batch, positions):
+def step_bytes(cfg, quant, batch, positions, embed_quant="bf16"):
     """Algorithmic bytes of one decode step at the given positions (per sequence
     the position of its new token).  Weights: every linear, the tied lm_head
     and the norm gains are read once per step; the per-layer table is gathered
     (one row per token).  K/V: unique bytes of the caches read (sharing layers
-    read their source's cache, counted once) plus the new token's K/V write."""
+    read their source's cache, counted once) plus the new token's K/V write.
+    embed_quant "w4a16": the vocabulary tables (lm_head, gathers) are int4
+    codes plus a bf16 scale per 32."""
     import synth
     L, H, P, V = cfg["num_hidden_layers"], cfg["hidden_size"], cfg["hidden_size_per_layer_input"], cfg["vocab_size"]
     lin = gain = 0
@@ -77,11 +79,13 @@ def step_bytes(cfg, quant, batch, positions):
             lin += n // 2 + 2 * (n // 32) if quant == "w4a16" else 2 * n
         elif s.kind in ("gain", "scalar"):
             gain += 2 * n
-    weights = lin + 2 * V * H + gain
+    def table(n):   # bytes of n vocabulary-table values
+        return n // 2 + 2 * (n // 32) if embed_quant == "w4a16" else 2 * n
+    weights = lin + table(V * H) + gain
     kv_read = sum(kv_bytes(cfg, p, unique=True) for p in positions) / len(positions)
     first = L - cfg["num_kv_shared_layers"]
     kv_write = 2 * 2 * sum(synth.layer_head_dim(cfg, l) for l in range(first))
-    gathers = 2 * H + 2 * L * P
+    gathers = table(H) + table(L * P)
     per_step = weights + kv_read * batch + batch * (kv_write + gathers)
     return per_step, weights
 
@@ -122,14 +126,14 @@ def pmc_traffic(pattern):
                for k in hits) / n
 
 
-def kernel_pattern(kind, quant, batch):
+def kernel_pattern(kind, quant, batch, embed_quant="bf16"):
     """Regular expression of the kernel symbols (as rocprof names them) that
     run this kind at this batch: the one-row matvec, or the matrix-core
     product with its m-tiles per block."""
     if kind not in TAGS:
         return None
     tag = TAGS[kind]
-    wq = 0 if kind == "lm_head" else int(quant == "w4a16")
+    wq = int((embed_quant if kind == "lm_head" else quant) == "w4a16")
     if batch == 1:
         return rf"void e2b::k_gemv<{wq}, \d+, \d+, {tag}>"
     mt = 1 if batch <= 16 else (2 if batch <= 32 else 4)
@@ -182,7 +186,8 @@ def quantiles(xs):
     return q[0], statistics.median(xs), q[2]
 
 
-def measure(cfg, quant, B, P, K, W, prof_steps, repeats, eager=False, cpu_steps=0, label=""):
+def measure(cfg, quant, B, P, K, W, prof_steps, repeats, eager=False, cpu_steps=0, label="",
+            embed_quant="bf16"):
     import numpy as np
     import torch
 
@@ -191,7 +196,7 @@ def measure(cfg, quant, B, P, K, W, prof_steps, repeats, eager=False, cpu_steps=
 
     V = cfg["vocab_size"]
     t0 = time.time()
-    w = synth.generate(cfg, quant, seed=0)
+    w = synth.generate(cfg, quant, seed=0, embed_quant=embed_quant)
     max_ctx = P + max(K, W, prof_steps) + 8
     eng = Engine(cfg, quant, w, max_batch=B, max_ctx=max_ctx, max_rows=min(128, max(B, P)))
     dev = eng.device
@@ -242,7 +247,7 @@ def measure(cfg, quant, B, P, K, W, prof_steps, repeats, eager=False, cpu_steps=
     log(f"[{label}] {repeats} x {K} steps: median {ms:.2f} ms (IQR {q1:.2f}-{q3:.2f}); "
         f"prefill {statistics.median(pre_ms):.2f} ms")
     ms_step = ms / K
-    sb, wbytes = step_bytes(cfg, quant, B, list(range(P, P + K)))
+    sb, wbytes = step_bytes(cfg, quant, B, list(range(P, P + K)), embed_quant)
 
     # per-kernel timing: eager steps at the same positions, each queued behind
     # a spin kernel; each launch of one kind records its own start and end
@@ -311,12 +316,12 @@ def measure(cfg, quant, B, P, K, W, prof_steps, repeats, eager=False, cpu_steps=
     return res
 
 
-def roofline_of(res, quant, B, calib):
+def roofline_of(res, quant, B, calib, embed_quant="bf16"):
     prof = {k: v for k, v in res["kinds"].items()}
     dom = max(prof, key=lambda k: prof[k]["ms"] * prof[k]["launches"])
     d = prof[dom]
     achieved = d["bytes"] / (d["ms"] / 1e3)
-    pat = kernel_pattern(dom, quant, B)
+    pat = kernel_pattern(dom, quant, B, embed_quant)
     traffic = pmc_traffic(pat) if pat else None
     return {"scope": "dominant kernel", "bound": "hbm", "kernel": dom, "symbols": pat,
             "achieved": round(achieved / 1e9, 1), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
@@ -471,13 +476,15 @@ def main():
                    f"{args.quant} B={B}")
     also = []
     if not args.no_aux:
-        for q, b in (("w4a16", 1), ("bf16", 64), ("w4a16", 64)):
-            if (q, b) == (args.quant, B):
+        for q, b, eq in (("w4a16", 1, "bf16"), ("w4a16", 1, "w4a16"), ("bf16", 64, "bf16"),
+                         ("w4a16", 64, "bf16"), ("w4a16", 64, "w4a16")):
+            if (q, b, eq) == (args.quant, B, "bf16"):
                 continue
-            r = measure(cfg, q, b, P, K, W, 8, R, False, 0, f"{q} B={b}")
-            also.append({"quant": q, "batch": b, "tok_s": round(r["value"], 2),
+            lab = f"{q}{' + int4 vocabulary tables' if eq == 'w4a16' else ''} B={b}"
+            r = measure(cfg, q, b, P, K, W, 8, R, False, 0, lab, eq)
+            also.append({"quant": q, "embed_quant": eq, "batch": b, "tok_s": round(r["value"], 2),
                          "ms_per_step": round(r["ms_per_step"], 4), "repeats": r["repeats"],
-                         "step_roofline": step_roofline(r, calib), "roofline": roofline_of(r, q, b, calib),
+                         "step_roofline": step_roofline(r, calib), "roofline": roofline_of(r, q, b, calib, eq),
                          "kernel_kinds": kinds_summary(r, 8), "prefill": r["prefill"]})
         if not args.no_long:
             for b in (1, 8):

@@ -4,6 +4,7 @@
  *
  * What the step computes is defined on the pages
  *   [P1] "Gemma 4 E2B in JAX on One TPU v5e: bf16 or 4-Bit, Python or Rust"
+ *   [P2] "Six Serving Engines on One Cloud TPU v5e Chip"
  *   [P3] "Porting Gemma 4 E2B to SGLang-JAX on One Cloud TPU v5e"
  *   [P4] "Gemma 4 E2B in Pure JAX on a Colab TPU: Google's 4-Bit Export
  *        Against an Exact Repack"
@@ -52,7 +53,11 @@ enum { E2B_DTYPE_BF16 = 0, E2B_DTYPE_INT32 = 1 };
  * l % layer_pattern_period == layer_pattern_period - 1.  quant selects how
  * every linear layer is stored: bf16 [N, K], or W4A16 = int4 codes eight per
  * int32 with one bf16 scale per group_size (32) consecutive K ([P5] The
- * engine; [P4] intro table). */
+ * engine; [P4] intro table).  embed_quant selects the same for the two
+ * vocabulary tables: bf16, or W4A16 (the int4 vocabulary tables and int4
+ * lm_head of [P2] "Six Serving Engines on One Cloud TPU v5e Chip", What
+ * Changes and What Stays and Step 3), decoded exactly for the gathers and
+ * streamed as int4 by the tied lm_head. */
 typedef struct {
   int32_t num_hidden_layers;
   int32_t num_kv_shared_layers;
@@ -67,8 +72,10 @@ typedef struct {
   int32_t use_double_wide_mlp;  /* 2x width from the first shared layer on */
   int32_t hidden_size_per_layer_input;
   int32_t vocab_size;
-  int32_t quant;      /* E2B_QUANT_* */
-  int32_t group_size; /* 32 */
+  int32_t quant;       /* E2B_QUANT_*: every linear layer */
+  int32_t embed_quant; /* E2B_QUANT_*: the two vocabulary tables (the tied token
+                          embedding / lm_head and the per-layer table) */
+  int32_t group_size;  /* 32 */
   float rms_eps;
   float rope_theta_sliding;
   float rope_theta_full;
@@ -83,7 +90,8 @@ typedef struct {
  *  post_per_layer_input_norm}.weight", "...self_attn.{q,k,v,o}_proj.weight",
  * "...self_attn.{q,k}_norm.weight", "...mlp.{gate,up,down}_proj.weight",
  * "...per_layer_input_gate.weight", "...per_layer_projection.weight",
- * "...layer_scalar").  Under W4A16 a linear "X.weight" is given as
+ * "...layer_scalar").  Under W4A16 a linear "X.weight" (and, with
+ * embed_quant W4A16, each vocabulary table) is given as
  * "X.weight_packed" (int32 [N, K/8]; word j holds K-elements 8j..8j+7, element
  * 8j+i in bits [4i, 4i+4) as the code q+8, q in -8..7) and "X.weight_scale"
  * (bf16 [N, K/32]).  Row-major, C-contiguous. */
@@ -100,7 +108,8 @@ typedef struct e2b_model e2b_model;
 /* Fill *out with a preset: "toy" (5 layers, hidden 256), "toy10" (10 layers,
  * 2 full, last 5 shared) or "e2b" (35 layers, hidden 1536, 8 query heads,
  * head dims 256/512, window 512, MLP 6144/12288, per-layer input 256, vocab
- * 262144).  quant is set to bf16; change it before e2b_create.
+ * 262144).  quant and embed_quant are set to bf16; change them before
+ * e2b_create.
  * E2B_EINVAL for an unknown name. */
 int e2b_config_preset(const char* name, e2b_config* out);
 

@@ -201,12 +201,13 @@ def test_matvec_random_matches_oracle(torch_dev, quant, N, K, rows):
 
 # ---------------------------------------------------------------- whole step, toy
 @pytest.mark.parametrize("name", ["toy", "toy10"])
-@pytest.mark.parametrize("quant", ["bf16", "w4a16"])
-def test_toy_greedy_parity(torch_dev, name, quant):
-    """8-token prompt, 32 greedy steps (crosses the 16-wide window)."""
+@pytest.mark.parametrize("quant,embed_quant", [("bf16", "bf16"), ("w4a16", "bf16"), ("w4a16", "w4a16")])
+def test_toy_greedy_parity(torch_dev, name, quant, embed_quant):
+    """8-token prompt, 32 greedy steps (crosses the 16-wide window); the
+    vocabulary tables in bf16 or int4."""
     torch, dev = torch_dev
     cfg = synth.get_config(name)
-    w = synth.generate(cfg, quant, seed=0)
+    w = synth.generate(cfg, quant, seed=0, embed_quant=embed_quant)
     eng = _engine(cfg, quant, w, 1, 48, 8)
     orc = oracle.Oracle(cfg, quant, w, 1, 48)
     run_greedy(torch, eng, orc, [synth.tokens(8, 1, cfg["vocab_size"])], 32, quant)
@@ -362,12 +363,16 @@ def test_device_error_word(torch_dev):
 
 # ---------------------------------------------------------------- E2B shape
 E2B_PROMPT, E2B_STEPS, E2B_BATCH = 128, 512, 64
+# the E2B workloads: bf16, W4A16 (bf16 vocabulary tables), and W4A16 with the
+# vocabulary tables in int4 too (the int4 lm_head; shorter runs)
+E2B_WORKLOADS = {"bf16": ("bf16", "bf16"), "w4a16": ("w4a16", "bf16"), "w4a16-emb4": ("w4a16", "w4a16")}
 
 
-@pytest.fixture(scope="module", params=["bf16", "w4a16"])
+@pytest.fixture(scope="module", params=list(E2B_WORKLOADS))
 def e2b_model(request):
     cfg = synth.get_config("e2b")
-    return cfg, request.param, synth.generate(cfg, request.param, seed=0)
+    quant, eq = E2B_WORKLOADS[request.param]
+    return cfg, quant, synth.generate(cfg, quant, seed=0, embed_quant=eq)
 
 
 @pytest.fixture(scope="module")
@@ -381,8 +386,9 @@ def e2b_engine(torch_dev, e2b_model):
 
 
 def test_e2b_gathers_bit_exact(torch_dev, e2b_model, e2b_engine):
-    """The embedding gathers of the step (a1, a2's table row) equal the widened
-    bf16 table rows times sqrt(H) / sqrt(P) rounded once to fp32, bit for bit,
+    """The embedding gathers of the step (a1, a2's table row) equal the table
+    rows (widened bf16, or int4 decoded exactly) times sqrt(H) / sqrt(P)
+    rounded once to fp32, bit for bit,
     for the first and last vocabulary rows and random ones; the oracle's fp64
     embedding agrees to within the fp32 rounding of the constant and the
     product."""
@@ -397,9 +403,15 @@ def test_e2b_gathers_bit_exact(torch_dev, e2b_model, e2b_engine):
     eng.embed(torch.from_numpy(toks).to(dev), h, tp)
     eng.check()
     got_h, got_tp = h.cpu().numpy(), tp.cpu().numpy()
-    E, Ep = w["model.embed_tokens.weight"], w["model.embed_tokens_per_layer.weight"]
-    want_h = synth.bf16_to_f32(E[toks]) * np.float32(np.sqrt(H))
-    want_tp = synth.bf16_to_f32(Ep[toks]) * np.float32(np.sqrt(cfg["hidden_size_per_layer_input"]))
+    def rows(name):   # the table rows as fp32: widened bf16, or decoded int4 (exact in fp32)
+        if name in w:
+            return synth.bf16_to_f32(w[name][toks])
+        u = w[name + "_packed"][toks].view(np.uint32)
+        codes = np.stack([(u >> np.uint32(4 * i)) & np.uint32(15) for i in range(8)], -1)
+        codes = codes.reshape(len(toks), -1).astype(np.float32) - 8
+        return codes * np.repeat(synth.bf16_to_f32(w[name + "_scale"][toks]), 32, axis=1)
+    want_h = rows("model.embed_tokens.weight") * np.float32(np.sqrt(H))
+    want_tp = rows("model.embed_tokens_per_layer.weight") * np.float32(np.sqrt(cfg["hidden_size_per_layer_input"]))
     assert want_h.dtype == np.float32 and want_tp.dtype == np.float32
     assert np.array_equal(got_h, want_h)
     assert np.array_equal(got_tp, want_tp)   # sqrt(256) = 16: exact, no rounding at all
@@ -425,8 +437,13 @@ def test_e2b_greedy_512_parity(torch_dev, e2b_model, e2b_engine):
     cfg, quant, w = e2b_model
     eng = e2b_engine
     V, P, S = cfg["vocab_size"], E2B_PROMPT, E2B_STEPS
+    if eng.embed_quant == "w4a16":
+        S = 128       # the int4-table variant: a shorter run
+        quant_label = "w4a16 + int4 vocabulary tables"
+    else:
+        quant_label = quant
     prompt = synth.tokens(P, 1, V)
-    print(f"\n[e2b {quant} B=1] GPU: {P}-token prefill, {S} graph steps", flush=True)
+    print(f"\n[e2b {quant_label} B=1] GPU: {P}-token prefill, {S} graph steps", flush=True)
     s = torch.cuda.Stream(dev)
     gl = np.empty((S, V), np.float32)
     fed, gt = [], []
@@ -456,10 +473,10 @@ def test_e2b_greedy_512_parity(torch_dev, e2b_model, e2b_engine):
         _, ref, _ = orc.step(0, fed[i], P + i)
         st.add(gl[i], gt[i], ref, f"step {i} (position {P + i})")
         if i % 64 == 63:
-            print(f"[e2b {quant} B=1] oracle at step {i + 1}/{S}: worst rel err {st.worst:.3e}, "
+            print(f"[e2b {quant_label} B=1] oracle at step {i + 1}/{S}: worst rel err {st.worst:.3e}, "
                   f"agree {st.agree}/{st.n}", flush=True)
     orc.close()
-    st.finish(f"e2b {quant} B=1, {P}-token prompt + {S} steps", min_agree=0.99)
+    st.finish(f"e2b {quant_label} B=1, {P}-token prompt + {S} steps", min_agree=0.99)
 
 
 def test_e2b_batch64_prefill_graph_parity(torch_dev, e2b_model, e2b_engine):
@@ -472,6 +489,8 @@ def test_e2b_batch64_prefill_graph_parity(torch_dev, e2b_model, e2b_engine):
     eng = e2b_engine
     V, P, B, S = cfg["vocab_size"], E2B_PROMPT, E2B_BATCH, 24
     rows = [0, 31, 63]
+    if eng.embed_quant == "w4a16":   # the int4-table variant: a shorter run
+        S, rows = 8, [0, 63]
     prompts = [synth.tokens(P, 1 + b, V) for b in range(B)]
     s = torch.cuda.Stream(dev)
     pre = {}

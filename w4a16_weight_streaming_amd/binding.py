@@ -34,7 +34,7 @@ class Config(ctypes.Structure):
         "num_hidden_layers", "num_kv_shared_layers", "hidden_size", "num_attention_heads",
         "num_key_value_heads", "head_dim", "global_head_dim", "sliding_window",
         "layer_pattern_period", "intermediate_size", "use_double_wide_mlp",
-        "hidden_size_per_layer_input", "vocab_size", "quant", "group_size")] + \
+        "hidden_size_per_layer_input", "vocab_size", "quant", "embed_quant", "group_size")] + \
         [(n, ctypes.c_float) for n in ("rms_eps", "rope_theta_sliding", "rope_theta_full")]
 
     def as_dict(self) -> dict:
@@ -111,17 +111,23 @@ def _check(rc: int):
         raise E2BError(rc, load_library().e2b_last_error().decode())
 
 
-def config_preset(name: str, quant: str = "bf16") -> Config:
+def config_preset(name: str, quant: str = "bf16", embed_quant: str = "bf16") -> Config:
     c = Config()
     _check(load_library().e2b_config_preset(name.encode(), ctypes.byref(c)))
     c.quant = QUANT[quant]
+    c.embed_quant = QUANT[embed_quant]
     return c
 
 
-def config_from_dict(d: dict, quant: str) -> Config:
+def config_from_dict(d: dict, quant: str, embed_quant: str = "bf16") -> Config:
     c = Config()
     for n, _ in Config._fields_:
-        setattr(c, n, QUANT[quant] if n == "quant" else d[n])
+        if n == "quant":
+            c.quant = QUANT[quant]
+        elif n == "embed_quant":
+            c.embed_quant = QUANT[embed_quant]
+        else:
+            setattr(c, n, d[n])
     return c
 
 
@@ -227,7 +233,10 @@ class Engine:
         arch = torch.cuda.get_device_properties(self.device).gcnArchName
         if not arch.startswith("gfx950"):
             raise E2BError(E2B_ESTATE, f"device is {arch}; libe2b is built for gfx950 only")
-        c = config_preset(cfg, quant) if isinstance(cfg, str) else config_from_dict(cfg, quant)
+        # the vocabulary tables' format follows the tensors given
+        eq = "w4a16" if "model.embed_tokens.weight_packed" in tensors else "bf16"
+        c = config_preset(cfg, quant, eq) if isinstance(cfg, str) else config_from_dict(cfg, quant, eq)
+        self.embed_quant = eq
         self.model = Model(c)
         self.cfg = c
         self.quant = quant

@@ -163,9 +163,9 @@ struct QkvPostArgs {
 };
 
 // ---- launchers (kernels.hip) ----------------------------------------------
-hipError_t launch_embed(const Rows& R, const uint16_t* E, const uint16_t* Eple, int H, int LP,
-                        float sqrtH, float sqrtP, float* h, float* tokple, int* err,
-                        const RopeTable& rt, hipStream_t st);
+// E [V, H] and Eple [V, L*P]: both bf16 (w) or both int4 (q + s)
+hipError_t launch_embed(const Rows& R, const Lin& E, const Lin& Eple, float sqrtH, float sqrtP,
+                        float* h, float* tokple, int* err, const RopeTable& rt, hipStream_t st);
 // u: u_parts partials u_pstride floats apart, each [rows][L*P]
 hipError_t launch_ple_finish(const Rows& R, const float* u, int u_parts, size_t u_pstride,
                              const float* tokple, const uint16_t* g, int L, int P,

@@ -46,6 +46,7 @@ struct LayerInfo {
 };
 
 struct LinOff {  // a linear layer as offsets into the arena
+  int quant = 0;  // E2B_QUANT_*
   size_t w = 0, q = 0, s = 0;
   bool tiled = false;   // a copy tiled for the matrix cores: tw (bf16) or tq, ts (W4A16)
   size_t tw = 0, tq = 0, ts = 0;
@@ -76,19 +77,22 @@ struct LayerDev {
 struct e2b_model {
   e2b_config c{};
   int L = 0, H = 0, P = 0, V = 0, nq = 0, first = 0, quant = 0;
+  int equant = 0;  // format of the two vocabulary tables (E2B_QUANT_*)
   std::vector<LayerInfo> li;
   // arena plan
   std::vector<Copy> plan;
   size_t arena_bytes = 0, weight_bytes = 0;
-  size_t off_embed = 0, off_ple = 0, off_plpn = 0, off_final = 0, off_invf[2] = {0, 0};
-  size_t off_embed_t = 0;  // the tied embedding tiled for the batched lm_head (0: none)
+  size_t off_plpn = 0, off_final = 0, off_invf[2] = {0, 0};
+  // the vocabulary tables as linears [V, H] and [V, L*P] (the tied embedding
+  // also tiled for the batched lm_head)
+  LinOff embed_off, ple_off;
   LinOff plmp_off;
   std::vector<LayerOff> lo;
   // device views (valid after load)
   char* arena = nullptr;
   bool loaded = false;
-  const uint16_t *embed = nullptr, *ple = nullptr, *g_plpn = nullptr, *g_final = nullptr;
-  const uint16_t* embed_t = nullptr;
+  const uint16_t *g_plpn = nullptr, *g_final = nullptr;
+  Lin embed, ple;  // the vocabulary tables (bf16 w, or W4A16 q + s)
   const double* invf[2] = {nullptr, nullptr};
   Lin plmp;
   std::vector<LayerDev> ld;
@@ -156,13 +160,14 @@ struct Planner {
   // linears stacked along N into one matrix [sum N, K]; tiled: also keep a
   // copy in the matrix-core fragment order (batched passes)
   LinOff lin(const std::vector<std::string>& names, const std::vector<int>& Ns, int K,
-             bool tiled = true) {
+             bool tiled = true, int quant = -1) {
     LinOff L;
     int N = 0;
     for (int n : Ns) N += n;
     L.N = N;
     L.K = K;
-    if (m->quant == E2B_QUANT_BF16) {
+    L.quant = quant < 0 ? m->quant : quant;
+    if (L.quant == E2B_QUANT_BF16) {
       L.w = alloc((size_t)N * K * 2);
       if (tiled && N % 16 == 0) {
         L.tiled = true;
@@ -197,9 +202,8 @@ struct Planner {
 int build_plan(e2b_model* m) {
   Planner p{m};
   const int L = m->L, H = m->H, P = m->P, V = m->V, nq = m->nq;
-  m->off_embed = p.mat("model.embed_tokens.weight", V, H);
-  if (V % 16 == 0) m->off_embed_t = p.alloc((size_t)V * H * 2);
-  m->off_ple = p.mat("model.embed_tokens_per_layer.weight", V, (int64_t)L * P);
+  m->embed_off = p.lin({"model.embed_tokens.weight"}, {V}, H, true, m->equant);
+  m->ple_off = p.lin({"model.embed_tokens_per_layer.weight"}, {V}, L * P, false, m->equant);
   m->plmp_off = p.lin({"model.per_layer_model_projection.weight"}, {L * P}, H);
   m->off_plpn = p.vec("model.per_layer_projection_norm.weight", P);
   m->off_final = p.vec("model.norm.weight", H);
@@ -250,7 +254,7 @@ Lin resolve(const e2b_model* m, const LinOff& o) {
   Lin L;
   L.N = o.N;
   L.K = o.K;
-  if (m->quant == E2B_QUANT_BF16) {
+  if (o.quant == E2B_QUANT_BF16) {
     L.w = reinterpret_cast<const uint16_t*>(m->arena + o.w);
     if (o.tiled) L.tw = reinterpret_cast<const uint16_t*>(m->arena + o.tw);
   } else {
@@ -444,7 +448,7 @@ int run_rows(e2b_model* m, const e2b::Rows& R, bool head, int head_row, float* d
   rt.inv_f = m->invf[1];
   rt.hd_s = m->c.head_dim;
   rt.hd_f = m->c.global_head_dim;
-  CK(launch_embed(R, m->embed, m->ple, H, LP, std::sqrt((float)H), std::sqrt((float)P), F(W.h0),
+  CK(launch_embed(R, m->embed, m->ple, std::sqrt((float)H), std::sqrt((float)P), F(W.h0),
                   F(W.tokple), err, rt, st),
      "embed");
   {
@@ -631,11 +635,7 @@ int run_rows(e2b_model* m, const e2b::Rows& R, bool head, int head_row, float* d
   if (!head) return E2B_OK;
   const int hr = head_row < 0 ? 0 : head_row;
   const int nh = head_row < 0 ? n : 1;
-  Lin E;
-  E.w = m->embed;
-  E.tw = m->embed_t;
-  E.N = m->V;
-  E.K = H;
+  const Lin& E = m->embed;  // the tied lm_head
   Prologue pr;
   pr.kind = kResNorm;
   pr.a = cur + (size_t)hr * H;
@@ -653,7 +653,7 @@ int run_rows(e2b_model* m, const e2b::Rows& R, bool head, int head_row, float* d
   ep.cand_val = F(W.cv);
   ep.cand_idx = reinterpret_cast<int32_t*>(ws + W.ci);
   int nblk = 0;
-  CK(matmul(m, E2B_QUANT_BF16, kTagLmHead, E, nh, bat, pr, ep, false, nullptr, &nblk, ws, W, st),
+  CK(matmul(m, m->equant, kTagLmHead, E, nh, bat, pr, ep, false, nullptr, &nblk, ws, W, st),
      "lm_head");
   if (nblk > W.ncand) return fail(E2B_EINVAL, "lm_head: %d candidate blocks", nblk);
   CK(launch_argmax_final(nh, nblk, ep.cand_val, ep.cand_idx, d_argmax, adv_pos, st), "argmax");
@@ -674,6 +674,7 @@ int e2b_config_preset(const char* name, e2b_config* out) {
   c.layer_pattern_period = 5;
   c.use_double_wide_mlp = 1;
   c.quant = E2B_QUANT_BF16;
+  c.embed_quant = E2B_QUANT_BF16;
   c.group_size = 32;
   c.rms_eps = 1e-6f;
   c.rope_theta_sliding = 1.0e4f;
@@ -730,6 +731,11 @@ int e2b_create(const e2b_config* cfg, e2b_model** out) {
     return fail(E2B_EINVAL, "vocab_size / hidden_size_per_layer_input out of range");
   if (c.quant != E2B_QUANT_BF16 && c.quant != E2B_QUANT_W4A16)
     return fail(E2B_EINVAL, "unknown quant mode %d", c.quant);
+  if (c.embed_quant != E2B_QUANT_BF16 && c.embed_quant != E2B_QUANT_W4A16)
+    return fail(E2B_EINVAL, "unknown vocabulary-table format %d", c.embed_quant);
+  if (c.embed_quant == E2B_QUANT_W4A16 &&
+      (c.hidden_size % 32 || (c.num_hidden_layers * c.hidden_size_per_layer_input) % 32))
+    return fail(E2B_EINVAL, "int4 vocabulary tables need rows in whole 32-groups");
   if (!(c.rms_eps > 0) || !(c.rope_theta_sliding > 1) || !(c.rope_theta_full > 1))
     return fail(E2B_EINVAL, "rms_eps / rope thetas out of range");
   e2b_model* m = new e2b_model();
@@ -741,6 +747,7 @@ int e2b_create(const e2b_config* cfg, e2b_model** out) {
   m->nq = c.num_attention_heads;
   m->first = c.num_hidden_layers - c.num_kv_shared_layers;
   m->quant = c.quant;
+  m->equant = c.embed_quant;
   m->li.resize(m->L);
   for (int l = 0; l < m->L; ++l) {
     LayerInfo& y = m->li[l];
@@ -845,8 +852,8 @@ int e2b_load_weights(e2b_model* m, const e2b_tensor* t, int n, void* d_arena, si
   }
   m->arena = A;
   auto U = [&](size_t off) { return reinterpret_cast<const uint16_t*>(A + off); };
-  m->embed = U(m->off_embed);
-  m->ple = U(m->off_ple);
+  m->embed = resolve(m, m->embed_off);
+  m->ple = resolve(m, m->ple_off);
   m->g_plpn = U(m->off_plpn);
   m->g_final = U(m->off_final);
   m->invf[0] = reinterpret_cast<const double*>(A + m->off_invf[0]);
@@ -876,20 +883,12 @@ int e2b_load_weights(e2b_model* m, const e2b_tensor* t, int n, void* d_arena, si
   auto tile = [&](const LinOff& o) -> hipError_t {
     if (!o.tiled) return hipSuccess;
     const Lin W = resolve(m, o);
-    if (m->quant == E2B_QUANT_BF16) return e2b::launch_tile_bf16(W, reinterpret_cast<uint16_t*>(A + o.tw), st);
+    if (o.quant == E2B_QUANT_BF16) return e2b::launch_tile_bf16(W, reinterpret_cast<uint16_t*>(A + o.tw), st);
     return e2b::launch_tile_w4(W, reinterpret_cast<uint32_t*>(A + o.tq),
                                reinterpret_cast<uint16_t*>(A + o.ts), st);
   };
   CK(tile(m->plmp_off), "weight tiling");
-  m->embed_t = nullptr;
-  if (m->off_embed_t) {
-    Lin E;
-    E.w = m->embed;
-    E.N = m->V;
-    E.K = m->H;
-    CK(e2b::launch_tile_bf16(E, reinterpret_cast<uint16_t*>(A + m->off_embed_t), st), "embedding tiling");
-    m->embed_t = U(m->off_embed_t);
-  }
+  CK(tile(m->embed_off), "embedding tiling");
   for (int l = 0; l < m->L; ++l) {
     const LayerOff& o = m->lo[l];
     for (const LinOff* x : {&o.qkv, &o.o, &o.gu, &o.down, &o.pg, &o.pp}) CK(tile(*x), "weight tiling");
@@ -1243,7 +1242,7 @@ int e2b_embed(e2b_model* m, const int32_t* d_tokens, int n, float* d_h, float* d
   rt.inv_f = m->invf[1];
   rt.hd_s = m->c.head_dim;
   rt.hd_f = m->c.global_head_dim;
-  CK(e2b::launch_embed(R, m->embed, m->ple, m->H, m->L * m->P, std::sqrt((float)m->H),
+  CK(e2b::launch_embed(R, m->embed, m->ple, std::sqrt((float)m->H),
                        std::sqrt((float)m->P), d_h, d_tokple, reinterpret_cast<int*>(ws + W.err), rt,
                        reinterpret_cast<hipStream_t>(stream)),
      "embed");

@@ -43,11 +43,14 @@ bool take_launch_events(hipEvent_t* start, hipEvent_t* stop) {
 }
 
 // ---------------------------------------------------------------- embedding
-// h[r] = E[tok] * sqrt(H);  tokple[r] = E_ple[tok] * sqrt(P)
-__global__ __launch_bounds__(256) void k_embed(Rows R, const uint16_t* __restrict__ E,
-                                               const uint16_t* __restrict__ Eple, int H, int LP,
-                                               float sqrtH, float sqrtP, float* __restrict__ h,
-                                               float* __restrict__ tokple, int* err, RopeTable rt) {
+// h[r] = E[tok] * sqrt(H);  tokple[r] = E_ple[tok] * sqrt(P).  bf16 tables
+// (EQ = 0) are widened; int4 tables (EQ = 1) decode (c - 8) * s, exact in
+// fp32, first.  Either way the one rounding is the product with the fp32
+// constant.
+template <int EQ>
+__global__ __launch_bounds__(256) void k_embed(Rows R, Lin E, Lin Ep, float sqrtH, float sqrtP,
+                                               float* __restrict__ h, float* __restrict__ tokple,
+                                               int* err, RopeTable rt) {
   const int r = blockIdx.x;
   int tok = R.tokens[r];
   if (tok < 0 || tok >= R.vocab) {
@@ -64,34 +67,52 @@ __global__ __launch_bounds__(256) void k_embed(Rows R, const uint16_t* __restric
     atomicExch(err + 2, pos);
     atomicExch(err + 3, r);
   }
-  // 8 values per item (H and LP are multiples of 8), the loads of up to 8
-  // items per thread issued before any store
-  const uint16_t* e = E + (size_t)tok * H;
-  const uint16_t* t = Eple + (size_t)tok * LP;
+  const int H = E.K, LP = Ep.K;
+  // 8 values per item (H and LP are multiples of 8; of 32 for int4), the
+  // loads of up to 8 items per thread issued before any store
   const int nh = H / 8, nw = nh + LP / 8;
   for (int b0 = 0; b0 < nw; b0 += 8 * 256) {
     uint4 v[8];
+    uint32_t sc[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       int w = b0 + threadIdx.x + 256 * k;
       w = w < nw ? w : nw - 1;
-      v[k] = *reinterpret_cast<const uint4*>(w < nh ? e + 8 * w : t + 8 * (w - nh));
+      if constexpr (EQ) {  // one packed word (8 codes) and its group scale
+        const bool is_h = w < nh;
+        const int ww = is_h ? w : w - nh;
+        const uint32_t* q = is_h ? E.q + (size_t)tok * (H / 8) : Ep.q + (size_t)tok * (LP / 8);
+        const uint16_t* gs = is_h ? E.s + (size_t)tok * (H / 32) : Ep.s + (size_t)tok * (LP / 32);
+        v[k].x = q[ww];
+        sc[k] = gs[ww / 4];
+      } else {
+        v[k] = *reinterpret_cast<const uint4*>(w < nh ? E.w + (size_t)tok * H + 8 * w
+                                                      : Ep.w + (size_t)tok * LP + 8 * (w - nh));
+        sc[k] = 0u;
+      }
     }
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const int w = b0 + threadIdx.x + 256 * k;
       if (w >= nw) break;
       const bool is_h = w < nh;
-      const float sc = is_h ? sqrtH : sqrtP;
+      const float c = is_h ? sqrtH : sqrtP;
       float* dst = is_h ? h + (size_t)r * H + 8 * w : tokple + (size_t)r * LP + 8 * (w - nh);
-      const uint32_t q[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
-      float4 lo, hi;
-      lo.x = bf2f(q[0]) * sc; lo.y = bf2f(q[0] >> 16) * sc;
-      lo.z = bf2f(q[1]) * sc; lo.w = bf2f(q[1] >> 16) * sc;
-      hi.x = bf2f(q[2]) * sc; hi.y = bf2f(q[2] >> 16) * sc;
-      hi.z = bf2f(q[3]) * sc; hi.w = bf2f(q[3] >> 16) * sc;
-      reinterpret_cast<float4*>(dst)[0] = lo;
-      reinterpret_cast<float4*>(dst)[1] = hi;
+      float x[8];
+      if constexpr (EQ) {
+        const float gsv = bf2f(sc[k]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = (float)((int)((v[k].x >> (4 * i)) & 15u) - 8) * gsv;
+      } else {
+        const uint32_t q[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[2 * i] = bf2f(q[i]);
+          x[2 * i + 1] = bf2f(q[i] >> 16);
+        }
+      }
+      reinterpret_cast<float4*>(dst)[0] = make_float4(x[0] * c, x[1] * c, x[2] * c, x[3] * c);
+      reinterpret_cast<float4*>(dst)[1] = make_float4(x[4] * c, x[5] * c, x[6] * c, x[7] * c);
     }
   }
   // RoPE angles of this row's position for both layer types, from fp64
@@ -110,13 +131,18 @@ __global__ __launch_bounds__(256) void k_embed(Rows R, const uint16_t* __restric
   }
 }
 
-hipError_t launch_embed(const Rows& R, const uint16_t* E, const uint16_t* Eple, int H, int LP,
-                        float sqrtH, float sqrtP, float* h, float* tokple, int* err,
-                        const RopeTable& rt, hipStream_t st) {
+hipError_t launch_embed(const Rows& R, const Lin& E, const Lin& Eple, float sqrtH, float sqrtP,
+                        float* h, float* tokple, int* err, const RopeTable& rt, hipStream_t st) {
   if (!rt.out || !rt.inv_s || !rt.inv_f) return hipErrorInvalidValue;
-  if (H % 8 || LP % 8 || H + LP < 8) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_embed, dim3(R.n), dim3(256), 0, st, R, E, Eple, H, LP, sqrtH, sqrtP, h,
-                     tokple, err, rt);
+  const bool q = E.q != nullptr;
+  if (q != (Eple.q != nullptr) || (q && (!E.s || !Eple.s)) || (!q && (!E.w || !Eple.w)))
+    return hipErrorInvalidValue;
+  const int g = q ? 32 : 8;
+  if (E.K % g || Eple.K % g || E.K < 8) return hipErrorInvalidValue;
+  if (q)
+    hipLaunchKernelGGL(k_embed<1>, dim3(R.n), dim3(256), 0, st, R, E, Eple, sqrtH, sqrtP, h, tokple, err, rt);
+  else
+    hipLaunchKernelGGL(k_embed<0>, dim3(R.n), dim3(256), 0, st, R, E, Eple, sqrtH, sqrtP, h, tokple, err, rt);
   return hipGetLastError();
 }
 
@@ -410,7 +436,6 @@ hipError_t launch_gemv(int quant, int tag, const Lin& W, int rows, const Prologu
        pro.nchunk < 1 || pro.nchunk > kMaxChunks))
     return hipErrorInvalidValue;
   if (epi.argmax && gemv_splits(W.K) != 1) return hipErrorInvalidValue;
-  if (epi.argmax && quant) return hipErrorInvalidValue;  // the tied lm_head is bf16
   // the kernel is specialised on the product's prologue (argmax: the lm_head's)
   const int tk = epi.argmax ? kTagLmHead : tag;
   if (tag_kind(tk) >= 0 && pro.kind != tag_kind(tk)) return hipErrorInvalidValue;
@@ -418,7 +443,9 @@ hipError_t launch_gemv(int quant, int tag, const Lin& W, int rows, const Prologu
     const int ndmax = tag_kind(tk) >= 0 ? tag_nd(tk) : kMaxSplitK;
     if (pro.nd < 1 || pro.nd > ndmax) return hipErrorInvalidValue;
   }
-  if (epi.argmax) return dispatch_gemv<0, kTagLmHead>(W, rows, pro, epi, blocks_hint, blocks_out, st);
+  if (epi.argmax)  // the tied lm_head: bf16 or int4 vocabulary table
+    return quant ? dispatch_gemv<1, kTagLmHead>(W, rows, pro, epi, blocks_hint, blocks_out, st)
+                 : dispatch_gemv<0, kTagLmHead>(W, rows, pro, epi, blocks_hint, blocks_out, st);
   return quant ? dispatch_tag<1>(tag, W, rows, pro, epi, blocks_hint, blocks_out, st)
                : dispatch_tag<0>(tag, W, rows, pro, epi, blocks_hint, blocks_out, st);
 }
@@ -754,7 +781,7 @@ hipError_t launch_gemm(int quant, int tag, const Lin& W, int rows, const GemmA& 
   const int nks = plan.nks;
   if (rows < 1 || nks < 1 || nks > kMaxGemmSplit || W.K % nks || (W.K / nks) % 32)
     return hipErrorInvalidValue;
-  if (epi.argmax && (quant || nks != 1)) return hipErrorInvalidValue;
+  if (epi.argmax && nks != 1) return hipErrorInvalidValue;
   if (A.a ? A.kind != kPlain || A.na != 1 || A.lda % 8
           : (!A.xh || !A.xl || (quant && !A.xg)))
     return hipErrorInvalidValue;
