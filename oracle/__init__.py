@@ -41,7 +41,7 @@ class OrcConfig(ctypes.Structure):
         "layer_pattern_period", "intermediate_size", "use_double_wide_mlp",
         "hidden_size_per_layer_input", "vocab_size", "quant", "group_size")] + \
         [(n, ctypes.c_double) for n in ("rms_eps", "rope_theta_sliding", "rope_theta_full")] + \
-        [("kv_bf16", ctypes.c_int), ("embed_quant", ctypes.c_int)]
+        [("kv_bf16", ctypes.c_int), ("embed_quant", ctypes.c_int), ("kv_quant", ctypes.c_int)]
 
 
 def build(force: bool = False) -> str:
@@ -91,6 +91,7 @@ def lib():
         L.orc_debug_inputs.restype = i32
         L.orc_debug_inputs.argtypes = [vp, i32, dp, dp]
         L.orc_set_threads.argtypes = [i32]
+        L.orc_quant_int8.argtypes = [dp, i32, vp, vp]
         L.orc_get_threads.restype = i32
         _lib = L
     return _lib
@@ -100,7 +101,8 @@ def _ptr(a: np.ndarray) -> int:
     return a.ctypes.data
 
 
-def make_config(cfg: dict, quant: str, kv_bf16: bool = True, embed_quant: str = "bf16") -> OrcConfig:
+def make_config(cfg: dict, quant: str, kv_bf16: bool = True, embed_quant: str = "bf16",
+                kv_quant: str = "bf16") -> OrcConfig:
     c = OrcConfig()
     for name, _ in OrcConfig._fields_:
         if name == "quant":
@@ -109,6 +111,8 @@ def make_config(cfg: dict, quant: str, kv_bf16: bool = True, embed_quant: str = 
             c.kv_bf16 = 1 if kv_bf16 else 0
         elif name == "embed_quant":
             c.embed_quant = 1 if embed_quant == "w4a16" else 0
+        elif name == "kv_quant":
+            c.kv_quant = 1 if kv_quant == "int8" else 0
         else:
             setattr(c, name, cfg[name])
     return c
@@ -118,7 +122,7 @@ class Oracle:
     """The C reference over one synthetic model (tensors from ``synth``)."""
 
     def __init__(self, cfg: dict, quant: str, tensors: Dict[str, np.ndarray], max_seq: int,
-                 max_ctx: int, kv_bf16: bool = True, embed_quant: str = None):
+                 max_ctx: int, kv_bf16: bool = True, embed_quant: str = None, kv_quant: str = "bf16"):
         self.cfg, self.quant = cfg, quant
         self.V, self.H = cfg["vocab_size"], cfg["hidden_size"]
         self._keep = {k: np.ascontiguousarray(v) for k, v in tensors.items()}
@@ -128,7 +132,8 @@ class Oracle:
         if embed_quant is None:   # the vocabulary tables' format, read off the tensors
             embed_quant = "w4a16" if "model.embed_tokens.weight_packed" in tensors else "bf16"
         self.embed_quant = embed_quant
-        self._cfg = make_config(cfg, quant, kv_bf16, embed_quant)
+        self.kv_quant = kv_quant   # "bf16" (or fp64 without kv_bf16) / "int8"
+        self._cfg = make_config(cfg, quant, kv_bf16, embed_quant, kv_quant)
         self.max_seq, self.max_ctx = max_seq, max_ctx
         h = lib().orc_create(ctypes.byref(self._cfg), len(names), self._names, self._ptrs,
                              max_seq, max_ctx)
@@ -236,6 +241,15 @@ def attend(q, K, V, j0: int, j1: int) -> np.ndarray:
     o = np.empty(len(q), np.float64)
     lib().orc_attend(_ptr(q), len(q), _ptr(K), _ptr(V), j0, j1, _ptr(o))
     return o
+
+
+def quant_int8(x):
+    """(codes int8 [n], scale) of one cached row, as the int8 cache stores it."""
+    x = np.ascontiguousarray(x, np.float64)
+    q = np.empty(len(x), np.int8)
+    sc = np.empty(1, np.float32)
+    lib().orc_quant_int8(_ptr(x), len(x), _ptr(q), _ptr(sc))
+    return q, float(sc[0])
 
 
 def argmax(x) -> int:

@@ -29,6 +29,17 @@ def _round_bf16(a):
     return u.astype(np.uint32).view(np.float32).astype(np.float64)
 
 
+def _int8_rows(a):
+    """Each row (one token's K or V) as symmetric int8 with one scale, decided
+    in float32: scale = max |x| / 127, codes nearest-even, read back as
+    code * scale."""
+    a32 = np.asarray(a, np.float32)
+    sc = np.max(np.abs(a32), axis=-1, keepdims=True) / np.float32(127)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = np.where(sc > 0, np.rint(a32 / sc), np.float32(0))
+    return np.clip(q, -127, 127).astype(np.float64) * sc.astype(np.float64)
+
+
 def _layer_is_full(cfg, l):
     return l % cfg["layer_pattern_period"] == cfg["layer_pattern_period"] - 1
 
@@ -67,8 +78,8 @@ def _rope(x, positions, theta):
 
 
 class Naive:
-    def __init__(self, cfg: dict, quant: str, tensors: dict, kv_bf16: bool = True):
-        self.cfg, self.quant, self.kv_bf16 = cfg, quant, kv_bf16
+    def __init__(self, cfg: dict, quant: str, tensors: dict, kv_bf16: bool = True, kv_quant: str = "bf16"):
+        self.cfg, self.quant, self.kv_bf16, self.kv_quant = cfg, quant, kv_bf16, kv_quant
         c = cfg
         self.L, self.H, self.P = c["num_hidden_layers"], c["hidden_size"], c["hidden_size_per_layer_input"]
         self.nq, self.V = c["num_attention_heads"], c["vocab_size"]
@@ -126,7 +137,9 @@ class Naive:
             if d["src"] == l:
                 k = _rope(_norm(a @ d["self_attn.k_proj"].T, d["k_norm"]), pos, d["theta"])
                 v = _norm(a @ d["self_attn.v_proj"].T)
-                if self.kv_bf16:
+                if self.kv_quant == "int8":
+                    k, v = _int8_rows(k), _int8_rows(v)
+                elif self.kv_bf16:
                     k, v = _round_bf16(k), _round_bf16(v)
                 kv[l] = (k, v)
             k, v = kv[d["src"]]

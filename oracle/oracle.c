@@ -48,6 +48,7 @@ typedef struct {
   double rms_eps, rope_theta_sliding, rope_theta_full;
   int kv_bf16; /* 1: K/V stored in the cache rounded to bf16 (the pages' cache dtype) */
   int embed_quant; /* 0: bf16 vocabulary tables; 1: W4A16 (int4 codes, bf16 group scales) */
+  int kv_quant;    /* 1: K/V cached as int8 with one fp32 scale per cached row (overrides kv_bf16) */
 } orc_config;
 
 typedef struct {
@@ -105,6 +106,30 @@ void orc_set_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
 int orc_get_threads(void) { return omp_get_max_threads(); }
 
 /* ---------------------------------------------------------------- pieces */
+
+/* Symmetric int8 of one cached row (one token's K or V of one layer), the
+ * int8 KV cache of "One TPU chip, eight agents" (Measured: int8 KV donated;
+ * KV memory math): the pages fix the element size (one byte) but not the
+ * scale granularity; the reading here is one scale per cached row, s =
+ * max |x| / 127, code = nearest-even(x / s).  The codes are decided in fp32,
+ * the kernels' precision, so that the same fp32 row gives the same codes on
+ * both sides; a row of zeros has scale 0 and codes 0. */
+void orc_quant_int8(const double* x, int n, int8_t* q, float* s) {
+  float amax = 0.0f;
+  for (int i = 0; i < n; ++i) {
+    const float a = fabsf((float)x[i]);
+    if (a > amax) amax = a;
+  }
+  const float sc = amax / 127.0f;
+  for (int i = 0; i < n; ++i) {
+    float c = sc > 0.0f ? rintf((float)x[i] / sc) : 0.0f;
+    if (c > 127.0f) c = 127.0f;
+    if (c < -127.0f) c = -127.0f;
+    q[i] = (int8_t)c;
+  }
+  *s = sc;
+}
+
 
 /* decoded weight W[n][k] */
 static double lin_w(const orc_lin* L, int64_t n, int64_t k) {
@@ -413,11 +438,22 @@ int orc_step_ex(void* p, int seq, int x, int pos, int head, double* logits, doub
       orc_rope(kr, hd, pos, y->theta);
       linear(&y->v, m->a, m->kv);
       orc_rmsnorm(m->kv, hd, NULL, eps, vr);
-      if (c->kv_bf16)
+      if (c->kv_quant) {
+        /* the cache holds codes and a scale; attention reads code * scale */
+        int8_t qk[512], qv[512];
+        float sk, sv;
+        orc_quant_int8(kr, hd, qk, &sk);
+        orc_quant_int8(vr, hd, qv, &sv);
+        for (int i = 0; i < hd; ++i) {
+          kr[i] = (double)qk[i] * (double)sk;
+          vr[i] = (double)qv[i] * (double)sv;
+        }
+      } else if (c->kv_bf16) {
         for (int i = 0; i < hd; ++i) {
           kr[i] = round_bf16(kr[i]);
           vr[i] = round_bf16(vr[i]);
         }
+      }
     }
     {
       const double* K = m->kc[y->src] + (size_t)seq * m->max_ctx * hd;

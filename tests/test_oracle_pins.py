@@ -297,6 +297,50 @@ def test_int4_vocabulary_tables_reduce_to_bf16_tables(name):
         assert np.array_equal(l4, lb) and r4 == rb, p
 
 
+def test_int8_cache_rows_are_symmetric_absmax_quantization():
+    """The int8 cache's row quantizer ("One TPU chip, eight agents": int8 KV,
+    one byte per element): the scale is max |x| / 127 (fp32), the extreme
+    element lands on +-127, every element is within half a step of its code
+    times the scale, signs are kept, and a row of zeros gives scale 0."""
+    rng = np.random.default_rng(3)
+    rows = [rng.normal(size=256), rng.normal(size=512) * 1e-3, -np.abs(rng.normal(size=64)),
+            np.eye(1, 128, 5)[0] * 7.0, np.linspace(-1, 1, 256)]
+    for x in rows:
+        q, sc = oracle.quant_int8(x)
+        xf = x.astype(np.float32)
+        amax = np.float32(np.max(np.abs(xf)))
+        assert np.float32(sc) == amax / np.float32(127)
+        assert np.all(np.abs(q.astype(np.int64)) <= 127)
+        assert abs(int(q[np.argmax(np.abs(xf))])) == 127
+        err = np.abs(xf.astype(np.float64) - q.astype(np.float64) * sc)
+        assert np.all(err <= 0.5 * sc * (1 + 2.0 ** -20)), np.max(err / sc)
+        big = np.abs(xf) >= 0.5 * sc
+        assert np.all(np.sign(q[big]) == np.sign(xf[big]))
+    q, sc = oracle.quant_int8(np.zeros(64))
+    assert sc == 0.0 and not np.any(q)
+
+
+@pytest.mark.parametrize("name", ["toy", "toy10"])
+@pytest.mark.parametrize("quant", ["bf16", "w4a16"])
+def test_int8_cache_oracle_matches_bruteforce(name, quant):
+    """Cached decode with the int8 cache == re-running the whole sequence with
+    every key and value row quantized the same way (numpy), across the
+    sliding-window edge."""
+    cfg, w = _small(name, quant)
+    o = oracle.Oracle(cfg, quant, w, 1, 40, kv_quant="int8")
+    nv = Naive(cfg, quant, w, kv_quant="int8")
+    toks = list(synth.tokens(26, 12, cfg["vocab_size"]))
+    ref = nv.forward(toks)
+    for p, t in enumerate(toks):
+        r, lg, _ = o.step(0, t, p)
+        assert np.max(np.abs(lg - ref[p])) < 1e-11 * max(1.0, np.abs(ref[p]).max())
+        assert r == int(np.argmax(ref[p]))
+    # and it is a different cache than bf16: the logits move
+    ob = oracle.Oracle(cfg, quant, w, 1, 40)
+    lb = [ob.step(0, t, p)[1] for p, t in enumerate(toks)]
+    assert max(np.max(np.abs(lb[p] - ref[p])) for p in range(len(toks))) > 1e-6
+
+
 def test_greedy_prefill_then_decode_matches_bruteforce():
     cfg, w = _small("toy", "w4a16")
     prompt = list(synth.tokens(8, 1, cfg["vocab_size"]))
