@@ -60,7 +60,7 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def step_bytes(cfg, quant, batch, positions, embed_quant="bf16"):
+def step_bytes(cfg, quant, batch, positions, embed_quant="bf16", kv_quant="bf16"):
     """Algorithmic bytes of one decode step at the given positions (per sequence
     the position of its new token).  Weights: every linear, the tied lm_head
     and the norm gains are read once per step; the per-layer table is gathered
@@ -82,15 +82,20 @@ def step_bytes(cfg, quant, batch, positions, embed_quant="bf16"):
     def table(n):   # bytes of n vocabulary-table values
         return n // 2 + 2 * (n // 32) if embed_quant == "w4a16" else 2 * n
     weights = lin + table(V * H) + gain
-    kv_read = sum(kv_bytes(cfg, p, unique=True) for p in positions) / len(positions)
+    kv_read = sum(kv_bytes(cfg, p, True, kv_quant) for p in positions) / len(positions)
     first = L - cfg["num_kv_shared_layers"]
-    kv_write = 2 * 2 * sum(synth.layer_head_dim(cfg, l) for l in range(first))
+    kv_write = 2 * sum(row_bytes(synth.layer_head_dim(cfg, l), kv_quant) for l in range(first))
     gathers = table(H) + table(L * P)
     per_step = weights + kv_read * batch + batch * (kv_write + gathers)
     return per_step, weights
 
 
-def kv_bytes(cfg, pos, unique):
+def row_bytes(hd, kv_quant):
+    """Bytes of one cached K or V row: bf16, or int8 codes plus an fp32 scale."""
+    return hd + 4 if kv_quant == "int8" else 2 * hd
+
+
+def kv_bytes(cfg, pos, unique, kv_quant="bf16"):
     """K/V bytes one sequence's attention reads at position pos: every layer
     that owns K/V (unique) or every layer (logical: sharing layers re-read
     their source's cache)."""
@@ -101,7 +106,7 @@ def kv_bytes(cfg, pos, unique):
     for l in range(first if unique else L):
         hd = synth.layer_head_dim(cfg, l)
         t = T if synth.layer_is_full(cfg, l) else min(T, cfg["sliding_window"])
-        tot += 2 * 2 * hd * t
+        tot += 2 * row_bytes(hd, kv_quant) * t
     return tot
 
 
@@ -350,7 +355,7 @@ def kinds_summary(res, steps):
     return out
 
 
-def long_context(quant, B, lengths=None, steps=64, chunk=500, top=8000):
+def long_context(quant, B, lengths=None, steps=64, chunk=500, top=8000, kv_quant="bf16"):
     """Context 500 -> 8,000 in 500-token prefill chunks; `steps` timed decode
     steps at each measured length, then the decoded positions are rolled back.
     Returns per-length rows (tok/s, step fraction, prefill ms of the chunk)."""
@@ -362,7 +367,7 @@ def long_context(quant, B, lengths=None, steps=64, chunk=500, top=8000):
     cfg = synth.get_config("e2b")
     V = cfg["vocab_size"]
     w = synth.generate(cfg, quant, seed=0)
-    eng = Engine(cfg, quant, w, max_batch=B, max_ctx=top + steps, max_rows=128)
+    eng = Engine(cfg, quant, w, max_batch=B, max_ctx=top + steps, max_rows=128, kv_quant=kv_quant)
     dev = eng.device
     stream = torch.cuda.Stream(dev)
     rows = []
@@ -400,11 +405,11 @@ def long_context(quant, B, lengths=None, steps=64, chunk=500, top=8000):
             torch.cuda.synchronize()
             eng.check()
             ms = e0.elapsed_time(e1) / steps
-            sb, _ = step_bytes(cfg, quant, B, list(range(L, L + steps)))
+            sb, _ = step_bytes(cfg, quant, B, list(range(L, L + steps)), kv_quant=kv_quant)
             rows.append({"context": L, "tok_s": round(B / (ms / 1e3), 2), "ms_per_step": round(ms, 4),
                          "step_bytes": int(sb), "frac": round(sb / (ms / 1e3) / HBM_PEAK, 4),
                          "prefill_chunk_ms": round(pre_ms, 3)})
-            log(f"[long {quant} B={B}] context {L}: {rows[-1]['tok_s']} tok/s, {ms:.3f} ms/step, "
+            log(f"[long {quant} {kv_quant} cache B={B}] context {L}: {rows[-1]['tok_s']} tok/s, {ms:.3f} ms/step, "
                 f"{chunk}-token chunk prefill {pre_ms:.2f} ms per sequence")
             tok.copy_(tok_ctx)
     graph.close()
@@ -430,6 +435,7 @@ def main():
     ap.add_argument("--no-aux", action="store_true", help="skip the W4A16 / batch-64 / long-context lines")
     ap.add_argument("--no-long", action="store_true", help="skip the long-context lines")
     ap.add_argument("--long", action="store_true", help="long-context workload alone (see above)")
+    ap.add_argument("--kv", choices=["bf16", "int8"], default="bf16", help="K/V cache format (--long)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a 1 GiB device copy (reference kernel for PMC byte counters)")
     args = ap.parse_args()
@@ -453,7 +459,7 @@ def main():
     if args.quant is None:
         args.quant = "w4a16" if args.long else "bf16"
     if args.long:
-        rows = long_context(args.quant, args.batch)
+        rows = long_context(args.quant, args.batch, kv_quant=args.kv)
         cfg = synth.get_config("e2b")
         mean = sum(r["tok_s"] for r in rows) / len(rows)
         ms_mean = sum(r["ms_per_step"] for r in rows) / len(rows)
@@ -461,7 +467,7 @@ def main():
                "steps": 64 * len(rows), "warmup": 2 * len(rows), "ms_per_step": round(ms_mean, 4),
                "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": args.quant,
                "data": "synthetic",
-               "config": {"workload": f"E2B shape, {args.quant} weights, long-context decode: batch "
+               "config": {"workload": f"E2B shape, {args.quant} weights, {args.kv} K/V cache, long-context decode: batch "
                                       f"{args.batch}, context grown 500 -> 8,000 by 500-token random "
                                       f"prefill chunks, 64 greedy decode steps timed at each length "
                                       f"(mean over lengths)", "quant": args.quant, "batch": args.batch},
@@ -487,11 +493,12 @@ def main():
                          "step_roofline": step_roofline(r, calib), "roofline": roofline_of(r, q, b, calib, eq),
                          "kernel_kinds": kinds_summary(r, 8), "prefill": r["prefill"]})
         if not args.no_long:
-            for b in (1, 8):
-                rows = long_context("w4a16", b, lengths=(500, 4000, 8000))
-                also.append({"workload": f"long context, w4a16, batch {b}: context grown by 500-token "
-                                         f"prefill chunks, 64 graph-replayed steps timed at each listed length",
-                             "quant": "w4a16", "batch": b, "per_length": rows})
+            for b, kq in ((1, "bf16"), (8, "bf16"), (1, "int8"), (8, "int8")):
+                rows = long_context("w4a16", b, lengths=(500, 4000, 8000), kv_quant=kq)
+                also.append({"workload": f"long context, w4a16, {kq} K/V cache, batch {b}: context grown by "
+                                         f"500-token prefill chunks, 64 graph-replayed steps timed at each "
+                                         f"listed length", "quant": "w4a16", "kv_quant": kq, "batch": b,
+                             "per_length": rows})
     wl = (f"E2B shape ({cfg['num_hidden_layers']} layers, hidden {cfg['hidden_size']}, vocab "
           f"{cfg['vocab_size']}), {args.quant} weights, batch {B}, {P}-token random prompt then {K} greedy "
           f"decode steps (KV length {P + 1}..{P + K})")

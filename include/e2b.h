@@ -43,6 +43,7 @@ enum {
 };
 
 enum { E2B_QUANT_BF16 = 0, E2B_QUANT_W4A16 = 1 };
+enum { E2B_KV_BF16 = 0, E2B_KV_INT8 = 1 };
 enum { E2B_DTYPE_BF16 = 0, E2B_DTYPE_INT32 = 1 };
 
 /* Model configuration.  Field names follow the checkpoint config fields
@@ -57,7 +58,11 @@ enum { E2B_DTYPE_BF16 = 0, E2B_DTYPE_INT32 = 1 };
  * vocabulary tables: bf16, or W4A16 (the int4 vocabulary tables and int4
  * lm_head of [P2] "Six Serving Engines on One Cloud TPU v5e Chip", What
  * Changes and What Stays and Step 3), decoded exactly for the gathers and
- * streamed as int4 by the tied lm_head. */
+ * streamed as int4 by the tied lm_head.  kv_quant selects the K/V cache
+ * format: bf16, or int8 ([P5] Measured: int8 KV with donation; KV memory
+ * math: one byte per element) with one fp32 scale per cached row (a token's
+ * K or V of one layer): s = max |x| / 127, code = nearest-even(x / s), read
+ * back as code * s. */
 typedef struct {
   int32_t num_hidden_layers;
   int32_t num_kv_shared_layers;
@@ -75,6 +80,7 @@ typedef struct {
   int32_t quant;       /* E2B_QUANT_*: every linear layer */
   int32_t embed_quant; /* E2B_QUANT_*: the two vocabulary tables (the tied token
                           embedding / lm_head and the per-layer table) */
+  int32_t kv_quant;    /* E2B_KV_*: the K/V cache */
   int32_t group_size;  /* 32 */
   float rms_eps;
   float rope_theta_sliding;
@@ -138,9 +144,11 @@ size_t e2b_weight_bytes(const e2b_model* model);
  * tied embedding), built on the device at load time. */
 size_t e2b_arena_bytes(const e2b_model* model);
 
-/* K/V cache bytes for max_batch sequences of max_ctx positions: bf16 K and V
- * of every layer that owns K/V, one KV head; 18,432 B per token per sequence
- * at E2B ([P5] Feasibility part 1: 9,216 elements per token). */
+/* K/V cache bytes for max_batch sequences of max_ctx positions: K and V of
+ * every layer that owns K/V, one KV head; bf16: 18,432 B per token per
+ * sequence at E2B ([P5] Feasibility part 1: 9,216 elements per token); int8:
+ * 9,216 B of codes plus 2 x 15 fp32 row scales (each scale array padded to
+ * 256 bytes). */
 size_t e2b_kv_bytes(const e2b_model* model, int max_batch, int max_ctx);
 
 /* Workspace bytes for calls that process up to max_rows rows (decode batch,
@@ -162,7 +170,8 @@ int e2b_load_weights(e2b_model* model, const e2b_tensor* tensors, int n, void* d
 
 /* Bind caller-owned device memory as the K/V cache: bytes >=
  * e2b_kv_bytes(model, max_batch, max_ctx), else E2B_ENOMEM.  Layout per
- * owning layer: K [max_batch][max_ctx][hd] then V, bf16.  Slot = position
+ * owning layer: K [max_batch][max_ctx][hd] then V, bf16 or int8; for int8
+ * then the K and V row scales, fp32 [max_batch][max_ctx] each.  Slot = position
  * ([P5] The engine: RoPE follows the logical position).  Contents need no
  * initialisation: a position is always written before it is read. */
 int e2b_kv_alloc(e2b_model* model, void* d_kv, size_t bytes, int max_batch, int max_ctx);
@@ -200,7 +209,8 @@ int e2b_prefill(e2b_model* model, int seq, const int32_t* d_tokens, int n_tokens
                 void* stream);
 
 /* Device address of the K (which 0) or V (which 1) cache region that layer
- * `layer` reads, [max_batch][max_ctx][hd] bf16: the layer's own region if it
+ * `layer` reads, [max_batch][max_ctx][hd] bf16 or int8, or (int8 cache) its
+ * K (2) or V (3) row scales, fp32 [max_batch][max_ctx]: the layer's own region if it
  * owns K/V, else its source layer's region (the same address, so shared
  * layers see bit-identical K/V; [P3] Step 1, [P5] The engine).  Requires
  * e2b_kv_alloc.  E2B_EINVAL for a bad layer or which. */

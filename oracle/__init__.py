@@ -78,6 +78,9 @@ def lib():
         L.orc_kv_row.argtypes = [vp, i32, i32, i32, i32]
         L.orc_kv_load.restype = i32
         L.orc_kv_load.argtypes = [vp, i32, i32, i32, i32, vp, vp]
+        L.orc_set_kv_jitter.argtypes = [vp, ctypes.c_double, ctypes.c_uint64]
+        L.orc_kv_set.restype = i32
+        L.orc_kv_set.argtypes = [vp, i32, i32, i32, i32, dp]
         L.orc_linear_apply.argtypes = [i32, vp, vp, i32, i32, i32, dp, dp]
         L.orc_decode_weight.restype = ctypes.c_double
         L.orc_decode_weight.argtypes = [i32, vp, vp, i32, i32, i32, i64, i64]
@@ -182,6 +185,19 @@ class Oracle:
     def kv_row(self, l: int, which: int, seq: int, pos: int, hd: int) -> np.ndarray:
         p = lib().orc_kv_row(self._h, l, which, seq, pos)
         return np.ctypeslib.as_array(p, shape=(hd,)).copy()
+
+    def set_kv_jitter(self, rel: float, seed: int = 1) -> None:
+        """Test hook: multiply each new K/V element by (1 + rel * u), u uniform in
+        [-1, 1) (seeded), before the cache rounds it -- an implementation that
+        computes the same rows with relative error ~rel.  0 turns it off."""
+        lib().orc_set_kv_jitter(self._h, float(rel), int(seed))
+
+    def kv_set(self, l: int, which: int, seq: int, pos: int, row) -> None:
+        """Overwrite one cached K (0) or V (1) row of a K/V-owning layer with the
+        given values (test set-up: a controlled perturbation of the cache)."""
+        r = np.ascontiguousarray(row, np.float64)
+        if lib().orc_kv_set(self._h, l, which, seq, pos, _ptr(r)) != 0:
+            raise RuntimeError("oracle: bad kv_set arguments")
 
     def kv_load(self, l: int, seq: int, pos0: int, k_bits: np.ndarray, v_bits: np.ndarray):
         """Set cached positions pos0.. of a K/V-owning layer from bf16 bits [n, hd]

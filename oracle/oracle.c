@@ -75,6 +75,8 @@ typedef struct {
   orc_layer* layers;
   int max_seq, max_ctx;
   double **kc, **vc; /* per layer; non-NULL only where the layer owns K/V */
+  double jitter;     /* test hook: relative jitter of K/V before the cache rounds them */
+  uint64_t jitter_seed;
   /* scratch */
   double *e, *tok, *u, *pli, *h, *a, *q, *kv, *o, *t, *g, *up, *r, *y;
 } orc_model;
@@ -382,6 +384,39 @@ int orc_kv_load(void* p, int l, int seq, int pos0, int n, const uint16_t* k, con
   return 0;
 }
 
+/* Test hook (conditioning checks): before the cache rounds a new K/V row,
+ * multiply each element by (1 + rel * u), u uniform in [-1, 1) from a
+ * SplitMix64 hash of (seed, layer, K/V, position, element).  It stands for an
+ * implementation that computes the same row with a relative error of about
+ * rel (fp32 against this fp64 reference); rel 0 turns it off. */
+void orc_set_kv_jitter(void* p, double rel, uint64_t seed) {
+  orc_model* m = (orc_model*)p;
+  m->jitter = rel;
+  m->jitter_seed = seed;
+}
+
+static double jitter_u(uint64_t seed, int l, int which, int pos, int i) {
+  uint64_t z = seed ^ ((uint64_t)l << 48) ^ ((uint64_t)which << 47) ^ ((uint64_t)pos << 16) ^ (uint64_t)i;
+  z += 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  z ^= z >> 31;
+  return (double)(z >> 11) * (1.0 / 9007199254740992.0) * 2.0 - 1.0;
+}
+
+/* Test set-up: overwrite one cached row (layer l must own its K/V) with the
+ * given values, exactly as given.  0, or -1 on a bad argument. */
+int orc_kv_set(void* p, int l, int which, int seq, int pos, const double* row) {
+  orc_model* m = (orc_model*)p;
+  if (l < 0 || l >= m->L || m->layers[l].src != l || seq < 0 || seq >= m->max_seq || pos < 0 ||
+      pos >= m->max_ctx || (which != 0 && which != 1))
+    return -1;
+  const int hd = m->layers[l].hd;
+  double* dst = (which ? m->vc[l] : m->kc[l]) + ((size_t)seq * m->max_ctx + pos) * hd;
+  memcpy(dst, row, sizeof(double) * hd);
+  return 0;
+}
+
 /* ------------------------------------------------------------- the step */
 
 /* Embedding e = E[x] * sqrt(H), and the per-layer inputs pli [L, P]: the
@@ -438,6 +473,11 @@ int orc_step_ex(void* p, int seq, int x, int pos, int head, double* logits, doub
       orc_rope(kr, hd, pos, y->theta);
       linear(&y->v, m->a, m->kv);
       orc_rmsnorm(m->kv, hd, NULL, eps, vr);
+      if (m->jitter != 0.0)
+        for (int i = 0; i < hd; ++i) {
+          kr[i] *= 1.0 + m->jitter * jitter_u(m->jitter_seed, l, 0, pos, i);
+          vr[i] *= 1.0 + m->jitter * jitter_u(m->jitter_seed, l, 1, pos, i);
+        }
       if (c->kv_quant) {
         /* the cache holds codes and a scale; attention reads code * scale */
         int8_t qk[512], qv[512];

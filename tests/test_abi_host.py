@@ -41,7 +41,7 @@ def test_presets_match_workload_configs(lib, name):
     c = lib.config_preset(name).as_dict()
     want = synth.get_config(name)
     for k, v in c.items():
-        if k in ("quant", "embed_quant"):
+        if k in ("quant", "embed_quant", "kv_quant"):
             continue
         assert v == pytest.approx(want[k], rel=1e-6), k
 

@@ -36,9 +36,10 @@ def torch_dev():
     return torch, torch.device("cuda:0")
 
 
-def _engine(cfg, quant, w, max_batch, max_ctx, max_rows):
+def _engine(cfg, quant, w, max_batch, max_ctx, max_rows, kv_quant="bf16"):
     from w4a16_weight_streaming_amd import Engine
-    return Engine(cfg, quant, w, max_batch=max_batch, max_ctx=max_ctx, max_rows=max_rows)
+    return Engine(cfg, quant, w, max_batch=max_batch, max_ctx=max_ctx, max_rows=max_rows,
+                  kv_quant=kv_quant)
 
 
 class Stats:
@@ -213,15 +214,35 @@ def test_toy_greedy_parity(torch_dev, name, quant, embed_quant):
     run_greedy(torch, eng, orc, [synth.tokens(8, 1, cfg["vocab_size"])], 32, quant)
 
 
-def test_toy_batched_ragged(torch_dev):
+@pytest.mark.parametrize("name", ["toy", "toy10"])
+@pytest.mark.parametrize("quant", ["bf16", "w4a16"])
+def test_toy_int8_cache_greedy_parity(torch_dev, name, quant):
+    """The int8 K/V cache (one fp32 scale per cached row): 8-token prompt, 32
+    greedy steps across the 16-wide window, against the oracle with the same
+    cache format.  W4A16 scales U(0.002, 0.0066), the E2B range: with the
+    int8 cache the toy's U(0.002, 0.02) range turns a 1e-5 difference of a
+    cached row into logit changes near the bound in the oracle itself
+    (tests/test_workload_conditioning.py)."""
+    torch, dev = torch_dev
+    cfg = synth.get_config(name)
+    w = synth.generate(cfg, quant, seed=0, scale_lo=0.002, scale_hi=0.0066)
+    eng = _engine(cfg, quant, w, 1, 48, 8, kv_quant="int8")
+    orc = oracle.Oracle(cfg, quant, w, 1, 48, kv_quant="int8")
+    run_greedy(torch, eng, orc, [synth.tokens(8, 1, cfg["vocab_size"])], 32, quant)
+
+
+@pytest.mark.parametrize("kv_quant", ["bf16", "int8"])
+def test_toy_batched_ragged(torch_dev, kv_quant):
     """Four sequences at different positions in one batched step; a long
     context (max_ctx 2048: 64 attention chunks of 32 keys) with prefill split
-    into several passes (max_rows 16)."""
+    into several passes (max_rows 16); bf16 or int8 cache (W4A16 scales of
+    the E2B range for the int8 cache, as in the int8 greedy test)."""
     torch, dev = torch_dev
     cfg = synth.get_config("toy10")
-    w = synth.generate(cfg, "w4a16", seed=3)
-    eng = _engine(cfg, "w4a16", w, 4, 2048, 16)
-    orc = oracle.Oracle(cfg, "w4a16", w, 4, 2048)
+    sc = (0.002, 0.0066) if kv_quant == "int8" else (None, None)
+    w = synth.generate(cfg, "w4a16", seed=3, scale_lo=sc[0], scale_hi=sc[1])
+    eng = _engine(cfg, "w4a16", w, 4, 2048, 16, kv_quant=kv_quant)
+    orc = oracle.Oracle(cfg, "w4a16", w, 4, 2048, kv_quant=kv_quant)
     prompts = [synth.tokens(n, 20 + n, cfg["vocab_size"]) for n in (8, 37, 1, 70)]
     run_greedy(torch, eng, orc, prompts, 12, "w4a16")
 
@@ -316,6 +337,40 @@ def test_kv_sharing_and_cache_contents(torch_dev):
                 else:
                     tol = 2.0 ** -7 * np.abs(ref) + 2e-3 * np.max(np.abs(ref))
                 assert np.all(np.abs(got[pos] - ref) <= tol), (l, which, pos)
+    assert exact >= 0.99 * total, (exact, total)
+
+
+def test_int8_cache_contents(torch_dev):
+    """The int8 cache holds, for every cached row, the codes and the scale the
+    oracle's quantizer gives (decided in fp32 on both sides): layer 0's rows
+    depend on the token alone, so their codes agree almost everywhere (a code
+    may move by one where the kernel's row, carried at about 2^-17 relative,
+    and the oracle's fp64 one round differently at a half step) and the
+    scales to that precision."""
+    torch, dev = torch_dev
+    cfg = synth.get_config("toy10")
+    w = synth.generate(cfg, "bf16", seed=6)
+    eng = _engine(cfg, "bf16", w, 1, 32, 16, kv_quant="int8")
+    orc = oracle.Oracle(cfg, "bf16", w, 1, 32, kv_quant="int8")
+    p = synth.tokens(12, 2, cfg["vocab_size"])
+    a = torch.zeros(1, dtype=torch.int32, device=dev)
+    eng.prefill(0, torch.from_numpy(p).to(dev), 0, a)
+    eng.check()
+    orc.prefill(0, p)
+    hd = synth.layer_head_dim(cfg, 0)
+    exact = total = 0
+    for which in (0, 1):
+        codes = eng.kv_tensor(0, which, hd)[0, :12].cpu().numpy().astype(np.int64)
+        sc = eng.kv_scales(0, which)[0, :12].cpu().numpy().astype(np.float64)
+        for pos in range(12):
+            ref = orc.kv_row(0, which, 0, pos, hd)              # code * scale, exact in fp64
+            rs = np.float32(np.max(np.abs(ref)) / 127.0)        # the oracle's scale (fp32 grid)
+            assert abs(sc[pos] - rs) <= 1e-4 * rs, (which, pos, sc[pos], rs)
+            rc = np.rint(ref / float(rs)).astype(np.int64)
+            assert np.all(np.abs(codes[pos] - rc) <= 1), (which, pos)
+            assert np.max(np.abs(codes[pos])) == 127
+            exact += int(np.sum(codes[pos] == rc))
+            total += hd
     assert exact >= 0.99 * total, (exact, total)
 
 
@@ -575,6 +630,47 @@ def _graph_decode_vs_oracle(torch, eng, orc, cfg, quant, T_of, rows, steps, seed
                 st.add(got_l[b], int(got_t[b]), ref, f"step {i} row {b} (position {T_of[b] + i})")
         g.close()
     st.finish(f"{quant} B={B} from seeded caches")
+
+
+def test_e2b_w4a16_int8_cache_parity(torch_dev):
+    """E2B shape, W4A16 weights with the int8 K/V cache: a 128-token prompt
+    through one 128-row prefill pass (K/V written by the prefill kernel), then
+    96 greedy steps of the captured decode graph (K/V written by the attention
+    kernel), every step's logits against the oracle with the same cache."""
+    torch, dev = torch_dev
+    cfg = synth.get_config("e2b")
+    w = synth.generate(cfg, "w4a16", seed=0)
+    V, P, S = cfg["vocab_size"], 128, 96
+    eng = _engine(cfg, "w4a16", w, 1, P + S + 8, 128, kv_quant="int8")
+    prompt = synth.tokens(P, 1, V)
+    s = torch.cuda.Stream(dev)
+    gl, fed, gt = np.empty((S, V), np.float32), [], []
+    with torch.cuda.stream(s):
+        a = torch.zeros(1, dtype=torch.int32, device=dev)
+        l1 = torch.zeros(1, V, dtype=torch.float32, device=dev)
+        eng.prefill(0, torch.from_numpy(prompt).to(dev), 0, a, l1)
+        eng.check()
+        pre_l, pre_t = l1.cpu().numpy()[0], int(a.item())
+        tok, pos = a.clone(), torch.tensor([P], dtype=torch.int32, device=dev)
+        lg = torch.zeros(1, V, dtype=torch.float32, device=dev)
+        g = eng.capture(tok, pos, tok, lg, advance=True)
+        for i in range(S):
+            fed.append(int(tok.item()))
+            g.replay()
+            s.synchronize()
+            gl[i] = lg.cpu().numpy()[0]
+            gt.append(int(tok.item()))
+        eng.check()
+        g.close()
+    orc = oracle.Oracle(cfg, "w4a16", w, 1, P + S + 1, kv_quant="int8")
+    st = Stats("w4a16")
+    _, ref = orc.prefill(0, prompt)
+    st.add(pre_l, pre_t, ref, "prefill (last row)")
+    for i in range(S):
+        _, ref, _ = orc.step(0, fed[i], P + i)
+        st.add(gl[i], gt[i], ref, f"step {i} (position {P + i})")
+    orc.close()
+    st.finish(f"e2b w4a16 int8 cache B=1, {P}-token prompt + {S} steps", min_agree=0.99)
 
 
 @pytest.mark.parametrize("B", [1, 8])

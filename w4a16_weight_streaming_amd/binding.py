@@ -20,6 +20,7 @@ E2B_OK, E2B_EINVAL, E2B_ERANGE, E2B_ENOMEM, E2B_EHIP, E2B_EDEVICE, E2B_ESTATE = 
 KINDS = {"qkv": 1, "o": 2, "gate_up": 3, "down": 4, "ple_gate": 5, "ple_proj": 6, "ple_model": 7,
          "lm_head": 8, "attn": 9}
 QUANT = {"bf16": 0, "w4a16": 1}
+KVQ = {"bf16": 0, "int8": 1}
 DTYPE_BF16, DTYPE_INT32 = 0, 1
 
 
@@ -34,7 +35,8 @@ class Config(ctypes.Structure):
         "num_hidden_layers", "num_kv_shared_layers", "hidden_size", "num_attention_heads",
         "num_key_value_heads", "head_dim", "global_head_dim", "sliding_window",
         "layer_pattern_period", "intermediate_size", "use_double_wide_mlp",
-        "hidden_size_per_layer_input", "vocab_size", "quant", "embed_quant", "group_size")] + \
+        "hidden_size_per_layer_input", "vocab_size", "quant", "embed_quant", "kv_quant",
+        "group_size")] + \
         [(n, ctypes.c_float) for n in ("rms_eps", "rope_theta_sliding", "rope_theta_full")]
 
     def as_dict(self) -> dict:
@@ -111,21 +113,25 @@ def _check(rc: int):
         raise E2BError(rc, load_library().e2b_last_error().decode())
 
 
-def config_preset(name: str, quant: str = "bf16", embed_quant: str = "bf16") -> Config:
+def config_preset(name: str, quant: str = "bf16", embed_quant: str = "bf16",
+                  kv_quant: str = "bf16") -> Config:
     c = Config()
     _check(load_library().e2b_config_preset(name.encode(), ctypes.byref(c)))
     c.quant = QUANT[quant]
     c.embed_quant = QUANT[embed_quant]
+    c.kv_quant = KVQ[kv_quant]
     return c
 
 
-def config_from_dict(d: dict, quant: str, embed_quant: str = "bf16") -> Config:
+def config_from_dict(d: dict, quant: str, embed_quant: str = "bf16", kv_quant: str = "bf16") -> Config:
     c = Config()
     for n, _ in Config._fields_:
         if n == "quant":
             c.quant = QUANT[quant]
         elif n == "embed_quant":
             c.embed_quant = QUANT[embed_quant]
+        elif n == "kv_quant":
+            c.kv_quant = KVQ[kv_quant]
         else:
             setattr(c, n, d[n])
     return c
@@ -224,7 +230,8 @@ class Engine:
     """
 
     def __init__(self, cfg, quant: str, tensors: Dict[str, np.ndarray], max_batch: int,
-                 max_ctx: int, max_rows: Optional[int] = None, device: str = "cuda:0"):
+                 max_ctx: int, max_rows: Optional[int] = None, device: str = "cuda:0",
+                 kv_quant: str = "bf16"):
         import torch
         self.torch = torch
         if not torch.cuda.is_available():
@@ -235,8 +242,9 @@ class Engine:
             raise E2BError(E2B_ESTATE, f"device is {arch}; libe2b is built for gfx950 only")
         # the vocabulary tables' format follows the tensors given
         eq = "w4a16" if "model.embed_tokens.weight_packed" in tensors else "bf16"
-        c = config_preset(cfg, quant, eq) if isinstance(cfg, str) else config_from_dict(cfg, quant, eq)
-        self.embed_quant = eq
+        c = (config_preset(cfg, quant, eq, kv_quant) if isinstance(cfg, str)
+             else config_from_dict(cfg, quant, eq, kv_quant))
+        self.embed_quant, self.kv_quant = eq, kv_quant
         self.model = Model(c)
         self.cfg = c
         self.quant = quant
@@ -302,12 +310,23 @@ class Engine:
         return out.value or 0
 
     def kv_tensor(self, layer: int, which: int, hd: int):
-        """The K or V region layer `layer` reads, as a bf16-bits int16 view
-        [max_batch, max_ctx, hd] of the K/V buffer (no copy)."""
+        """The K or V region layer `layer` reads, as a view [max_batch, max_ctx,
+        hd] of the K/V buffer (no copy): bf16 bits (int16), or int8 codes."""
         addr = self.kv_view(layer, which)
         off = addr - self.kv.data_ptr()
         n = self.max_batch * self.max_ctx * hd
+        if self.kv_quant == "int8":
+            return self.kv[off:off + n].view(self.torch.int8).view(self.max_batch, self.max_ctx, hd)
         return self.kv[off:off + 2 * n].view(self.torch.int16).view(self.max_batch, self.max_ctx, hd)
+
+    def kv_scales(self, layer: int, which: int):
+        """int8 cache: the K (0) or V (1) row scales layer `layer` reads, float32
+        view [max_batch, max_ctx]."""
+        assert self.kv_quant == "int8"
+        addr = self.kv_view(layer, 2 + which)
+        off = addr - self.kv.data_ptr()
+        n = self.max_batch * self.max_ctx
+        return self.kv[off:off + 4 * n].view(self.torch.float32).view(self.max_batch, self.max_ctx)
 
     def capture(self, tokens, positions, argmax_out, logits_out=None, advance: bool = True):
         """Capture one decode step (+ positions += 1) as a graph on the current

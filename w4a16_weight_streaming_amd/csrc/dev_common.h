@@ -613,11 +613,14 @@ __device__ __forceinline__ void head_vec(const float* raw, int nparts, size_t ps
   head_finish<HD>(y, hs, gain != nullptr, rope, lane, eps);
 }
 
-// One wave's K/V rows for a group of 4 keys, kept packed (bf16) until used.
-template <int DPL>
+// One wave's K/V rows for a group of 4 keys, kept packed until used: bf16
+// (KQ = 0), or int8 codes with each key's row scale (KQ = 1).
+template <int DPL, int KQ = 0>
 struct KvGroup {
-  static constexpr int W = DPL >= 2 ? DPL / 2 : 1;  // 32-bit words per lane per row
+  // 32-bit words per lane per row
+  static constexpr int W = KQ ? (DPL >= 4 ? DPL / 4 : 1) : (DPL >= 2 ? DPL / 2 : 1);
   uint32_t k[4][W], v[4][W];
+  float ks[4], vs[4];  // int8: the keys' row scales
 };
 
 template <int DPL>
@@ -645,6 +648,58 @@ __device__ __forceinline__ void unpack(const uint32_t (&w)[KvGroup<DPL>::W], flo
   }
 }
 
+// int8 rows: a lane's DPL codes (DPL bytes)
+template <int DPL>
+__device__ __forceinline__ void load_codes(const int8_t* p, uint32_t (&w)[KvGroup<DPL, 1>::W]) {
+  if constexpr (DPL == 8) {
+    const uint2 u = *reinterpret_cast<const uint2*>(p);
+    w[0] = u.x; w[1] = u.y;
+  } else if constexpr (DPL == 4) {
+    w[0] = *reinterpret_cast<const uint32_t*>(p);
+  } else if constexpr (DPL == 2) {
+    w[0] = *reinterpret_cast<const uint16_t*>(p);
+  } else {
+    w[0] = *reinterpret_cast<const uint8_t*>(p);
+  }
+}
+
+// code * row scale, as fp32 (one rounding)
+template <int DPL>
+__device__ __forceinline__ void unpack_i8(const uint32_t (&w)[KvGroup<DPL, 1>::W], float s, float (&out)[DPL]) {
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) out[i] = (float)(int8_t)((w[i / 4] >> (8 * (i % 4))) & 0xFFu) * s;
+}
+
+// One cached row held by a wave (lane l: values l*DPL ..) stored as int8:
+// scale s = max |y| / 127, code = nearest-even(y / s) (0 for a row of
+// zeros), decided in fp32; deq receives code * s, what a read of the cache
+// gives back.  The whole wave must be active.
+template <int DPL>
+__device__ __forceinline__ void store_int8_row(const float (&y)[DPL], int8_t* codes, float* scale, int lane,
+                                               float (&deq)[DPL]) {
+  float am = 0.f;
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) am = fmaxf(am, fabsf(y[i]));
+  am = wave_max(am);
+  const float s = am / 127.0f;
+  uint32_t w[KvGroup<DPL, 1>::W];
+#pragma unroll
+  for (int j = 0; j < KvGroup<DPL, 1>::W; ++j) w[j] = 0u;
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) {
+    float c = s > 0.f ? rintf(y[i] / s) : 0.f;
+    c = fminf(fmaxf(c, -127.f), 127.f);
+    w[i / 4] |= ((uint32_t)(int)c & 0xFFu) << (8 * (i % 4));
+    deq[i] = c * s;
+  }
+  int8_t* dst = codes + lane * DPL;
+  if constexpr (DPL == 8) *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
+  else if constexpr (DPL == 4) *reinterpret_cast<uint32_t*>(dst) = w[0];
+  else if constexpr (DPL == 2) *reinterpret_cast<uint16_t*>(dst) = (uint16_t)w[0];
+  else *reinterpret_cast<uint8_t*>(dst) = (uint8_t)w[0];
+  if (lane == 0) *scale = s;
+}
+
 // Block (chunk c, row r): the keys j0..j1-1 of chunk c of the row's window,
 // all query heads against the single K/V head.  The block normalises and
 // rotates the row's queries itself (q_norm with gain, rotate-half RoPE at the
@@ -666,11 +721,11 @@ __device__ __forceinline__ void unpack(const uint32_t (&w)[KvGroup<DPL>::W], flo
 // k_attn_combine merges them.  (Merging in the row's last block instead needs
 // a device-scope fence per block, which writes back the L2 and costs more
 // than the extra launch.)
-template <int HD>
+template <int HD, int KQ>
 __device__ void attn_chunk(const Rows& R, const AttnArgs& a, int c, int r) {
   constexpr int DPL = HD / 64;
   constexpr int NH = kMaxHeads;
-  using G = KvGroup<DPL>;
+  using G = KvGroup<DPL, KQ>;
   __shared__ float qs[NH * HD];
   __shared__ float kv_own[2][HD];
   __shared__ float pw[4][32];
@@ -692,8 +747,14 @@ __device__ void attn_chunk(const Rows& R, const AttnArgs& a, int c, int r) {
 
   if (j0 < j1) {
     const bool own = a.kc_own != nullptr && j1 == pos + 1;
-    const uint16_t* kb = a.kc + (size_t)seq * R.max_ctx * HD + lane * DPL;
-    const uint16_t* vb = a.vc + (size_t)seq * R.max_ctx * HD + lane * DPL;
+    // bf16 rows, or int8 rows plus one scale per key
+    const size_t row0 = (size_t)seq * R.max_ctx;
+    const uint16_t* kb = static_cast<const uint16_t*>(a.kc) + row0 * HD + lane * DPL;
+    const uint16_t* vb = static_cast<const uint16_t*>(a.vc) + row0 * HD + lane * DPL;
+    const int8_t* kb8 = static_cast<const int8_t*>(a.kc) + row0 * HD + lane * DPL;
+    const int8_t* vb8 = static_cast<const int8_t*>(a.vc) + row0 * HD + lane * DPL;
+    const float* ksb = a.ks + (KQ ? row0 : 0);
+    const float* vsb = a.vs + (KQ ? row0 : 0);
     const int ngroups = (j1 - j0 + 3) / 4;
     // K/V rows of a group.  Keys past the chunk, and the own position (which
     // this block writes), read the zero row instead (loads are unconditional:
@@ -704,10 +765,18 @@ __device__ void attn_chunk(const Rows& R, const AttnArgs& a, int c, int r) {
       for (int k = 0; k < 4; ++k) {
         const int key = j0 + 4 * gi + k;
         const bool ok = gi < ngroups && key < j1 && !(own && key == pos);
-        const uint16_t* kr = ok ? kb + (size_t)key * HD : kZeroRow + lane * DPL;
-        const uint16_t* vr = ok ? vb + (size_t)key * HD : kZeroRow + lane * DPL;
-        load_packed<DPL>(kr, g.k[k]);
-        load_packed<DPL>(vr, g.v[k]);
+        if constexpr (KQ) {
+          const int8_t* z = reinterpret_cast<const int8_t*>(kZeroRow) + lane * DPL;
+          load_codes<DPL>(ok ? kb8 + (size_t)key * HD : z, g.k[k]);
+          load_codes<DPL>(ok ? vb8 + (size_t)key * HD : z, g.v[k]);
+          g.ks[k] = *(ok ? ksb + key : zero_f());
+          g.vs[k] = *(ok ? vsb + key : zero_f());
+        } else {
+          const uint16_t* kr = ok ? kb + (size_t)key * HD : kZeroRow + lane * DPL;
+          const uint16_t* vr = ok ? vb + (size_t)key * HD : kZeroRow + lane * DPL;
+          load_packed<DPL>(kr, g.k[k]);
+          load_packed<DPL>(vr, g.v[k]);
+        }
       }
     };
     G cur;
@@ -744,12 +813,21 @@ __device__ void attn_chunk(const Rows& R, const AttnArgs& a, int c, int r) {
     if (own_kv) {
       const bool is_v = wave == 1;
       head_finish<HD>(yk, sk, !is_v && a.gk != nullptr, !is_v, lane, a.eps);
-      uint16_t* dst = (is_v ? a.vc_own : a.kc_own) + ((size_t)seq * R.max_ctx + pos) * HD;
+      const size_t slot = (size_t)seq * R.max_ctx + pos;
+      if constexpr (KQ) {
+        float deq[DPL];
+        store_int8_row<DPL>(yk, static_cast<int8_t*>(is_v ? a.vc_own : a.kc_own) + slot * HD,
+                            (is_v ? a.vs_own : a.ks_own) + slot, lane, deq);
 #pragma unroll
-      for (int i = 0; i < DPL; ++i) {
-        const uint32_t b = f2bf(yk[i]);
-        st16(dst + lane * DPL + i, (uint16_t)b);
-        kv_own[wave][lane * DPL + i] = bf2f(b);
+        for (int i = 0; i < DPL; ++i) kv_own[wave][lane * DPL + i] = deq[i];
+      } else {
+        uint16_t* dst = static_cast<uint16_t*>(is_v ? a.vc_own : a.kc_own) + slot * HD;
+#pragma unroll
+        for (int i = 0; i < DPL; ++i) {
+          const uint32_t b = f2bf(yk[i]);
+          st16(dst + lane * DPL + i, (uint16_t)b);
+          kv_own[wave][lane * DPL + i] = bf2f(b);
+        }
       }
     }
     __syncthreads();
@@ -781,6 +859,8 @@ __device__ void attn_chunk(const Rows& R, const AttnArgs& a, int c, int r) {
         if (own && key0 + k == pos) {
 #pragma unroll
           for (int i = 0; i < DPL; ++i) x[i] = kv_own[which][lane * DPL + i];
+        } else if constexpr (KQ) {
+          unpack_i8<DPL>(which ? cur.v[k] : cur.k[k], which ? cur.vs[k] : cur.ks[k], x);
         } else {
           unpack<DPL>(which ? cur.v[k] : cur.k[k], x);
         }

@@ -127,10 +127,15 @@ struct AttnArgs {
   const float* qkv = nullptr;   // raw projections [rows][(nq + 2 * (kc_own != null)) * hd]
   const uint16_t* gq = nullptr; // q_norm gain
   const uint16_t* gk = nullptr; // k_norm gain (own K/V)
-  const uint16_t* kc = nullptr; // K cache read (the source layer's) [max_batch][max_ctx][hd]
-  const uint16_t* vc = nullptr;
-  uint16_t* kc_own = nullptr;   // decode: cache to write this position's K/V into (layer owns
-  uint16_t* vc_own = nullptr;   // K/V); null when the layer shares or the K/V are already written
+  const void* kc = nullptr;     // K cache read (the source layer's) [max_batch][max_ctx][hd],
+  const void* vc = nullptr;     // bf16, or int8 codes (kvq) with one fp32 scale per row (ks, vs)
+  const float* ks = nullptr;    // [max_batch][max_ctx] (int8)
+  const float* vs = nullptr;
+  void* kc_own = nullptr;       // decode: cache to write this position's K/V into (layer owns
+  void* vc_own = nullptr;       // K/V); null when the layer shares or the K/V are already written
+  float* ks_own = nullptr;      // (int8: the row scales)
+  float* vs_own = nullptr;
+  int kvq = 0;                  // cache format: 0 bf16, 1 int8
   float* part = nullptr;        // [rows][nq][kMaxChunks][hd + 2]
   float* out = nullptr;         // [rows][nq * hd]
   uint16_t* xh = nullptr;       // non-null: the merge writes its output as the O product's
@@ -154,8 +159,11 @@ struct QkvPostArgs {
   const uint16_t* gk = nullptr;
   const float* rope = nullptr;  // RoPE table (see AttnArgs)
   int rope_ld = 0, rope_off = 0;
-  uint16_t* kc = nullptr;       // this layer's cache when it owns K/V, else null
-  uint16_t* vc = nullptr;
+  void* kc = nullptr;           // this layer's cache when it owns K/V, else null (bf16 or int8)
+  void* vc = nullptr;
+  float* ks = nullptr;          // int8: the row scales
+  float* vs = nullptr;
+  int kvq = 0;                  // cache format: 0 bf16, 1 int8
   int nq = 0, hd = 0;
   int qkv_parts = 1;
   size_t qkv_pstride = 0;

@@ -78,6 +78,7 @@ struct e2b_model {
   e2b_config c{};
   int L = 0, H = 0, P = 0, V = 0, nq = 0, first = 0, quant = 0;
   int equant = 0;  // format of the two vocabulary tables (E2B_QUANT_*)
+  int kv_quant = 0;  // format of the K/V cache (E2B_KV_*)
   std::vector<LayerInfo> li;
   // arena plan
   std::vector<Copy> plan;
@@ -99,7 +100,9 @@ struct e2b_model {
   // K/V binding
   char* kv = nullptr;
   int max_batch = 0, max_ctx = 0;
-  std::vector<uint16_t*> kc, vc;
+  int kvq = 0;                // cache format: E2B_KV_BF16 / E2B_KV_INT8
+  std::vector<char*> kc, vc;  // per layer: the K / V rows it reads (its source's)
+  std::vector<float*> ks, vs; // int8: the row scales
   // per-kernel timing
   int prof_kind = 0;
   struct Mark {
@@ -507,6 +510,9 @@ int run_rows(e2b_model* m, const e2b::Rows& R, bool head, int head_row, float* d
       a.rope_off = y.full ? m->c.head_dim : 0;
       a.kc = m->kc[l];
       a.vc = m->vc[l];
+      a.ks = m->ks[l];
+      a.vs = m->vs[l];
+      a.kvq = m->kv_quant;
       a.nq = m->nq;
       a.hd = y.hd;
       a.qkv_parts = nd_qkv;
@@ -524,8 +530,13 @@ int run_rows(e2b_model* m, const e2b::Rows& R, bool head, int head_row, float* d
       a.rope_off = y.full ? m->c.head_dim : 0;
       a.kc = m->kc[y.src];
       a.vc = m->vc[y.src];
+      a.ks = m->ks[y.src];
+      a.vs = m->vs[y.src];
+      a.kvq = m->kv_quant;
       a.kc_own = (owns && fused_kv) ? m->kc[l] : nullptr;
       a.vc_own = (owns && fused_kv) ? m->vc[l] : nullptr;
+      a.ks_own = (owns && fused_kv) ? m->ks[l] : nullptr;
+      a.vs_own = (owns && fused_kv) ? m->vs[l] : nullptr;
       a.owns = owns;
       a.part = F(W.part);
       a.out = F(W.attn);
@@ -675,6 +686,7 @@ int e2b_config_preset(const char* name, e2b_config* out) {
   c.use_double_wide_mlp = 1;
   c.quant = E2B_QUANT_BF16;
   c.embed_quant = E2B_QUANT_BF16;
+  c.kv_quant = E2B_KV_BF16;
   c.group_size = 32;
   c.rms_eps = 1e-6f;
   c.rope_theta_sliding = 1.0e4f;
@@ -733,6 +745,8 @@ int e2b_create(const e2b_config* cfg, e2b_model** out) {
     return fail(E2B_EINVAL, "unknown quant mode %d", c.quant);
   if (c.embed_quant != E2B_QUANT_BF16 && c.embed_quant != E2B_QUANT_W4A16)
     return fail(E2B_EINVAL, "unknown vocabulary-table format %d", c.embed_quant);
+  if (c.kv_quant != E2B_KV_BF16 && c.kv_quant != E2B_KV_INT8)
+    return fail(E2B_EINVAL, "unknown K/V cache format %d", c.kv_quant);
   if (c.embed_quant == E2B_QUANT_W4A16 &&
       (c.hidden_size % 32 || (c.num_hidden_layers * c.hidden_size_per_layer_input) % 32))
     return fail(E2B_EINVAL, "int4 vocabulary tables need rows in whole 32-groups");
@@ -748,6 +762,7 @@ int e2b_create(const e2b_config* cfg, e2b_model** out) {
   m->first = c.num_hidden_layers - c.num_kv_shared_layers;
   m->quant = c.quant;
   m->equant = c.embed_quant;
+  m->kv_quant = c.kv_quant;
   m->li.resize(m->L);
   for (int l = 0; l < m->L; ++l) {
     LayerInfo& y = m->li[l];
@@ -790,9 +805,15 @@ size_t e2b_arena_bytes(const e2b_model* m) { return m ? m->arena_bytes : 0; }
 
 size_t e2b_kv_bytes(const e2b_model* m, int max_batch, int max_ctx) {
   if (!m || max_batch < 1 || max_ctx < 1) return 0;
+  const size_t rows = (size_t)max_batch * max_ctx;
   size_t b = 0;
-  for (int l = 0; l < m->L; ++l)
-    if (m->li[l].src == l) b += 2ull * max_batch * max_ctx * m->li[l].hd * sizeof(uint16_t);
+  for (int l = 0; l < m->L; ++l) {
+    if (m->li[l].src != l) continue;
+    if (m->kv_quant == E2B_KV_INT8)  // int8 codes, then one fp32 scale per row, for K and V
+      b += 2 * (rows * m->li[l].hd + align_up(rows * sizeof(float)));
+    else
+      b += 2 * rows * m->li[l].hd * sizeof(uint16_t);
+  }
   return b;
 }
 
@@ -910,18 +931,32 @@ int e2b_kv_alloc(e2b_model* m, void* d_kv, size_t bytes, int max_batch, int max_
   m->max_ctx = max_ctx;
   m->kc.assign(m->L, nullptr);
   m->vc.assign(m->L, nullptr);
+  m->ks.assign(m->L, nullptr);
+  m->vs.assign(m->L, nullptr);
+  const bool i8 = m->kv_quant == E2B_KV_INT8;
+  const size_t rows = (size_t)max_batch * max_ctx;
   size_t off = 0;
   for (int l = 0; l < m->L; ++l) {
     if (m->li[l].src != l) continue;
-    const size_t one = (size_t)max_batch * max_ctx * m->li[l].hd * sizeof(uint16_t);
-    m->kc[l] = reinterpret_cast<uint16_t*>(m->kv + off);
-    m->vc[l] = reinterpret_cast<uint16_t*>(m->kv + off + one);
+    // K rows, V rows (bf16, or int8 codes), then for int8 the K and V row scales
+    const size_t one = rows * m->li[l].hd * (i8 ? 1 : sizeof(uint16_t));
+    m->kc[l] = m->kv + off;
+    m->vc[l] = m->kv + off + one;
     off += 2 * one;
+    if (i8) {
+      const size_t sb = align_up(rows * sizeof(float));
+      m->ks[l] = reinterpret_cast<float*>(m->kv + off);
+      m->vs[l] = reinterpret_cast<float*>(m->kv + off + sb);
+      off += 2 * sb;
+    }
   }
   for (int l = 0; l < m->L; ++l)  // sharing layers read their source's region
     if (m->li[l].src != l) {
-      m->kc[l] = m->kc[m->li[l].src];
-      m->vc[l] = m->vc[m->li[l].src];
+      const int s = m->li[l].src;
+      m->kc[l] = m->kc[s];
+      m->vc[l] = m->vc[s];
+      m->ks[l] = m->ks[s];
+      m->vs[l] = m->vs[s];
     }
   return E2B_OK;
 }
@@ -1009,10 +1044,12 @@ int e2b_prefill(e2b_model* m, int seq, const int32_t* d_tokens, int n_tokens, in
 int e2b_kv_view(const e2b_model* m, int layer, int which, void** out) {
   if (!m || !out) return fail(E2B_EINVAL, "null argument");
   if (!m->kv) return fail(E2B_ESTATE, "kv cache not bound");
-  if (layer < 0 || layer >= m->L || (which != 0 && which != 1))
+  const int nwhich = m->kv_quant == E2B_KV_INT8 ? 4 : 2;
+  if (layer < 0 || layer >= m->L || which < 0 || which >= nwhich)
     return fail(E2B_EINVAL, "bad layer %d / which %d", layer, which);
   const int s = m->li[layer].src;
-  *out = which ? static_cast<void*>(m->vc[s]) : static_cast<void*>(m->kc[s]);
+  void* v[4] = {m->kc[s], m->vc[s], m->ks[s], m->vs[s]};
+  *out = v[which];
   return E2B_OK;
 }
 

@@ -455,9 +455,9 @@ hipError_t launch_gemv(int quant, int tag, const Lin& W, int rows, const Prologu
 // K/V is written before attention: block per row, wave 0 the key (norm with
 // gain + RoPE), wave 1 the value (norm), bf16 at slot = position.
 // ------------------------------------------------------------ decode attention
-template <int HD>
+template <int HD, int KQ>
 __global__ __launch_bounds__(256) void k_attn_dec(Rows R, AttnArgs a) {
-  attn_chunk<HD>(R, a, blockIdx.x, blockIdx.y);
+  attn_chunk<HD, KQ>(R, a, blockIdx.x, blockIdx.y);
 }
 
 __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a) {
@@ -467,7 +467,7 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a) {
 // Prefill: K/V of every row written before attention.  Block per row, wave 0
 // the key (norm with gain + RoPE), wave 1 the value (norm), bf16 at slot =
 // position (the same arithmetic as the decode path's own-K/V write).
-template <int HD>
+template <int HD, int KQ>
 __global__ __launch_bounds__(128) void k_kv_write(Rows R, QkvPostArgs a) {
   constexpr int DPL = HD / 64;
   const int r = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -479,18 +479,43 @@ __global__ __launch_bounds__(128) void k_kv_write(Rows R, QkvPostArgs a) {
   const bool is_v = wave == 1;
   float y[DPL];
   head_vec<HD>(raw, a.qkv_parts, a.qkv_pstride, is_v ? nullptr : a.gk, !is_v, cs, sn, lane, a.eps, y);
-  uint16_t* dst = (is_v ? a.vc : a.kc) + ((size_t)seq * R.max_ctx + pos) * HD;
+  const size_t slot = (size_t)seq * R.max_ctx + pos;
+  if constexpr (KQ) {
+    float deq[DPL];
+    store_int8_row<DPL>(y, static_cast<int8_t*>(is_v ? a.vc : a.kc) + slot * HD, (is_v ? a.vs : a.ks) + slot,
+                        lane, deq);
+  } else {
+    uint16_t* dst = static_cast<uint16_t*>(is_v ? a.vc : a.kc) + slot * HD;
 #pragma unroll
-  for (int i = 0; i < DPL; ++i) dst[lane * DPL + i] = (uint16_t)f2bf(y[i]);
+    for (int i = 0; i < DPL; ++i) dst[lane * DPL + i] = (uint16_t)f2bf(y[i]);
+  }
+}
+
+template <int KQ>
+static hipError_t kv_write_q(const Rows& R, const QkvPostArgs& a, hipStream_t st) {
+  switch (a.hd) {
+    case 64: hipLaunchKernelGGL((k_kv_write<64, KQ>), dim3(R.n), dim3(128), 0, st, R, a); break;
+    case 128: hipLaunchKernelGGL((k_kv_write<128, KQ>), dim3(R.n), dim3(128), 0, st, R, a); break;
+    case 256: hipLaunchKernelGGL((k_kv_write<256, KQ>), dim3(R.n), dim3(128), 0, st, R, a); break;
+    case 512: hipLaunchKernelGGL((k_kv_write<512, KQ>), dim3(R.n), dim3(128), 0, st, R, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_qkv_post(const Rows& R, const QkvPostArgs& a, hipStream_t st) {
-  if (!a.kc || !a.vc || !a.rope) return hipErrorInvalidValue;
+  if (!a.kc || !a.vc || !a.rope || (a.kvq && (!a.ks || !a.vs))) return hipErrorInvalidValue;
+  return a.kvq ? kv_write_q<1>(R, a, st) : kv_write_q<0>(R, a, st);
+}
+
+template <int KQ>
+static hipError_t attn_q(const Rows& R, const AttnArgs& a, hipStream_t st) {
+  dim3 grid(a.nchunk, R.n);
   switch (a.hd) {
-    case 64: hipLaunchKernelGGL(k_kv_write<64>, dim3(R.n), dim3(128), 0, st, R, a); break;
-    case 128: hipLaunchKernelGGL(k_kv_write<128>, dim3(R.n), dim3(128), 0, st, R, a); break;
-    case 256: hipLaunchKernelGGL(k_kv_write<256>, dim3(R.n), dim3(128), 0, st, R, a); break;
-    case 512: hipLaunchKernelGGL(k_kv_write<512>, dim3(R.n), dim3(128), 0, st, R, a); break;
+    case 64: E2B_TIMED_LAUNCH((k_attn_dec<64, KQ>), grid, dim3(256), 0, st, R, a); break;
+    case 128: E2B_TIMED_LAUNCH((k_attn_dec<128, KQ>), grid, dim3(256), 0, st, R, a); break;
+    case 256: E2B_TIMED_LAUNCH((k_attn_dec<256, KQ>), grid, dim3(256), 0, st, R, a); break;
+    case 512: E2B_TIMED_LAUNCH((k_attn_dec<512, KQ>), grid, dim3(256), 0, st, R, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -499,15 +524,8 @@ hipError_t launch_qkv_post(const Rows& R, const QkvPostArgs& a, hipStream_t st) 
 hipError_t launch_attention(const Rows& R, const AttnArgs& a, hipStream_t st) {
   if (a.nq > kMaxHeads || a.nchunk > kMaxChunks || a.nchunk < 1 || a.chunk < 1 || !a.rope)
     return hipErrorInvalidValue;
-  dim3 grid(a.nchunk, R.n);
-  switch (a.hd) {
-    case 64: E2B_TIMED_LAUNCH(k_attn_dec<64>, grid, dim3(256), 0, st, R, a); break;
-    case 128: E2B_TIMED_LAUNCH(k_attn_dec<128>, grid, dim3(256), 0, st, R, a); break;
-    case 256: E2B_TIMED_LAUNCH(k_attn_dec<256>, grid, dim3(256), 0, st, R, a); break;
-    case 512: E2B_TIMED_LAUNCH(k_attn_dec<512>, grid, dim3(256), 0, st, R, a); break;
-    default: return hipErrorInvalidValue;
-  }
-  hipError_t e = hipGetLastError();
+  if (a.kvq && (!a.ks || !a.vs || (a.kc_own && (!a.ks_own || !a.vs_own)))) return hipErrorInvalidValue;
+  hipError_t e = a.kvq ? attn_q<1>(R, a, st) : attn_q<0>(R, a, st);
   if (e != hipSuccess || !a.combine) return e;
   hipLaunchKernelGGL(k_attn_combine, dim3(R.n, a.nq), dim3(256), 0, st, a);
   return hipGetLastError();
