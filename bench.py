@@ -419,6 +419,93 @@ def long_context(quant, B, lengths=None, steps=64, chunk=500, top=8000, kv_quant
     return rows
 
 
+def serve_uneven(quant="w4a16", n_req=32, slots=16, prompt=128, lo=16, hi=512, seed=5):
+    """Continuous batching over the paged cache against lockstep batches, on
+    requests of uneven output length (uniform in [lo, hi]), each a `prompt`-
+    token random prompt: useful tokens per second of wall time (prefills
+    included), eager decode steps in both modes.  Lockstep runs `slots`
+    requests at a time until the longest finishes (finished rows keep
+    decoding, their tokens not counted); continuous batching admits a request
+    as soon as a slot and its pages free up and moves the last live slot into
+    a finished one (no K/V copied)."""
+    import numpy as np
+    import torch
+
+    import synth
+    from w4a16_weight_streaming_amd import Engine
+
+    cfg = synth.get_config("e2b")
+    V = cfg["vocab_size"]
+    w = synth.generate(cfg, quant, seed=0)
+    rng = np.random.default_rng(seed)
+    olen = [int(x) for x in rng.integers(lo, hi + 1, size=n_req)]
+    prompts = [torch.from_numpy(synth.tokens(prompt, 200 + i, V)) for i in range(n_req)]
+    useful = sum(olen)
+    max_ctx = prompt + hi
+    per_req = (max_ctx + 127) // 128
+    out = {"requests": n_req, "slots": slots, "prompt": prompt, "output_lengths": [lo, hi],
+           "useful_tokens": useful}
+    for mode in ("lockstep", "continuous"):
+        paged = mode == "continuous"
+        eng = Engine(cfg, quant, w, max_batch=slots, max_ctx=max_ctx, max_rows=128,
+                     n_pages=slots * per_req if paged else 0)
+        dev = eng.device
+        ps = [p.to(dev) for p in prompts]
+        stream = torch.cuda.Stream(dev)
+        steps = 0
+        with torch.cuda.stream(stream):
+            torch.cuda.synchronize()
+            t0 = time.time()
+            if not paged:
+                for b0 in range(0, n_req, slots):
+                    grp = list(range(b0, min(n_req, b0 + slots)))
+                    tok = torch.zeros(len(grp), dtype=torch.int32, device=dev)
+                    for j, i in enumerate(grp):
+                        eng.prefill(j, ps[i], 0, tok[j:j + 1])
+                    pos = torch.full((len(grp),), prompt, dtype=torch.int32, device=dev)
+                    for _ in range(max(olen[i] for i in grp)):
+                        eng.decode_step(tok, pos, tok)
+                        pos.add_(1)
+                        steps += 1
+            else:
+                pending, live = list(range(n_req)), []   # live: [request, steps left]
+                tok = torch.zeros(slots, dtype=torch.int32, device=dev)
+                pos = torch.zeros(slots, dtype=torch.int32, device=dev)
+                while pending or live:
+                    while pending and len(live) < slots and eng.pages_free() >= per_req:
+                        i = pending.pop(0)
+                        b = len(live)
+                        eng.reserve(b, prompt + olen[i])
+                        eng.prefill(b, ps[i], 0, tok[b:b + 1])
+                        pos[b] = prompt
+                        live.append([i, olen[i]])
+                    B = len(live)
+                    eng.decode_step(tok[:B], pos[:B], tok[:B])
+                    pos[:B] += 1
+                    steps += 1
+                    for b in reversed(range(B)):
+                        live[b][1] -= 1
+                        if live[b][1] == 0:
+                            eng.release(b)
+                            last = len(live) - 1
+                            if b != last:
+                                eng.move(last, b)
+                                tok[b] = tok[last]
+                                pos[b] = pos[last]
+                                live[b] = live[last]
+                            live.pop()
+            torch.cuda.synchronize()
+            dt = time.time() - t0
+            eng.check()
+        out[mode] = {"seconds": round(dt, 3), "decode_steps": steps, "useful_tok_s": round(useful / dt, 1)}
+        log(f"[serve {quant}] {mode}: {useful} useful tokens in {dt:.2f} s ({steps} steps), "
+            f"{useful / dt:.0f} tok/s")
+        del eng
+        torch.cuda.empty_cache()
+    out["speedup"] = round(out["continuous"]["useful_tok_s"] / out["lockstep"]["useful_tok_s"], 3)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -493,6 +580,9 @@ def main():
                          "step_roofline": step_roofline(r, calib), "roofline": roofline_of(r, q, b, calib, eq),
                          "kernel_kinds": kinds_summary(r, 8), "prefill": r["prefill"]})
         if not args.no_long:
+            sv = serve_uneven()
+            also.append(dict(workload="serving uneven requests: continuous batching over the paged K/V cache "
+                                      "(128-position pages) vs lockstep batches, E2B W4A16", **sv))
             for b, kq in ((1, "bf16"), (8, "bf16"), (1, "int8"), (8, "int8")):
                 rows = long_context("w4a16", b, lengths=(500, 4000, 8000), kv_quant=kq)
                 also.append({"workload": f"long context, w4a16, {kq} K/V cache, batch {b}: context grown by "

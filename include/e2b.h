@@ -176,6 +176,41 @@ int e2b_load_weights(e2b_model* model, const e2b_tensor* tensors, int n, void* d
  * initialisation: a position is always written before it is read. */
 int e2b_kv_alloc(e2b_model* model, void* d_kv, size_t bytes, int max_batch, int max_ctx);
 
+/* ---- paged K/V cache ------------------------------------------------------
+ * The cache as a pool of pages of E2B_PAGE (128) positions ([P3] Step 7 and
+ * [P2] Step 3: page size 128, with which a server keeps 64 requests running
+ * where page size 1 held 8), so that sequences of uneven length share one
+ * pool and a finished sequence's pages go straight to a new one: the
+ * continuous batching that [P5] Feasibility part 2 contrasts with lockstep
+ * batches.  Every K/V-owning layer has its own pool of n_pages * 128 rows
+ * (layout as e2b_kv_alloc with max_batch * max_ctx replaced by (n_pages +
+ * 1) * 128: the pool, then the spare page); one page id covers the same 128
+ * positions in every layer.  The
+ * decode step's row b and a prefill's `seq` name a sequence slot whose row of
+ * the page table maps position p to page table[slot][p / 128], row p % 128.
+ * The library's allocator (e2b_seq_reserve / release / move) owns the table;
+ * a cached position outside the slot's reserved pages is never read or
+ * written through a stale entry: the kernels flag it on the device error
+ * word (e2b_check) and use a spare page past the pool that no sequence owns. */
+enum { E2B_PAGE = 128 };
+size_t e2b_kv_paged_bytes(const e2b_model* model, int n_pages);
+/* Bind d_kv (>= e2b_kv_paged_bytes) as a pool of n_pages pages and
+ * d_page_table (caller-owned device int32 [max_batch][ceil(max_ctx / 128)])
+ * as its page table, all entries free.  Synchronises `stream`. */
+int e2b_kv_alloc_paged(e2b_model* model, void* d_kv, size_t bytes, int n_pages, int32_t* d_page_table,
+                       int max_batch, int max_ctx, void* stream);
+/* Give slot `slot` pages for positions [0, n_positions) (it keeps the ones it
+ * has; E2B_ENOMEM, nothing changed, if the pool is short).  Synchronises. */
+int e2b_seq_reserve(e2b_model* model, int slot, int n_positions, void* stream);
+/* Return slot `slot`'s pages to the pool.  Synchronises. */
+int e2b_seq_release(e2b_model* model, int slot, void* stream);
+/* Move a sequence from slot `from` to the empty slot `to` (its page-table row;
+ * no K/V is copied), e.g. to keep a batch's live sequences in rows 0..B-1.
+ * E2B_ESTATE if `to` holds pages.  Synchronises. */
+int e2b_seq_move(e2b_model* model, int from, int to, void* stream);
+/* Pages left in the pool (0 for a contiguous cache). */
+int e2b_pages_free(const e2b_model* model);
+
 /* One greedy decode step for `batch` sequences b = 0..batch-1 (sequence b
  * uses cache slot row b): token d_tokens[b] at position d_positions[b]
  * (int32 device arrays).  The step is the decoder pass the pages define:
@@ -209,8 +244,9 @@ int e2b_prefill(e2b_model* model, int seq, const int32_t* d_tokens, int n_tokens
                 void* stream);
 
 /* Device address of the K (which 0) or V (which 1) cache region that layer
- * `layer` reads, [max_batch][max_ctx][hd] bf16 or int8, or (int8 cache) its
- * K (2) or V (3) row scales, fp32 [max_batch][max_ctx]: the layer's own region if it
+ * `layer` reads, [max_batch][max_ctx][hd] bf16 or int8 ([(n_pages + 1) * 128]
+ * [hd] for a paged cache), or (int8 cache) its K (2) or V (3) row scales,
+ * fp32 [max_batch][max_ctx] ([(n_pages + 1) * 128]): the layer's own region if it
  * owns K/V, else its source layer's region (the same address, so shared
  * layers see bit-identical K/V; [P3] Step 1, [P5] The engine).  Requires
  * e2b_kv_alloc.  E2B_EINVAL for a bad layer or which. */

@@ -169,3 +169,22 @@ def test_matvec_validation(lib):
             if slices:
                 assert K % slices == 0 and (K // slices) % 32 == 0
     assert L.e2b_matvec_workspace_bytes(2, 1536, 1536, 3) == 0   # unknown quant
+
+
+def test_paged_cache_sizes_and_state(lib):
+    """Paged pool bytes: (n_pages + 1) pages of 128 rows per K/V-owning layer
+    (the last a spare), bf16 or int8 rows; the allocator calls refuse a
+    contiguous cache."""
+    L = lib.load_library()
+    m = lib.Model(lib.config_preset("e2b"))
+    per_token = m.kv_bytes(1, 1)
+    assert L.e2b_kv_paged_bytes(m.handle, 10) == 11 * 128 * per_token
+    assert L.e2b_kv_paged_bytes(m.handle, 0) == 0
+    assert L.e2b_seq_reserve(m.handle, 0, 10, None) == lib.E2B_ESTATE
+    assert L.e2b_seq_release(m.handle, 0, None) == lib.E2B_ESTATE
+    assert L.e2b_pages_free(m.handle) == 0
+    m8 = lib.Model(lib.config_preset("e2b", kv_quant="int8"))
+    rows = 11 * 128
+    up = lambda x: (x + 255) // 256 * 256
+    want = sum(2 * (rows * hd + up(rows * 4)) for hd in [256] * 12 + [512] * 3)
+    assert L.e2b_kv_paged_bytes(m8.handle, 10) == want

@@ -374,6 +374,106 @@ def test_int8_cache_contents(torch_dev):
     assert exact >= 0.99 * total, (exact, total)
 
 
+def _continuous_batching(torch, eng, orc, V, prompts, lengths, quant, label):
+    """Serve `prompts` (request i wants lengths[i] decode steps) through the
+    paged cache with at most eng.max_batch live rows: admit a request when a
+    slot and its pages are free (reserve, prefill into its slot), decode the
+    live rows together, and on finishing release the slot's pages and move
+    the last live slot into its place.  Every live row of every step is
+    compared with the oracle's own run of that request (oracle sequence i)."""
+    dev = eng.device
+    st = Stats(quant)
+    pending = list(range(len(prompts)))
+    live = []                      # per row: [request, next token, position, steps done]
+    admitted_late = 0
+    lg = torch.zeros(eng.max_batch, V, dtype=torch.float32, device=dev)
+    steps = 0
+    while pending or live:
+        while pending and len(live) < eng.max_batch:
+            i = pending[0]
+            need = len(prompts[i]) + lengths[i]
+            if eng.pages_free() < (need + 127) // 128:
+                break
+            pending.pop(0)
+            slot = len(live)
+            eng.reserve(slot, need)
+            a = torch.zeros(1, dtype=torch.int32, device=dev)
+            l1 = torch.zeros(1, V, dtype=torch.float32, device=dev)
+            eng.prefill(slot, torch.from_numpy(prompts[i]).to(dev), 0, a, l1)
+            eng.check()
+            _, ref = orc.prefill(i, prompts[i])
+            st.add(l1.cpu().numpy()[0], int(a.item()), ref, f"request {i} prefill (slot {slot})")
+            live.append([i, int(a.item()), len(prompts[i]), 0])
+            admitted_late += int(steps > 0)
+        assert live, "no request fits the pool"
+        B = len(live)
+        tok = torch.tensor([r[1] for r in live], dtype=torch.int32, device=dev)
+        pos = torch.tensor([r[2] for r in live], dtype=torch.int32, device=dev)
+        am = torch.zeros(B, dtype=torch.int32, device=dev)
+        eng.decode_step(tok, pos, am, lg)
+        eng.check()
+        got_l, got_t = lg[:B].cpu().numpy(), am.cpu().numpy()
+        steps += 1
+        for b, r in enumerate(live):
+            _, ref, _ = orc.step(r[0], r[1], r[2])
+            st.add(got_l[b], int(got_t[b]), ref, f"request {r[0]} step {r[3]} (row {b}, position {r[2]})")
+            r[1], r[2], r[3] = int(got_t[b]), r[2] + 1, r[3] + 1
+        for b in reversed(range(len(live))):          # retire, then compact
+            i = live[b][0]
+            if live[b][3] >= lengths[i]:
+                eng.release(b)
+                last = len(live) - 1
+                if b != last:
+                    eng.move(last, b)
+                    live[b] = live[last]
+                live.pop()
+    assert eng.pages_free() == eng.n_pages
+    assert admitted_late > 0      # requests joined a running batch
+    st.finish(label)
+
+
+@pytest.mark.parametrize("kv_quant", ["bf16", "int8"])
+def test_toy_paged_continuous_batching(torch_dev, kv_quant):
+    """Paged cache (128-position pages, a pool too small for every request at
+    once), 8 requests of uneven prompt and output lengths through 4 slots;
+    positions cross page boundaries."""
+    torch, dev = torch_dev
+    cfg = synth.get_config("toy10")
+    w = synth.generate(cfg, "w4a16", seed=9, scale_lo=0.002, scale_hi=0.0066)
+    V = cfg["vocab_size"]
+    plen = [5, 140, 1, 120, 17, 64, 200, 9]
+    olen = [20, 7, 33, 12, 3, 25, 10, 40]
+    prompts = [synth.tokens(n, 60 + i, V) for i, n in enumerate(plen)]
+    from w4a16_weight_streaming_amd import Engine
+    eng_p = Engine(cfg, "w4a16", w, max_batch=4, max_ctx=256, max_rows=64, kv_quant=kv_quant, n_pages=7)
+    orc = oracle.Oracle(cfg, "w4a16", w, len(prompts), 256, kv_quant=kv_quant)
+    _continuous_batching(torch, eng_p, orc, V, prompts, olen, "w4a16", f"toy10 paged {kv_quant} cache")
+
+
+def test_paged_position_without_page_is_flagged(torch_dev):
+    """A decode row whose position lies past its slot's reserved pages is
+    flagged on the device error word (its cache row goes to the pool's spare
+    page, which no sequence owns), and a valid step afterwards passes."""
+    torch, dev = torch_dev
+    from w4a16_weight_streaming_amd import E2BError, Engine
+    cfg = synth.get_config("toy")
+    w = synth.generate(cfg, "bf16", seed=8)
+    eng = Engine(cfg, "bf16", w, max_batch=2, max_ctx=256, max_rows=8, n_pages=4)
+    eng.reserve(0, 100)                        # one page: positions 0..127
+    a = torch.zeros(1, dtype=torch.int32, device=dev)
+    eng.prefill(0, torch.from_numpy(synth.tokens(8, 1, cfg["vocab_size"])).to(dev), 0, a)
+    eng.check()
+    eng.decode_step(a.clone(), torch.tensor([130], dtype=torch.int32, device=dev), a)
+    with pytest.raises(E2BError) as e:
+        eng.check()
+    assert "reserved page" in str(e.value)
+    eng.decode_step(a.clone(), torch.tensor([8], dtype=torch.int32, device=dev), a)
+    eng.check()
+    with pytest.raises(E2BError):
+        eng.reserve(1, 5 * 128)                # more pages than are free
+    assert eng.pages_free() == 3
+
+
 def test_deterministic_replay(torch_dev):
     torch, dev = torch_dev
     cfg = synth.get_config("toy")
@@ -671,6 +771,22 @@ def test_e2b_w4a16_int8_cache_parity(torch_dev):
         st.add(gl[i], gt[i], ref, f"step {i} (position {P + i})")
     orc.close()
     st.finish(f"e2b w4a16 int8 cache B=1, {P}-token prompt + {S} steps", min_agree=0.99)
+
+
+def test_e2b_paged_continuous_batching(torch_dev):
+    """Full E2B shape (W4A16), paged cache: 5 requests (prompts 150, 40, 1,
+    130 and 20 tokens, 3-10 decode steps) through 3 slots; head dims 256/512
+    over positions that cross the 128-position page boundary."""
+    torch, dev = torch_dev
+    from w4a16_weight_streaming_amd import Engine
+    cfg = synth.get_config("e2b")
+    w = synth.generate(cfg, "w4a16", seed=0)
+    V = cfg["vocab_size"]
+    plen, olen = [150, 40, 1, 130, 20], [6, 10, 8, 3, 5]
+    prompts = [synth.tokens(n, 80 + i, V) for i, n in enumerate(plen)]
+    eng = Engine(cfg, "w4a16", w, max_batch=3, max_ctx=512, max_rows=128, n_pages=5)
+    orc = oracle.Oracle(cfg, "w4a16", w, len(prompts), 512)
+    _continuous_batching(torch, eng, orc, V, prompts, olen, "w4a16", "e2b w4a16 paged")
 
 
 @pytest.mark.parametrize("B", [1, 8])

@@ -97,11 +97,19 @@ def load_library():
     L.e2b_matvec_noalloc_max_bytes.argtypes = []
     L.e2b_matvec_noalloc.argtypes = [i32, vp, vp, i32, i32, vp, i32, vp, vp]
     L.e2b_stream_reduce.argtypes = [vp, sz, vp, vp]
+    L.e2b_kv_paged_bytes.restype = sz
+    L.e2b_kv_paged_bytes.argtypes = [vp, i32]
+    L.e2b_kv_alloc_paged.argtypes = [vp, vp, sz, i32, vp, i32, i32, vp]
+    L.e2b_seq_reserve.argtypes = [vp, i32, i32, vp]
+    L.e2b_seq_release.argtypes = [vp, i32, vp]
+    L.e2b_seq_move.argtypes = [vp, i32, i32, vp]
+    L.e2b_pages_free.argtypes = [vp]
     L.e2b_stream_reduce_blocks.argtypes = []
     for f in ("e2b_config_preset", "e2b_create", "e2b_kv_share_map", "e2b_load_weights",
               "e2b_kv_alloc", "e2b_decode_step", "e2b_prefill", "e2b_check", "e2b_kv_view",
               "e2b_matvec", "e2b_matvec_noalloc", "e2b_embed", "e2b_stream_reduce",
-              "e2b_stream_reduce_blocks", "e2b_graph_capture", "e2b_graph_replay", "e2b_profile_begin",
+              "e2b_stream_reduce_blocks", "e2b_kv_alloc_paged", "e2b_seq_reserve", "e2b_seq_release",
+              "e2b_seq_move", "e2b_pages_free", "e2b_graph_capture", "e2b_graph_replay", "e2b_profile_begin",
               "e2b_profile_read"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
@@ -231,7 +239,7 @@ class Engine:
 
     def __init__(self, cfg, quant: str, tensors: Dict[str, np.ndarray], max_batch: int,
                  max_ctx: int, max_rows: Optional[int] = None, device: str = "cuda:0",
-                 kv_quant: str = "bf16"):
+                 kv_quant: str = "bf16", n_pages: int = 0):
         import torch
         self.torch = torch
         if not torch.cuda.is_available():
@@ -257,10 +265,19 @@ class Engine:
             _check(L.e2b_load_weights(self.model.handle, table, len(tensors), self.arena.data_ptr(),
                                       self.arena.numel(), self._stream()))
             del keep
-            self.kv = torch.empty(max(self.model.kv_bytes(max_batch, max_ctx), 1),
-                                  dtype=torch.uint8, device=self.device)
-            _check(L.e2b_kv_alloc(self.model.handle, self.kv.data_ptr(), self.kv.numel(),
-                                  max_batch, max_ctx))
+            self.n_pages = n_pages
+            if n_pages:   # paged cache: a pool of n_pages pages and its page table
+                self.kv = torch.empty(max(L.e2b_kv_paged_bytes(self.model.handle, n_pages), 1),
+                                      dtype=torch.uint8, device=self.device)
+                stride = (max_ctx + 127) // 128
+                self.page_table = torch.full((max_batch, stride), -1, dtype=torch.int32, device=self.device)
+                _check(L.e2b_kv_alloc_paged(self.model.handle, self.kv.data_ptr(), self.kv.numel(), n_pages,
+                                            self.page_table.data_ptr(), max_batch, max_ctx, self._stream()))
+            else:
+                self.kv = torch.empty(max(self.model.kv_bytes(max_batch, max_ctx), 1),
+                                      dtype=torch.uint8, device=self.device)
+                _check(L.e2b_kv_alloc(self.model.handle, self.kv.data_ptr(), self.kv.numel(),
+                                      max_batch, max_ctx))
             self.ws = torch.zeros(self.model.workspace_bytes(self.max_rows), dtype=torch.uint8,
                                   device=self.device)
 
@@ -302,6 +319,19 @@ class Engine:
         _check(self.model._lib.e2b_embed(self.model.handle, tokens.data_ptr(), n, h_out.data_ptr(),
                                          tokple_out.data_ptr(), self.ws.data_ptr(), self.ws.numel(),
                                          self._stream()))
+
+    # ---- paged cache: the library's page allocator
+    def reserve(self, slot: int, n_positions: int):
+        _check(self.model._lib.e2b_seq_reserve(self.model.handle, slot, n_positions, self._stream()))
+
+    def release(self, slot: int):
+        _check(self.model._lib.e2b_seq_release(self.model.handle, slot, self._stream()))
+
+    def move(self, src: int, dst: int):
+        _check(self.model._lib.e2b_seq_move(self.model.handle, src, dst, self._stream()))
+
+    def pages_free(self) -> int:
+        return self.model._lib.e2b_pages_free(self.model.handle)
 
     def kv_view(self, layer: int, which: int) -> int:
         """Device address of the K (0) / V (1) region layer `layer` reads."""

@@ -174,6 +174,19 @@ __device__ __forceinline__ int clamp_pos(const Rows& R, int p) {
 }
 __device__ __forceinline__ int row_seq(const Rows& R, int r) { return R.seq0 + r * R.seq_stride; }
 
+// Cache row of (sequence slot, position): contiguous, or through the page
+// table.  A page entry outside the pool flags the error word and maps to the
+// pool's spare page (index n_pages), which no sequence owns.
+__device__ __forceinline__ size_t cache_row(const Rows& R, int seq, int pos) {
+  if (!R.pages) return (size_t)seq * R.max_ctx + pos;
+  int pg = R.pages[(size_t)seq * R.page_stride + (pos >> kPageShift)];
+  if ((unsigned)pg >= (unsigned)R.n_pages) {
+    if (R.err) atomicOr(R.err, kErrPage);
+    pg = R.n_pages;
+  }
+  return (size_t)pg * kPageSize + (pos & (kPageSize - 1));
+}
+
 // eight consecutive fp32 values (16-byte aligned)
 __device__ __forceinline__ void ld8(const float* p, float (&v)[8]) {
   const float4 a = *reinterpret_cast<const float4*>(p);
@@ -747,14 +760,11 @@ __device__ void attn_chunk(const Rows& R, const AttnArgs& a, int c, int r) {
 
   if (j0 < j1) {
     const bool own = a.kc_own != nullptr && j1 == pos + 1;
-    // bf16 rows, or int8 rows plus one scale per key
-    const size_t row0 = (size_t)seq * R.max_ctx;
-    const uint16_t* kb = static_cast<const uint16_t*>(a.kc) + row0 * HD + lane * DPL;
-    const uint16_t* vb = static_cast<const uint16_t*>(a.vc) + row0 * HD + lane * DPL;
-    const int8_t* kb8 = static_cast<const int8_t*>(a.kc) + row0 * HD + lane * DPL;
-    const int8_t* vb8 = static_cast<const int8_t*>(a.vc) + row0 * HD + lane * DPL;
-    const float* ksb = a.ks + (KQ ? row0 : 0);
-    const float* vsb = a.vs + (KQ ? row0 : 0);
+    // bf16 rows, or int8 rows plus one scale per key; row of a key: cache_row
+    const uint16_t* kb = static_cast<const uint16_t*>(a.kc) + lane * DPL;
+    const uint16_t* vb = static_cast<const uint16_t*>(a.vc) + lane * DPL;
+    const int8_t* kb8 = static_cast<const int8_t*>(a.kc) + lane * DPL;
+    const int8_t* vb8 = static_cast<const int8_t*>(a.vc) + lane * DPL;
     const int ngroups = (j1 - j0 + 3) / 4;
     // K/V rows of a group.  Keys past the chunk, and the own position (which
     // this block writes), read the zero row instead (loads are unconditional:
@@ -765,15 +775,16 @@ __device__ void attn_chunk(const Rows& R, const AttnArgs& a, int c, int r) {
       for (int k = 0; k < 4; ++k) {
         const int key = j0 + 4 * gi + k;
         const bool ok = gi < ngroups && key < j1 && !(own && key == pos);
+        const size_t row = cache_row(R, seq, ok ? key : lo);
         if constexpr (KQ) {
           const int8_t* z = reinterpret_cast<const int8_t*>(kZeroRow) + lane * DPL;
-          load_codes<DPL>(ok ? kb8 + (size_t)key * HD : z, g.k[k]);
-          load_codes<DPL>(ok ? vb8 + (size_t)key * HD : z, g.v[k]);
-          g.ks[k] = *(ok ? ksb + key : zero_f());
-          g.vs[k] = *(ok ? vsb + key : zero_f());
+          load_codes<DPL>(ok ? kb8 + row * HD : z, g.k[k]);
+          load_codes<DPL>(ok ? vb8 + row * HD : z, g.v[k]);
+          g.ks[k] = *(ok ? a.ks + row : zero_f());
+          g.vs[k] = *(ok ? a.vs + row : zero_f());
         } else {
-          const uint16_t* kr = ok ? kb + (size_t)key * HD : kZeroRow + lane * DPL;
-          const uint16_t* vr = ok ? vb + (size_t)key * HD : kZeroRow + lane * DPL;
+          const uint16_t* kr = ok ? kb + row * HD : kZeroRow + lane * DPL;
+          const uint16_t* vr = ok ? vb + row * HD : kZeroRow + lane * DPL;
           load_packed<DPL>(kr, g.k[k]);
           load_packed<DPL>(vr, g.v[k]);
         }
@@ -813,7 +824,7 @@ __device__ void attn_chunk(const Rows& R, const AttnArgs& a, int c, int r) {
     if (own_kv) {
       const bool is_v = wave == 1;
       head_finish<HD>(yk, sk, !is_v && a.gk != nullptr, !is_v, lane, a.eps);
-      const size_t slot = (size_t)seq * R.max_ctx + pos;
+      const size_t slot = cache_row(R, seq, pos);
       if constexpr (KQ) {
         float deq[DPL];
         store_int8_row<DPL>(yk, static_cast<int8_t*>(is_v ? a.vc_own : a.kc_own) + slot * HD,

@@ -13,6 +13,8 @@ constexpr int kMaxGemmSplit = 16;  // K slices of one batched (matrix-core) prod
 constexpr int kGemvThreads = 256;
 constexpr int kLmBlocks = 1024;  // blocks of the lm_head pass (argmax candidates)
 constexpr int kStreamBlocks = 1024;  // blocks of the streaming-read calibration
+constexpr int kPageShift = 7;        // paged K/V cache: 128 positions per page
+constexpr int kPageSize = 1 << kPageShift;
 
 // Matrix kinds; each gets its own kernel symbol so profiles tell them apart.
 enum : int {
@@ -22,7 +24,7 @@ enum : int {
 };
 
 // Device error word bits (first 16 bytes of the workspace).
-enum : int { kErrToken = 1, kErrPos = 2 };
+enum : int { kErrToken = 1, kErrPos = 2, kErrPage = 4 };
 
 // One linear layer resident in the weight arena.  bf16: w [N, K].
 // W4A16: q [N, K/8] packed int4 codes, s [N, K/32] bf16 group scales.  Both
@@ -46,6 +48,12 @@ struct Rows {
   const int32_t* positions = nullptr;  // null: pos0 + row
   int pos0 = 0, seq0 = 0, seq_stride = 1, n = 0;
   int max_ctx = 0, vocab = 0;
+  // paged cache (pages != null): the cache row of (sequence slot s, position
+  // p) is pages[s * page_stride + p / kPageSize] * kPageSize + p % kPageSize
+  // (the pool holds n_pages + 1 pages, the last a spare); else s * max_ctx + p
+  const int32_t* pages = nullptr;
+  int page_stride = 0, n_pages = 0;
+  int* err = nullptr;  // device error word (a page entry outside the pool)
 };
 
 // How a matrix-vector product builds its fp32 input x for one row.

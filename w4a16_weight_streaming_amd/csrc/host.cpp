@@ -103,6 +103,14 @@ struct e2b_model {
   int kvq = 0;                // cache format: E2B_KV_BF16 / E2B_KV_INT8
   std::vector<char*> kc, vc;  // per layer: the K / V rows it reads (its source's)
   std::vector<float*> ks, vs; // int8: the row scales
+  // paged cache: n_pages pages of kPageSize positions per K/V-owning layer; the
+  // device page table [max_batch][page_stride] (caller-owned) and its host
+  // mirror; pages per slot and the free list (the allocator)
+  int n_pages = 0, page_stride = 0;
+  int32_t* d_pages = nullptr;
+  std::vector<int32_t> h_pages;
+  std::vector<int> slot_pages;
+  std::vector<int32_t> free_pages;
   // per-kernel timing
   int prof_kind = 0;
   struct Mark {
@@ -803,9 +811,11 @@ int e2b_kv_share_map(const e2b_model* m, int32_t* out) {
 size_t e2b_weight_bytes(const e2b_model* m) { return m ? m->weight_bytes : 0; }
 size_t e2b_arena_bytes(const e2b_model* m) { return m ? m->arena_bytes : 0; }
 
-size_t e2b_kv_bytes(const e2b_model* m, int max_batch, int max_ctx) {
-  if (!m || max_batch < 1 || max_ctx < 1) return 0;
-  const size_t rows = (size_t)max_batch * max_ctx;
+}  // extern "C"
+
+namespace {
+// bytes of a K/V pool of `rows` cached rows per K/V-owning layer
+size_t kv_pool_bytes(const e2b_model* m, size_t rows) {
   size_t b = 0;
   for (int l = 0; l < m->L; ++l) {
     if (m->li[l].src != l) continue;
@@ -815,6 +825,64 @@ size_t e2b_kv_bytes(const e2b_model* m, int max_batch, int max_ctx) {
       b += 2 * rows * m->li[l].hd * sizeof(uint16_t);
   }
   return b;
+}
+
+// bind d_kv as a pool of `rows` rows per K/V-owning layer: K rows, V rows
+// (bf16 or int8 codes), then for int8 the K and V row scales
+void bind_pool(e2b_model* m, char* kv, size_t rows) {
+  m->kv = kv;
+  m->kc.assign(m->L, nullptr);
+  m->vc.assign(m->L, nullptr);
+  m->ks.assign(m->L, nullptr);
+  m->vs.assign(m->L, nullptr);
+  const bool i8 = m->kv_quant == E2B_KV_INT8;
+  size_t off = 0;
+  for (int l = 0; l < m->L; ++l) {
+    if (m->li[l].src != l) continue;
+    const size_t one = rows * m->li[l].hd * (i8 ? 1 : sizeof(uint16_t));
+    m->kc[l] = m->kv + off;
+    m->vc[l] = m->kv + off + one;
+    off += 2 * one;
+    if (i8) {
+      const size_t sb = align_up(rows * sizeof(float));
+      m->ks[l] = reinterpret_cast<float*>(m->kv + off);
+      m->vs[l] = reinterpret_cast<float*>(m->kv + off + sb);
+      off += 2 * sb;
+    }
+  }
+  for (int l = 0; l < m->L; ++l)  // sharing layers read their source's region
+    if (m->li[l].src != l) {
+      const int s = m->li[l].src;
+      m->kc[l] = m->kc[s];
+      m->vc[l] = m->vc[s];
+      m->ks[l] = m->ks[s];
+      m->vs[l] = m->vs[s];
+    }
+}
+
+// upload one slot's row of the page table (synchronous: the host mirror may
+// change right after)
+int upload_page_row(e2b_model* m, int slot, hipStream_t st) {
+  const size_t n = m->page_stride;
+  CK(hipMemcpyAsync(m->d_pages + slot * n, m->h_pages.data() + slot * n, n * sizeof(int32_t),
+                    hipMemcpyHostToDevice, st),
+     "page table upload");
+  CK(hipStreamSynchronize(st), "page table upload sync");
+  return E2B_OK;
+}
+}  // namespace
+
+extern "C" {
+
+size_t e2b_kv_bytes(const e2b_model* m, int max_batch, int max_ctx) {
+  if (!m || max_batch < 1 || max_ctx < 1) return 0;
+  return kv_pool_bytes(m, (size_t)max_batch * max_ctx);
+}
+
+size_t e2b_kv_paged_bytes(const e2b_model* m, int n_pages) {
+  if (!m || n_pages < 1) return 0;
+  // one spare page past the pool: where a position with no reserved page goes
+  return kv_pool_bytes(m, (size_t)(n_pages + 1) * e2b::kPageSize);
 }
 
 size_t e2b_workspace_bytes(const e2b_model* m, int max_rows) {
@@ -926,44 +994,103 @@ int e2b_kv_alloc(e2b_model* m, void* d_kv, size_t bytes, int max_batch, int max_
   const size_t need = e2b_kv_bytes(m, max_batch, max_ctx);
   if (bytes < need) return fail(E2B_ENOMEM, "kv buffer of %zu bytes < %zu required", bytes, need);
   if (reinterpret_cast<uintptr_t>(d_kv) % 16) return fail(E2B_EINVAL, "kv buffer must be 16-byte aligned");
-  m->kv = reinterpret_cast<char*>(d_kv);
   m->max_batch = max_batch;
   m->max_ctx = max_ctx;
-  m->kc.assign(m->L, nullptr);
-  m->vc.assign(m->L, nullptr);
-  m->ks.assign(m->L, nullptr);
-  m->vs.assign(m->L, nullptr);
-  const bool i8 = m->kv_quant == E2B_KV_INT8;
-  const size_t rows = (size_t)max_batch * max_ctx;
-  size_t off = 0;
-  for (int l = 0; l < m->L; ++l) {
-    if (m->li[l].src != l) continue;
-    // K rows, V rows (bf16, or int8 codes), then for int8 the K and V row scales
-    const size_t one = rows * m->li[l].hd * (i8 ? 1 : sizeof(uint16_t));
-    m->kc[l] = m->kv + off;
-    m->vc[l] = m->kv + off + one;
-    off += 2 * one;
-    if (i8) {
-      const size_t sb = align_up(rows * sizeof(float));
-      m->ks[l] = reinterpret_cast<float*>(m->kv + off);
-      m->vs[l] = reinterpret_cast<float*>(m->kv + off + sb);
-      off += 2 * sb;
-    }
-  }
-  for (int l = 0; l < m->L; ++l)  // sharing layers read their source's region
-    if (m->li[l].src != l) {
-      const int s = m->li[l].src;
-      m->kc[l] = m->kc[s];
-      m->vc[l] = m->vc[s];
-      m->ks[l] = m->ks[s];
-      m->vs[l] = m->vs[s];
-    }
+  m->n_pages = 0;
+  m->d_pages = nullptr;
+  bind_pool(m, reinterpret_cast<char*>(d_kv), (size_t)max_batch * max_ctx);
   return E2B_OK;
 }
+
+int e2b_kv_alloc_paged(e2b_model* m, void* d_kv, size_t bytes, int n_pages, int32_t* d_page_table,
+                       int max_batch, int max_ctx, void* stream) {
+  if (!m || !d_kv || !d_page_table) return fail(E2B_EINVAL, "null argument");
+  if (n_pages < 1 || max_batch < 1 || max_ctx < 1)
+    return fail(E2B_EINVAL, "n_pages, max_batch and max_ctx must be >= 1");
+  if (max_batch > kMaxCtlRows) return fail(E2B_EINVAL, "max_batch above %d", kMaxCtlRows);
+  const size_t need = e2b_kv_paged_bytes(m, n_pages);
+  if (bytes < need) return fail(E2B_ENOMEM, "kv buffer of %zu bytes < %zu required", bytes, need);
+  if (reinterpret_cast<uintptr_t>(d_kv) % 16 || reinterpret_cast<uintptr_t>(d_page_table) % 4)
+    return fail(E2B_EINVAL, "kv buffer must be 16-byte aligned, page table 4-byte aligned");
+  m->max_batch = max_batch;
+  m->max_ctx = max_ctx;
+  m->n_pages = n_pages;
+  m->page_stride = (max_ctx + e2b::kPageSize - 1) / e2b::kPageSize;
+  m->d_pages = d_page_table;
+  m->h_pages.assign((size_t)max_batch * m->page_stride, -1);
+  m->slot_pages.assign(max_batch, 0);
+  m->free_pages.clear();
+  for (int p = n_pages - 1; p >= 0; --p) m->free_pages.push_back(p);  // page 0 handed out first
+  bind_pool(m, reinterpret_cast<char*>(d_kv), (size_t)(n_pages + 1) * e2b::kPageSize);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  CK(hipMemcpyAsync(m->d_pages, m->h_pages.data(), m->h_pages.size() * sizeof(int32_t),
+                    hipMemcpyHostToDevice, st),
+     "page table upload");
+  CK(hipStreamSynchronize(st), "page table upload sync");
+  return E2B_OK;
+}
+
+int e2b_seq_reserve(e2b_model* m, int slot, int n_positions, void* stream) {
+  if (!m) return fail(E2B_EINVAL, "null argument");
+  if (!m->d_pages) return fail(E2B_ESTATE, "the cache is not paged");
+  if (slot < 0 || slot >= m->max_batch) return fail(E2B_ERANGE, "slot %d outside [0, %d)", slot, m->max_batch);
+  if (n_positions < 0 || n_positions > m->max_ctx)
+    return fail(E2B_ERANGE, "positions %d outside [0, %d]", n_positions, m->max_ctx);
+  const int need = (n_positions + e2b::kPageSize - 1) / e2b::kPageSize;
+  const int more = need - m->slot_pages[slot];
+  if (more <= 0) return E2B_OK;
+  if (more > (int)m->free_pages.size())
+    return fail(E2B_ENOMEM, "%d more pages needed, %zu free", more, m->free_pages.size());
+  for (int k = m->slot_pages[slot]; k < need; ++k) {
+    m->h_pages[(size_t)slot * m->page_stride + k] = m->free_pages.back();
+    m->free_pages.pop_back();
+  }
+  m->slot_pages[slot] = need;
+  return upload_page_row(m, slot, reinterpret_cast<hipStream_t>(stream));
+}
+
+int e2b_seq_release(e2b_model* m, int slot, void* stream) {
+  if (!m) return fail(E2B_EINVAL, "null argument");
+  if (!m->d_pages) return fail(E2B_ESTATE, "the cache is not paged");
+  if (slot < 0 || slot >= m->max_batch) return fail(E2B_ERANGE, "slot %d outside [0, %d)", slot, m->max_batch);
+  for (int k = m->slot_pages[slot] - 1; k >= 0; --k) {
+    int32_t& e = m->h_pages[(size_t)slot * m->page_stride + k];
+    m->free_pages.push_back(e);
+    e = -1;
+  }
+  m->slot_pages[slot] = 0;
+  return upload_page_row(m, slot, reinterpret_cast<hipStream_t>(stream));
+}
+
+int e2b_seq_move(e2b_model* m, int from, int to, void* stream) {
+  if (!m) return fail(E2B_EINVAL, "null argument");
+  if (!m->d_pages) return fail(E2B_ESTATE, "the cache is not paged");
+  if (from < 0 || from >= m->max_batch || to < 0 || to >= m->max_batch)
+    return fail(E2B_ERANGE, "slots %d, %d outside [0, %d)", from, to, m->max_batch);
+  if (from == to) return E2B_OK;
+  if (m->slot_pages[to]) return fail(E2B_ESTATE, "slot %d still holds pages", to);
+  const size_t n = m->page_stride;
+  std::copy(m->h_pages.begin() + from * n, m->h_pages.begin() + (from + 1) * n, m->h_pages.begin() + to * n);
+  std::fill(m->h_pages.begin() + from * n, m->h_pages.begin() + (from + 1) * n, -1);
+  m->slot_pages[to] = m->slot_pages[from];
+  m->slot_pages[from] = 0;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int rc = upload_page_row(m, to, st);
+  return rc ? rc : upload_page_row(m, from, st);
+}
+
+int e2b_pages_free(const e2b_model* m) { return m && m->d_pages ? (int)m->free_pages.size() : 0; }
 
 }  // extern "C"
 
 namespace {
+void set_paging(const e2b_model* m, e2b::Rows& R, void* d_ws) {
+  R.pages = m->d_pages;
+  R.page_stride = m->page_stride;
+  R.n_pages = m->n_pages;
+  R.err = reinterpret_cast<int*>(d_ws);
+}
+
 // adv_pos (graph capture): also advance the positions, by the final argmax
 // kernel of the per-phase path (*advanced set) or not at all
 int decode_impl(e2b_model* m, const int32_t* d_tokens, const int32_t* d_positions, int batch,
@@ -989,6 +1116,7 @@ int decode_impl(e2b_model* m, const int32_t* d_tokens, const int32_t* d_position
   R.n = batch;
   R.max_ctx = m->max_ctx;
   R.vocab = m->V;
+  set_paging(m, R, d_ws);
   const int rc = run_rows(m, R, true, -1, d_logits, d_argmax, reinterpret_cast<char*>(d_ws), W,
                          reinterpret_cast<hipStream_t>(stream), adv_pos);
   if (rc == E2B_OK && advanced) *advanced = adv_pos != nullptr;
@@ -1033,6 +1161,7 @@ int e2b_prefill(e2b_model* m, int seq, const int32_t* d_tokens, int n_tokens, in
     R.n = r;
     R.max_ctx = m->max_ctx;
     R.vocab = m->V;
+    set_paging(m, R, d_ws);
     const bool last = off + r == n_tokens;
     int rc = run_rows(m, R, last, r - 1, d_logits_last, d_argmax_last,
                       reinterpret_cast<char*>(d_ws), ws_layout(m, r), st);
@@ -1390,9 +1519,10 @@ int e2b_check(e2b_model* m, void* d_ws, void* stream) {
   if (!w[0]) return E2B_OK;
   const int zero[4] = {0, 0, 0, 0};
   CK(hipMemcpy(d_ws, zero, sizeof zero, hipMemcpyHostToDevice), "check: clear error word");
-  return fail(E2B_EDEVICE, "device flagged%s%s (token %d, position %d, row %d)",
+  return fail(E2B_EDEVICE, "device flagged%s%s%s (token %d, position %d, row %d)",
               (w[0] & e2b::kErrToken) ? " a token outside the vocabulary" : "",
-              (w[0] & e2b::kErrPos) ? " a position outside [0, max_ctx)" : "", w[1], w[2], w[3]);
+              (w[0] & e2b::kErrPos) ? " a position outside [0, max_ctx)" : "",
+              (w[0] & e2b::kErrPage) ? " a cached position on no reserved page" : "", w[1], w[2], w[3]);
 }
 
 }  // extern "C"

@@ -479,7 +479,7 @@ __global__ __launch_bounds__(128) void k_kv_write(Rows R, QkvPostArgs a) {
   const bool is_v = wave == 1;
   float y[DPL];
   head_vec<HD>(raw, a.qkv_parts, a.qkv_pstride, is_v ? nullptr : a.gk, !is_v, cs, sn, lane, a.eps, y);
-  const size_t slot = (size_t)seq * R.max_ctx + pos;
+  const size_t slot = cache_row(R, seq, pos);
   if constexpr (KQ) {
     float deq[DPL];
     store_int8_row<DPL>(y, static_cast<int8_t*>(is_v ? a.vc : a.kc) + slot * HD, (is_v ? a.vs : a.ks) + slot,
