@@ -260,6 +260,45 @@ def test_wide_heads_long_window(torch_dev):
     run_greedy(torch, eng, orc, prompts, 8, "bf16")
 
 
+@pytest.mark.parametrize("nq,kv_quant", [(8, "bf16"), (2, "bf16"), (4, "int8")])
+def test_wide_heads_chunked_prefill(torch_dev, nq, kv_quant):
+    """The matrix-core prefill attention (head dims 256/512, 16 queries of
+    16 / nq rows per block) over many key chunks: a 700-token prompt in three
+    prefill passes (300 rows at position 0, 257 at 300, 143 at 557: odd row
+    counts leave a part-filled query tile), window 160 (two chunks per
+    sliding-layer group), max_ctx 1024 (full layers over eight), then 6
+    greedy steps; every pass's last-row logits and every step against the
+    oracle."""
+    torch, dev = torch_dev
+    cfg = dict(synth.get_config("toy10"), name="wide", num_attention_heads=nq, head_dim=256,
+               global_head_dim=512, sliding_window=160)
+    w = synth.generate(cfg, "bf16", seed=11)
+    V = cfg["vocab_size"]
+    eng = _engine(cfg, "bf16", w, 1, 1024, 300, kv_quant=kv_quant)
+    orc = oracle.Oracle(cfg, "bf16", w, 1, 1024, kv_quant=kv_quant)
+    prompt = synth.tokens(700, 12, V)
+    st = Stats("bf16")
+    a1 = torch.zeros(1, dtype=torch.int32, device=dev)
+    l1 = torch.zeros(1, V, dtype=torch.float32, device=dev)
+    for p0, p1 in ((0, 300), (300, 557), (557, 700)):
+        eng.prefill(0, torch.from_numpy(prompt[p0:p1]).to(dev), p0, a1, l1)
+        eng.check()
+        _, ref = orc.prefill(0, prompt[p0:p1], pos0=p0)
+        st.add(l1.cpu().numpy()[0], int(a1.item()), ref, f"prefill {p0}..{p1 - 1}")
+    nxt, pos = int(a1.item()), 700
+    am = torch.zeros(1, dtype=torch.int32, device=dev)
+    lg = torch.zeros(1, V, dtype=torch.float32, device=dev)
+    for i in range(6):
+        eng.decode_step(torch.tensor([nxt], dtype=torch.int32, device=dev),
+                        torch.tensor([pos], dtype=torch.int32, device=dev), am, lg)
+        eng.check()
+        _, ref, _ = orc.step(0, nxt, pos)
+        st.add(lg.cpu().numpy()[0], int(am.item()), ref, f"step {i} (position {pos})")
+        nxt, pos = int(am.item()), pos + 1
+    orc.close()
+    st.finish(f"wide heads nq={nq} {kv_quant} cache, chunked prefill")
+
+
 def test_batched_passes_agree_bitwise(torch_dev):
     """A row of a batched pass is computed independently of the other rows:
     a 20-token prefill (one batched pass) and the same tokens decoded as row 2
@@ -816,3 +855,32 @@ def test_e2b_long_context_graph_parity(torch_dev, B):
     orc = oracle.Oracle(cfg, "w4a16", w, len(rows), 8064)
     _seed_cache(torch, eng, cfg, T_of, orc, rows)
     _graph_decode_vs_oracle(torch, eng, orc, cfg, "w4a16", T_of, rows, 2, 78)
+
+
+def test_e2b_chunk_prefill_at_long_context(torch_dev):
+    """A prefill pass deep into a long context at full size (W4A16): seeded
+    caches up to position 3000, then 97 tokens in one pass at 3000..3096
+    (full layers: ~3,100 keys over 25 chunks per query tile, sliding layers
+    over 512 plus the tile), the pass's last-row logits and 2 graph steps
+    after it against the oracle."""
+    torch, dev = torch_dev
+    cfg = synth.get_config("e2b")
+    w = e2b_weights("w4a16")
+    V, T0, P = cfg["vocab_size"], 3000, 97
+    eng = _engine(cfg, "w4a16", w, 1, 3200, 128)
+    orc = oracle.Oracle(cfg, "w4a16", w, 1, 3200)
+    _seed_cache(torch, eng, cfg, [T0], orc, [0])
+    prompt = synth.tokens(P, 31, V)
+    st = Stats("w4a16")
+    s = torch.cuda.Stream(dev)
+    with torch.cuda.stream(s):
+        a1 = torch.zeros(1, dtype=torch.int32, device=dev)
+        l1 = torch.zeros(1, V, dtype=torch.float32, device=dev)
+        eng.prefill(0, torch.from_numpy(prompt).to(dev), T0, a1, l1)
+        s.synchronize()
+        eng.check()
+    _, ref = orc.prefill(0, prompt, pos0=T0)
+    st.add(l1.cpu().numpy()[0], int(a1.item()), ref, f"prefill {T0}..{T0 + P - 1}")
+    st.finish(f"w4a16 prefill pass at context {T0}")
+    _graph_decode_vs_oracle(torch, eng, orc, cfg, "w4a16", [T0 + P], [0], 2, 79)
+    orc.close()

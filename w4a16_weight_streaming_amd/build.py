@@ -8,7 +8,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libe2b.so")
-SOURCES = [os.path.join(CSRC, f) for f in ("kernels.hip", "gemm_bf16.hip", "gemm_w4.hip", "host.cpp")]
+SOURCES = [os.path.join(CSRC, f) for f in ("kernels.hip", "attn_prefill.hip", "gemm_bf16.hip", "gemm_w4.hip", "host.cpp")]
 HEADERS = [os.path.join(CSRC, "e2b_internal.h"), os.path.join(CSRC, "dev_common.h"),
            os.path.join(CSRC, "gemm_impl.h"),
            os.path.join(ROOT, "include", "e2b.h")]

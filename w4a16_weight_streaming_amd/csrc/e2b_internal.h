@@ -205,6 +205,12 @@ hipError_t launch_tile_w4(const Lin& W, uint32_t* tq, uint16_t* ts, hipStream_t 
 hipError_t launch_tile_bf16(const Lin& W, uint16_t* tw, hipStream_t st);
 hipError_t launch_qkv_post(const Rows& R, const QkvPostArgs& a, hipStream_t st);
 hipError_t launch_attention(const Rows& R, const AttnArgs& a, hipStream_t st);
+// Prefill attention on the matrix cores: rows of one sequence (seq_stride 0),
+// head dims 256 / 512, nq in {1, 2, 4, 8}, K/V already in the cache; chunk a
+// multiple of 32.  Writes the chunk partials; the merge is launch_attention's.
+bool attn_prefill_supported(int hd, int nq);
+hipError_t launch_attn_prefill(const Rows& R, const AttnArgs& a, hipStream_t st);
+constexpr int kPrefillMinChunk = 128;
 hipError_t launch_advance(int32_t* pos, int n, hipStream_t st);
 hipError_t launch_stream_reduce(const void* buf, size_t bytes, float* out, hipStream_t st);
 // batched rows (>= 2): prologue into bf16 hi/lo rows + group sums, then MFMA

@@ -352,7 +352,21 @@ Ws ws_layout(const e2b_model* m, int R) {
 // better).  The grid covers the longest span max_ctx allows (at most
 // kMaxChunks blocks); each row splits its live span over those blocks on the
 // device, so a short context is not left to a few long blocks.
-void attn_chunks(const e2b_model* m, bool full, int rows, int* chunk, int* nchunk) {
+//
+// A prefill pass on the matrix-core kernel takes 16 queries (RW = 16 / nq
+// rows) per block, and at least kPrefillMinChunk keys (whole 32-key tiles)
+// per block: the group's span is at most max_ctx (full) or the window plus
+// RW - 1 positions (sliding).
+void attn_chunks(const e2b_model* m, bool full, int rows, bool prefill, int hd, int* chunk,
+                 int* nchunk) {
+  if (prefill && e2b::attn_prefill_supported(hd, m->nq)) {
+    const int rw = 16 / m->nq;
+    const int span = full ? m->max_ctx : std::min(m->c.sliding_window + rw - 1, m->max_ctx);
+    int n = (span + e2b::kPrefillMinChunk - 1) / e2b::kPrefillMinChunk;
+    *nchunk = std::max(1, std::min(n, e2b::kMaxChunks));
+    *chunk = e2b::kPrefillMinChunk;
+    return;
+  }
   const int span = full ? m->max_ctx : std::min(m->c.sliding_window, m->max_ctx);
   const int w = rows == 1 ? 16 : 32;
   int n = (span + w - 1) / w;
@@ -554,7 +568,7 @@ int run_rows(e2b_model* m, const e2b::Rows& R, bool head, int head_row, float* d
       a.qkv_parts = nd_qkv;
       a.qkv_pstride = (size_t)n * d.qkv.N;
       a.eps = eps;
-      attn_chunks(m, y.full, n, &a.chunk, &a.nchunk);
+      attn_chunks(m, y.full, n, R.seq_stride == 0 && !a.kc_own, y.hd, &a.chunk, &a.nchunk);
       // one row: the O product merges the chunk partials itself; batched: the
       // merge writes the O product's prepared input
       a.combine = bat ? 1 : 0;

@@ -26,7 +26,7 @@ GIB = float(1 << 30)
 HERE = os.path.dirname(os.path.abspath(__file__))
 
 
-KERNEL_SOURCES = ("kernels.hip", "gemm_impl.h", "gemm_bf16.hip", "gemm_w4.hip", "dev_common.h",
+KERNEL_SOURCES = ("kernels.hip", "attn_prefill.hip", "gemm_impl.h", "gemm_bf16.hip", "gemm_w4.hip", "dev_common.h",
                   "e2b_internal.h")
 
 
