@@ -25,6 +25,8 @@
 // decode kernel writes, and k_attn_combine merges the chunks.
 #include "dev_common.h"
 
+#include <type_traits>
+
 namespace e2b {
 
 namespace {
@@ -151,11 +153,17 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill(Rows R, AttnArgs a) {
   const int8_t* kc8 = static_cast<const int8_t*>(a.kc);
   const int8_t* vc8 = static_cast<const int8_t*>(a.vc);
 
-  for (int kt = k0; kt < k1; kt += kKT) {
-    // V tile: thread t takes key t / 8 and the 16-byte pieces t % 8 + 8 i
-    // (issued first; stored to LDS after the score product)
-    uint4 vr[VPT];
-    float vscale = 0.f;
+  // One key tile's cache reads, kept raw (int8 codes are widened when used):
+  // V: thread t takes key t / 8 and the 16-byte (int8: 8-byte) pieces
+  // t % 8 + 8 i; K: this wave's quarter of d for keys 16 half + col.  Keys
+  // past the chunk read the zero row.
+  using VW = typename std::conditional<KQ != 0, uint2, uint4>::type;
+  struct Tile {
+    VW v[VPT];
+    VW k[2][KSW];
+    float vs, ks[2];
+  };
+  auto load_tile = [&](int kt, Tile& T) {
     {
       const int j = t >> 3, key = kt + j;
       const bool ok = key < k1;
@@ -165,17 +173,14 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill(Rows R, AttnArgs a) {
         const int d = 8 * ((t & 7) + 8 * i);
         if constexpr (KQ) {
           const int8_t* p = ok ? vc8 + row * HD + d : reinterpret_cast<const int8_t*>(kZeroRow);
-          vr[i] = codes_to_bf16(*reinterpret_cast<const uint2*>(p));
+          T.v[i] = *reinterpret_cast<const uint2*>(p);
         } else {
           const uint16_t* p = ok ? vc16 + row * HD + d : kZeroRow;
-          vr[i] = *reinterpret_cast<const uint4*>(p);
+          T.v[i] = *reinterpret_cast<const uint4*>(p);
         }
       }
-      if constexpr (KQ) vscale = *(ok ? a.vs + row : zero_f());
+      T.vs = KQ ? *(ok ? a.vs + row : zero_f()) : 0.f;
     }
-    // K fragments of this wave's quarter of d: key kt + 16 half + col
-    uint4 kb[2][KSW];
-    float ksc[2];
 #pragma unroll
     for (int jh = 0; jh < 2; ++jh) {
       const int key = kt + 16 * jh + col;
@@ -186,13 +191,32 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill(Rows R, AttnArgs a) {
         const int d = HDW * wave + 32 * s + 8 * grp;
         if constexpr (KQ) {
           const int8_t* p = ok ? kc8 + row * HD + d : reinterpret_cast<const int8_t*>(kZeroRow);
-          kb[jh][s] = codes_to_bf16(*reinterpret_cast<const uint2*>(p));
+          T.k[jh][s] = *reinterpret_cast<const uint2*>(p);
         } else {
           const uint16_t* p = ok ? kc16 + row * HD + d : kZeroRow;
-          kb[jh][s] = *reinterpret_cast<const uint4*>(p);
+          T.k[jh][s] = *reinterpret_cast<const uint4*>(p);
         }
       }
-      ksc[jh] = KQ ? *(ok ? a.ks + row : zero_f()) : 1.f;
+      T.ks[jh] = KQ ? *(ok ? a.ks + row : zero_f()) : 1.f;
+    }
+  };
+  auto widen = [](VW w) -> uint4 {
+    if constexpr (KQ) return codes_to_bf16(w);
+    else return w;
+  };
+
+  // the next tile's reads are issued before this tile's arithmetic
+  Tile cur, nxt;
+  if (k0 < k1) load_tile(k0, cur);
+  for (int kt = k0; kt < k1; kt += kKT) {
+    if (kt + kKT < k1) load_tile(kt + kKT, nxt);
+    uint4 kb[2][KSW];
+    float ksc[2];
+#pragma unroll
+    for (int jh = 0; jh < 2; ++jh) {
+#pragma unroll
+      for (int s = 0; s < KSW; ++s) kb[jh][s] = widen(cur.k[jh][s]);
+      ksc[jh] = cur.ks[jh];
     }
     // partial scores over this wave's quarter of d
 #pragma unroll
@@ -209,8 +233,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill(Rows R, AttnArgs a) {
     {
       const int j = t >> 3;
 #pragma unroll
-      for (int i = 0; i < VPT; ++i) *reinterpret_cast<uint4*>(vt + j * VP + 8 * ((t & 7) + 8 * i)) = vr[i];
-      if (KQ && (t & 7) == 0) vsc[j] = vscale;
+      for (int i = 0; i < VPT; ++i) *reinterpret_cast<uint4*>(vt + j * VP + 8 * ((t & 7) + 8 * i)) = widen(cur.v[i]);
+      if (KQ && (t & 7) == 0) vsc[j] = cur.vs;
     }
     __syncthreads();
 
@@ -271,6 +295,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill(Rows R, AttnArgs a) {
       acc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf8(pl), vb, acc[d], 0, 0, 0);
     }
     __syncthreads();  // the next tile overwrites the V tile and the scores
+    cur = nxt;
   }
 
   // the chunk's partial for each (row, head): unnormalised o, running max, sum

@@ -156,6 +156,8 @@ struct AttnArgs {
   int nchunk = 0;  // nchunk blocks of max(chunk, ceil(span / nchunk)) keys
   int owns = 0;                 // the layer computes K/V (raw rows hold q, k, v)
   int combine = 1;              // merge the chunk partials into out (else the O product does)
+  int mfma = 0;                 // the matrix-core kernel (launch_attn_prefill): a prefill pass
+                                // whose K/V are all written, chunk plan for it
   int qkv_parts = 1;            // qkv is the sum of this many partials
   size_t qkv_pstride = 0;       // floats between partials
   float eps = 1e-6f;

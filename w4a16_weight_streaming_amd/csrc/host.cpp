@@ -348,8 +348,9 @@ Ws ws_layout(const e2b_model* m, int R) {
 
 // Attention blocks per (row, layer) and the fewest keys per block: 16 for a
 // single row (each wave then takes one group of 4 keys: the shortest chain,
-// and the chip has room for the blocks), else 32 (64 or 128 measured no
-// better).  The grid covers the longest span max_ctx allows (at most
+// and the chip has room for the blocks), 32 for a few rows, 64 from 32 rows
+// on (measured: B = 8 at context 500 is fastest with 32, B = 64 at context
+// 140 with 64; 128 is slower for both).  The grid covers the longest span max_ctx allows (at most
 // kMaxChunks blocks); each row splits its live span over those blocks on the
 // device, so a short context is not left to a few long blocks.
 //
@@ -357,9 +358,8 @@ Ws ws_layout(const e2b_model* m, int R) {
 // rows) per block, and at least kPrefillMinChunk keys (whole 32-key tiles)
 // per block: the group's span is at most max_ctx (full) or the window plus
 // RW - 1 positions (sliding).
-void attn_chunks(const e2b_model* m, bool full, int rows, bool prefill, int hd, int* chunk,
-                 int* nchunk) {
-  if (prefill && e2b::attn_prefill_supported(hd, m->nq)) {
+void attn_chunks(const e2b_model* m, bool full, int rows, bool mfma, int* chunk, int* nchunk) {
+  if (mfma) {
     const int rw = 16 / m->nq;
     const int span = full ? m->max_ctx : std::min(m->c.sliding_window + rw - 1, m->max_ctx);
     int n = (span + e2b::kPrefillMinChunk - 1) / e2b::kPrefillMinChunk;
@@ -368,7 +368,7 @@ void attn_chunks(const e2b_model* m, bool full, int rows, bool prefill, int hd, 
     return;
   }
   const int span = full ? m->max_ctx : std::min(m->c.sliding_window, m->max_ctx);
-  const int w = rows == 1 ? 16 : 32;
+  const int w = rows == 1 ? 16 : rows < 32 ? 32 : 64;
   int n = (span + w - 1) / w;
   if (n > e2b::kMaxChunks) n = e2b::kMaxChunks;
   if (n < 1) n = 1;
@@ -521,7 +521,8 @@ int run_rows(e2b_model* m, const e2b::Rows& R, bool head, int head_row, float* d
     }
     // decode rows are distinct sequences: the attention kernel writes the new
     // K/V itself; prefill rows attend to each other's K/V, written first
-    const bool fused_kv = R.seq_stride != 0;
+    const bool mfma_attn = R.seq_stride == 0 && attn_prefill_supported(y.hd, m->nq);
+    const bool fused_kv = R.seq_stride != 0 && !mfma_attn;
     if (owns && !fused_kv) {
       QkvPostArgs a;
       a.qkv = F(W.qkv);
@@ -568,7 +569,8 @@ int run_rows(e2b_model* m, const e2b::Rows& R, bool head, int head_row, float* d
       a.qkv_parts = nd_qkv;
       a.qkv_pstride = (size_t)n * d.qkv.N;
       a.eps = eps;
-      attn_chunks(m, y.full, n, R.seq_stride == 0 && !a.kc_own, y.hd, &a.chunk, &a.nchunk);
+      a.mfma = mfma_attn;
+      attn_chunks(m, y.full, n, mfma_attn, &a.chunk, &a.nchunk);
       // one row: the O product merges the chunk partials itself; batched: the
       // merge writes the O product's prepared input
       a.combine = bat ? 1 : 0;

@@ -525,10 +525,7 @@ hipError_t launch_attention(const Rows& R, const AttnArgs& a, hipStream_t st) {
   if (a.nq > kMaxHeads || a.nchunk > kMaxChunks || a.nchunk < 1 || a.chunk < 1 || !a.rope)
     return hipErrorInvalidValue;
   if (a.kvq && (!a.ks || !a.vs || (a.kc_own && (!a.ks_own || !a.vs_own)))) return hipErrorInvalidValue;
-  // a pass over rows of one sequence whose K/V are written: the matrix-core
-  // kernel (its chunk plan is the host's, see attn_chunks)
-  const bool mfma = R.seq_stride == 0 && !a.kc_own && attn_prefill_supported(a.hd, a.nq);
-  hipError_t e = mfma ? launch_attn_prefill(R, a, st) : a.kvq ? attn_q<1>(R, a, st) : attn_q<0>(R, a, st);
+  hipError_t e = a.mfma ? launch_attn_prefill(R, a, st) : a.kvq ? attn_q<1>(R, a, st) : attn_q<0>(R, a, st);
   if (e != hipSuccess || !a.combine) return e;
   hipLaunchKernelGGL(k_attn_combine, dim3(R.n, a.nq), dim3(256), 0, st, a);
   return hipGetLastError();
