@@ -153,14 +153,14 @@ def test_matvec_validation(lib):
         assert L.e2b_matvec_workspace_bytes(0, 64, K, 3) == 0, K
         assert L.e2b_matvec(0, 256, None, 8, K, 256, 3, 256, 256, 1 << 20, None) == lib.E2B_EINVAL, K
     # several rows: the K-slice partials of the matrix-core product, then (N %
-    # 16 == 0) the weights tiled in fragment order
+    # 16 == 0, and for W4A16 K % 128 == 0) the weights tiled in fragment order
     up = lambda x: (x + 255) // 256 * 256
     for quant in (0, 1):
         for N, K, r in ((1536, 1536, 3), (1536, 12288, 70), (1536, 4096, 2), (24576, 1536, 64),
                         (40, 1536, 3)):
             total = L.e2b_matvec_workspace_bytes(quant, N, K, r)
             tiled = 0
-            if N % 16 == 0:
+            if N % 16 == 0 and (not quant or K % 128 == 0):
                 tiled = up(N * K // 2) + up(N * (K // 32) * 2) if quant else up(N * K * 2)
             part = total - tiled
             slices = part // (r * N * 4)

@@ -16,6 +16,20 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
+// 16- and 8-byte loads into registers, built from scalars (a plain struct
+// copy of a load into a register array can become a memory copy that keeps
+// the array in scratch memory)
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint4 ld16(const void* p) {
+  const u32x4_t v = *reinterpret_cast<const u32x4_t*>(p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 ld8u(const void* p) {
+  const u32x2_t v = *reinterpret_cast<const u32x2_t*>(p);
+  return make_uint2(v.x, v.y);
+}
+
 // eight int4 codes (one packed word) -> eight bf16 values 128 + c
 __device__ __forceinline__ uint4 w4_to_bf16(uint32_t word) {
   const uint32_t lo = word & 0x0F0F0F0Fu, hi = (word >> 4) & 0x0F0F0F0Fu;
@@ -39,7 +53,7 @@ constexpr int kAP = kKC + 8;    // padded LDS row of bf16: 16-byte reads conflic
 // A chunks (16*MT rows x 128 k, hi and lo) are double-buffered in LDS, one
 // barrier per chunk; each wave's weight fragments for the next chunk are
 // loaded into registers while the current chunk is multiplied.
-template <int WQ, int NT, int MT, int FA, int TAG>
+template <int WQ, int NT, int MT, int FA, int TAG, int TQ>
 __global__ __launch_bounds__(256, 2) void k_gemm(Lin W, int rows, GemmA A, int KS, Epilogue epi) {
   constexpr int MB = 16 * MT;
   const uint16_t* __restrict__ xh = A.xh;
@@ -66,12 +80,15 @@ __global__ __launch_bounds__(256, 2) void k_gemm(Lin W, int rows, GemmA A, int K
   // weight fragments of one chunk (4 k-steps)
   // weight fragments: a ring of D chunks, D - 1 of them in flight ahead
   constexpr int D = WQ ? (NT >= 4 ? 2 : 4) : (NT >= 2 ? 3 : 4);
+  // (loaded values are kept raw until the multiply: an operation on a loaded
+  // value right after the load would wait for it, and with it for every load
+  // issued before it)
   uint4 bw[D][WQ ? 1 : 4][WQ ? 1 : NT];
   uint32_t bq[D][WQ ? 4 : 1][WQ ? NT : 1];
-  float bs[D][WQ ? 4 : 1][WQ ? NT : 1];
+  uint32_t bs[D][WQ ? 2 : 1][WQ ? NT : 1];  // W4A16 scales: bf16 pairs (groups 2i, 2i + 1)
   // A chunk staged through registers
   uint4 rah[MT], ral[MT];
-  float rg = 0.f, rgs[MT];
+  float rg = 0.f, rgs[MT];  // (rg: the raw group sum, scaled when staged)
 #pragma unroll
   for (int j = 0; j < MT; ++j) rgs[j] = 0.f;
   float raf[FA ? MT : 1][8];  // fp32 input slots (FA)
@@ -84,41 +101,59 @@ __global__ __launch_bounds__(256, 2) void k_gemm(Lin W, int rows, GemmA A, int K
 #pragma unroll
     for (int s = 0; s < (WQ ? 4 : 1); ++s)
 #pragma unroll
-      for (int j = 0; j < (WQ ? NT : 1); ++j) {
-        bq[x][s][j] = 0x88888888u;
-        bs[x][s][j] = 0.f;
-      }
+      for (int j = 0; j < (WQ ? NT : 1); ++j) bq[x][s][j] = 0x88888888u;
+#pragma unroll
+    for (int s = 0; s < (WQ ? 2 : 1); ++s)
+#pragma unroll
+      for (int j = 0; j < (WQ ? NT : 1); ++j) bs[x][s][j] = 0u;
   }
 
   const int kbeg = ks * KS, kend = kbeg + KS;
   // (buffer indices are compile-time constants so the fragments stay in registers)
+  // Out-of-range operands are read at a valid address and never zeroed: a
+  // column past N (row 0 read) or a row past the pass (element 0 read) only
+  // reaches its own output column or row, which is never stored, and k past
+  // the slice is never multiplied (the k-steps stop at kcn, a multiple of 32).
   auto load_b = [&](auto BUF, int kc, int kcn) {
     constexpr int buf = decltype(BUF)::value;
+    if constexpr (WQ && TQ) {
+      {
+        // the tiled copy: a lane's four code words of the chunk (k-steps
+        // 0..3) in 16 bytes, its column's four group scales in 8 (the chunk
+        // is one 128-k block: slices are whole blocks on this path)
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+          const size_t row = ncol[j] < N ? (size_t)ncol[j] : 0;
+          const size_t blk = (row / 16) * (K / 128) + (size_t)kc / 128;
+          const uint4 qv = ld16(W.tq + (blk * 64 + lane) * 4);
+          const uint2 sv = ld8u(W.ts + (blk * 16 + (lane & 15)) * 4);
+          bq[buf][0][j] = qv.x;
+          bq[buf][1][j] = qv.y;
+          bq[buf][2][j] = qv.z;
+          bq[buf][3][j] = qv.w;
+          bs[buf][0][j] = sv.x;
+          bs[buf][1][j] = sv.y;
+        }
+        return;
+      }
+    }
+    // (every k-step is read, a k-step past kcn at the chunk's first group:
+    // the same loads on every path keep the compiler's wait counts exact)
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      if (32 * s >= kcn) break;
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
-        // columns past N read row 0 (always valid) and are zeroed
-        const bool ok = ncol[j] < N;
-        const size_t row = ok ? (size_t)ncol[j] : 0;
-        if constexpr (WQ) {
-          // (the tiled copy when there is one: the same word, 256 contiguous
-          // bytes per wave; the address is selected, the load is not)
-          const size_t g = (size_t)(kc + 32 * s) / 32, tile = row / 16;
-          const uint32_t* qp = W.tq ? W.tq + (tile * (K / 32) + g) * 64 + lane : W.q + row * (K / 8) + 4 * g + kq;
-          const uint16_t* sp = W.ts ? W.ts + (tile * (K / 32) + g) * 16 + (lane & 15) : W.s + row * (K / 32) + g;
-          const uint32_t qv = *qp;
-          const float sv = bf2f(*sp);
-          bq[buf][s][j] = ok ? qv : 0x88888888u;
-          bs[buf][s][j] = ok ? sv : 0.f;
+        const size_t row = ncol[j] < N ? (size_t)ncol[j] : 0;
+        const size_t g = (size_t)(kc + (32 * s < kcn ? 32 * s : 0)) / 32;
+        if constexpr (WQ) {  // (no tiled copy: one word and one scale per k-step)
+          bq[buf][s][j] = W.q[row * (K / 8) + 4 * g + kq];
+          const uint32_t sv = W.s[row * (K / 32) + g];
+          bs[buf][s >> 1][j] = (s & 1) ? (bs[buf][s >> 1][j] | (sv << 16)) : sv;
         } else {
           // (the tiled copy when there is one: one contiguous kilobyte per wave)
-          const size_t g = (size_t)(kc + 32 * s) / 32, tile = row / 16;
-          const uint16_t* wp = W.tw ? W.tw + ((tile * (K / 32) + g) * 64 + lane) * 8 : W.w + row * K + kc + 32 * s + 8 * kq;
-          uint4 v = *reinterpret_cast<const uint4*>(wp);
-          if (!ok) v = make_uint4(0, 0, 0, 0);
-          bw[buf][s][j] = v;
+          const uint16_t* wp = W.tw ? W.tw + (((row / 16) * (K / 32) + g) * 64 + lane) * 8
+                                    : W.w + row * K + 32 * g + 8 * kq;
+          bw[buf][s][j] = ld16(wp);
         }
       }
     }
@@ -130,29 +165,21 @@ __global__ __launch_bounds__(256, 2) void k_gemm(Lin W, int rows, GemmA A, int K
         const int idx = t + 256 * j, m = idx >> 4, k8 = idx & 15;
         const bool ok = m < mrows && 8 * k8 < kcn;
         ld8(A.a + (ok ? (size_t)(m0 + m) * A.lda + kc + 8 * k8 : 0), raf[j]);
-        if (!ok)
-#pragma unroll
-          for (int x = 0; x < 8; ++x) raf[j][x] = 0.f;
       }
       return;
     }
 #pragma unroll
     for (int j = 0; j < MT; ++j) {
       const int idx = t + 256 * j, m = idx >> 4, k8 = idx & 15;
-      // out-of-range slots read element 0 (always valid) and are zeroed
       const bool ok = m < mrows && 8 * k8 < kcn;
       const size_t o = ok ? (size_t)(m0 + m) * K + kc + 8 * k8 : 0;
-      uint4 vh = *reinterpret_cast<const uint4*>(xh + o);
-      uint4 vl = *reinterpret_cast<const uint4*>(xl + o);
-      if (!ok) vh = vl = make_uint4(0, 0, 0, 0);
-      rah[j] = vh;
-      ral[j] = vl;
+      rah[j] = ld16(xh + o);
+      ral[j] = ld16(xl + o);
     }
     if (WQ) {
       const int m = t >> 2, g = t & 3;
       const bool ok = m < mrows && 32 * g < kcn;
-      const float v = xg[ok ? (size_t)(m0 + m) * (K / 32) + kc / 32 + g : 0];
-      rg = ok ? 136.0f * v : 0.f;
+      rg = xg[ok ? (size_t)(m0 + m) * (K / 32) + kc / 32 + g : 0];
     }
   };
   auto store_a = [&](int st) {
@@ -187,7 +214,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm(Lin W, int rows, GemmA A, int K
         if ((k8 & 3) == 0) sg[st][k8 >> 2][m] = rgs[j];
       }
     } else if (WQ) {
-      if ((t >> 2) < MB) sg[st][t & 3][t >> 2] = rg;
+      if ((t >> 2) < MB) sg[st][t & 3][t >> 2] = 136.0f * rg;
     }
   };
 
@@ -196,15 +223,24 @@ __global__ __launch_bounds__(256, 2) void k_gemm(Lin W, int rows, GemmA A, int K
   // loads of chunk c + 1, multiply chunk c, stage chunk c + 1 in LDS
   auto chunk = [&](auto BUF, int c) {
     constexpr int buf = decltype(BUF)::value;
-    const int kc = kbeg + c * kKC, kcn = min(kKC, kend - kc), st = c & 1;
+    // A chunk past the slice (the ring's tail) multiplies nothing, but it
+    // issues the same loads, at the last chunk's addresses: every path then
+    // has the same loads in flight, so the compiler waits only for the ones
+    // the multiply uses
+    const bool live = c < nch;
+    const int cl = live ? c : nch - 1;
+    const int kc = kbeg + cl * kKC, kcn = min(kKC, kend - kc), st = cl & 1;
     const bool more = c + 1 < nch;
     // (activation loads first: loads complete in issue order, and staging
     // chunk c + 1 must not wait for the weight loads issued after it)
-    if (more) load_a(kc + kKC, min(kKC, kend - kc - kKC));
-    if (c + D - 1 < nch) {
-      const int kf = kc + (D - 1) * kKC;
+    const int ka = more ? kc + kKC : kc;
+    load_a(ka, min(kKC, kend - ka));
+    __builtin_amdgcn_sched_barrier(0);  // (keep every activation load ahead of the weights)
+    {
+      const int cf = min(c + D - 1, nch - 1), kf = kbeg + cf * kKC;
       load_b(std::integral_constant<int, (buf + D - 1) % D>(), kf, min(kKC, kend - kf));
     }
+    if (!live) return;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       if (32 * s >= kcn) break;
@@ -226,7 +262,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm(Lin W, int rows, GemmA A, int K
             f32x4_t d = f32x4_t{0.f, 0.f, 0.f, 0.f};
             d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ah, B[j], d, 0, 0, 0);
             d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Al, B[j], d, 0, 0, 0);
-            const float sc = bs[buf][s][j];
+            const float sc = bf2f((s & 1) ? bs[buf][s >> 1][j] >> 16 : bs[buf][s >> 1][j]);
             acc[mt][j][0] = fmaf(sc, d[0] - g4.x, acc[mt][j][0]);
             acc[mt][j][1] = fmaf(sc, d[1] - g4.y, acc[mt][j][1]);
             acc[mt][j][2] = fmaf(sc, d[2] - g4.z, acc[mt][j][2]);
@@ -251,19 +287,21 @@ __global__ __launch_bounds__(256, 2) void k_gemm(Lin W, int rows, GemmA A, int K
 
   load_a(kbeg, min(kKC, KS));
   load_b(C0(), kbeg, min(kKC, KS));
-  if constexpr (D > 2)
-    if (1 < nch) load_b(C1(), kbeg + kKC, min(kKC, KS - kKC));
-  if constexpr (D > 3)
-    if (2 < nch) load_b(C2(), kbeg + 2 * kKC, min(kKC, KS - 2 * kKC));
+  if constexpr (D > 2) {
+    const int k1 = kbeg + min(1, nch - 1) * kKC;
+    load_b(C1(), k1, min(kKC, kend - k1));
+  }
+  if constexpr (D > 3) {
+    const int k2 = kbeg + min(2, nch - 1) * kKC;
+    load_b(C2(), k2, min(kKC, kend - k2));
+  }
   store_a(0);
   __syncthreads();
   for (int c = 0; c < nch; c += D) {
     chunk(C0(), c);
-    if (c + 1 < nch) chunk(C1(), c + 1);
-    if constexpr (D > 2)
-      if (c + 2 < nch) chunk(C2(), c + 2);
-    if constexpr (D > 3)
-      if (c + 3 < nch) chunk(C3(), c + 3);
+    chunk(C1(), c + 1);
+    if constexpr (D > 2) chunk(C2(), c + 2);
+    if constexpr (D > 3) chunk(C3(), c + 3);
   }
 
   if (!epi.argmax) {
@@ -326,12 +364,23 @@ static hipError_t run_gemm(const Lin& W, int rows, const GemmA& A, int nks, cons
   // on which rows share its block)
   const int mt = rows <= 16 ? 1 : (rows <= 32 ? 2 : 4);
   dim3 grid(nbx, nks, (rows + 16 * mt - 1) / (16 * mt));
+  // a W4A16 matrix without the tiled copy (a shape the copy does not cover,
+  // through the matvec entry point) takes the one-word-per-k-step loads
+  if (WQ && !W.tq) {
+    if (mt == 1)
+      E2B_TIMED_LAUNCH((k_gemm<WQ, NT, 1, FA, kTagOther, 0>), grid, dim3(256), 0, st, W, rows, A, W.K / nks, epi);
+    else if (mt == 2)
+      E2B_TIMED_LAUNCH((k_gemm<WQ, NT, 2, FA, kTagOther, 0>), grid, dim3(256), 0, st, W, rows, A, W.K / nks, epi);
+    else
+      E2B_TIMED_LAUNCH((k_gemm<WQ, NT, 4, FA, kTagOther, 0>), grid, dim3(256), 0, st, W, rows, A, W.K / nks, epi);
+    return hipGetLastError();
+  }
   if (mt == 1)
-    E2B_TIMED_LAUNCH((k_gemm<WQ, NT, 1, FA, TAG>), grid, dim3(256), 0, st, W, rows, A, W.K / nks, epi);
+    E2B_TIMED_LAUNCH((k_gemm<WQ, NT, 1, FA, TAG, 1>), grid, dim3(256), 0, st, W, rows, A, W.K / nks, epi);
   else if (mt == 2)
-    E2B_TIMED_LAUNCH((k_gemm<WQ, NT, 2, FA, TAG>), grid, dim3(256), 0, st, W, rows, A, W.K / nks, epi);
+    E2B_TIMED_LAUNCH((k_gemm<WQ, NT, 2, FA, TAG, 1>), grid, dim3(256), 0, st, W, rows, A, W.K / nks, epi);
   else
-    E2B_TIMED_LAUNCH((k_gemm<WQ, NT, 4, FA, TAG>), grid, dim3(256), 0, st, W, rows, A, W.K / nks, epi);
+    E2B_TIMED_LAUNCH((k_gemm<WQ, NT, 4, FA, TAG, 1>), grid, dim3(256), 0, st, W, rows, A, W.K / nks, epi);
   return hipGetLastError();
 }
 

@@ -192,7 +192,7 @@ struct Planner {
     } else {
       L.q = alloc((size_t)N * K / 2);
       L.s = alloc((size_t)N * (K / 32) * 2);
-      if (tiled && N % 16 == 0) {
+      if (tiled && N % 16 == 0 && K % 128 == 0) {
         L.tiled = true;
         L.tq = alloc((size_t)N * K / 2);
         L.ts = alloc((size_t)N * (K / 32) * 2);
@@ -1215,7 +1215,7 @@ MvWs matvec_ws(int quant, int N, int K, int rows) {
   size_t cur = 0;
   w.part = 0;
   if (w.nks > 1) cur = align_up((size_t)w.nks * rows * N * sizeof(float));
-  w.tiled = rows > 1 && N % 16 == 0;
+  w.tiled = rows > 1 && N % 16 == 0 && (quant == E2B_QUANT_BF16 || K % 128 == 0);
   if (w.tiled) {
     w.tq = cur;
     cur = align_up(cur + (quant ? (size_t)N * K / 2 : (size_t)N * K * 2));

@@ -531,14 +531,18 @@ hipError_t launch_attention(const Rows& R, const AttnArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// The matrix-core copy of a W4A16 matrix, per 16-row tile t and 128-k block
+// b: for each lane l its four code words (row 16t + l%16, groups 4b..4b+3,
+// quarter l/16 of each group) in 16 contiguous bytes, then per row of the
+// tile its four group scales in 8.  (K a multiple of 128.)
 __global__ __launch_bounds__(256) void k_tile_w4(const uint32_t* __restrict__ q,
                                                  const uint16_t* __restrict__ s, int N, int K,
                                                  uint32_t* __restrict__ tq, uint16_t* __restrict__ ts) {
-  const size_t G = K / 32, n_words = (size_t)N * K / 8;
+  const size_t G = K / 32, NB = K / 128, n_words = (size_t)N * K / 8;
   for (size_t i = blockIdx.x * (size_t)256 + threadIdx.x; i < n_words; i += (size_t)gridDim.x * 256) {
-    const size_t l = i % 64, tg = i / 64, t = tg / G, g = tg % G;
+    const size_t st = i % 4, l = (i / 4) % 64, tb = i / 256, t = tb / NB, g = 4 * (tb % NB) + st;
     tq[i] = q[(16 * t + l % 16) * (K / 8) + 4 * g + l / 16];
-    if (l < 16) ts[tg * 16 + l] = s[(16 * t + l) * G + g];
+    if (l < 16) ts[(tb * 16 + l) * 4 + st] = s[(16 * t + l) * G + g];
   }
 }
 
@@ -562,7 +566,7 @@ hipError_t launch_tile_bf16(const Lin& W, uint16_t* tw, hipStream_t st) {
 }
 
 hipError_t launch_tile_w4(const Lin& W, uint32_t* tq, uint16_t* ts, hipStream_t st) {
-  if (!W.q || !W.s || !tq || !ts || W.N % 16 || W.K % 32 || W.N < 16) return hipErrorInvalidValue;
+  if (!W.q || !W.s || !tq || !ts || W.N % 16 || W.K % 128 || W.N < 16) return hipErrorInvalidValue;
   const size_t n_words = (size_t)W.N * W.K / 8;
   size_t blocks = (n_words + 255) / 256;
   if (blocks > 8192) blocks = 8192;
@@ -777,9 +781,12 @@ GemmPlan gemm_plan(int quant, int N, int K, bool partial_ok) {
   // its K split (each activation fragment read from LDS then feeds two
   // products, half the LDS traffic per weight byte); bf16 products too narrow
   // for that (q/k/v, the sliding layers' O) keep one.
+  // (a W4A16 matrix with K a multiple of 128 has a tiled copy, read in
+  // whole 128-k blocks: its K slices are whole blocks)
+  const int kq = quant && K % 128 == 0 ? 128 : 32;
   int kmax = 1;
   for (int c : {2, 3, 4, 6, 8, 12, 16})
-    if (K % (32 * c) == 0 && K / c >= 256) kmax = c;
+    if (K % (kq * c) == 0 && K / c >= 256) kmax = c;
   p.nt = quant ? 4 : 2;
   const int nt_min = quant || cols(2) * (partial_ok ? kmax : 1) >= 192 ? 2 : 1;
   while (p.nt > nt_min && cols(p.nt) < kTarget) p.nt >>= 1;
@@ -788,7 +795,7 @@ GemmPlan gemm_plan(int quant, int N, int K, bool partial_ok) {
     static const int cand[] = {2, 3, 4, 6, 8, 12, 16};
     for (int c : cand) {
       if (cols(p.nt) * p.nks >= kTarget) break;
-      if (K % (32 * c) == 0 && K / c >= 256) p.nks = c;
+      if (K % (kq * c) == 0 && K / c >= 256) p.nks = c;
     }
   }
   return p;
@@ -800,6 +807,7 @@ hipError_t launch_gemm(int quant, int tag, const Lin& W, int rows, const GemmA& 
   if (rows < 1 || nks < 1 || nks > kMaxGemmSplit || W.K % nks || (W.K / nks) % 32)
     return hipErrorInvalidValue;
   if (epi.argmax && nks != 1) return hipErrorInvalidValue;
+  if (quant && W.tq && (!W.ts || (W.K / nks) % 128)) return hipErrorInvalidValue;
   if (A.a ? A.kind != kPlain || A.na != 1 || A.lda % 8
           : (!A.xh || !A.xl || (quant && !A.xg)))
     return hipErrorInvalidValue;
