@@ -231,6 +231,9 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv(Lin W, int rows, Prologue
   int u0 = blockIdx.x * 4 + wave;
   Batch A, Bq;
   load_batch(A, u0);                  // then the weights (independent of x)
+  // (no arithmetic on the inputs may move above the weight loads: it would
+  // wait for the inputs before the weights are requested)
+  __builtin_amdgcn_sched_barrier(0);
   pr.finish(pro, b, K, xs, red, blockIdx.x == 0 && blockIdx.y == 0);
   pack_x<WQ, KS>(xs, xp);
 
