@@ -25,6 +25,13 @@ import synth
 pytestmark = pytest.mark.gpu
 
 TOL = {"bf16": 2e-2, "w4a16": 3e-2}
+# The E2B bf16 workload's own logits move by this fraction of max |logit| when
+# every cached K/V element changes by 3e-6 relative before its bf16 rounding
+# (test_workload_conditioning.py::test_e2b_bf16_cache_rounding_sensitivity):
+# two logits closer than twice that can trade places in any implementation
+# that is not bit-identical to the fp64 oracle.  (The W4A16 workload moves by
+# ~1e-5 under the same change: its rule stays the fixed 1e-2 gap.)
+E2B_BF16_DRIFT = 5.5e-3
 
 
 @pytest.fixture(scope="module")
@@ -43,8 +50,9 @@ def _engine(cfg, quant, w, max_batch, max_ctx, max_rows, kv_quant="bf16"):
 
 
 class Stats:
-    def __init__(self, quant):
+    def __init__(self, quant, drift=0.0):
         self.tol, self.n, self.agree, self.worst = TOL[quant], 0, 0, 0.0
+        self.drift = drift   # workload sensitivity (see E2B_BF16_DRIFT)
         self.flips = []
         self.min_gap = float("inf")
 
@@ -59,7 +67,10 @@ class Stats:
         top2 = np.sort(ref_logits)[-2:]
         gap = top2[1] - top2[0]
         self.min_gap = min(self.min_gap, float(gap))
-        if gap > 1e-2:
+        # a different token is a near-tie below a 1e-2 gap, or below twice the
+        # workload's pinned drift (relative to max |logit|) where that is larger
+        gap_min = max(1e-2, 2 * self.drift * float(np.max(np.abs(ref_logits))))
+        if gap > gap_min:
             assert got_tok == ref_tok, f"{where}: token {got_tok} != oracle {ref_tok} (gap {gap:.3e})"
         e = float(np.max(np.abs(got - ref_logits)))
         assert ref_logits[got_tok] >= ref_logits[ref_tok] - 2 * e, \
@@ -413,7 +424,7 @@ def test_int8_cache_contents(torch_dev):
     assert exact >= 0.99 * total, (exact, total)
 
 
-def _continuous_batching(torch, eng, orc, V, prompts, lengths, quant, label):
+def _continuous_batching(torch, eng, orc, V, prompts, lengths, quant, label, drift=0.0):
     """Serve `prompts` (request i wants lengths[i] decode steps) through the
     paged cache with at most eng.max_batch live rows: admit a request when a
     slot and its pages are free (reserve, prefill into its slot), decode the
@@ -421,7 +432,7 @@ def _continuous_batching(torch, eng, orc, V, prompts, lengths, quant, label):
     the last live slot into its place.  Every live row of every step is
     compared with the oracle's own run of that request (oracle sequence i)."""
     dev = eng.device
-    st = Stats(quant)
+    st = Stats(quant, drift)
     pending = list(range(len(prompts)))
     live = []                      # per row: [request, next token, position, steps done]
     admitted_late = 0
@@ -671,7 +682,7 @@ def test_e2b_greedy_512_parity(torch_dev, e2b_model, e2b_engine):
         assert int(pos.item()) == P + S
         g.close()
     orc = oracle.Oracle(cfg, quant, w, 1, P + S + 1)
-    st = Stats(quant)
+    st = Stats(quant, E2B_BF16_DRIFT if quant == "bf16" else 0.0)
     _, ref = orc.prefill(0, prompt)
     st.add(pre_l, pre_t, ref, "prefill (last row)")
     for i in range(S):
@@ -722,7 +733,7 @@ def test_e2b_batch64_prefill_graph_parity(torch_dev, e2b_model, e2b_engine):
         eng.check()
         g.close()
     orc = oracle.Oracle(cfg, quant, w, len(rows), P + S + 1)
-    st = Stats(quant)
+    st = Stats(quant, E2B_BF16_DRIFT if quant == "bf16" else 0.0)
     for j, b in enumerate(rows):
         _, ref = orc.prefill(j, prompts[b])
         st.add(pre[b], int(pre_t[b]), ref, f"prefill seq {b}")
@@ -838,7 +849,7 @@ def test_e2b_paged_continuous_batching(torch_dev):
     prompts = [synth.tokens(n, 80 + i, V) for i, n in enumerate(plen)]
     eng = Engine(cfg, "bf16", w, max_batch=3, max_ctx=512, max_rows=128, n_pages=5)
     orc = oracle.Oracle(cfg, "bf16", w, len(prompts), 512)
-    _continuous_batching(torch, eng, orc, V, prompts, olen, "bf16", "e2b bf16 paged")
+    _continuous_batching(torch, eng, orc, V, prompts, olen, "bf16", "e2b bf16 paged", E2B_BF16_DRIFT)
 
 
 @pytest.mark.parametrize("B", [1, 8])
