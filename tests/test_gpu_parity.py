@@ -16,6 +16,8 @@ Tolerances (fixed by the workload definition, not tuned):
     the measured error e = max |GPU - oracle|: oracle[gpu token] >=
     max(oracle) - 2e.
 """
+import sys
+
 import numpy as np
 import pytest
 
@@ -32,6 +34,27 @@ TOL = {"bf16": 2e-2, "w4a16": 3e-2}
 # that is not bit-identical to the fp64 oracle.  (The W4A16 workload moves by
 # ~1e-5 under the same change: its rule stays the fixed 1e-2 gap.)
 E2B_BF16_DRIFT = 5.5e-3
+
+
+_CAPMAN = None
+
+
+@pytest.fixture(scope="session", autouse=True)
+def _progress_channel(request):
+    global _CAPMAN
+    _CAPMAN = request.config.pluginmanager.getplugin("capturemanager")
+    yield
+
+
+def progress(msg):
+    """A progress line of a long test, written past pytest's output capture:
+    a run that prints nothing for minutes is taken to be hung."""
+    if _CAPMAN is None:
+        print(msg, flush=True)
+        return
+    with _CAPMAN.global_and_fixture_disabled():
+        sys.stderr.write(msg + "\n")
+        sys.stderr.flush()
 
 
 @pytest.fixture(scope="module")
@@ -580,6 +603,7 @@ def e2b_weights(quant, embed_quant="bf16"):
     """Seed-0 E2B tensors, generated once per format for the whole module."""
     key = (quant, embed_quant)
     if key not in _E2B_WEIGHTS:
+        progress(f"[e2b] generating seed-0 {quant} weights ({embed_quant} vocabulary tables)")
         _E2B_WEIGHTS[key] = synth.generate(synth.get_config("e2b"), quant, seed=0, embed_quant=embed_quant)
     return _E2B_WEIGHTS[key]
 
@@ -659,7 +683,7 @@ def test_e2b_greedy_512_parity(torch_dev, e2b_model, e2b_engine):
     else:
         quant_label = quant
     prompt = synth.tokens(P, 1, V)
-    print(f"\n[e2b {quant_label} B=1] GPU: {P}-token prefill, {S} graph steps", flush=True)
+    progress(f"\n[e2b {quant_label} B=1] GPU: {P}-token prefill, {S} graph steps")
     s = torch.cuda.Stream(dev)
     gl = np.empty((S, V), np.float32)
     fed, gt = [], []
@@ -689,8 +713,8 @@ def test_e2b_greedy_512_parity(torch_dev, e2b_model, e2b_engine):
         _, ref, _ = orc.step(0, fed[i], P + i)
         st.add(gl[i], gt[i], ref, f"step {i} (position {P + i})")
         if i % 64 == 63:
-            print(f"[e2b {quant_label} B=1] oracle at step {i + 1}/{S}: worst rel err {st.worst:.3e}, "
-                  f"agree {st.agree}/{st.n}", flush=True)
+            progress(f"[e2b {quant_label} B=1] oracle at step {i + 1}/{S}: worst rel err {st.worst:.3e}, "
+                     f"agree {st.agree}/{st.n}")
     orc.close()
     st.finish(f"e2b {quant_label} B=1, {P}-token prompt + {S} steps", min_agree=0.99)
 
@@ -737,7 +761,7 @@ def test_e2b_batch64_prefill_graph_parity(torch_dev, e2b_model, e2b_engine):
     for j, b in enumerate(rows):
         _, ref = orc.prefill(j, prompts[b])
         st.add(pre[b], int(pre_t[b]), ref, f"prefill seq {b}")
-        print(f"[e2b {quant} B=64] oracle prefill of sequence {b} done", flush=True)
+        progress(f"[e2b {quant} B=64] oracle prefill of sequence {b} done")
     for i in range(S):
         for j, b in enumerate(rows):
             _, ref, _ = orc.step(j, int(fed[i][b]), P + i)
@@ -754,6 +778,7 @@ def _seed_cache(torch, eng, cfg, T_of, orc=None, orc_rows=()):
     generator, not from either implementation."""
     dev = eng.device
     smap = eng.model.kv_share_map()
+    progress(f"[seeded caches] contexts {T_of}")
     for l in range(cfg["num_hidden_layers"]):
         if smap[l] != l:
             continue
@@ -790,6 +815,7 @@ def _graph_decode_vs_oracle(torch, eng, orc, cfg, quant, T_of, rows, steps, seed
             for j, b in enumerate(rows):
                 _, ref, _ = orc.step(j, int(fed[b]), T_of[b] + i)
                 st.add(got_l[b], int(got_t[b]), ref, f"step {i} row {b} (position {T_of[b] + i})")
+            progress(f"[{quant} B={B} seeded caches] step {i + 1}/{steps} checked")
         g.close()
     st.finish(f"{quant} B={B} from seeded caches")
 
