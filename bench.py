@@ -142,7 +142,7 @@ def kernel_pattern(kind, quant, batch, embed_quant="bf16"):
     if batch == 1:
         return rf"void e2b::k_gemv<{wq}, \d+, \d+, {tag}>"
     mt = 1 if batch <= 16 else (2 if batch <= 32 else 4)
-    return rf"void e2b::k_gemm<{wq}, \d+, {mt}, \d+, {tag}>"
+    return rf"void e2b::k_gemm<{wq}, \d+, {mt}, \d+, {tag}, \d+>"
 
 
 def spin(torch, ms):

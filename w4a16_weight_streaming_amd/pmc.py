@@ -7,7 +7,14 @@ dispatches):
 
     python -m w4a16_weight_streaming_amd.pmc FETCH_DIR WRITE_DIR OUT.json
 
-Both counters are reported in KiB per dispatch.  Each is scaled by what it
+or, for any other counters (one or more `--pmc` runs):
+
+    python -m w4a16_weight_streaming_amd.pmc --counters PATTERN DIR [DIR ...]
+
+which prints, as a markdown table, the mean per-dispatch value of every
+counter found under the DIRs for each kernel whose name contains PATTERN.
+
+Both FETCH_SIZE and WRITE_SIZE are reported in KiB per dispatch.  Each is scaled by what it
 reads for the reference copy (1 GiB read, 1 GiB written), so the factors
 absorb any unit or sampling convention of the counters.  OUT.json records the
 mean per-dispatch values of every kernel of this library, the two factors,
@@ -87,7 +94,36 @@ def main(fetch_dir, write_dir, out):
           f"for 1 GiB each; {len(res['kernels'])} kernels -> {out}")
 
 
+def counters_table(pattern, dirs):
+    """Markdown table: mean per-dispatch value of each counter, per kernel
+    whose name contains `pattern`."""
+    per = defaultdict(lambda: defaultdict(lambda: defaultdict(float)))  # kernel -> counter -> dispatch
+    for d in dirs:
+        for fn in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(fn, newline="") as f:
+                for row in csv.DictReader(f):
+                    name = row["Kernel_Name"].strip()
+                    if pattern not in name:
+                        continue
+                    disp = row.get("Dispatch_Id") or row.get("Correlation_Id")
+                    per[short(name)][row["Counter_Name"].strip()][disp] += float(row["Counter_Value"])
+    names = sorted({c for k in per.values() for c in k})
+    lines = ["| kernel | dispatches | " + " | ".join(names) + " |",
+             "|---|---:|" + "---:|" * len(names)]
+    for k in sorted(per):
+        n = max(len(v) for v in per[k].values())
+        cells = []
+        for c in names:
+            v = per[k].get(c, {})
+            cells.append(f"{sum(v.values()) / len(v):.4g}" if v else "")
+        lines.append(f"| `{k}` | {n} | " + " | ".join(cells) + " |")
+    return "\n".join(lines)
+
+
 if __name__ == "__main__":
-    if len(sys.argv) != 4:
+    if len(sys.argv) >= 4 and sys.argv[1] == "--counters":
+        print(counters_table(sys.argv[2], sys.argv[3:]))
+    elif len(sys.argv) == 4:
+        main(*sys.argv[1:])
+    else:
         raise SystemExit(__doc__)
-    main(*sys.argv[1:])
