@@ -862,8 +862,12 @@ __device__ void attn_chunk(const Rows& R, const AttnArgs& a, int c, int r) {
       for (int i = 0; i < DPL; ++i) o[h][i] = 0.f;
 
     for (int gi = wave; gi < ngroups; gi += 4) {
+      // the next group's reads, if this wave has one (a wave's last group
+      // must not wait for reads that nothing uses)
+      const bool more = gi + 4 < ngroups;
       G nxt;
-      if constexpr (DPL < 8) load_group(gi + 4, nxt);  // hd 512: registers too tight
+      if constexpr (DPL < 8)
+        if (more) load_group(gi + 4, nxt);  // hd 512: registers too tight
       const int key0 = j0 + 4 * gi;
       // key / value row k of the group as fp32 (unpacked when used)
       auto row_of = [&](int k, int which, float (&x)[DPL]) {
@@ -925,8 +929,10 @@ __device__ void attn_chunk(const Rows& R, const AttnArgs& a, int c, int r) {
       }
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
       __builtin_amdgcn_wave_barrier();
-      if constexpr (DPL < 8) cur = nxt;
-      else if (gi + 4 < ngroups) load_group(gi + 4, cur);
+      if (more) {
+        if constexpr (DPL < 8) cur = nxt;
+        else load_group(gi + 4, cur);
+      }
     }
     // merge the four waves: per head max M, then rescale and sum.  Each wave
     // parks its o in LDS (wave 0 in qs, whose queries are in registers); the
