@@ -28,11 +28,17 @@ Prints one JSON line on stdout (progress goes to stderr):
              this device sustains (best of 5)
   kernel_kinds   per-launch time and achieved GB/s of every profiled kind
              (attention: unique and logical K/V bytes)
-  prefill    the 128-token prompt through e2b_prefill (one 128-row pass): ms
+  prefill    the 128-token prompt through e2b_prefill (one 128-row pass,
+             through the first greedy token): ms, = time to first token on
+             the device (median of 5 at batch 1; each sequence once at 64)
   cpu_baseline   the fp64 oracle on this host's cores (and on one core),
              teacher-forced on the GPU's tokens, over a bounded sample
-  also       W4A16 B=1, bf16 and W4A16 B=64, and the long-context workload
-             (W4A16, B=1 and 8, contexts 500 / 4,000 / 8,000) unless --no-aux
+  also       W4A16 B=1 (bf16 and int4 vocabulary tables), bf16 and W4A16
+             B=64, serving uneven requests (continuous vs lockstep
+             batching), and the long-context workload (W4A16, bf16 and int8
+             caches, B=1 and 8, contexts 500 / 4,000 / 8,000, with each
+             500-token chunk's prefill and the prefill of the whole context so
+             far) unless --no-aux (--no-long: without serving and long context)
 
 --long: the long-context workload alone (W4A16, batch 1 or 8 via --batch,
 context grown 500 -> 8,000 by 500-token prefill chunks, 64 timed decode
@@ -213,8 +219,11 @@ def measure(cfg, quant, B, P, K, W, prof_steps, repeats, eager=False, cpu_steps=
         pdev = [torch.from_numpy(p).to(dev) for p in prompts]
         eng.prefill(0, pdev[0], 0, tok[0:1])       # untimed first pass
         stream.synchronize()
+        # prefill = time to first token on the device: the prompt's passes
+        # through the first greedy token (a lone sequence is prefilled 5 times
+        # over the same positions; each of B sequences once)
         pre_ms = []
-        for b in range(B):
+        for b in ([0] * 5 if B == 1 else range(B)):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
             eng.prefill(b, pdev[b], 0, tok[b:b + 1])
@@ -280,7 +289,11 @@ def measure(cfg, quant, B, P, K, W, prof_steps, repeats, eager=False, cpu_steps=
            "repeats": {"n": repeats, "loop_ms": [round(x, 3) for x in loops], "median_ms": round(ms, 3),
                        "iqr_ms": [round(q1, 3), round(q3, 3)]},
            "prefill": {"tokens": P, "rows_per_pass": min(128, P), "ms_median": round(statistics.median(pre_ms), 3),
-                       "ms_min": round(min(pre_ms), 3), "sequences": B}}
+                       "ms_iqr": [round(x, 3) for x in quantiles(pre_ms)[::2]],
+                       "ms_min": round(min(pre_ms), 3), "timings": len(pre_ms), "sequences": B,
+                       "ttft_ms": round(statistics.median(pre_ms), 3),
+                       "ttft": "device time from the first prefill kernel to the first greedy token, "
+                               "prompt resident in HBM"}}
     if prof:
         log(f"[{label}] kernel kinds: " + ", ".join(
             f"{k}: {v['ms'] * 1e3:.1f} us x{v['launches'] // prof_steps} = {v['bytes'] / (v['ms'] / 1e3) / 1e9:.0f} GB/s"
@@ -371,6 +384,7 @@ def long_context(quant, B, lengths=None, steps=64, chunk=500, top=8000, kv_quant
     dev = eng.device
     stream = torch.cuda.Stream(dev)
     rows = []
+    cum_ms = 0.0  # prefill of the context so far, per sequence (time to first token of that prompt)
     with torch.cuda.stream(stream):
         tok = torch.zeros(B, dtype=torch.int32, device=dev)
         pos = torch.zeros(B, dtype=torch.int32, device=dev)
@@ -387,6 +401,7 @@ def long_context(quant, B, lengths=None, steps=64, chunk=500, top=8000, kv_quant
             e1.record(stream)
             eng.check()
             pre_ms = e0.elapsed_time(e1) / B
+            cum_ms += pre_ms
             if lengths is not None and L not in lengths:
                 continue
             tok_ctx = tok.clone()
@@ -408,7 +423,7 @@ def long_context(quant, B, lengths=None, steps=64, chunk=500, top=8000, kv_quant
             sb, _ = step_bytes(cfg, quant, B, list(range(L, L + steps)), kv_quant=kv_quant)
             rows.append({"context": L, "tok_s": round(B / (ms / 1e3), 2), "ms_per_step": round(ms, 4),
                          "step_bytes": int(sb), "frac": round(sb / (ms / 1e3) / HBM_PEAK, 4),
-                         "prefill_chunk_ms": round(pre_ms, 3)})
+                         "prefill_chunk_ms": round(pre_ms, 3), "prefill_to_here_ms": round(cum_ms, 2)})
             log(f"[long {quant} {kv_quant} cache B={B}] context {L}: {rows[-1]['tok_s']} tok/s, {ms:.3f} ms/step, "
                 f"{chunk}-token chunk prefill {pre_ms:.2f} ms per sequence")
             tok.copy_(tok_ctx)
