@@ -861,6 +861,57 @@ def test_e2b_w4a16_int8_cache_parity(torch_dev):
     st.finish(f"e2b w4a16 int8 cache B=1, {P}-token prompt + {S} steps", min_agree=0.99)
 
 
+def test_e2b_w4a16_int8_cache_batched_parity(torch_dev):
+    """The int8 K/V cache under batched decode at full size: 4 sequences of
+    uneven prompts (40, 64, 17, 90 tokens) prefilled into their slots, then 12
+    steps of the captured 4-row decode graph (each row's attention split over
+    chunks and merged by the combine kernel, each row writing its own int8 K/V
+    row); rows 0 and 3 against the oracle with the same cache."""
+    torch, dev = torch_dev
+    cfg = synth.get_config("e2b")
+    w = e2b_weights("w4a16")
+    V, S = cfg["vocab_size"], 12
+    lens = [40, 64, 17, 90]
+    rows = [0, 3]
+    B = len(lens)
+    eng = _engine(cfg, "w4a16", w, B, max(lens) + S + 8, 128, kv_quant="int8")
+    prompts = [synth.tokens(n, 40 + b, V) for b, n in enumerate(lens)]
+    s = torch.cuda.Stream(dev)
+    pre, gl, gt, fed = {}, np.empty((S, len(rows), V), np.float32), [], []
+    with torch.cuda.stream(s):
+        tok = torch.zeros(B, dtype=torch.int32, device=dev)
+        l1 = torch.zeros(1, V, dtype=torch.float32, device=dev)
+        for b in range(B):
+            eng.prefill(b, torch.from_numpy(prompts[b]).to(dev), 0, tok[b:b + 1], l1)
+            if b in rows:
+                pre[b] = l1.cpu().numpy()[0].copy()
+        eng.check()
+        pre_t = tok.cpu().numpy().copy()
+        pos = torch.tensor(lens, dtype=torch.int32, device=dev)
+        lg = torch.zeros(B, V, dtype=torch.float32, device=dev)
+        g = eng.capture(tok, pos, tok, lg, advance=True)
+        for i in range(S):
+            fed.append(tok.cpu().numpy().copy())
+            g.replay()
+            s.synchronize()
+            gl[i] = lg[rows].cpu().numpy()
+            gt.append(tok.cpu().numpy().copy())
+        eng.check()
+        g.close()
+    orc = oracle.Oracle(cfg, "w4a16", w, len(rows), max(lens) + S + 1, kv_quant="int8")
+    st = Stats("w4a16")
+    for j, b in enumerate(rows):
+        _, ref = orc.prefill(j, prompts[b])
+        st.add(pre[b], int(pre_t[b]), ref, f"prefill seq {b}")
+        progress(f"[e2b w4a16 int8 cache B={B}] oracle prefill of sequence {b} done")
+    for i in range(S):
+        for j, b in enumerate(rows):
+            _, ref, _ = orc.step(j, int(fed[i][b]), lens[b] + i)
+            st.add(gl[i, j], int(gt[i][b]), ref, f"step {i} seq {b} (position {lens[b] + i})")
+    orc.close()
+    st.finish(f"e2b w4a16 int8 cache B={B}, sequences {rows}")
+
+
 def test_e2b_paged_continuous_batching(torch_dev):
     """Full E2B shape (bf16 weights: the paging is the same for both formats
     and the bf16 oracle is the faster), paged cache: 5 requests (prompts 150,
