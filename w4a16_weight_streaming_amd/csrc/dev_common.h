@@ -433,6 +433,23 @@ __device__ __forceinline__ void split_pair(float a, float b, uint32_t& hi, uint3
   lo = la | (lb << 16);
 }
 
+// Writes x[i0 .. i0+7] as bf16 hi/lo and, from the four threads that cover
+// one 32-group (consecutive threads, all active together), its group sum.
+__device__ __forceinline__ void emit8(const float (&v)[8], uint16_t* xh, uint16_t* xl, float* xg,
+                                      int i0) {
+  uint32_t h[4], l[4];
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    split_pair(v[2 * j], v[2 * j + 1], h[j], l[j]);
+    s += (bf2f(h[j]) + bf2f(l[j])) + (bf2f(h[j] >> 16) + bf2f(l[j] >> 16));
+  }
+  *reinterpret_cast<uint4*>(xh + i0) = make_uint4(h[0], h[1], h[2], h[3]);
+  *reinterpret_cast<uint4*>(xl + i0) = make_uint4(l[0], l[1], l[2], l[3]);
+  s = group_sum<4>(s);
+  if ((threadIdx.x & 3) == 0) xg[i0 / 32] = s;
+}
+
 // LDS words of the packed input: bf16 layout 8 words per (chunk, lane slot)
 // [4 hi pairs | 4 lo pairs]; W4A16 layout 36 words per 32-group
 // [16 hi pairs | 16 lo pairs | group sum | pad].

@@ -109,6 +109,7 @@ struct Prologue {
   int nchunk = 0;                    // kAttnMerge: attention chunks written per head
   int slice = 0;                     // kAttnMerge: head dim (the K slice of one head)
   float eps = 1e-6f;
+  int alt = 0;                       // kPrepared: the second prepared buffer (a product's epilogue wrote it)
 };
 
 // Output of a matrix-vector product: y [nks][rows][N] fp32 partial sums over
@@ -119,6 +120,14 @@ struct Epilogue {
   float* logits = nullptr;      // argmax mode: optional fp32 [rows, N]
   float* cand_val = nullptr;    // [rows][gridDim.x]
   int32_t* cand_idx = nullptr;  // [rows][gridDim.x]
+  // batched gate/up product ([W_g; W_u], N = 2 * gi): each block pairs gate
+  // and up columns and writes gelu_tanh(gate) * up, the down product's input,
+  // in prepared form (bf16 hi/lo [rows][gi], group sums [rows][gi / 32])
+  // instead of y
+  uint16_t* gh = nullptr;
+  uint16_t* gl = nullptr;
+  float* gg = nullptr;
+  int gi = 0;
 };
 
 // Per-row RoPE cos/sin for both layer types, built once per pass by the
@@ -221,8 +230,13 @@ hipError_t launch_xprep(const Prologue& p, int rows, int K, uint16_t* xh, uint16
 struct GemmPlan {
   int nt = 1;   // 16-column tiles per wave (block covers 64 * nt columns)
   int nks = 1;  // K slices (partials written [nks][rows][N])
+  int mt = 0;   // 16-row tiles per block at most (0: from the row count alone)
 };
 GemmPlan gemm_plan(int quant, int N, int K, bool partial_ok);
+// The gate/up product with the GeGLU in its epilogue (I gate and I up rows)
+// for a pass of `rows` rows: no K slices; nt = 0 where I does not split into
+// whole blocks.
+GemmPlan gemm_plan_geglu(int quant, int I, int K, int rows);
 // Input rows of a batched product: either prepared by k_xprep (bf16 hi/lo
 // [rows][K] + fp32 group sums [rows][K/32]) or, for a plain input (kPlain,
 // one partial), fp32 rows [rows][lda] read and split by the product itself.

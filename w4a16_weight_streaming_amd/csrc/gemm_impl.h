@@ -68,8 +68,13 @@ __global__ __launch_bounds__(256, 2) void k_gemm(Lin W, int rows, GemmA A, int K
   const int K = W.K, N = W.N;
   const int mrows = min(MB, rows - m0);
   int ncol[NT];
+  // (GeGLU epilogue: waves 0-1 take gate columns c0 .. c0 + 32 NT - 1, waves
+  // 2-3 the matching up columns gi + c0 ..)
+  const bool geglu = TAG == kTagGateUp && epi.gh != nullptr;
 #pragma unroll
-  for (int j = 0; j < NT; ++j) ncol[j] = blockIdx.x * 64 * NT + wave * 16 * NT + 16 * j + (lane & 15);
+  for (int j = 0; j < NT; ++j)
+    ncol[j] = geglu ? (wave >> 1) * epi.gi + blockIdx.x * 32 * NT + (wave & 1) * 16 * NT + 16 * j + (lane & 15)
+                    : blockIdx.x * 64 * NT + wave * 16 * NT + 16 * j + (lane & 15);
 
   f32x4_t acc[MT][NT];
 #pragma unroll
@@ -304,6 +309,38 @@ __global__ __launch_bounds__(256, 2) void k_gemm(Lin W, int rows, GemmA A, int K
     if constexpr (D > 3) chunk(C3(), c + 3);
   }
 
+  if constexpr (TAG == kTagGateUp) {
+    if (geglu) {
+      // gate and up tiles side by side in LDS (the A stages are free: every
+      // wave has passed the last chunk's barrier), then gelu_tanh(gate) * up
+      // for 8 consecutive columns per thread, emitted as the down product's
+      // prepared input (four consecutive threads cover one 32-column group)
+      constexpr int SP = 64 * NT + 4;
+      static_assert(sizeof(sa) >= sizeof(float) * MB * SP, "GeGLU tile fits in the A stages");
+      float* ep = reinterpret_cast<float*>(&sa[0][0][0][0]);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < NT; ++j)
+            ep[(16 * mt + 4 * kq + i) * SP + (wave >> 1) * 32 * NT + (wave & 1) * 16 * NT + 16 * j + (lane & 15)] =
+                acc[mt][j][i];
+      __syncthreads();
+      const int c0 = blockIdx.x * 32 * NT, I = epi.gi;
+      for (int it = t; it < MB * 4 * NT; it += 256) {
+        const int m = it / (4 * NT), c8 = it % (4 * NT);
+        if (m >= mrows) continue;  // (the four threads of a group share m)
+        const float* g = ep + m * SP + 8 * c8;
+        float v[8];
+#pragma unroll
+        for (int x = 0; x < 8; ++x) v[x] = gelu_tanh(g[x]) * g[32 * NT + x];
+        const size_t r = (size_t)(m0 + m);
+        emit8(v, epi.gh + r * I, epi.gl + r * I, epi.gg + r * (I / 32), c0 + 8 * c8);
+      }
+      return;
+    }
+  }
   if (!epi.argmax) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
@@ -356,13 +393,14 @@ __global__ __launch_bounds__(256, 2) void k_gemm(Lin W, int rows, GemmA A, int K
 }
 
 template <int WQ, int NT, int FA, int TAG>
-static hipError_t run_gemm(const Lin& W, int rows, const GemmA& A, int nks, const Epilogue& epi,
+static hipError_t run_gemm(const Lin& W, int rows, const GemmA& A, int nks, int mtmax, const Epilogue& epi,
                            int* nblk, hipStream_t st) {
   const int nbx = (W.N + 64 * NT - 1) / (64 * NT);
   if (nblk) *nblk = nbx;
-  // m-tiles per block from the row count (a row's arithmetic does not depend
-  // on which rows share its block)
-  const int mt = rows <= 16 ? 1 : (rows <= 32 ? 2 : 4);
+  // m-tiles per block from the row count, at most mtmax where the plan sets
+  // it (a row's arithmetic does not depend on which rows share its block)
+  int mt = rows <= 16 ? 1 : (rows <= 32 ? 2 : 4);
+  if (mtmax > 0 && mt > mtmax) mt = mtmax >= 4 ? 4 : (mtmax >= 2 ? 2 : 1);
   dim3 grid(nbx, nks, (rows + 16 * mt - 1) / (16 * mt));
   // a W4A16 matrix without the tiled copy (a shape the copy does not cover,
   // through the matvec entry point) takes the one-word-per-k-step loads
@@ -385,24 +423,24 @@ static hipError_t run_gemm(const Lin& W, int rows, const GemmA& A, int nks, cons
 }
 
 template <int WQ, int NT>
-static hipError_t gemm_tag(int tag, const Lin& W, int rows, const GemmA& A, int nks,
+static hipError_t gemm_tag(int tag, const Lin& W, int rows, const GemmA& A, int nks, int mtmax,
                            const Epilogue& epi, int* nblk, hipStream_t st) {
   if (A.a) {  // fp32 input rows: the products whose input is a plain copy
     switch (tag) {
-      case kTagO: return run_gemm<WQ, NT, 1, kTagO>(W, rows, A, nks, epi, nblk, st);
-      case kTagPleModel: return run_gemm<WQ, NT, 1, kTagPleModel>(W, rows, A, nks, epi, nblk, st);
-      default: return run_gemm<WQ, NT, 1, kTagOther>(W, rows, A, nks, epi, nblk, st);
+      case kTagO: return run_gemm<WQ, NT, 1, kTagO>(W, rows, A, nks, mtmax, epi, nblk, st);
+      case kTagPleModel: return run_gemm<WQ, NT, 1, kTagPleModel>(W, rows, A, nks, mtmax, epi, nblk, st);
+      default: return run_gemm<WQ, NT, 1, kTagOther>(W, rows, A, nks, mtmax, epi, nblk, st);
     }
   }
   switch (tag) {
-    case kTagO: return run_gemm<WQ, NT, 0, kTagO>(W, rows, A, nks, epi, nblk, st);
-    case kTagQkv: return run_gemm<WQ, NT, 0, kTagQkv>(W, rows, A, nks, epi, nblk, st);
-    case kTagGateUp: return run_gemm<WQ, NT, 0, kTagGateUp>(W, rows, A, nks, epi, nblk, st);
-    case kTagDown: return run_gemm<WQ, NT, 0, kTagDown>(W, rows, A, nks, epi, nblk, st);
-    case kTagPleGate: return run_gemm<WQ, NT, 0, kTagPleGate>(W, rows, A, nks, epi, nblk, st);
-    case kTagPleProj: return run_gemm<WQ, NT, 0, kTagPleProj>(W, rows, A, nks, epi, nblk, st);
-    case kTagLmHead: return run_gemm<WQ, NT, 0, kTagLmHead>(W, rows, A, nks, epi, nblk, st);
-    default: return run_gemm<WQ, NT, 0, kTagOther>(W, rows, A, nks, epi, nblk, st);
+    case kTagO: return run_gemm<WQ, NT, 0, kTagO>(W, rows, A, nks, mtmax, epi, nblk, st);
+    case kTagQkv: return run_gemm<WQ, NT, 0, kTagQkv>(W, rows, A, nks, mtmax, epi, nblk, st);
+    case kTagGateUp: return run_gemm<WQ, NT, 0, kTagGateUp>(W, rows, A, nks, mtmax, epi, nblk, st);
+    case kTagDown: return run_gemm<WQ, NT, 0, kTagDown>(W, rows, A, nks, mtmax, epi, nblk, st);
+    case kTagPleGate: return run_gemm<WQ, NT, 0, kTagPleGate>(W, rows, A, nks, mtmax, epi, nblk, st);
+    case kTagPleProj: return run_gemm<WQ, NT, 0, kTagPleProj>(W, rows, A, nks, mtmax, epi, nblk, st);
+    case kTagLmHead: return run_gemm<WQ, NT, 0, kTagLmHead>(W, rows, A, nks, mtmax, epi, nblk, st);
+    default: return run_gemm<WQ, NT, 0, kTagOther>(W, rows, A, nks, mtmax, epi, nblk, st);
   }
 }
 
@@ -411,11 +449,14 @@ hipError_t launch_gemm_q(int tag, const Lin& W, int rows, const GemmA& A, const 
                          const Epilogue& epi, int* nblk, hipStream_t st) {
   const int nks = plan.nks;
   if constexpr (WQ) {
-    if (plan.nt == 4) return gemm_tag<1, 4>(tag, W, rows, A, nks, epi, nblk, st);
-    if (plan.nt == 2) return gemm_tag<1, 2>(tag, W, rows, A, nks, epi, nblk, st);
+    if (plan.nt == 4) return gemm_tag<1, 4>(tag, W, rows, A, nks, plan.mt, epi, nblk, st);
+    if (plan.nt == 2) return gemm_tag<1, 2>(tag, W, rows, A, nks, plan.mt, epi, nblk, st);
+    // (one tile per wave: the gate/up product with the GeGLU epilogue only)
+    if (plan.nt == 1 && tag == kTagGateUp && !A.a)
+      return run_gemm<1, 1, 0, kTagGateUp>(W, rows, A, nks, plan.mt, epi, nblk, st);
   } else {
-    if (plan.nt == 2) return gemm_tag<0, 2>(tag, W, rows, A, nks, epi, nblk, st);
-    if (plan.nt == 1) return gemm_tag<0, 1>(tag, W, rows, A, nks, epi, nblk, st);
+    if (plan.nt == 2) return gemm_tag<0, 2>(tag, W, rows, A, nks, plan.mt, epi, nblk, st);
+    if (plan.nt == 1) return gemm_tag<0, 1>(tag, W, rows, A, nks, plan.mt, epi, nblk, st);
   }
   return hipErrorInvalidValue;
 }

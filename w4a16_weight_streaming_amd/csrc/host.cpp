@@ -282,7 +282,7 @@ Lin resolve(const e2b_model* m, const LinOff& o) {
 // ---- workspace layout ------------------------------------------------------
 struct Ws {
   size_t err, rope, h0, h1, tokple, u, pli, qkv, part, attn, oo, gu, dn, pgy, ppo, cv, ci, xh, xl, xg,
-      total;
+      xh2, xl2, xg2, total;
   int ncand;  // argmax candidates per row
 };
 
@@ -301,11 +301,12 @@ Ws ws_layout(const e2b_model* m, int R) {
     return std::max(e2b::gemv_splits(K), e2b::gemm_plan(m->quant, N, K, true).nks);
   };
   const int H = m->H, P = m->P, LPn = m->L * m->P;
-  int Kmax = std::max(H, P);
+  int Kmax = std::max(H, P), Imax = 0;
   size_t qkv_f = 0, gu_f = 0, oo_f = 0, dn_f = 0, pgy_f = 0, ppo_f = 0;
   for (const LayerInfo& y : m->li) {
     const int nqkv = (m->nq + (y.src == &y - &m->li[0] ? 2 : 0)) * y.hd;
     Kmax = std::max(Kmax, std::max(y.I, m->nq * y.hd));
+    Imax = std::max(Imax, y.I);
     qkv_f = std::max(qkv_f, (size_t)parts(nqkv, H) * nqkv);
     gu_f = std::max(gu_f, (size_t)parts(2 * y.I, H) * 2 * y.I);
     oo_f = std::max(oo_f, (size_t)parts(H, m->nq * y.hd) * H);
@@ -339,8 +340,13 @@ Ws ws_layout(const e2b_model* m, int R) {
     w.xh = take(2 * (size_t)R * Kmax);
     w.xl = take(2 * (size_t)R * Kmax);
     w.xg = take(f * (size_t)R * (Kmax / 32));
+    // the down product's input, written by the gate/up product's epilogue
+    // while that product still reads its own input from xh / xl / xg
+    w.xh2 = take(2 * (size_t)R * Imax);
+    w.xl2 = take(2 * (size_t)R * Imax);
+    w.xg2 = take(f * (size_t)R * (Imax / 32));
   } else {
-    w.xh = w.xl = w.xg = 0;
+    w.xh = w.xl = w.xg = w.xh2 = w.xl2 = w.xg2 = 0;
   }
   w.total = cur;
   return w;
@@ -423,7 +429,8 @@ hipError_t matmul(e2b_model* m, int quant, int tag, const Lin& W, int rows, bool
     if (prof) e2b::set_launch_events(mk.a, mk.b);
     e = e2b::launch_gemv(quant, gemv_tag, W, rows, pr, ep, 0, nblk, st);
   } else {
-    const e2b::GemmPlan plan = e2b::gemm_plan(quant, W.N, W.K, partial_ok);
+    const e2b::GemmPlan plan = ep.gh ? e2b::gemm_plan_geglu(quant, W.N / 2, W.K, rows)
+                                     : e2b::gemm_plan(quant, W.N, W.K, partial_ok);
     splits = plan.nks;
     e2b::GemmA A;
     if (pr.kind == e2b::kPlain && pr.na == 1 && plan.nt <= 2) {  // read fp32 rows directly
@@ -431,9 +438,9 @@ hipError_t matmul(e2b_model* m, int quant, int tag, const Lin& W, int rows, bool
       A.kind = pr.kind;
       A.lda = pr.lda;
     } else if (pr.kind == e2b::kPrepared) {  // written in prepared form by the producer
-      A.xh = reinterpret_cast<uint16_t*>(ws + L.xh);
-      A.xl = reinterpret_cast<uint16_t*>(ws + L.xl);
-      A.xg = reinterpret_cast<float*>(ws + L.xg);
+      A.xh = reinterpret_cast<uint16_t*>(ws + (pr.alt ? L.xh2 : L.xh));
+      A.xl = reinterpret_cast<uint16_t*>(ws + (pr.alt ? L.xl2 : L.xl));
+      A.xg = reinterpret_cast<float*>(ws + (pr.alt ? L.xg2 : L.xg));
     } else {
       A.xh = reinterpret_cast<uint16_t*>(ws + L.xh);
       A.xl = reinterpret_cast<uint16_t*>(ws + L.xl);
@@ -497,6 +504,8 @@ int run_rows(e2b_model* m, const e2b::Rows& R, bool head, int head_row, float* d
   const uint16_t *pend_g = nullptr, *pend_s = nullptr;
   for (int l = 0; l < L; ++l) {
     const LayerInfo& y = m->li[l];
+    // batched: the GeGLU runs in the gate/up product's epilogue
+    const bool geglu_fold = bat && gemm_plan_geglu(q, y.I, H, n).nt > 0;
     const LayerDev& d = m->ld[l];
     const bool owns = y.src == l;
     int nd_qkv = 1, nd_o = 1, nd_gu = 1, nd_dn = 1, nd_pg = 1;  // K-slice partials written
@@ -617,6 +626,12 @@ int run_rows(e2b_model* m, const e2b::Rows& R, bool head, int head_row, float* d
       pr.eps = eps;
       Epilogue ep;
       ep.y = F(W.gu);
+      if (geglu_fold) {  // the product writes the down product's input itself
+        ep.gh = reinterpret_cast<uint16_t*>(ws + W.xh2);
+        ep.gl = reinterpret_cast<uint16_t*>(ws + W.xl2);
+        ep.gg = F(W.xg2);
+        ep.gi = y.I;
+      }
       CK(matmul(m, q, kTagGateUp, d.gu, n, bat, pr, ep, true, &nd_gu, nullptr, ws, W, st),
          "gate/up projection");
       std::swap(cur, oth);
@@ -628,6 +643,11 @@ int run_rows(e2b_model* m, const e2b::Rows& R, bool head, int head_row, float* d
       pr.lda = 2 * y.I;
       pr.na = nd_gu;
       pr.a_pstride = (size_t)n * 2 * y.I;
+      if (geglu_fold) {
+        pr = Prologue();
+        pr.kind = kPrepared;
+        pr.alt = 1;
+      }
       Epilogue ep;
       ep.y = F(W.dn);
       CK(matmul(m, q, kTagDown, d.down, n, bat, pr, ep, true, &nd_dn, nullptr, ws, W, st),

@@ -626,23 +626,6 @@ __device__ __forceinline__ void ld8_parts(const float* p, int n, size_t stride, 
   }
 }
 
-// Writes x[i0 .. i0+7] as bf16 hi/lo and, from the four threads that cover
-// one 32-group (consecutive threads, all active together), its group sum.
-__device__ __forceinline__ void emit8(const float (&v)[8], uint16_t* xh, uint16_t* xl, float* xg,
-                                      int i0) {
-  uint32_t h[4], l[4];
-  float s = 0.f;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    split_pair(v[2 * j], v[2 * j + 1], h[j], l[j]);
-    s += (bf2f(h[j]) + bf2f(l[j])) + (bf2f(h[j] >> 16) + bf2f(l[j] >> 16));
-  }
-  *reinterpret_cast<uint4*>(xh + i0) = make_uint4(h[0], h[1], h[2], h[3]);
-  *reinterpret_cast<uint4*>(xl + i0) = make_uint4(l[0], l[1], l[2], l[3]);
-  s = group_sum<4>(s);
-  if ((threadIdx.x & 3) == 0) xg[i0 / 32] = s;
-}
-
 // Two operands (the second optional) with their partials, all reads in
 // flight together (the first 4 partials of each unconditionally, as above)
 __device__ __forceinline__ void ld8_parts2(const float* p0, const float* p1, bool two, int n,
@@ -804,12 +787,33 @@ GemmPlan gemm_plan(int quant, int N, int K, bool partial_ok) {
   return p;
 }
 
+// No K slices (the epilogue needs whole sums), for every row count, so a
+// row's result still does not depend on its pass.  Narrow column tiles and
+// few rows per block keep the block count up (measured at K = 1536: bf16 one
+// tile of 16 columns per wave and at most 32 rows per block; W4A16 16 rows
+// per block, one tile for up to 16 rows and two from 17, whose weights re-read
+// by the row blocks come from L2).  Tiles and rows per block do not change
+// the arithmetic of an output.
+GemmPlan gemm_plan_geglu(int quant, int I, int K, int rows) {
+  GemmPlan p;
+  p.nks = 1;
+  p.nt = quant && rows > 16 ? 2 : 1;
+  p.mt = quant ? 1 : 2;
+  // (whole blocks for every tile width the row count may pick: the fold is
+  // taken or not for all passes alike)
+  if (I % (quant ? 64 : 32) || K % 128) p.nt = 0;
+  return p;
+}
+
 hipError_t launch_gemm(int quant, int tag, const Lin& W, int rows, const GemmA& A,
                        const GemmPlan& plan, const Epilogue& epi, int* nblk, hipStream_t st) {
   const int nks = plan.nks;
   if (rows < 1 || nks < 1 || nks > kMaxGemmSplit || W.K % nks || (W.K / nks) % 32)
     return hipErrorInvalidValue;
   if (epi.argmax && nks != 1) return hipErrorInvalidValue;
+  if (epi.gh && (tag != kTagGateUp || epi.argmax || nks != 1 || plan.nt < 1 || !epi.gl || !epi.gg ||
+                 epi.gi < 1 || W.N != 2 * epi.gi || epi.gi % (32 * plan.nt)))
+    return hipErrorInvalidValue;
   if (quant && W.tq && (!W.ts || (W.K / nks) % 128)) return hipErrorInvalidValue;
   if (A.a ? A.kind != kPlain || A.na != 1 || A.lda % 8
           : (!A.xh || !A.xl || (quant && !A.xg)))
