@@ -812,6 +812,7 @@ hipError_t launch_gemm(int quant, int tag, const Lin& W, int rows, const GemmA& 
     return hipErrorInvalidValue;
   if (epi.argmax && nks != 1) return hipErrorInvalidValue;
   if (epi.gh && (tag != kTagGateUp || epi.argmax || nks != 1 || plan.nt < 1 || !epi.gl || !epi.gg ||
+                 (quant && !W.tq) ||  // (the untiled W4A16 kernel has no GeGLU epilogue)
                  epi.gi < 1 || W.N != 2 * epi.gi || epi.gi % (32 * plan.nt)))
     return hipErrorInvalidValue;
   if (quant && W.tq && (!W.ts || (W.K / nks) % 128)) return hipErrorInvalidValue;
