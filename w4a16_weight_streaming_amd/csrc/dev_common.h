@@ -577,6 +577,47 @@ __device__ __forceinline__ void head_raw(const float* raw, int nparts, size_t ps
   }
 }
 
+// head_raw for NH heads at once: where the partials number at most MP
+// (registers: NH * MP * HD / 64 floats), every read of every head is issued
+// before the first sum (one memory round trip instead of one or more per
+// head); the sums run in the same order.
+template <int HD, int NH, int MP>
+__device__ __forceinline__ void heads_raw(const float* const (&raw)[NH], int nparts, size_t pstride,
+                                          int lane, float (&y)[NH][HD / 64]) {
+  constexpr int DPL = HD / 64;
+  if (nparts == 1) {  // (a product not split along K: one read per value)
+#pragma unroll
+    for (int h = 0; h < NH; ++h)
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) y[h][i] = ld32(raw[h] + lane * DPL + i);
+    return;
+  }
+  if (nparts > MP) {
+#pragma unroll
+    for (int h = 0; h < NH; ++h) head_raw<HD>(raw[h], nparts, pstride, lane, y[h]);
+    return;
+  }
+  float v[NH][MP][DPL];
+#pragma unroll
+  for (int h = 0; h < NH; ++h)
+#pragma unroll
+    for (int k = 0; k < MP; ++k) {
+      const float* src = k < nparts ? raw[h] + (size_t)k * pstride : zero_f();
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) v[h][k][i] = ld32(src + lane * DPL + i);
+    }
+#pragma unroll
+  for (int h = 0; h < NH; ++h) {
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) y[h][i] = v[h][0][i];
+#pragma unroll
+    for (int k = 1; k < MP; ++k)
+      if (k < nparts)
+#pragma unroll
+        for (int i = 0; i < DPL; ++i) y[h][i] += v[h][k][i];
+  }
+}
+
 template <int HD>
 struct HeadSide {
   static constexpr int DPL = HD / 64;
@@ -823,12 +864,27 @@ __device__ void attn_chunk(const Rows& R, const AttnArgs& a, int c, int r) {
     HeadSide<HD> sq, sk;
     head_side<HD>(a.gq, cs, sn, lane, sq);
     head_side<HD>(own_kv && wave == 0 ? a.gk : nullptr, cs, sn, lane, sk);
-    float yq[HW][DPL], yk[DPL];
+    float yq[HW][DPL], yk[DPL];  // this wave's query heads, its own K or V row
+    if constexpr (HD >= 512 && KQ) {  // (too few registers left for all reads at once)
 #pragma unroll
-    for (int x = 0; x < HW; ++x)
-      head_raw<HD>(raw + (wave + 4 * x < nq ? wave + 4 * x : 0) * HD, a.qkv_parts, a.qkv_pstride,
-                        lane, yq[x]);
-    head_raw<HD>(raw + (own_kv ? nq + wave : 0) * HD, a.qkv_parts, a.qkv_pstride, lane, yk);
+      for (int x = 0; x < HW; ++x)
+        head_raw<HD>(raw + (wave + 4 * x < nq ? wave + 4 * x : 0) * HD, a.qkv_parts, a.qkv_pstride,
+                     lane, yq[x]);
+      head_raw<HD>(raw + (own_kv ? nq + wave : 0) * HD, a.qkv_parts, a.qkv_pstride, lane, yk);
+    } else {
+      const float* srcs[HW + 1];
+#pragma unroll
+      for (int x = 0; x < HW; ++x) srcs[x] = raw + (wave + 4 * x < nq ? wave + 4 * x : 0) * HD;
+      srcs[HW] = raw + (own_kv ? nq + wave : 0) * HD;
+      float yy[HW + 1][DPL];
+      heads_raw<HD, HW + 1, HD >= 512 ? 4 : 8>(srcs, a.qkv_parts, a.qkv_pstride, lane, yy);
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) {
+#pragma unroll
+        for (int x = 0; x < HW; ++x) yq[x][i] = yy[x][i];
+        yk[i] = yy[HW][i];
+      }
+    }
 #pragma unroll
     for (int x = 0; x < HW; ++x) {
       const int h = wave + 4 * x;
