@@ -12,7 +12,14 @@ or, for any other counters (one or more `--pmc` runs):
     python -m w4a16_weight_streaming_amd.pmc --counters PATTERN DIR [DIR ...]
 
 which prints, as a markdown table, the mean per-dispatch value of every
-counter found under the DIRs for each kernel whose name contains PATTERN.
+counter found under the DIRs for each kernel whose name contains PATTERN;
+or, for a `--kernel-trace` run of the decode loop,
+
+    python -m w4a16_weight_streaming_amd.pmc --steps N DIR
+
+which splits the trace into decode steps (each ends with the argmax's final
+kernel) and tabulates the last N: kernels per step, their summed durations
+and the step's span on the GPU clock, and each kernel's share.
 
 Both FETCH_SIZE and WRITE_SIZE are reported in KiB per dispatch.  Each is scaled by what it
 reads for the reference copy (1 GiB read, 1 GiB written), so the factors
@@ -120,8 +127,44 @@ def counters_table(pattern, dirs):
     return "\n".join(lines)
 
 
+def step_chain(trace_dir, last):
+    """Markdown summary of the last `last` decode steps of a kernel trace: a
+    step is the run of dispatches that ends with `k_argmax_final`."""
+    rows = []
+    for fn in glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True):
+        with open(fn, newline="") as f:
+            for r in csv.DictReader(f):
+                rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"].strip()))
+    rows.sort()
+    ends = [i for i, r in enumerate(rows) if "k_argmax_final" in r[2]]
+    steps = [rows[a + 1:b + 1] for a, b in zip(ends[:-1], ends[1:])][-last:]
+    if not steps:
+        raise SystemExit("no decode steps in the trace")
+    med = lambda xs: sorted(xs)[len(xs) // 2]
+    n = [len(s) for s in steps]
+    busy = [sum(e - b for b, e, _ in s) / 1e3 for s in steps]
+    span = [(s[-1][1] - s[0][0]) / 1e3 for s in steps]
+    per = defaultdict(list)
+    for s in steps:
+        for b, e, k in s:
+            per[short(k)].append((e - b) / 1e3)
+    lines = [f"{len(steps)} steps: median {med(n)} kernels per step (min {min(n)}, max {max(n)}); "
+             f"summed kernel time {med(busy):.1f} us, span from the first kernel's start to the last "
+             f"kernel's end {med(span):.1f} us (median), so {med(span) - med(busy):.1f} us "
+             f"({(med(span) - med(busy)) / max(med(n) - 1, 1):.2f} us per boundary) lie between kernels.",
+             "", "| kernel | per step | mean us | us per step | share of kernel time |",
+             "|---|---:|---:|---:|---:|"]
+    tot = sum(sum(v) for v in per.values())
+    for k, v in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"| `{k}` | {len(v) / len(steps):.1f} | {sum(v) / len(v):.2f} | "
+                     f"{sum(v) / len(steps):.1f} | {100 * sum(v) / tot:.1f}% |")
+    return "\n".join(lines)
+
+
 if __name__ == "__main__":
-    if len(sys.argv) >= 4 and sys.argv[1] == "--counters":
+    if len(sys.argv) == 4 and sys.argv[1] == "--steps":
+        print(step_chain(sys.argv[3], int(sys.argv[2])))
+    elif len(sys.argv) >= 4 and sys.argv[1] == "--counters":
         print(counters_table(sys.argv[2], sys.argv[3:]))
     elif len(sys.argv) == 4:
         main(*sys.argv[1:])
