@@ -185,12 +185,17 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv(Lin W, int rows, Prologue
   float* xs = smem;                                              // KS floats
   uint32_t* xp = reinterpret_cast<uint32_t*>(smem + KS);         // packed pairs
   float* red = smem + KS + Packed<WQ, KS>::words;                // reduction scratch
-  const int ks = blockIdx.y, b = blockIdx.z;
+  // (the per-layer input gate of a batched pass: blockIdx.x is the row, so a
+  // row's blocks run on one XCD and its partial inputs are fetched into that
+  // L2 once instead of once per block)
+  constexpr bool kRowMajor = TAG == kTagPleGateRows;
+  const int ks = blockIdx.y, b = kRowMajor ? blockIdx.x : blockIdx.z;
+  const int bxi = kRowMajor ? blockIdx.z : blockIdx.x, gxn = kRowMajor ? gridDim.z : gridDim.x;
   const int K = W.K, N = W.N;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int ls = lane % Y::S, rsub = lane / Y::S;
   const int NU = (N + Y::RPL - 1) / Y::RPL;
-  const int stride = gridDim.x * 4;
+  const int stride = gxn * 4;
   const size_t ldq = (size_t)K / 8, lds = (size_t)K / 32;
 
   // A batch is U units (RPL rows each) of this wave; batches are double
@@ -228,13 +233,13 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv(Lin W, int rows, Prologue
   // every wave's input reads enter the memory pipeline before the block's
   // weight reads (otherwise they queue behind the other waves' weights)
   __syncthreads();
-  int u0 = blockIdx.x * 4 + wave;
+  int u0 = bxi * 4 + wave;
   Batch A, Bq;
   load_batch(A, u0);                  // then the weights (independent of x)
   // (no arithmetic on the inputs may move above the weight loads: it would
   // wait for the inputs before the weights are requested)
   __builtin_amdgcn_sched_barrier(0);
-  pr.finish(pro, b, K, xs, red, blockIdx.x == 0 && blockIdx.y == 0);
+  pr.finish(pro, b, K, xs, red, bxi == 0 && blockIdx.y == 0);
   pack_x<WQ, KS>(xs, xp);
 
   // this lane's x pairs (and group sums for W4A16), read once
@@ -345,8 +350,8 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv(Lin W, int rows, Prologue
           bv = red[w];
           bi = redi[w];
         }
-      epi.cand_val[(size_t)b * gridDim.x + blockIdx.x] = bv;
-      epi.cand_idx[(size_t)b * gridDim.x + blockIdx.x] = bi;
+      epi.cand_val[(size_t)b * gxn + bxi] = bv;
+      epi.cand_idx[(size_t)b * gxn + bxi] = bi;
     }
   }
 }
@@ -387,8 +392,8 @@ static hipError_t run_gemv(const Lin& W, int rows, const Prologue& pro, const Ep
   if (bx < 1) bx = 1;
   if (blocks_out) *blocks_out = bx;
   const size_t shm = ((size_t)KS + Packed<WQ, KS>::words + 32) * sizeof(float);
-  E2B_TIMED_LAUNCH((k_gemv<WQ, KS, U, TAG>), dim3(bx, nks, rows), dim3(kGemvThreads), shm, st, W,
-                   rows, pro, epi);
+  const dim3 grid = TAG == kTagPleGateRows ? dim3(rows, nks, bx) : dim3(bx, nks, rows);
+  E2B_TIMED_LAUNCH((k_gemv<WQ, KS, U, TAG>), grid, dim3(kGemvThreads), shm, st, W, rows, pro, epi);
   return hipGetLastError();
 }
 
