@@ -80,7 +80,9 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill(Rows R, AttnArgs a) {
 
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6, col = lane & 15, grp = lane >> 4;
   const int nq = a.nq, RW = 16 / nq;
-  const int r0 = blockIdx.y * RW, c = blockIdx.x;
+  // (grid: query tiles x chunks, a tile's chunks dispatched a row of tiles
+  // apart)
+  const int r0 = blockIdx.x * RW, c = blockIdx.y;
   const int rlast = min(r0 + RW, R.n) - 1;
   const int seq = row_seq(R, r0);  // every row of a prefill pass is one sequence
   // keys of this chunk: the group's span (the window start of its earliest
@@ -323,7 +325,7 @@ hipError_t launch_attn_prefill(const Rows& R, const AttnArgs& a, hipStream_t st)
     return hipErrorInvalidValue;
   if (a.kvq && (!a.ks || !a.vs)) return hipErrorInvalidValue;
   const int rw = 16 / a.nq;
-  dim3 grid(a.nchunk, (R.n + rw - 1) / rw);
+  dim3 grid((R.n + rw - 1) / rw, a.nchunk);
   if (a.hd == 256) {
     if (a.kvq) E2B_TIMED_LAUNCH((k_attn_prefill<256, 1>), grid, dim3(256), 0, st, R, a);
     else E2B_TIMED_LAUNCH((k_attn_prefill<256, 0>), grid, dim3(256), 0, st, R, a);

@@ -463,9 +463,12 @@ hipError_t launch_gemv(int quant, int tag, const Lin& W, int rows, const Prologu
 // K/V is written before attention: block per row, wave 0 the key (norm with
 // gain + RoPE), wave 1 the value (norm), bf16 at slot = position.
 // ------------------------------------------------------------ decode attention
+// (grid: rows x chunks, so a row's chunks are dispatched R.n apart and, for
+// R.n a multiple of 8, run on one XCD: the row's query partials are fetched
+// into one L2, where the merge of its chunk partials finds them)
 template <int HD, int KQ>
 __global__ __launch_bounds__(256) void k_attn_dec(Rows R, AttnArgs a) {
-  attn_chunk<HD, KQ>(R, a, blockIdx.x, blockIdx.y);
+  attn_chunk<HD, KQ>(R, a, blockIdx.y, blockIdx.x);
 }
 
 __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a) {
@@ -518,7 +521,7 @@ hipError_t launch_qkv_post(const Rows& R, const QkvPostArgs& a, hipStream_t st) 
 
 template <int KQ>
 static hipError_t attn_q(const Rows& R, const AttnArgs& a, hipStream_t st) {
-  dim3 grid(a.nchunk, R.n);
+  dim3 grid(R.n, a.nchunk);
   switch (a.hd) {
     case 64: E2B_TIMED_LAUNCH((k_attn_dec<64, KQ>), grid, dim3(256), 0, st, R, a); break;
     case 128: E2B_TIMED_LAUNCH((k_attn_dec<128, KQ>), grid, dim3(256), 0, st, R, a); break;
