@@ -65,7 +65,7 @@ def test_kernel_patterns():
     assert re.fullmatch(pat[("gate_up", "bf16", 1)], "void e2b::k_gemv<0, 1536, 4, 3>")
     assert re.fullmatch(pat[("gate_up", "w4a16", 1)], "void e2b::k_gemv<1, 1536, 3, 3>")
     # the batched gate/up carries the GeGLU epilogue: bf16 <= 2 m-tiles, W4A16 1
-    assert re.fullmatch(pat[("gate_up", "bf16", 64)], "void e2b::k_gemm<0, 1, 2, 0, 3, 1>")
+    assert re.fullmatch(pat[("gate_up", "bf16", 64)], "void e2b::k_gemm<0, 2, 2, 0, 3, 1>")
     assert re.fullmatch(pat[("gate_up", "w4a16", 64)], "void e2b::k_gemm<1, 2, 1, 0, 3, 1>")
     assert re.fullmatch(pat[("down", "bf16", 64)], "void e2b::k_gemm<0, 2, 4, 0, 4, 1>")
     assert re.fullmatch(pat[("down", "w4a16", 8)], "void e2b::k_gemm<1, 2, 1, 0, 4, 1>")

@@ -797,19 +797,19 @@ GemmPlan gemm_plan(int quant, int N, int K, bool partial_ok) {
 
 // No K slices (the epilogue needs whole sums), for every row count, so a
 // row's result still does not depend on its pass.  Narrow column tiles and
-// few rows per block keep the block count up (measured at K = 1536: bf16 one
-// tile of 16 columns per wave and at most 32 rows per block; W4A16 16 rows
-// per block, one tile for up to 16 rows and two from 17, whose weights re-read
-// by the row blocks come from L2).  Tiles and rows per block do not change
-// the arithmetic of an output.
+// few rows per block keep the block count up (measured at K = 1536: bf16 at
+// most 32 rows per block, one tile of 16 columns per wave up to 32 rows and
+// two beyond; W4A16 16 rows per block, one tile up to 16 rows and two from
+// 17, whose weights re-read by the row blocks come from L2).  Tiles and rows
+// per block do not change the arithmetic of an output.
 GemmPlan gemm_plan_geglu(int quant, int I, int K, int rows) {
   GemmPlan p;
   p.nks = 1;
-  p.nt = quant && rows > 16 ? 2 : 1;
+  p.nt = rows > (quant ? 16 : 32) ? 2 : 1;
   p.mt = quant ? 1 : 2;
   // (whole blocks for every tile width the row count may pick: the fold is
   // taken or not for all passes alike)
-  if (I % (quant ? 64 : 32) || K % 128) p.nt = 0;
+  if (I % 64 || K % 128) p.nt = 0;
   return p;
 }
 
