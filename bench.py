@@ -546,7 +546,7 @@ def main():
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the library has no multi-GPU path "
-              "(sequences shard across GPUs with no per-step exchange; see the design notes).",
+              "(sequences shard across GPUs with no per-step exchange).",
               file=sys.stderr)
         sys.exit(2)
 
