@@ -31,7 +31,8 @@
  * 1/sqrt(hd), rotate-half RoPE, sandwich norms, v-norm without gain, layer
  * scalar multiplying the whole residual, lowest index on argmax ties, window
  * = W keys ending at the current one, a shared layer with no same-type
- * source owning its K/V) are listed in the design notes of the repository.
+ * source owning its K/V) are readings, not statements of the pages; each is
+ * applied the same way throughout.
  */
 #include <math.h>
 #include <omp.h>
