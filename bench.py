@@ -148,8 +148,10 @@ def kernel_pattern(kind, quant, batch, embed_quant="bf16"):
     if batch == 1:
         return rf"void e2b::k_gemv<{wq}, \d+, \d+, {tag}>"
     mt = 1 if batch <= 16 else (2 if batch <= 32 else 4)
-    if kind == "gate_up":  # (with the GeGLU epilogue: at most 2 m-tiles, W4A16 1)
+    if kind == "gate_up" or (kind in ("qkv", "o") and not wq):  # (at most 2 m-tiles, W4A16 1)
         mt = min(mt, 1 if wq else 2)
+    if wq and kind in ("qkv", "o", "down"):
+        mt = 1
     return rf"void e2b::k_gemm<{wq}, \d+, {mt}, \d+, {tag}, \d+>"
 
 

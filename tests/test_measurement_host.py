@@ -69,6 +69,10 @@ def test_kernel_patterns():
     assert re.fullmatch(pat[("gate_up", "w4a16", 64)], "void e2b::k_gemm<1, 2, 1, 0, 3, 1>")
     assert re.fullmatch(pat[("down", "bf16", 64)], "void e2b::k_gemm<0, 2, 4, 0, 4, 1>")
     assert re.fullmatch(pat[("down", "w4a16", 8)], "void e2b::k_gemm<1, 2, 1, 0, 4, 1>")
+    # W4A16 q/k/v, O and down in 16-row blocks; bf16 q/k/v and O above 32 rows in 32-row blocks
+    assert re.fullmatch(pat[("down", "w4a16", 64)], "void e2b::k_gemm<1, 2, 1, 0, 4, 1>")
+    assert re.fullmatch(bench.kernel_pattern("qkv", "w4a16", 64), "void e2b::k_gemm<1, 2, 1, 0, 1, 1>")
+    assert re.fullmatch(bench.kernel_pattern("o", "bf16", 64), "void e2b::k_gemm<0, 2, 2, 0, 2, 1>")
     assert not re.fullmatch(pat[("down", "bf16", 64)], "void e2b::k_gemm<0, 2, 1, 0, 4, 1>")
     # the lm_head follows the vocabulary table's format, not the linears'
     assert re.fullmatch(bench.kernel_pattern("lm_head", "w4a16", 1), "void e2b::k_gemv<0, 1536, 4, 8>")
