@@ -142,3 +142,29 @@ def test_step_chain_table(tmp_path):
     # 1 us of it in the two gaps
     assert "25.0 us (median)" in first and "1.0 us (0.50 us per boundary)" in first
     assert "| `void e2b::k_gemv<0, 1536, 4, 3>` | 1.0 | 11.50 | 11.5 |" in out
+
+
+def test_sq_ratios_table(tmp_path):
+    """The shares of the shader-counter profile: waiting and VALU-active over
+    wave cycles, bank conflicts over LDS-active cycles, MFMA-busy over
+    busy-CU cycles; per-dispatch means first (two dispatches here)."""
+    k = "void e2b::k_gemm<0, 2, 2, 0, 3, 1>(e2b::Lin, int, e2b::GemmA, int, e2b::Epilogue)"
+    vals = {"SQ_WAVE_CYCLES": (1000.0, 3000.0), "SQ_WAIT_INST_ANY": (300.0, 500.0),
+            "SQ_ACTIVE_INST_VALU": (100.0, 300.0), "SQ_LDS_IDX_ACTIVE": (50.0, 150.0),
+            "SQ_LDS_BANK_CONFLICT": (20.0, 20.0), "SQ_BUSY_CU_CYCLES": (400.0, 400.0),
+            "SQ_VALU_MFMA_BUSY_CYCLES": (200.0, 600.0), "SQ_INSTS_VALU": (10.0, 30.0),
+            "SQ_INSTS_MFMA": (4.0, 4.0), "SQ_INSTS_LDS": (6.0, 8.0)}
+    d = tmp_path / "sq"
+    d.mkdir()
+    with open(d / "run_counter_collection.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        for name, (a, b) in vals.items():
+            w.writerow([1, k, name, a])
+            w.writerow([2, k, name, b])
+    row = pmc.ratios_table("e2b::k_", [str(d)]).splitlines()[2]
+    cells = [c.strip() for c in row.strip("|").split("|")]
+    assert cells[0] == "`void e2b::k_gemm<0, 2, 2, 0, 3, 1>`" and cells[1] == "2"
+    # means: wave 2000, wait 400, valu 200, lds-active 100, conflicts 20, busy-CU 400, MFMA 400
+    assert cells[2:6] == ["0.20", "0.10", "0.20", "1.00"]
+    assert cells[6:] == ["20", "4", "7"]

@@ -12,8 +12,11 @@ or, for any other counters (one or more `--pmc` runs):
     python -m w4a16_weight_streaming_amd.pmc --counters PATTERN DIR [DIR ...]
 
 which prints, as a markdown table, the mean per-dispatch value of every
-counter found under the DIRs for each kernel whose name contains PATTERN;
-or, for a `--kernel-trace` run of the decode loop,
+counter found under the DIRs for each kernel whose name contains PATTERN
+(`--ratios` instead of `--counters`: the shares formed from the SQ counters
+of the two passes the shader-counter profile takes: waiting, VALU-active and
+LDS bank-conflict shares and the MFMA-busy ratio); or, for a `--kernel-trace`
+run of the decode loop,
 
     python -m w4a16_weight_streaming_amd.pmc --steps N DIR
 
@@ -101,6 +104,44 @@ def main(fetch_dir, write_dir, out):
           f"for 1 GiB each; {len(res['kernels'])} kernels -> {out}")
 
 
+def counter_means(pattern, dirs):
+    """{kernel: (dispatches, {counter: mean per-dispatch value})} for the
+    kernels whose name contains `pattern`."""
+    per = defaultdict(lambda: defaultdict(lambda: defaultdict(float)))  # kernel -> counter -> dispatch
+    for d in dirs:
+        for fn in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(fn, newline="") as f:
+                for row in csv.DictReader(f):
+                    name = row["Kernel_Name"].strip()
+                    if pattern not in name:
+                        continue
+                    disp = row.get("Dispatch_Id") or row.get("Correlation_Id")
+                    per[short(name)][row["Counter_Name"].strip()][disp] += float(row["Counter_Value"])
+    return {k: (max(len(v) for v in c.values()), {n: sum(v.values()) / len(v) for n, v in c.items()})
+            for k, c in per.items()}
+
+
+def ratios_table(pattern, dirs):
+    """Markdown table of the shares the SQ counters give per kernel: cycles
+    waiting on a dependency and VALU-active cycles (of the wave cycles), LDS
+    bank-conflict cycles (of the LDS-active cycles), MFMA-busy cycles over
+    busy-CU cycles (two units: compare between kernels), and the instruction
+    counts; heaviest kernels (dispatches x wave cycles) first."""
+    m = counter_means(pattern, dirs)
+    g = lambda c, n: c.get(n, 0.0)
+    lines = ["| kernel | dispatches | wait / wave cycles | VALU active / wave cycles | LDS bank-conflict / "
+             "LDS-active cycles | MFMA-busy / busy-CU cycles | VALU insts | MFMA insts | LDS insts |",
+             "|---|---:|---:|---:|---:|---:|---:|---:|---:|"]
+    for k, (n, c) in sorted(m.items(), key=lambda kv: -kv[1][0] * g(kv[1][1], "SQ_WAVE_CYCLES")):
+        wc = g(c, "SQ_WAVE_CYCLES") or 1.0
+        lds = g(c, "SQ_LDS_IDX_ACTIVE")
+        lines.append(f"| `{k}` | {n} | {g(c, 'SQ_WAIT_INST_ANY') / wc:.2f} | {g(c, 'SQ_ACTIVE_INST_VALU') / wc:.2f} | "
+                     f"{(g(c, 'SQ_LDS_BANK_CONFLICT') / lds if lds else 0.0):.2f} | "
+                     f"{g(c, 'SQ_VALU_MFMA_BUSY_CYCLES') / (g(c, 'SQ_BUSY_CU_CYCLES') or 1.0):.2f} | "
+                     f"{g(c, 'SQ_INSTS_VALU'):.3g} | {g(c, 'SQ_INSTS_MFMA'):.3g} | {g(c, 'SQ_INSTS_LDS'):.3g} |")
+    return "\n".join(lines)
+
+
 def counters_table(pattern, dirs):
     """Markdown table: mean per-dispatch value of each counter, per kernel
     whose name contains `pattern`."""
@@ -166,6 +207,8 @@ if __name__ == "__main__":
         print(step_chain(sys.argv[3], int(sys.argv[2])))
     elif len(sys.argv) >= 4 and sys.argv[1] == "--counters":
         print(counters_table(sys.argv[2], sys.argv[3:]))
+    elif len(sys.argv) >= 4 and sys.argv[1] == "--ratios":
+        print(ratios_table(sys.argv[2], sys.argv[3:]))
     elif len(sys.argv) == 4:
         main(*sys.argv[1:])
     else:
